@@ -1,0 +1,166 @@
+"""Plain, slow, obviously-correct CPU reference (test infrastructure only).
+
+Conventions: every input arrives as raw bits (uint8 / uint16 NumPy arrays) in
+the layouts the pages give; decoding happens here from the bit fields, so no
+conversion routine of the code under test is reused.
+
+Readings of points the pages leave open:
+  * NVFP4 nibble order is taken to be the int4 card's (low nibble = even
+    column); the VoxCPM2 card only says "4-bit float".
+  * E2M1 is the OCP microscaling FP4: bit 3 sign, bits 2..1 exponent with
+    bias 1, bit 0 mantissa.
+  * float8_e4m3fn is the OCP FP8 E4M3 "fn" variant: bias 7, no infinities,
+    S.1111.111 is NaN, largest finite 448.
+  * The per-matrix global scale G multiplies: w = e2m1 * e4m3 * G, rounded to
+    fp32 once.
+  * y = x . W^T with W stored [N, K] (the nn.Linear convention the per-module
+    names imply); no bias.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP_Q4 = 128      # rumik-oss-1-int4 card, "Format": scale/min are [N, K/128]
+GROUP_NVFP4 = 16    # VoxCPM2-NVFP4 card, "What was quantized": group size 16
+
+
+def _u(a, dtype):
+    return np.ascontiguousarray(np.asarray(a)).astype(dtype, copy=False)
+
+
+# ----------------------------------------------------------------------------
+# nibble unpacking  (rumik-oss-1-int4, "Format": two 4-bit codes per byte,
+# low nibble = even column)
+# ----------------------------------------------------------------------------
+def unpack_nibbles(qweight) -> np.ndarray:
+    """uint8 [N, K/2] -> codes uint8 [N, K]: code[n, 2j] = low nibble of
+    byte [n, j], code[n, 2j+1] = high nibble."""
+    b = _u(qweight, np.uint8)
+    assert b.ndim == 2
+    n, half = b.shape
+    codes = np.empty((n, 2 * half), dtype=np.uint8)
+    codes[:, 0::2] = b & 0x0F
+    codes[:, 1::2] = b >> 4
+    return codes
+
+
+# ----------------------------------------------------------------------------
+# scalar formats, decoded from their bit fields into exact float64 values
+# ----------------------------------------------------------------------------
+def fp16_value(bits) -> np.ndarray:
+    """IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.
+    Subnormals decode exactly (no flush to zero)."""
+    b = _u(bits, np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = b & 0x3FF
+    normal = np.ldexp((f + 1024).astype(np.float64), (e - 25).astype(np.int64))
+    sub = np.ldexp(f.astype(np.float64), -24)
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def bf16_value(bits) -> np.ndarray:
+    """bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits (the upper
+    half of an IEEE binary32)."""
+    b = _u(bits, np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    f = b & 0x7F
+    normal = np.ldexp((f + 128).astype(np.float64), (e - 134).astype(np.int64))
+    sub = np.ldexp(f.astype(np.float64), -133)
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where(e == 255, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def e4m3fn_value(bits) -> np.ndarray:
+    """float8_e4m3fn: 1 sign, 4 exponent (bias 7), 3 fraction bits; exponent 0
+    is subnormal (f * 2^-9); S.1111.111 is NaN; there is no infinity."""
+    b = _u(bits, np.uint8).astype(np.int64)
+    sign = np.where((b >> 7) & 1, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    f = b & 0x7
+    normal = np.ldexp((f + 8).astype(np.float64), (e - 10).astype(np.int64))
+    sub = np.ldexp(f.astype(np.float64), -9)
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where((e == 15) & (f == 7), np.nan, mag)
+    return sign * mag
+
+
+def e2m1_value(codes) -> np.ndarray:
+    """E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa;
+    exponent 0 is subnormal (m * 0.5).  Code 8 is -0."""
+    c = _u(codes, np.uint8).astype(np.int64)
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    normal = np.ldexp((m + 2).astype(np.float64), (e - 2).astype(np.int64))
+    sub = 0.5 * m.astype(np.float64)
+    return sign * np.where(e == 0, sub, normal)
+
+
+# ----------------------------------------------------------------------------
+# dequantization to fp32
+# ----------------------------------------------------------------------------
+def q4g128_dequant_f32(qweight, scale_bits, min_bits) -> np.ndarray:
+    """rumik-oss-1-int4, "Format": w[n,k] = code[n,k]*scale[n,k//128] +
+    min[n,k//128], with scale and min fp16 [N, K/128].
+
+    The fp64 evaluation is exact for finite inputs (code*scale has at most
+    4+11 significant bits and the sum spans at most 44 bits, all multiples of
+    2^-24 below 2^20), so casting to fp32 rounds exactly once."""
+    codes = unpack_nibbles(qweight).astype(np.float64)
+    n, k = codes.shape
+    assert k % GROUP_Q4 == 0
+    s = fp16_value(scale_bits).reshape(n, k // GROUP_Q4)
+    m = fp16_value(min_bits).reshape(n, k // GROUP_Q4)
+    w = codes * np.repeat(s, GROUP_Q4, axis=1) + np.repeat(m, GROUP_Q4, axis=1)
+    return w.astype(np.float32)
+
+
+def nvfp4g16_dequant_f32(qweight, scale_bits, global_scale) -> np.ndarray:
+    """VoxCPM2-NVFP4, "What was quantized": w[n,k] = e2m1(code[n,k]) *
+    e4m3(scale[n,k//16]) * G with G the per-matrix fp32 global scale.
+
+    e2m1*e4m3 is exact (<= 2+4 significant bits); times G (24 bits) is still
+    exact in fp64, so the cast to fp32 is the single rounding."""
+    codes = unpack_nibbles(qweight)
+    n, k = codes.shape
+    assert k % GROUP_NVFP4 == 0
+    v = e2m1_value(codes)
+    s = e4m3fn_value(scale_bits).reshape(n, k // GROUP_NVFP4)
+    g = np.float64(np.float32(global_scale))
+    w = (v * np.repeat(s, GROUP_NVFP4, axis=1)) * g
+    return w.astype(np.float32)
+
+
+def bf16_dequant_f32(w_bits) -> np.ndarray:
+    """BF16 weights widened to fp32 (exact)."""
+    return bf16_value(w_bits).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# the product
+# ----------------------------------------------------------------------------
+def gemv_f64(x_bits, w32) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * w[n, k] in fp64 (x BF16 bits [M, K], w fp32
+    [N, K]).  Returns fp64 [M, N]."""
+    x = bf16_value(x_bits)
+    x = x.reshape(-1, x.shape[-1])
+    w = np.asarray(w32, dtype=np.float32).astype(np.float64)
+    assert x.shape[1] == w.shape[1]
+    return x @ w.T
+
+
+def q4g128_gemv(x_bits, qweight, scale_bits, min_bits) -> np.ndarray:
+    return gemv_f64(x_bits, q4g128_dequant_f32(qweight, scale_bits, min_bits))
+
+
+def nvfp4g16_gemv(x_bits, qweight, scale_bits, global_scale) -> np.ndarray:
+    return gemv_f64(x_bits, nvfp4g16_dequant_f32(qweight, scale_bits, global_scale))
+
+
+def bf16_gemv(x_bits, w_bits) -> np.ndarray:
+    return gemv_f64(x_bits, bf16_dequant_f32(w_bits))
