@@ -1,0 +1,269 @@
+"""Decode-step weight-stream benchmark for the 4-bit dequant-GEMV library.
+
+One step = one pass of the whole hot path over one batch: 36 int4 g128 layers
+of the hidden-2048 shapes (q, k, v, o, gate, up, down; FFN width 8192), then
+the BF16 audio-head GEMV (16385 x 2048).  Weights are seeded synthetic
+(min/max-quantized N(0, 0.02) BF16 matrices), about 1.24 GB, generated on the
+GPU and resident in HBM before timing.  The step is captured once into a HIP
+graph and replayed; `value` is total algorithmic bytes (packed weights + group
+scales + activations read + outputs written) per second at batch M = 1.  The
+same step at M = 48 is reported alongside.
+
+Also reported on the same JSON line:
+  * roofline: the int4 GEMV kernel used at M = 1, its algorithmic bytes per
+    launch over its average launch duration (HIP events around each launch
+    on the launch stream), against the 8 TB/s HBM peak;
+  * cpu_baseline: the CPU oracle (NumPy, fp64) timed on a bounded sample of
+    the same workload on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) + decode steps/s, 4-bit GEMV at M=1 and M=48"
+PEAK_GBS = 8000.0
+N_LAYERS = 36
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def q4_wbytes(N, K):
+    """weight bytes of one int4 g128 matrix: codes + fp16 scale + fp16 min."""
+    return N * K // 2 + N * (K // 128) * 4
+
+
+def q4_bytes(N, K, M):
+    """algorithmic bytes of one int4 g128 GEMV: weights + x + y."""
+    return q4_wbytes(N, K) + M * K * 2 + M * N * 2
+
+
+class Workload:
+    def __init__(self, q4, synth, torch, head_rows: int):
+        self.q4, self.torch = q4, torch
+        dev = "cuda"
+        t0 = time.time()
+        self.layers = []
+        for i in range(N_LAYERS):
+            self.layers.append({p: synth.q4_matrix(*synth.LAYER_SHAPES[p], ("step", i, p), device=dev) for p in synth.LAYER_ORDER})
+        self.head = synth.bf16_matrix(head_rows, 2048, ("step-head", head_rows), device=dev)
+        torch.cuda.synchronize()
+        log(f"bench: generated {N_LAYERS} int4 layers + {head_rows}x2048 bf16 head in {time.time() - t0:.1f}s")
+        self.shapes = synth.LAYER_SHAPES
+        self.order = synth.LAYER_ORDER
+        self.head_rows = head_rows
+        self.io = {}
+
+    def buffers(self, M):
+        if M not in self.io:
+            t = self.torch
+            import synth
+            # input of q/k/v/gate/up, stand-in attention output for o, stand-in FFN activation for down
+            xin = synth.x_bf16(M, 2048, ("bench-xin", M), device="cuda")
+            xattn = synth.x_bf16(M, 2048, ("bench-xattn", M), device="cuda")
+            xffn = synth.x_bf16(M, 8192, ("bench-xffn", M), device="cuda")
+            xs = {"q": xin, "k": xin, "v": xin, "gate": xin, "up": xin, "o": xattn, "down": xffn}
+            ys = {p: t.empty((M, self.shapes[p][0]), dtype=t.bfloat16, device="cuda") for p in self.order}
+            yh = t.empty((M, self.head_rows), dtype=t.bfloat16, device="cuda")
+            self.io[M] = (xs, ys, xin, yh)
+        return self.io[M]
+
+    def launches(self, M, mode="grouped"):
+        """[(callable, weight_bytes, is_q4)] for one step, in stream order.
+
+        plain:   one launch per projection (7 per layer) and one for the head.
+        grouped: per layer, q, k, v, gate, up (they read the same activations)
+                 in one launch and o, down (independent of each other in a
+                 parallel block) in another; then the head.
+        """
+        xs, ys, xin, yh = self.buffers(M)
+        out = []
+        q4 = self.q4
+        for lay in self.layers:
+            if mode == "plain":
+                for p in self.order:
+                    qw, sc, mn = lay[p]
+                    N, K = self.shapes[p]
+                    out.append((lambda x=xs[p], qw=qw, sc=sc, mn=mn, y=ys[p]: q4.q4g128_gemv(x, qw, sc, mn, out=y),
+                                q4_wbytes(N, K), True))
+            else:
+                for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
+                    items = [(xs[p], *lay[p], ys[p]) for p in stage]
+                    wb = sum(q4_wbytes(*self.shapes[p]) for p in stage)
+                    out.append((lambda items=items: q4.q4g128_gemv_grouped(items), wb, True))
+        out.append((lambda: q4.bf16_gemv(xin, self.head, out=yh), self.head_rows * 2048 * 2, False))
+        return out
+
+    def step_bytes(self, M):
+        """Algorithmic bytes of one step: packed weights + group scales, each
+        distinct activation vector read once (layer input, attention output,
+        FFN activation, head input), every output written once."""
+        w = sum(b for _, b, _ in self.launches(M, "plain"))
+        per_layer_x = (2048 + 2048 + 8192) * M * 2
+        per_layer_y = sum(self.shapes[p][0] for p in self.order) * M * 2
+        head_io = 2048 * M * 2 + self.head_rows * M * 2
+        return w + N_LAYERS * (per_layer_x + per_layer_y) + head_io
+
+
+def time_graph(torch, wl, M, steps, warmup, mode):
+    calls = wl.launches(M, mode)
+    for f, _, _ in calls:  # eager warm-up outside capture
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f, _, _ in calls:
+            f()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        g.replay()
+    e.record()
+    e.synchronize()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    return ms, g
+
+
+def time_q4_launches(torch, wl, M, mode, reps=3):
+    """Average duration of the int4 GEMV launches of a step, each bracketed by
+    HIP events on the stream it is launched on (eager launches).  Returns
+    (ms per launch, algorithmic bytes per launch)."""
+    xs, ys, xin, yh = wl.buffers(M)
+    calls = [c for c in wl.launches(M, mode) if c[2]]
+    act = sum(ys[p].numel() * 2 for p in wl.order) + (2048 + 2048 + 8192) * M * 2   # per layer
+    io_per_launch = act * N_LAYERS / len(calls)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+    tot_ms, tot_bytes, n = 0.0, 0, 0
+    for _ in range(reps):
+        for (f, b, _), (a, z) in zip(calls, evs):
+            a.record(stream)
+            f()
+            z.record(stream)
+        torch.cuda.synchronize()
+        for (f, b, _), (a, z) in zip(calls, evs):
+            tot_ms += a.elapsed_time(z)
+            tot_bytes += b + io_per_launch
+            n += 1
+    return tot_ms / n, tot_bytes / n
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The oracle (plain NumPy, fp64 product) on whole layers of the step's
+    weights, M = 1, until about budget_s seconds of CPU work."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = {K: synth.bits16(synth.x_bf16(1, K, ("cpu-x", K))) for K in (2048, 8192)}
+    done_bytes, t_used, layers = 0, 0.0, 0
+    for lay in wl.layers:
+        host = {p: (t[0].cpu().numpy(), synth.bits16(t[1]), synth.bits16(t[2])) for p, t in lay.items()}
+        t0 = time.perf_counter()
+        for p in wl.order:
+            N, K = wl.shapes[p]
+            oracle.q4g128_gemv(x[K], *host[p])
+            done_bytes += q4_bytes(N, K, 1)
+        t_used += time.perf_counter() - t0
+        layers += 1
+        if t_used >= budget_s:
+            break
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{layers} of {N_LAYERS} int4 layers (7 GEMVs each, M=1), NumPy dequant to fp32 + fp64 matmul, "
+                      f"{t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--head", choices=("full", "slice"), default="full")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_weight_only_q4g128_amd as q4
+    import synth
+
+    assert torch.cuda.is_available(), "no GPU"
+    torch.cuda.set_device(0)
+    head_rows = synth.HEAD_FULL[0] if args.head == "full" else synth.HEAD_SLICE[0]
+    wl = Workload(q4, synth, torch, head_rows)
+
+    res = {}
+    for M in (1, 48):
+        for mode in ("grouped", "plain"):
+            ms, g = time_graph(torch, wl, M, args.steps, args.warmup, mode)
+            by = wl.step_bytes(M)
+            res[(M, mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(wl.launches(M, mode)))
+            log(f"bench: M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(M, mode)]['gbs']:6.0f} GB/s, "
+                f"{1e3 / ms:6.0f} steps/s, {res[(M, mode)]['launches']} launches")
+            del g
+    kms, kbytes = time_q4_launches(torch, wl, 1, "grouped")
+    kname = f"gemv_dot2_kernel<FmtQ4, MT=1, CPL=1> ({q4.variant_name(q4.FMT_Q4G128, 0, 1, 2048, 2048)}), grouped launches"
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    log(f"bench: int4 GEMV launches at M=1: avg {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
+    head = res[(1, "grouped")]
+
+    out = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode step: {N_LAYERS} int4 g128 layers (hidden 2048, ffn 8192) + bf16 head {head_rows}x2048, M=1, "
+                        f"grouped launches (q,k,v,gate,up | o,down | head), hipGraph replay",
+            "M": 1,
+            "bytes_per_step": head["bytes"],
+            "steps_per_s": round(1e3 / head["ms"], 1),
+            "pct_of_8TBps": round(100 * head["gbs"] / PEAK_GBS, 2),
+            "launches_per_step": head["launches"],
+            "modes": {f"M{M}_{mode}": {"ms_per_step": round(r["ms"], 5), "GB_s": round(r["gbs"], 1),
+                                        "pct_of_8TBps": round(100 * r["gbs"] / PEAK_GBS, 2),
+                                        "steps_per_s": round(1e3 / r["ms"], 1), "tokens_per_s": round(M * 1e3 / r["ms"], 1),
+                                        "launches_per_step": r["launches"], "bytes_per_step": r["bytes"]}
+                      for (M, mode), r in res.items()},
+        },
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+"""Python binding of libq4gemv.so (4-bit weight-only dequant-GEMV for gfx950).
+
+Argument marshalling only: every step runs in the HIP library.  Tensors must
+be CUDA (ROCm) tensors, contiguous, with the dtypes the C header documents;
+calls are enqueued on torch's current stream of the tensors' device.  There is
+no CPU fallback: importing fails loudly if the library has not been built
+(``python -m bit_weight_only_q4g128_amd._build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
+    "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib",
+    "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4gemv.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with: python -m bit_weight_only_q4g128_amd._build")
+lib = ctypes.CDLL(LIB_PATH)
+
+VARIANT_AUTO, VARIANT_DOT2, VARIANT_MFMA = 0, 1, 2
+FMT_Q4G128, FMT_NVFP4G16, FMT_BF16 = 0, 1, 2
+
+_p, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+lib.q4g128_gemv_variant.argtypes = [_p, _i, _i, _p, _p, _p, _i, _p, _i, _p]
+lib.nvfp4g16_gemv_variant.argtypes = [_p, _i, _i, _p, _p, _f, _i, _p, _i, _p]
+lib.bf16_gemv_variant.argtypes = [_p, _i, _i, _p, _i, _p, _i, _p]
+lib.q4g128_gemv.argtypes = [_p, _i, _i, _p, _p, _p, _i, _p, _p]
+lib.nvfp4g16_gemv.argtypes = [_p, _i, _i, _p, _p, _f, _i, _p, _p]
+lib.bf16_gemv.argtypes = [_p, _i, _i, _p, _i, _p, _p]
+lib.q4g128_dequant_f32.argtypes = [_p, _p, _p, _i, _i, _p, _p]
+lib.nvfp4g16_dequant_f32.argtypes = [_p, _p, _f, _i, _i, _p, _p]
+for _fn in ("q4g128_gemv_variant", "nvfp4g16_gemv_variant", "bf16_gemv_variant", "q4g128_gemv", "nvfp4g16_gemv",
+            "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32"):
+    getattr(lib, _fn).restype = ctypes.c_int
+lib.q4gemv_variant_name.argtypes = [_i, _i, _i, _i, _i]
+lib.q4gemv_variant_name.restype = ctypes.c_char_p
+lib.q4gemv_strerror.argtypes = [_i]
+lib.q4gemv_strerror.restype = ctypes.c_char_p
+lib.q4gemv_version.argtypes = []
+lib.q4gemv_version.restype = ctypes.c_int
+
+
+class Q4Task(ctypes.Structure):
+    """Mirror of the C struct q4g128_task."""
+    _fields_ = [("x", _p), ("qweight", _p), ("scale", _p), ("minv", _p), ("y", _p), ("N", _i), ("K", _i)]
+
+
+lib.q4g128_gemv_grouped.argtypes = [ctypes.POINTER(Q4Task), _i, _i, _i, _p]
+lib.q4g128_gemv_grouped.restype = ctypes.c_int
+
+
+class Q4GemvError(ValueError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"q4gemv status {status}: {strerror(status)}")
+
+
+def strerror(status: int) -> str:
+    return lib.q4gemv_strerror(int(status)).decode()
+
+
+def variant_name(fmt: int, variant: int, M: int, N: int, K: int) -> str:
+    return lib.q4gemv_variant_name(fmt, variant, M, N, K).decode()
+
+
+def _check(t: torch.Tensor, name: str, dtypes, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _out(out, shape, dtype, like):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _check(out, "out", (dtype,), len(shape))
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    return out
+
+
+def _raise(rc: int):
+    if rc != 0:
+        raise Q4GemvError(rc)
+
+
+_U16 = (torch.bfloat16, torch.int16)
+_F16 = (torch.float16, torch.int16)
+_U8 = (torch.uint8,)
+_E4M3 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def q4g128_gemv(x, qweight, scale, minv, out=None, variant: int = VARIANT_AUTO):
+    """y[M, N] = x[M, K] . W^T, W int4 g128 min/max (qweight uint8 [N, K/2],
+    scale/min fp16 [N, K/128])."""
+    _check(x, "x", _U16, 2); _check(qweight, "qweight", _U8, 2)
+    _check(scale, "scale", _F16, 2); _check(minv, "min", _F16, 2)
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 2 != K or tuple(scale.shape) != (N, K // 128) or tuple(minv.shape) != (N, K // 128):
+        raise ValueError("inconsistent shapes")
+    y = _out(out, (M, N), torch.bfloat16, x)
+    _raise(lib.q4g128_gemv_variant(x.data_ptr(), M, K, qweight.data_ptr(), scale.data_ptr(), minv.data_ptr(), N,
+                                   y.data_ptr(), int(variant), _stream(x)))
+    return y
+
+
+def q4g128_gemv_grouped(items, variant: int = VARIANT_AUTO):
+    """Several independent int4 g128 GEMVs with one batch size, launched
+    together.  items: sequence of (x, qweight, scale, min, out-or-None).
+    Returns the list of outputs."""
+    items = list(items)
+    if not 1 <= len(items) <= 8:
+        raise ValueError("1..8 tasks per call")
+    arr = (Q4Task * len(items))()
+    outs = []
+    M = None
+    for i, (x, qweight, scale, minv, out) in enumerate(items):
+        _check(x, "x", _U16, 2); _check(qweight, "qweight", _U8, 2)
+        _check(scale, "scale", _F16, 2); _check(minv, "min", _F16, 2)
+        m, K = x.shape
+        N = qweight.shape[0]
+        if M is None:
+            M = m
+        if m != M:
+            raise ValueError("all tasks must share the batch size M")
+        if qweight.shape[1] * 2 != K or tuple(scale.shape) != (N, K // 128) or tuple(minv.shape) != (N, K // 128):
+            raise ValueError(f"task {i}: inconsistent shapes")
+        y = _out(out, (M, N), torch.bfloat16, x)
+        outs.append(y)
+        arr[i] = Q4Task(x.data_ptr(), qweight.data_ptr(), scale.data_ptr(), minv.data_ptr(), y.data_ptr(), N, K)
+    _raise(lib.q4g128_gemv_grouped(arr, len(items), M, int(variant), _stream(items[0][0])))
+    return outs
+
+
+def nvfp4g16_gemv(x, qweight, scale_e4m3, global_scale: float, out=None, variant: int = VARIANT_AUTO):
+    """y[M, N] = x . W^T, W NVFP4 (qweight uint8 [N, K/2] E2M1, scale_e4m3
+    [N, K/16], global_scale fp32 multiplier)."""
+    _check(x, "x", _U16, 2); _check(qweight, "qweight", _U8, 2); _check(scale_e4m3, "scale_e4m3", _E4M3, 2)
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 2 != K or tuple(scale_e4m3.shape) != (N, K // 16):
+        raise ValueError("inconsistent shapes")
+    y = _out(out, (M, N), torch.bfloat16, x)
+    _raise(lib.nvfp4g16_gemv_variant(x.data_ptr(), M, K, qweight.data_ptr(), scale_e4m3.data_ptr(), float(global_scale), N,
+                                     y.data_ptr(), int(variant), _stream(x)))
+    return y
+
+
+def bf16_gemv(x, w, out=None, variant: int = VARIANT_AUTO):
+    """y[M, N] = x . W^T with W bf16 [N, K]."""
+    _check(x, "x", _U16, 2); _check(w, "w", _U16, 2)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("inconsistent shapes")
+    y = _out(out, (M, N), torch.bfloat16, x)
+    _raise(lib.bf16_gemv_variant(x.data_ptr(), M, K, w.data_ptr(), N, y.data_ptr(), int(variant), _stream(x)))
+    return y
+
+
+def q4g128_dequant_f32(qweight, scale, minv, out=None):
+    _check(qweight, "qweight", _U8, 2); _check(scale, "scale", _F16, 2); _check(minv, "min", _F16, 2)
+    N, half = qweight.shape
+    K = 2 * half
+    w = _out(out, (N, K), torch.float32, qweight)
+    _raise(lib.q4g128_dequant_f32(qweight.data_ptr(), scale.data_ptr(), minv.data_ptr(), N, K, w.data_ptr(), _stream(qweight)))
+    return w
+
+
+def nvfp4g16_dequant_f32(qweight, scale_e4m3, global_scale: float, out=None):
+    _check(qweight, "qweight", _U8, 2); _check(scale_e4m3, "scale_e4m3", _E4M3, 2)
+    N, half = qweight.shape
+    K = 2 * half
+    w = _out(out, (N, K), torch.float32, qweight)
+    _raise(lib.nvfp4g16_dequant_f32(qweight.data_ptr(), scale_e4m3.data_ptr(), float(global_scale), N, K, w.data_ptr(),
+                                    _stream(qweight)))
+    return w

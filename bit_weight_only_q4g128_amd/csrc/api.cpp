@@ -1,0 +1,220 @@
+// C ABI of libq4gemv.so: host-side argument checks and kernel selection.
+// Declarations and the contract live in include/q4gemv.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/q4gemv.h"
+#include "internal.h"
+
+using q4::Fmt;
+using q4::GemvArgs;
+
+namespace {
+
+constexpr int kMaxM = 64;
+constexpr long kMaxK = 32768;
+constexpr long kMaxN = 1L << 24;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int check_common(const void* x, int M, int K, int N, const void* y) {
+    if (!x || !y) return Q4_EINVAL_PTR;
+    if (M < 1 || M > kMaxM || N < 1 || N > kMaxN || K < 1 || K > kMaxK) return Q4_EINVAL_SHAPE;
+    if (!aligned(x, 16) || !aligned(y, 2)) return Q4_EALIGN;
+    return Q4_OK;
+}
+
+bool variant_ok(int variant) { return variant == Q4_VARIANT_AUTO || variant == Q4_VARIANT_DOT2 || variant == Q4_VARIANT_MFMA; }
+
+// Kernel choice for Q4_VARIANT_AUTO.  Small batches stream through the
+// packed-dot kernel; larger ones go to the matrix cores.
+int pick(Fmt fmt, int variant, int M, int K) {
+    if (variant == Q4_VARIANT_DOT2) return q4::dot2_supported(fmt, K) ? Q4_VARIANT_DOT2 : -1;
+    if (variant == Q4_VARIANT_MFMA) return Q4_VARIANT_MFMA;
+    if (M <= 4 && q4::dot2_supported(fmt, K)) return Q4_VARIANT_DOT2;
+    return Q4_VARIANT_MFMA;
+}
+
+int run(Fmt fmt, int chosen, const GemvArgs* a, int count, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = (chosen == Q4_VARIANT_DOT2) ? q4::launch_dot2(fmt, a, count, s) : q4::launch_mfma(fmt, a, count, s);
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
+int run(Fmt fmt, int chosen, const GemvArgs& a, void* stream) { return run(fmt, chosen, &a, 1, stream); }
+
+// Validation of one int4 task; fills `a` and the input ranges.
+int check_q4(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
+             uint16_t* y, GemvArgs& a, Range in[4], Range& out) {
+    int rc = check_common(x, M, K, N, y);
+    if (rc) return rc;
+    if (!qweight || !scale || !minv) return Q4_EINVAL_PTR;
+    if (K % 128) return Q4_EINVAL_SHAPE;
+    if (!aligned(qweight, 16) || !aligned(scale, 2) || !aligned(minv, 2)) return Q4_EALIGN;
+    const size_t G = (size_t)K / 128;
+    in[0] = range_of(x, (size_t)M * K * 2);
+    in[1] = range_of(qweight, (size_t)N * K / 2);
+    in[2] = range_of(scale, (size_t)N * G * 2);
+    in[3] = range_of(minv, (size_t)N * G * 2);
+    out = range_of(y, (size_t)M * N * 2);
+    a = GemvArgs{};
+    a.x = x; a.w = qweight; a.scale = scale; a.minv = minv; a.y = y; a.M = M; a.N = N; a.K = K;
+    return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4g128_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv,
+                        int N, uint16_t* y, int variant, void* stream) {
+    GemvArgs a;
+    Range in[4], out;
+    int rc = check_q4(x, M, K, qweight, scale, minv, N, y, a, in, out);
+    if (rc) return rc;
+    if (!variant_ok(variant)) return Q4_EVARIANT;
+    for (const Range& r : in)
+        if (overlaps(out, r)) return Q4_EALIAS;
+    const int chosen = pick(q4::kFmtQ4, variant, M, K);
+    if (chosen < 0) return Q4_EVARIANT;
+    return run(q4::kFmtQ4, chosen, a, stream);
+}
+
+int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant, void* stream) {
+    if (!tasks) return Q4_EINVAL_PTR;
+    if (count < 1 || count > q4::kMaxTasks) return Q4_EINVAL_SHAPE;
+    if (!variant_ok(variant)) return Q4_EVARIANT;
+    GemvArgs a[q4::kMaxTasks];
+    Range in[q4::kMaxTasks][4], out[q4::kMaxTasks];
+    int chosen = -2;
+    for (int i = 0; i < count; ++i) {
+        const q4g128_task& t = tasks[i];
+        int rc = check_q4(t.x, M, t.K, t.qweight, t.scale, t.minv, t.N, t.y, a[i], in[i], out[i]);
+        if (rc) return rc;
+        const int c = pick(q4::kFmtQ4, variant, M, t.K);
+        if (c < 0) return Q4_EVARIANT;
+        if (chosen == -2 || c == Q4_VARIANT_MFMA) chosen = c;   // one kernel family for the whole group
+    }
+    if (chosen == Q4_VARIANT_DOT2) {
+        for (int i = 0; i < count; ++i)
+            if (!q4::dot2_supported(q4::kFmtQ4, tasks[i].K)) chosen = Q4_VARIANT_MFMA;
+    }
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j) {
+            for (const Range& r : in[j])
+                if (overlaps(out[i], r)) return Q4_EALIAS;
+            if (i != j && overlaps(out[i], out[j])) return Q4_EALIAS;
+        }
+    return run(q4::kFmtQ4, chosen, a, count, stream);
+}
+
+int q4g128_gemv(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
+                uint16_t* y, void* stream) {
+    return q4g128_gemv_variant(x, M, K, qweight, scale, minv, N, y, Q4_VARIANT_AUTO, stream);
+}
+
+int nvfp4g16_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint8_t* scale_e4m3, float global_scale,
+                          int N, uint16_t* y, int variant, void* stream) {
+    int rc = check_common(x, M, K, N, y);
+    if (rc) return rc;
+    if (!qweight || !scale_e4m3) return Q4_EINVAL_PTR;
+    if (K % 32) return Q4_EINVAL_SHAPE;
+    if (!aligned(qweight, 16)) return Q4_EALIGN;
+    if (!variant_ok(variant)) return Q4_EVARIANT;
+    const Range yr = range_of(y, (size_t)M * N * 2);
+    if (overlaps(yr, range_of(x, (size_t)M * K * 2)) || overlaps(yr, range_of(qweight, (size_t)N * K / 2)) ||
+        overlaps(yr, range_of(scale_e4m3, (size_t)N * K / 16)))
+        return Q4_EALIAS;
+    const int chosen = pick(q4::kFmtNvfp4, variant, M, K);
+    if (chosen < 0) return Q4_EVARIANT;
+    GemvArgs a{};
+    a.x = x; a.w = qweight; a.scale8 = scale_e4m3; a.gscale = global_scale; a.y = y; a.M = M; a.N = N; a.K = K;
+    return run(q4::kFmtNvfp4, chosen, a, stream);
+}
+
+int nvfp4g16_gemv(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint8_t* scale_e4m3, float global_scale, int N,
+                  uint16_t* y, void* stream) {
+    return nvfp4g16_gemv_variant(x, M, K, qweight, scale_e4m3, global_scale, N, y, Q4_VARIANT_AUTO, stream);
+}
+
+int bf16_gemv_variant(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* y, int variant, void* stream) {
+    int rc = check_common(x, M, K, N, y);
+    if (rc) return rc;
+    if (!w) return Q4_EINVAL_PTR;
+    if (K % 8) return Q4_EINVAL_SHAPE;
+    if (!aligned(w, 16)) return Q4_EALIGN;
+    if (!variant_ok(variant)) return Q4_EVARIANT;
+    const Range yr = range_of(y, (size_t)M * N * 2);
+    if (overlaps(yr, range_of(x, (size_t)M * K * 2)) || overlaps(yr, range_of(w, (size_t)N * K * 2))) return Q4_EALIAS;
+    const int chosen = pick(q4::kFmtBf16, variant, M, K);
+    if (chosen < 0) return Q4_EVARIANT;
+    GemvArgs a{};
+    a.x = x; a.w = reinterpret_cast<const uint8_t*>(w); a.y = y; a.M = M; a.N = N; a.K = K;
+    return run(q4::kFmtBf16, chosen, a, stream);
+}
+
+int bf16_gemv(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* y, void* stream) {
+    return bf16_gemv_variant(x, M, K, w, N, y, Q4_VARIANT_AUTO, stream);
+}
+
+int q4g128_dequant_f32(const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N, int K, float* w, void* stream) {
+    if (!qweight || !scale || !minv || !w) return Q4_EINVAL_PTR;
+    if (N < 1 || N > kMaxN || K < 128 || K > kMaxK || K % 128) return Q4_EINVAL_SHAPE;
+    if (!aligned(qweight, 16) || !aligned(scale, 2) || !aligned(minv, 2) || !aligned(w, 16)) return Q4_EALIGN;
+    const size_t G = (size_t)K / 128;
+    const Range wr = range_of(w, (size_t)N * K * 4);
+    if (overlaps(wr, range_of(qweight, (size_t)N * K / 2)) || overlaps(wr, range_of(scale, (size_t)N * G * 2)) ||
+        overlaps(wr, range_of(minv, (size_t)N * G * 2)))
+        return Q4_EALIAS;
+    hipError_t e = q4::launch_q4_dequant(qweight, scale, minv, N, K, w, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
+int nvfp4g16_dequant_f32(const uint8_t* qweight, const uint8_t* scale_e4m3, float global_scale, int N, int K, float* w,
+                         void* stream) {
+    if (!qweight || !scale_e4m3 || !w) return Q4_EINVAL_PTR;
+    if (N < 1 || N > kMaxN || K < 32 || K > kMaxK || K % 32) return Q4_EINVAL_SHAPE;
+    if (!aligned(qweight, 16) || !aligned(w, 16)) return Q4_EALIGN;
+    const Range wr = range_of(w, (size_t)N * K * 4);
+    if (overlaps(wr, range_of(qweight, (size_t)N * K / 2)) || overlaps(wr, range_of(scale_e4m3, (size_t)N * K / 16)))
+        return Q4_EALIAS;
+    hipError_t e = q4::launch_nvfp4_dequant(qweight, scale_e4m3, global_scale, N, K, w, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
+const char* q4gemv_variant_name(int fmt, int variant, int M, int N, int K) {
+    (void)N;
+    if (fmt < Q4_FMT_Q4G128 || fmt > Q4_FMT_BF16 || !variant_ok(variant) || M < 1 || M > kMaxM || K < 1) return "invalid";
+    const int c = pick(static_cast<Fmt>(fmt), variant, M, K);
+    if (c == Q4_VARIANT_DOT2) return "dot2";
+    if (c == Q4_VARIANT_MFMA) return "mfma";
+    return "invalid";
+}
+
+const char* q4gemv_strerror(int status) {
+    switch (status) {
+        case Q4_OK: return "ok";
+        case Q4_EINVAL_PTR: return "null pointer argument";
+        case Q4_EINVAL_SHAPE: return "M, N or K out of range for this format";
+        case Q4_EALIGN: return "misaligned pointer";
+        case Q4_EALIAS: return "output overlaps an input";
+        case Q4_ELAUNCH: return "kernel launch failed";
+        case Q4_EVARIANT: return "unknown variant or variant cannot run this shape";
+        default: return "unknown status";
+    }
+}
+
+int q4gemv_version(void) { return 100; }
+
+}  // extern "C"

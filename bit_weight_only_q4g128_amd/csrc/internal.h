@@ -1,0 +1,31 @@
+// Host-side launchers shared between the C ABI (api.cpp) and the kernel
+// translation units.  Everything here assumes the arguments were validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "formats.h"
+
+namespace q4 {
+
+enum Fmt { kFmtQ4 = 0, kFmtNvfp4 = 1, kFmtBf16 = 2 };
+
+// Most GEMVs one launch can carry.
+constexpr int kMaxTasks = 8;
+
+// Packed-dot GEMV (wave-per-row-slice, DPP reduction) over `count` <= kMaxTasks
+// independent GEMVs of one format and one batch size M (any N, K each).
+// Supports any M by looping over batch tiles of at most 8 rows.  Returns
+// hipSuccess or the launch error.
+hipError_t launch_dot2(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
+bool dot2_supported(Fmt fmt, int K);
+
+// 16x16x32 BF16 matrix-core GEMV (any M <= 64), one launch per task.
+hipError_t launch_mfma(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
+
+// Diagnostic dequantization to fp32 [N, K].
+hipError_t launch_q4_dequant(const uint8_t* qw, const uint16_t* sc, const uint16_t* mn, int N, int K, float* w, hipStream_t s);
+hipError_t launch_nvfp4_dequant(const uint8_t* qw, const uint8_t* sc, float G, int N, int K, float* w, hipStream_t s);
+
+}  // namespace q4

@@ -1,0 +1,147 @@
+/*
+ * q4gemv -- 4-bit weight-only dequantize-and-multiply for AMD MI355X (gfx950).
+ *
+ * C ABI of libq4gemv.so.  Every entry point computes
+ *
+ *     y[m, n] = sum_k x[m, k] * w[n, k]        (y = x . W^T, no bias)
+ *
+ * for a decode batch x of M rows against one weight matrix W of N rows
+ * (output features) and K columns (input features), without ever writing the
+ * dequantized W to memory.  Activations x and outputs y are BF16; the sum is
+ * accumulated in fp32 and rounded to BF16 (round to nearest even) once.
+ *
+ * Types.  BF16 and fp16 values travel as uint16_t bit patterns and
+ * float8_e4m3fn values as uint8_t, so C callers need no GPU half-precision
+ * headers.  `stream` is a hipStream_t (NULL = the default stream).
+ *
+ * Memory and ownership.  All array arguments are DEVICE pointers to
+ * contiguous, row-major arrays owned by the caller.  The library allocates
+ * nothing, keeps no pointer after returning, and never synchronizes the host:
+ * a call only enqueues kernels on `stream`, so it may be recorded into a HIP
+ * graph.  Calls are thread-safe.  `y` is fully overwritten.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued; a
+ * rejected call returns a negative Q4_E* code and writes nothing.  A kernel
+ * launch failure returns Q4_ELAUNCH.  Faults inside a kernel surface at the
+ * caller's next synchronization, as with any HIP kernel.
+ *
+ * Common limits: 1 <= M <= 64, 1 <= N <= 2^24, 1 <= K <= 32768; x and the packed weights
+ * 16-byte aligned; scale arrays 2-byte aligned (fp16) or 1-byte (e4m3); y
+ * 2-byte aligned and not overlapping any input.
+ */
+#ifndef Q4GEMV_H
+#define Q4GEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define Q4_OK 0
+#define Q4_EINVAL_PTR (-1)   /* a required pointer is NULL */
+#define Q4_EINVAL_SHAPE (-2) /* M, N or K out of range for the format */
+#define Q4_EALIGN (-3)       /* a pointer is not aligned as documented */
+#define Q4_EALIAS (-4)       /* the output overlaps an input */
+#define Q4_ELAUNCH (-5)      /* the HIP runtime refused a kernel launch */
+#define Q4_EVARIANT (-6)     /* unknown variant, or the variant cannot run this shape */
+
+/* kernel variants (the *_gemv_variant entry points) */
+#define Q4_VARIANT_AUTO 0 /* pick by (M, N, K) */
+#define Q4_VARIANT_DOT2 1 /* wave-per-row packed-BF16 dot products; batch tiles of <= 8 rows */
+#define Q4_VARIANT_MFMA 2 /* 16x16x32 BF16 matrix-core tiles, batch padded to 16 */
+
+/* weight formats (q4gemv_variant_name) */
+#define Q4_FMT_Q4G128 0
+#define Q4_FMT_NVFP4G16 1
+#define Q4_FMT_BF16 2
+
+/*
+ * int4 "g128 min/max" weights.
+ * Format: rumik-oss-1-int4 model card, section "Format":
+ *   qweight  uint8 [N, K/2]   two 4-bit codes per byte, LOW nibble = EVEN column
+ *   scale    fp16  [N, K/128]
+ *   min      fp16  [N, K/128]
+ *   w[n, k] = code[n, k] * scale[n, k/128] + min[n, k/128]
+ * x: bf16 [M, K]; y: bf16 [M, N].  Requires K % 128 == 0.
+ */
+int q4g128_gemv(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
+                uint16_t* y, void* stream);
+
+/* Same as q4g128_gemv with an explicit Q4_VARIANT_* choice. */
+int q4g128_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv,
+                        int N, uint16_t* y, int variant, void* stream);
+
+/*
+ * Several independent int4 g128 GEMVs with one batch size M, launched
+ * together (as few kernel launches as the shapes allow).  This is how
+ * projections that read the same activations (q, k, v, gate, up of a layer)
+ * or that are independent of each other (o and down of a parallel block) go
+ * out as one unit, as the Rumik TTS Fast Inference post ("What Made It
+ * Faster") does by packing projections that share an input -- here without
+ * re-laying out any weights.  1 <= count <= 8; every task obeys the
+ * q4g128_gemv rules; no task's y may overlap any task's inputs or another y.
+ */
+typedef struct q4g128_task {
+    const uint16_t* x;       /* bf16 [M, K] */
+    const uint8_t* qweight;  /* uint8 [N, K/2] */
+    const uint16_t* scale;   /* fp16 [N, K/128] */
+    const uint16_t* minv;    /* fp16 [N, K/128] */
+    uint16_t* y;             /* bf16 [M, N] */
+    int N;
+    int K;
+} q4g128_task;
+
+int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant, void* stream);
+
+/*
+ * NVFP4 weight-only weights.
+ * Format: VoxCPM2-NVFP4 model card, section "What was quantized": 4-bit float
+ * (E2M1) codes, symmetric, group size 16, float8_e4m3fn group scales and one
+ * fp32 global scale per matrix; activations stay BF16.
+ *   qweight      uint8 [N, K/2]   E2M1 codes, LOW nibble = EVEN column
+ *   scale_e4m3   uint8 [N, K/16]  OCP float8_e4m3fn bit patterns
+ *   global_scale fp32            multiplier G
+ *   w[n, k] = e2m1(code[n, k]) * e4m3(scale[n, k/16]) * G
+ * x: bf16 [M, K]; y: bf16 [M, N].  Requires K % 32 == 0.
+ */
+int nvfp4g16_gemv(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint8_t* scale_e4m3, float global_scale, int N,
+                  uint16_t* y, void* stream);
+int nvfp4g16_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint8_t* scale_e4m3, float global_scale,
+                          int N, uint16_t* y, int variant, void* stream);
+
+/*
+ * Dense BF16 weights (the audio head head.audio_weight [16385, 2048] of the
+ * rumik-oss-1-int4 card, section "Format"; its 2049-row codebook slice from
+ * the Rumik TTS Fast Inference post, section "What Made It Faster"; and the
+ * v/down projections the VoxCPM2-NVFP4 card keeps in BF16).
+ *   w bf16 [N, K]; x bf16 [M, K]; y bf16 [M, N].  Requires K % 8 == 0.
+ */
+int bf16_gemv(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* y, void* stream);
+int bf16_gemv_variant(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* y, int variant, void* stream);
+
+/*
+ * Diagnostic dequantization of a whole matrix to fp32 w [N, K] (16-byte
+ * aligned).  Bitwise equal to the format definitions above: int4 rounds
+ * code*scale+min once; NVFP4 rounds e2m1*e4m3*G once (the first product is
+ * exact).  Uses the device conversion helpers of the GEMV kernels.
+ */
+int q4g128_dequant_f32(const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N, int K, float* w, void* stream);
+int nvfp4g16_dequant_f32(const uint8_t* qweight, const uint8_t* scale_e4m3, float global_scale, int N, int K, float* w,
+                         void* stream);
+
+/* Name of the kernel a call would run ("dot2", "mfma"); host only, never fails. */
+const char* q4gemv_variant_name(int fmt, int variant, int M, int N, int K);
+
+/* Static text for a status code; host only. */
+const char* q4gemv_strerror(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int q4gemv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4GEMV_H */

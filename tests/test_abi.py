@@ -1,0 +1,134 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments on the host before any HIP
+call (only invalid argument sets are passed here, so nothing is launched)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+q4 = pytest.importorskip("bit_weight_only_q4g128_amd")
+lib = q4.lib
+
+OK, EPTR, ESHAPE, EALIGN, EALIAS, ELAUNCH, EVARIANT = 0, -1, -2, -3, -4, -5, -6
+A = 0x10000000  # a 16-byte aligned fake device address; never dereferenced
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:int|const\s+char\s*\*)\s+(\w+)\s*\(", src, flags=re.M)
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    for must in ("q4g128_gemv", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32"):
+        assert must in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_symbol_exported(name):
+    assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    assert lib.q4gemv_version() >= 100
+    for rc in (OK, EPTR, ESHAPE, EALIGN, EALIAS, ELAUNCH, EVARIANT):
+        assert q4.strerror(rc) and q4.strerror(rc) != "unknown status"
+    assert q4.strerror(-99) == "unknown status"
+
+
+def q4call(x=A, M=1, K=2048, qw=A + (1 << 24), sc=A + (2 << 24), mn=A + (3 << 24), N=2048, y=A + (4 << 24), variant=0):
+    return lib.q4g128_gemv_variant(x, M, K, qw, sc, mn, N, y, variant, None)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(x=None), EPTR), (dict(qw=None), EPTR), (dict(sc=None), EPTR), (dict(mn=None), EPTR), (dict(y=None), EPTR),
+    (dict(M=0), ESHAPE), (dict(M=65), ESHAPE), (dict(N=0), ESHAPE), (dict(K=0), ESHAPE), (dict(K=192), ESHAPE),
+    (dict(K=2048 + 64), ESHAPE), (dict(x=A + 2), EALIGN), (dict(qw=A + (1 << 24) + 8), EALIGN),
+    (dict(sc=A + (2 << 24) + 1), EALIGN), (dict(y=A + (4 << 24) + 1), EALIGN),
+    (dict(y=A + (1 << 24) + 64), EALIAS), (dict(y=A + 16), EALIAS), (dict(y=A + (3 << 24)), EALIAS),
+    (dict(variant=3), EVARIANT), (dict(variant=-1), EVARIANT),
+])
+def test_q4_validation(kw, rc):
+    assert q4call(**kw) == rc
+
+
+def nvcall(x=A, M=1, K=2048, qw=A + (1 << 24), sc=A + (2 << 24), G=1.0, N=2048, y=A + (4 << 24), variant=0):
+    return lib.nvfp4g16_gemv_variant(x, M, K, qw, sc, G, N, y, variant, None)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(x=None), EPTR), (dict(sc=None), EPTR), (dict(K=48), ESHAPE), (dict(M=100), ESHAPE),
+    (dict(qw=A + (1 << 24) + 4), EALIGN), (dict(y=A + (2 << 24)), EALIAS), (dict(variant=9), EVARIANT),
+])
+def test_nvfp4_validation(kw, rc):
+    assert nvcall(**kw) == rc
+
+
+def bfcall(x=A, M=1, K=2048, w=A + (1 << 24), N=2049, y=A + (4 << 24), variant=0):
+    return lib.bf16_gemv_variant(x, M, K, w, N, y, variant, None)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(w=None), EPTR), (dict(K=12), ESHAPE), (dict(N=-1), ESHAPE), (dict(w=A + (1 << 24) + 2), EALIGN),
+    (dict(y=A + (1 << 24) + 100), EALIAS), (dict(variant=5), EVARIANT),
+])
+def test_bf16_validation(kw, rc):
+    assert bfcall(**kw) == rc
+
+
+def test_dequant_validation():
+    assert lib.q4g128_dequant_f32(None, A, A, 1, 128, A, None) == EPTR
+    assert lib.q4g128_dequant_f32(A, A + (1 << 24), A + (2 << 24), 1, 100, A + (3 << 24), None) == ESHAPE
+    assert lib.q4g128_dequant_f32(A, A + (1 << 24), A + (2 << 24), 1, 128, A + (3 << 24) + 4, None) == EALIGN
+    assert lib.q4g128_dequant_f32(A, A + (1 << 24), A + (2 << 24), 4, 128, A, None) == EALIAS
+    assert lib.nvfp4g16_dequant_f32(A, None, 1.0, 1, 32, A, None) == EPTR
+    assert lib.nvfp4g16_dequant_f32(A, A + (1 << 24), 1.0, 1, 16, A + (2 << 24), None) == ESHAPE
+
+
+def test_variant_names():
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 1, 2048, 2048) == "dot2"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 2048) == "mfma"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_MFMA, 1, 2048, 2048) == "mfma"
+    assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_DOT2, 3, 16385, 2048) == "dot2"
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2048) == "mfma"
+    assert q4.variant_name(7, 0, 1, 1, 128) == "invalid"
+    assert q4.variant_name(0, 0, 0, 1, 128) == "invalid"
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        q4.q4g128_gemv(x, torch.zeros(1, 64, dtype=torch.uint8), torch.zeros(1, 1, dtype=torch.float16),
+                       torch.zeros(1, 1, dtype=torch.float16))
+
+
+def test_grouped_validation():
+    T = q4.Q4Task
+    def task(i, **kw):
+        base = dict(x=A + (i << 26), qweight=A + (i << 26) + (1 << 24), scale=A + (i << 26) + (2 << 24),
+                    minv=A + (i << 26) + (3 << 24), y=A + (i << 26) + (4 << 24), N=2048, K=2048)
+        base.update(kw)
+        return T(**base)
+    arr = (T * 3)(task(0), task(1), task(2))
+    assert lib.q4g128_gemv_grouped(None, 1, 1, 0, None) == EPTR
+    assert lib.q4g128_gemv_grouped(arr, 0, 1, 0, None) == ESHAPE
+    assert lib.q4g128_gemv_grouped(arr, 9, 1, 0, None) == ESHAPE
+    assert lib.q4g128_gemv_grouped(arr, 3, 0, 0, None) == ESHAPE
+    assert lib.q4g128_gemv_grouped(arr, 3, 1, 4, None) == EVARIANT
+    bad = (T * 2)(task(0), task(1, K=100))
+    assert lib.q4g128_gemv_grouped(bad, 2, 1, 0, None) == ESHAPE
+    # task 1 writes over task 0's weights
+    alias = (T * 2)(task(0), task(1, y=A + (1 << 24) + 4096))
+    assert lib.q4g128_gemv_grouped(alias, 2, 1, 0, None) == EALIAS
+    # two tasks share an output
+    same = (T * 2)(task(0), task(1, y=A + (4 << 24)))
+    assert lib.q4g128_gemv_grouped(same, 2, 1, 0, None) == EALIAS

@@ -1,0 +1,318 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bitwise: device dequantization, and one-hot activations (a single nonzero
+term makes every variant's sum exact, so y must equal RN_bf16(w32)).
+Within tolerance (gpu_util.check_gemv): every workload of the pages' shapes
+and the edge shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_gemv, gpu, onehot_x, rn_bf16_bits, same_bits_f32, x_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q4():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_weight_only_q4g128_amd as m
+    return m
+
+
+VARIANTS = [1, 2]  # dot2, mfma
+VNAME = {0: "auto", 1: "dot2", 2: "mfma"}
+
+
+# ----------------------------------------------------------------------------
+# dequantization, bitwise
+# ----------------------------------------------------------------------------
+def test_q4_dequant_bitwise(q4):
+    rng = np.random.default_rng(1)
+    for (N, K) in ((256, 512), (33, 1536), (4, 128)):
+        qw = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+        sc = rng.uniform(-3, 3, size=(N, K // 128)).astype(np.float16).view(np.uint16)
+        mn = rng.uniform(-3, 3, size=(N, K // 128)).astype(np.float16).view(np.uint16)
+        # sprinkle subnormal scales/mins and the fp16 extremes
+        sc.flat[::7] = rng.integers(1, 1024, size=sc.flat[::7].shape)
+        mn.flat[::5] = 0x8001
+        sc.flat[1] = 0x7BFF
+        ref = oracle.q4g128_dequant_f32(qw, sc, mn)
+        w = q4.q4g128_dequant_f32(gpu(torch.from_numpy(qw)), gpu(torch.from_numpy(sc.view(np.int16))).view(torch.float16),
+                                  gpu(torch.from_numpy(mn.view(np.int16))).view(torch.float16))
+        assert same_bits_f32(w.cpu().numpy(), ref), (N, K)
+
+
+def test_nvfp4_dequant_bitwise_exhaustive(q4):
+    # 256 rows = every e4m3 scale byte; each row holds all 16 codes twice
+    codes = torch.arange(16).repeat(2).view(1, 32)
+    qw = synth.pack_nibbles(codes).repeat(256, 1)
+    sc = torch.stack([torch.arange(256, dtype=torch.int64), torch.arange(256, dtype=torch.int64)], 1).to(torch.uint8)
+    for G in (1.0, float(np.float32(1 / 3)), float(np.float32(0.02 / 2688)), 2.0 ** -20, float(np.float32(1 + 2 ** -23))):
+        ref = oracle.nvfp4g16_dequant_f32(qw.numpy(), sc.numpy(), G)
+        w = q4.nvfp4g16_dequant_f32(gpu(qw), gpu(sc), G)
+        assert same_bits_f32(w.cpu().numpy(), ref), G
+
+
+# ----------------------------------------------------------------------------
+# one-hot activations: bitwise for every variant
+# ----------------------------------------------------------------------------
+def _onehot_ks(K, M, seed):
+    rng = np.random.default_rng(seed)
+    ks = list(rng.choice(K, size=M, replace=False)) if M <= K else list(rng.integers(0, K, size=M))
+    ks[0] = 0
+    if M > 1:
+        ks[-1] = K - 1
+    return [int(k) for k in ks]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 48])
+def test_q4_onehot_bitwise(q4, variant, M):
+    N, K = 200, 1024
+    qw, sc, mn = synth.q4_matrix(N, K, ("onehot", M))
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    ks = _onehot_ks(K, M, M)
+    x = onehot_x(K, ks)
+    y = q4.q4g128_gemv(gpu(x), gpu(qw), gpu(sc), gpu(mn), variant=variant)
+    got = y.cpu().float().numpy()
+    exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(got, exp), (VNAME[variant], M, np.argwhere(got != exp)[:4])
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("M", [1, 4, 17, 48])
+def test_nvfp4_onehot_bitwise(q4, variant, M):
+    N, K = 150, 512
+    qw, s8, G = synth.nvfp4_matrix(N, K, ("onehot-nv", M))
+    w32 = oracle.nvfp4g16_dequant_f32(qw.numpy(), s8.numpy(), G)
+    ks = _onehot_ks(K, M, 100 + M)
+    x = onehot_x(K, ks)
+    y = q4.nvfp4g16_gemv(gpu(x), gpu(qw), gpu(s8), G, variant=variant)
+    got = synth.bits16(y.cpu())
+    exp = rn_bf16_bits(w32[:, ks].T)
+    # +0 / -0 are equal values
+    gotv = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
+    expv = torch.from_numpy(exp.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(gotv, expv), (VNAME[variant], M)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("M", [1, 5, 32])
+def test_bf16_onehot_bitwise(q4, variant, M):
+    N, K = 77, 256
+    w = synth.bf16_matrix(N, K, ("onehot-bf", M))
+    ks = _onehot_ks(K, M, 200 + M)
+    y = q4.bf16_gemv(gpu(onehot_x(K, ks)), gpu(w), variant=variant)
+    assert np.array_equal(y.cpu().float().numpy(), w[:, ks].T.float().numpy()), (VNAME[variant], M)
+
+
+# ----------------------------------------------------------------------------
+# the pages' shapes, within tolerance
+# ----------------------------------------------------------------------------
+def test_config0_single_matrix(q4):
+    d = synth.config0(0)
+    w32 = oracle.q4g128_dequant_f32(d["qweight"].numpy(), synth.bits16(d["scale"]), synth.bits16(d["min"]))
+    ref = oracle.gemv_f64(synth.bits16(d["x"]), w32)
+    for v in (0, 1, 2):
+        y = q4.q4g128_gemv(gpu(d["x"]), gpu(d["qweight"]), gpu(d["scale"]), gpu(d["min"]), variant=v)
+        check_gemv(y, ref, w32, synth.bits16(d["x"]), f"config0 {VNAME[v]}")
+
+
+_LAYER_CACHE = {}
+
+
+def _layer_q4():
+    if "q4" not in _LAYER_CACHE:
+        lay = synth.q4_layer(("layer", 0))
+        w32 = {n: oracle.q4g128_dequant_f32(t[0].numpy(), synth.bits16(t[1]), synth.bits16(t[2])) for n, t in lay.items()}
+        _LAYER_CACHE["q4"] = (lay, w32)
+    return _LAYER_CACHE["q4"]
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 48])
+@pytest.mark.parametrize("proj", synth.LAYER_ORDER)
+def test_q4_layer(q4, proj, M):
+    lay, w32 = _layer_q4()
+    qw, sc, mn = lay[proj]
+    N, K = synth.LAYER_SHAPES[proj]
+    x = synth.x_bf16(M, K, ("layer-x", proj))
+    ref = oracle.gemv_f64(x_bits(x), w32[proj])
+    for v in (0, 1, 2):
+        y = q4.q4g128_gemv(gpu(x), gpu(qw), gpu(sc), gpu(mn), variant=v)
+        check_gemv(y, ref, w32[proj], x_bits(x), f"{proj} M={M} {VNAME[v]}")
+
+
+@pytest.mark.parametrize("M", [1, 48])
+@pytest.mark.parametrize("proj", synth.LAYER_ORDER)
+def test_nvfp4_layer(q4, proj, M):
+    N, K = synth.LAYER_SHAPES[proj]
+    x = synth.x_bf16(M, K, ("nv-x", proj))
+    if proj in synth.NVFP4_BF16_PROJ:
+        w = synth.bf16_matrix(N, K, ("nv-layer", proj))
+        w32 = oracle.bf16_dequant_f32(synth.bits16(w))
+        ref = oracle.gemv_f64(x_bits(x), w32)
+        for v in (0, 1, 2):
+            check_gemv(q4.bf16_gemv(gpu(x), gpu(w), variant=v), ref, w32, x_bits(x), f"bf16 {proj} M={M} {VNAME[v]}")
+        return
+    qw, s8, G = synth.nvfp4_matrix(N, K, ("nv-layer", proj))
+    w32 = oracle.nvfp4g16_dequant_f32(qw.numpy(), s8.numpy(), G)
+    ref = oracle.gemv_f64(x_bits(x), w32)
+    for v in (0, 1, 2):
+        y = q4.nvfp4g16_gemv(gpu(x), gpu(qw), gpu(s8), G, variant=v)
+        check_gemv(y, ref, w32, x_bits(x), f"nvfp4 {proj} M={M} {VNAME[v]}")
+
+
+@pytest.mark.parametrize("M", [1, 48])
+@pytest.mark.parametrize("shape", [synth.HEAD_FULL, synth.HEAD_SLICE])
+def test_bf16_head(q4, shape, M):
+    N, K = shape
+    w = synth.bf16_matrix(N, K, ("head", N))
+    x = synth.x_bf16(M, K, ("head-x", N))
+    w32 = oracle.bf16_dequant_f32(synth.bits16(w))
+    ref = oracle.gemv_f64(x_bits(x), w32)
+    for v in (0, 1, 2):
+        check_gemv(q4.bf16_gemv(gpu(x), gpu(w), variant=v), ref, w32, x_bits(x), f"head {N} M={M} {VNAME[v]}")
+
+
+# ----------------------------------------------------------------------------
+# edge shapes: ragged N, short/odd K, every batch size
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K", [(1, 128), (7, 256), (17, 384), (65, 1536), (130, 4096), (33, 11008), (5, 16384)])
+def test_q4_edge_shapes(q4, N, K):
+    qw, sc, mn = synth.q4_matrix(N, K, ("edge", N, K))
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    for M in (1, 2, 5, 8, 9, 16, 33, 64):
+        x = synth.x_bf16(M, K, ("edge-x", N, K, M))
+        ref = oracle.gemv_f64(x_bits(x), w32)
+        for v in (0, 1, 2):
+            y = q4.q4g128_gemv(gpu(x), gpu(qw), gpu(sc), gpu(mn), variant=v)
+            check_gemv(y, ref, w32, x_bits(x), f"edge N={N} K={K} M={M} {VNAME[v]}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (9, 96), (31, 160), (66, 2080)])
+def test_nvfp4_edge_shapes(q4, N, K):
+    qw, s8, G = synth.nvfp4_matrix(N, K, ("edge-nv", N, K))
+    w32 = oracle.nvfp4g16_dequant_f32(qw.numpy(), s8.numpy(), G)
+    for M in (1, 3, 8, 12, 40):
+        x = synth.x_bf16(M, K, ("edge-nv-x", N, K, M))
+        ref = oracle.gemv_f64(x_bits(x), w32)
+        for v in (0, 1, 2):
+            check_gemv(q4.nvfp4g16_gemv(gpu(x), gpu(qw), gpu(s8), G, variant=v), ref, w32, x_bits(x),
+                       f"nv edge N={N} K={K} M={M} {VNAME[v]}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 24), (19, 136), (40, 1000), (129, 2056)])
+def test_bf16_edge_shapes(q4, N, K):
+    w = synth.bf16_matrix(N, K, ("edge-bf", N, K))
+    w32 = oracle.bf16_dequant_f32(synth.bits16(w))
+    for M in (1, 2, 7, 16, 20):
+        x = synth.x_bf16(M, K, ("edge-bf-x", N, K, M))
+        ref = oracle.gemv_f64(x_bits(x), w32)
+        for v in (0, 1, 2):
+            check_gemv(q4.bf16_gemv(gpu(x), gpu(w), variant=v), ref, w32, x_bits(x), f"bf edge N={N} K={K} M={M} {VNAME[v]}")
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_q4_power_of_two_scaling_is_bitwise(q4, variant):
+    N, K, M = 300, 2048, 4
+    qw, sc, mn = (gpu(t) for t in synth.q4_matrix(N, K, ("pow2",)))
+    x = synth.x_bf16(M, K, ("pow2-x",))
+    y1 = q4.q4g128_gemv(gpu(x), qw, sc, mn, variant=variant)
+    y2 = q4.q4g128_gemv(gpu((x.float() * 8).to(torch.bfloat16)), qw, sc, mn, variant=variant)
+    assert torch.equal((y1.float() * 8).to(torch.bfloat16), y2)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_q4_row_permutation_is_bitwise(q4, variant):
+    N, K, M = 256, 2048, 16
+    qw, sc, mn = synth.q4_matrix(N, K, ("perm",))
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(0))
+    x = gpu(synth.x_bf16(M, K, ("perm-x",)))
+    y1 = q4.q4g128_gemv(x, gpu(qw), gpu(sc), gpu(mn), variant=variant)
+    y2 = q4.q4g128_gemv(x, gpu(qw[perm]), gpu(sc[perm]), gpu(mn[perm]), variant=variant)
+    assert torch.equal(y1[:, perm.cuda()], y2)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_q4_repeat_runs_are_bitwise_identical(q4, variant):
+    N, K, M = 2048, 8192, 3
+    qw, sc, mn = (gpu(t) for t in synth.q4_matrix(N, K, ("det",)))
+    x = gpu(synth.x_bf16(M, K, ("det-x",)))
+    y0 = q4.q4g128_gemv(x, qw, sc, mn, variant=variant)
+    for _ in range(20):
+        assert torch.equal(q4.q4g128_gemv(x, qw, sc, mn, variant=variant), y0)
+
+
+def test_q4_batched_equals_stacked_singles(q4):
+    N, K, M = 512, 2048, 6
+    qw, sc, mn = synth.q4_matrix(N, K, ("stack",))
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    x = synth.x_bf16(M, K, ("stack-x",))
+    yb = q4.q4g128_gemv(gpu(x), gpu(qw), gpu(sc), gpu(mn))
+    ys = torch.cat([q4.q4g128_gemv(gpu(x[m:m + 1]), gpu(qw), gpu(sc), gpu(mn)) for m in range(M)], 0)
+    ref = oracle.gemv_f64(x_bits(x), w32)
+    check_gemv(yb, ref, w32, x_bits(x), "batched")
+    check_gemv(ys, ref, w32, x_bits(x), "singles")
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_output_fully_overwritten(q4, variant):
+    N, K, M = 100, 512, 20
+    qw, sc, mn = (gpu(t) for t in synth.q4_matrix(N, K, ("poison",)))
+    x = gpu(synth.x_bf16(M, K, ("poison-x",)))
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    q4.q4g128_gemv(x, qw, sc, mn, out=out, variant=variant)
+    assert not torch.isnan(out).any()
+
+
+def test_stream_ordering_on_side_stream(q4):
+    N, K, M = 1024, 2048, 2
+    qw, sc, mn = (gpu(t) for t in synth.q4_matrix(N, K, ("stream",)))
+    x = gpu(synth.x_bf16(M, K, ("stream-x",)))
+    ref = q4.q4g128_gemv(x, qw, sc, mn)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = q4.q4g128_gemv(x, qw, sc, mn)
+    s.synchronize()
+    assert torch.equal(y, ref)
+
+
+# ----------------------------------------------------------------------------
+# grouped launches: same kernels, several GEMVs per launch
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M", [1, 3, 8, 48])
+def test_q4_grouped_equals_single_calls(q4, M):
+    lay, w32 = _layer_q4()
+    xin = gpu(synth.x_bf16(M, 2048, ("grp-xin", M)))
+    xat = gpu(synth.x_bf16(M, 2048, ("grp-xat", M)))
+    xff = gpu(synth.x_bf16(M, 8192, ("grp-xff", M)))
+    xs = {"q": xin, "k": xin, "v": xin, "gate": xin, "up": xin, "o": xat, "down": xff}
+    dev = {p: tuple(gpu(t) for t in lay[p]) for p in synth.LAYER_ORDER}
+    for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
+        for v in (0, 1, 2):
+            outs = q4.q4g128_gemv_grouped([(xs[p], *dev[p], None) for p in stage], variant=v)
+            for p, y in zip(stage, outs):
+                ys = q4.q4g128_gemv(xs[p], *dev[p], variant=v)
+                assert torch.equal(y, ys), (p, M, VNAME[v])
+                xb = x_bits(xs[p].cpu())
+                check_gemv(y, oracle.gemv_f64(xb, w32[p]), w32[p], xb, f"grouped {p} M={M} {VNAME[v]}")
+
+
+def test_q4_grouped_mixed_k(q4):
+    # K = 16384 needs two chunks per lane, K = 384 one: the call splits into two launches
+    shapes = [(64, 16384), (100, 384), (7, 2048)]
+    mats = [synth.q4_matrix(N, K, ("mix", N, K)) for N, K in shapes]
+    xs = [gpu(synth.x_bf16(2, K, ("mix-x", K))) for _, K in shapes]
+    outs = q4.q4g128_gemv_grouped([(x, *(gpu(t) for t in m), None) for x, m in zip(xs, mats)])
+    for (N, K), m, x, y in zip(shapes, mats, xs, outs):
+        w32 = oracle.q4g128_dequant_f32(m[0].numpy(), synth.bits16(m[1]), synth.bits16(m[2]))
+        xb = x_bits(x.cpu())
+        check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"mixed N={N} K={K}")
