@@ -140,27 +140,60 @@ def time_graph(torch, wl, M, steps, warmup, mode):
     return ms, g
 
 
-def time_q4_launches(torch, wl, M, mode, reps=3):
-    """Average duration of the int4 GEMV launches of a step, each bracketed by
-    HIP events on the stream it is launched on (eager launches).  Returns
-    (ms per launch, algorithmic bytes per launch)."""
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        assert self.hip.hipEventCreate(self.ct.byref(ev)) == 0
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        assert self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) == 0
+        return ms.value
+
+    def sync(self, e):
+        assert self.hip.hipEventSynchronize(e) == 0
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def time_q4_launches(torch, q4, wl, M, mode, reps=3):
+    """Average execution time of the int4 GEMV launches of one step.  Each
+    launch records a pair of HIP events at its own start and end on the stream
+    it runs on (q4gemv_time_next_launch), so host-side gaps between eager
+    launches are not counted.  Returns (ms per launch, algorithmic bytes per
+    launch: weights + activations read + outputs written)."""
     xs, ys, xin, yh = wl.buffers(M)
     calls = [c for c in wl.launches(M, mode) if c[2]]
     act = sum(ys[p].numel() * 2 for p in wl.order) + (2048 + 2048 + 8192) * M * 2   # per layer
     io_per_launch = act * N_LAYERS / len(calls)
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+    he = HipEvents()
+    evs = [(he.create(), he.create()) for _ in calls]
     tot_ms, tot_bytes, n = 0.0, 0, 0
     for _ in range(reps):
         for (f, b, _), (a, z) in zip(calls, evs):
-            a.record(stream)
+            q4.lib.q4gemv_time_next_launch(a, z)
             f()
-            z.record(stream)
         torch.cuda.synchronize()
+        he.sync(evs[-1][1])
         for (f, b, _), (a, z) in zip(calls, evs):
-            tot_ms += a.elapsed_time(z)
+            tot_ms += he.elapsed_ms(a, z)
             tot_bytes += b + io_per_launch
             n += 1
+    for a, z in evs:
+        he.destroy(a)
+        he.destroy(z)
     return tot_ms / n, tot_bytes / n
 
 
@@ -193,6 +226,55 @@ def cpu_baseline(wl, budget_s=15.0):
                       f"{t_used:.1f} s"}
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_q4_grouped_M1_traffic.json")
+
+
+def csrc_digest():
+    """sha256 over the HIP sources and headers the measured kernel is built from."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "bit_weight_only_q4g128_amd", "csrc", "*")))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the M=1 grouped int4 GEMV from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None if the kernel sources
+    changed since those counters were taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("csrc_digest") != csrc_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def counters_pass(q4, synth, torch, head_rows):
+    """Workload for hardware-counter runs (no timing): the M=1 grouped step
+    three times, eagerly, then a 256 MiB device-to-device copy whose byte
+    count is known (the reference that scales FETCH_SIZE / WRITE_SIZE)."""
+    wl = Workload(q4, synth, torch, head_rows)
+    calls = wl.launches(1, "grouped")
+    for _ in range(3):
+        for f, _, _ in calls:
+            f()
+    torch.cuda.synchronize()
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"bench: counters pass done ({len(calls)} launches per step, csrc digest {csrc_digest()})")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +282,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--head", choices=("full", "slice"), default="full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -212,6 +295,9 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     torch.cuda.set_device(0)
     head_rows = synth.HEAD_FULL[0] if args.head == "full" else synth.HEAD_SLICE[0]
+    if args.counters:
+        counters_pass(q4, synth, torch, head_rows)
+        return
     wl = Workload(q4, synth, torch, head_rows)
 
     res = {}
@@ -223,7 +309,7 @@ def main():
             log(f"bench: M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(M, mode)]['gbs']:6.0f} GB/s, "
                 f"{1e3 / ms:6.0f} steps/s, {res[(M, mode)]['launches']} launches")
             del g
-    kms, kbytes = time_q4_launches(torch, wl, 1, "grouped")
+    kms, kbytes = time_q4_launches(torch, q4, wl, 1, "grouped")
     kname = f"gemv_dot2_kernel<FmtQ4, MT=1, CPL=1> ({q4.variant_name(q4.FMT_Q4G128, 0, 1, 2048, 2048)}), grouped launches"
     achieved = kbytes / (kms * 1e-3) / 1e9
     log(f"bench: int4 GEMV launches at M=1: avg {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
@@ -257,7 +343,7 @@ def main():
                       for (M, mode), r in res.items()},
         },
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)},
     }
     if not args.no_cpu_baseline:

@@ -4,7 +4,7 @@ Argument marshalling only: every step runs in the HIP library.  Tensors must
 be CUDA (ROCm) tensors, contiguous, with the dtypes the C header documents;
 calls are enqueued on torch's current stream of the tensors' device.  There is
 no CPU fallback: importing fails loudly if the library has not been built
-(``python -m bit_weight_only_q4g128_amd._build``).
+(``python bit_weight_only_q4g128_amd/_build.py``).
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4gemv.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing; build it with: python -m bit_weight_only_q4g128_amd._build")
+    raise ImportError(f"{LIB_PATH} is missing; build it with: python bit_weight_only_q4g128_amd/_build.py")
 lib = ctypes.CDLL(LIB_PATH)
 
 VARIANT_AUTO, VARIANT_DOT2, VARIANT_MFMA = 0, 1, 2
@@ -43,6 +43,8 @@ lib.q4gemv_variant_name.argtypes = [_i, _i, _i, _i, _i]
 lib.q4gemv_variant_name.restype = ctypes.c_char_p
 lib.q4gemv_strerror.argtypes = [_i]
 lib.q4gemv_strerror.restype = ctypes.c_char_p
+lib.q4gemv_time_next_launch.argtypes = [_p, _p]
+lib.q4gemv_time_next_launch.restype = ctypes.c_int
 lib.q4gemv_version.argtypes = []
 lib.q4gemv_version.restype = ctypes.c_int
 

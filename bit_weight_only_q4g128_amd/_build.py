@@ -1,6 +1,7 @@
 """Build libq4gemv.so in-tree with hipcc for gfx950.
 
-Usage: python -m bit_weight_only_q4g128_amd._build   (or _build.build()).
+Usage: python bit_weight_only_q4g128_amd/_build.py   (run it as a script:
+importing the package needs the library this builds).
 Object files go to _build/ at the repository root; the shared library lands
 next to this file, where the Python binding loads it from.
 """

@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/q4gemv.h"
+#include "q4gemv.h"
 #include "internal.h"
 
 using q4::Fmt;
@@ -75,7 +75,21 @@ int check_q4(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint
 
 }  // namespace
 
+namespace q4 {
+LaunchEvents& pending_launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace q4
+
 extern "C" {
+
+int q4gemv_time_next_launch(void* start_event, void* stop_event) {
+    q4::LaunchEvents& ev = q4::pending_launch_events();
+    ev.start = reinterpret_cast<hipEvent_t>(start_event);
+    ev.stop = reinterpret_cast<hipEvent_t>(stop_event);
+    return Q4_OK;
+}
 
 int q4g128_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv,
                         int N, uint16_t* y, int variant, void* stream) {

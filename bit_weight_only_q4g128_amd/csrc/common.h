@@ -54,18 +54,40 @@ __device__ __forceinline__ f32x2 e2m1x2_to_f32x2(uint32_t w) {
 // int4 nibbles -> BF16 pairs holding 128 + code (exact)
 //
 // A dword holds 8 codes c0..c7 (c_i in bits 4i..4i+3; the even column sits in
-// the low nibble of each byte).  Writing a nibble into the low mantissa bits of
-// the BF16 pattern 0x4300 (= 128.0) gives exactly 128 + c.  The four pairs come
-// out as (c0,c4) (c1,c5) (c2,c6) (c3,c7); activations are paired the same way
-// by xq4_pairs() so the dot products see matching columns.
+// the low nibble of each byte).  A code in the low mantissa bits of the BF16
+// pattern 0x4300 (= 128.0) reads as exactly 128 + c.  The even nibbles
+// (c0 c2 c4 c6) and odd nibbles (c1 c3 c5 c7) are first isolated one per byte;
+// v_perm_b32 then interleaves them with the 0x43 high byte, 3 + 4 instructions
+// per 8 codes.  The pairs come out as (c0,c4) (c1,c5) (c2,c6) (c3,c7);
+// activations are paired the same way by xq4_pairs() so the dot products see
+// matching columns.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kMagic128 = 0x43004300u;
+constexpr uint32_t kMagicBytes = 0x43434343u;
 
 __device__ __forceinline__ void q4_pairs(uint32_t d, uint32_t p[4]) {
-    p[0] = (d & 0x000F000Fu) | kMagic128;
-    p[1] = ((d >> 4) & 0x000F000Fu) | kMagic128;
-    p[2] = ((d >> 8) & 0x000F000Fu) | kMagic128;
-    p[3] = ((d >> 12) & 0x000F000Fu) | kMagic128;
+    const uint32_t lo = d & 0x0F0F0F0Fu;          // bytes c0 c2 c4 c6
+    const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;   // bytes c1 c3 c5 c7
+    p[0] = __builtin_amdgcn_perm(kMagicBytes, lo, 0x04020400u);   // (c0, c4)
+    p[1] = __builtin_amdgcn_perm(kMagicBytes, hi, 0x04020400u);   // (c1, c5)
+    p[2] = __builtin_amdgcn_perm(kMagicBytes, lo, 0x04030401u);   // (c2, c6)
+    p[3] = __builtin_amdgcn_perm(kMagicBytes, hi, 0x04030401u);   // (c3, c7)
+}
+
+// ---------------------------------------------------------------------------
+// buffer resources: 128-bit loads with an SGPR base and a 32-bit lane offset;
+// offsets at or past num_records read as zero.
+// ---------------------------------------------------------------------------
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
+constexpr int kAuxStream = 2;              // nt: read-once streaming data
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kAuxStream));
+}
+__device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
 
 // 8 consecutive BF16 activations (4 dwords, natural order) -> the pairing

@@ -58,15 +58,13 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t* __res
 hipError_t launch_q4_dequant(const uint8_t* qw, const uint16_t* sc, const uint16_t* mn, int N, int K, float* w, hipStream_t s) {
     const size_t total = (size_t)N * (K >> 3);
     const unsigned grid = (unsigned)((total + 255) / 256);
-    hipLaunchKernelGGL(q4_dequant_kernel, dim3(grid), dim3(256), 0, s, qw, sc, mn, N, K, w);
-    return hipGetLastError();
+    return launch_kernel(q4_dequant_kernel, dim3(grid), dim3(256), 0, s, qw, sc, mn, N, K, w);
 }
 
 hipError_t launch_nvfp4_dequant(const uint8_t* qw, const uint8_t* sc, float G, int N, int K, float* w, hipStream_t s) {
     const size_t total = (size_t)N * (K >> 3);
     const unsigned grid = (unsigned)((total + 255) / 256);
-    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3(grid), dim3(256), 0, s, qw, sc, G, N, K, w);
-    return hipGetLastError();
+    return launch_kernel(nvfp4_dequant_kernel, dim3(grid), dim3(256), 0, s, qw, sc, G, N, K, w);
 }
 
 }  // namespace q4

@@ -3,8 +3,9 @@
 // A "chunk" is the 16 bytes of weight data one lane loads with one 128-bit
 // load.  For the 4-bit formats that is 32 consecutive weights of one row; for
 // BF16 it is 8.  Each policy says how to hold the matching activations in
-// registers, how to fetch the per-chunk group parameters, and how to turn a
-// chunk into a partial dot product for every batch row.
+// registers, how to fetch the per-chunk group parameters (through buffer
+// resources based at the wave's first row, so rows past N read as zero), and
+// how to turn a chunk into a partial dot product for every batch row.
 #pragma once
 
 #include "common.h"
@@ -34,9 +35,9 @@ struct GemvArgs {
 // ---------------------------------------------------------------------------
 struct FmtQ4 {
     static constexpr int WPC = 32;       // weights per chunk
-    static constexpr int XW = 16;        // activation dwords per chunk
     struct X { uint32_t p[16]; float sum; };
     struct Aux { float s, m; };
+    struct AuxRes { __amdgpu_buffer_rsrc_t s, m; };
 
     __device__ static void load_x(const uint16_t* xrow, int k0, bool active, X& xc) {
         if (!active) {
@@ -46,7 +47,6 @@ struct FmtQ4 {
             return;
         }
         const u32x4* src = reinterpret_cast<const u32x4*>(xrow + k0);
-        float s = 0.f;
         // 32 activations = 16 dwords; block d (8 activations) = dwords 4d..4d+3.
         uint32_t w[16];
 #pragma unroll
@@ -55,20 +55,63 @@ struct FmtQ4 {
             w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
         }
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            xq4_pairs(w[4 * d], w[4 * d + 1], w[4 * d + 2], w[4 * d + 3], &xc.p[4 * d]);
-        }
+        for (int d = 0; d < 4; ++d) xq4_pairs(w[4 * d], w[4 * d + 1], w[4 * d + 2], w[4 * d + 3], &xc.p[4 * d]);
+        // sum of the 32 activations: packed dot products against (1.0, 1.0)
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s += bf16lo(w[i]) + bf16hi(w[i]);
-        xc.sum = s;
+        for (int i = 0; i < 16; i += 2) {
+            s0 = dot2(w[i], 0x3F803F80u, s0);
+            s1 = dot2(w[i + 1], 0x3F803F80u, s1);
+        }
+        xc.sum = s0 + s1;
     }
 
-    __device__ static Aux load_aux(const GemvArgs& a, int row, int chunk) {
-        const size_t gi = (size_t)row * (a.K >> 7) + (chunk >> 2);
-        Aux r;
-        r.s = f16_to_f32(a.scale[gi]);
-        r.m = f16_to_f32(a.minv[gi]);
+    // Batch staging: the scale and min blocks of one batch of rows are
+    // contiguous ([rows][K/128] fp16 each, at most 512 bytes for the batch
+    // shapes the GEMV plans use), so lanes 0-31 fetch the scales and lanes
+    // 32-63 the mins with one 16-byte load each; the block then goes through
+    // LDS to the lanes that need it.  Used when every such load is 16-byte
+    // aligned: K % 1024 == 0 and both arrays 16-byte aligned (the host
+    // decides, per task).
+    static constexpr bool kStaged = true;
+    static constexpr int kStageBytes = 1024;
+    // row0: first row of the batch.  Plain global loads: the two halves of
+    // the wave read different arrays, which a buffer resource (uniform per
+    // wave) cannot express without a readfirstlane loop.  With K % 1024 == 0
+    // every array is a whole number of 16-byte pieces, so the bound check
+    // per piece is exact.
+    __device__ static u32x4 load_stage(const GemvArgs& a, int row0, int lane) {
+        const size_t G = (size_t)(a.K >> 7);
+        const size_t off = (size_t)row0 * G * 2 + (size_t)(lane & 31) * 16;
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(lane < 32 ? a.scale : a.minv);
+        return off < (size_t)a.N * G * 2 ? *reinterpret_cast<const u32x4*>(base + off) : u32x4{0, 0, 0, 0};
+    }
+    // row_in_batch: row offset inside the staged batch
+    __device__ static Aux read_stage(const uint16_t* st, const GemvArgs& a, int row_in_batch, int chunk) {
+        const int i = row_in_batch * (a.K >> 7) + (chunk >> 2);
+        Aux x;
+        x.s = f16_to_f32(st[i]);
+        x.m = f16_to_f32(st[256 + i]);
+        return x;
+    }
+
+    // group parameters of rows [row0, row0 + rows)
+    __device__ static AuxRes make_aux(const GemvArgs& a, int row0, int rows) {
+        const size_t G = (size_t)(a.K >> 7);
+        AuxRes r;
+        r.s = make_rsrc(a.scale + (size_t)row0 * G, (uint32_t)(rows * G * 2));
+        r.m = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)(rows * G * 2));
         return r;
+    }
+    __device__ static uint32_t aux_voff(const GemvArgs& a, int sub_row, int chunk) {
+        return (uint32_t)(sub_row * (a.K >> 7) + (chunk >> 2)) * 2;
+    }
+    __device__ static uint32_t aux_soff(const GemvArgs& a, int rows) { return (uint32_t)(rows * (a.K >> 7)) * 2; }
+    __device__ static Aux load_aux(const AuxRes& r, uint32_t voff, uint32_t soff) {
+        Aux x;
+        x.s = f16_to_f32(buf_load2(r.s, voff, soff));
+        x.m = f16_to_f32(buf_load2(r.m, voff, soff));
+        return x;
     }
 
     template <int MT>
@@ -107,9 +150,9 @@ struct FmtQ4 {
 // ---------------------------------------------------------------------------
 struct FmtNvfp4 {
     static constexpr int WPC = 32;
-    static constexpr int XW = 16;
     struct X { uint32_t p[16]; };
     struct Aux { float s0, s1; };
+    struct AuxRes { __amdgpu_buffer_rsrc_t s; };
 
     __device__ static void load_x(const uint16_t* xrow, int k0, bool active, X& xc) {
         const u32x4* src = reinterpret_cast<const u32x4*>(xrow + k0);
@@ -120,13 +163,27 @@ struct FmtNvfp4 {
         }
     }
 
-    __device__ static Aux load_aux(const GemvArgs& a, int row, int chunk) {
-        const uint8_t* p = a.scale8 + (size_t)row * (a.K >> 4) + 2 * chunk;
-        const uint32_t b = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
-        Aux r;
-        r.s0 = e4m3_to_f32<0>(b);
-        r.s1 = e4m3_to_f32<1>(b);
+    static constexpr bool kStaged = false;
+    static constexpr int kStageBytes = 0;
+    __device__ static u32x4 load_stage(const GemvArgs&, int, int) { return u32x4{0, 0, 0, 0}; }
+    __device__ static Aux read_stage(const uint16_t*, const GemvArgs&, int, int) { return Aux{}; }
+
+    __device__ static AuxRes make_aux(const GemvArgs& a, int row0, int rows) {
+        const size_t rb = (size_t)(a.K >> 4);
+        AuxRes r;
+        r.s = make_rsrc(a.scale8 + (size_t)row0 * rb, (uint32_t)(rows * rb));
         return r;
+    }
+    __device__ static uint32_t aux_voff(const GemvArgs& a, int sub_row, int chunk) {
+        return (uint32_t)(sub_row * (a.K >> 4) + 2 * chunk);
+    }
+    __device__ static uint32_t aux_soff(const GemvArgs& a, int rows) { return (uint32_t)(rows * (a.K >> 4)); }
+    __device__ static Aux load_aux(const AuxRes& r, uint32_t voff, uint32_t soff) {
+        const uint32_t b = buf_load2(r.s, voff, soff);
+        Aux x;
+        x.s0 = e4m3_to_f32<0>(b);
+        x.s1 = e4m3_to_f32<1>(b);
+        return x;
     }
 
     template <int MT>
@@ -161,15 +218,22 @@ struct FmtNvfp4 {
 // ---------------------------------------------------------------------------
 struct FmtBf16 {
     static constexpr int WPC = 8;
-    static constexpr int XW = 4;
     struct X { uint32_t p[4]; };
     struct Aux {};
+    struct AuxRes {};
 
     __device__ static void load_x(const uint16_t* xrow, int k0, bool active, X& xc) {
         u32x4 v = active ? *reinterpret_cast<const u32x4*>(xrow + k0) : u32x4{0, 0, 0, 0};
         xc.p[0] = v.x; xc.p[1] = v.y; xc.p[2] = v.z; xc.p[3] = v.w;
     }
-    __device__ static Aux load_aux(const GemvArgs&, int, int) { return Aux{}; }
+    static constexpr bool kStaged = false;
+    static constexpr int kStageBytes = 0;
+    __device__ static u32x4 load_stage(const GemvArgs&, int, int) { return u32x4{0, 0, 0, 0}; }
+    __device__ static Aux read_stage(const uint16_t*, const GemvArgs&, int, int) { return Aux{}; }
+    __device__ static AuxRes make_aux(const GemvArgs&, int, int) { return AuxRes{}; }
+    __device__ static uint32_t aux_voff(const GemvArgs&, int, int) { return 0; }
+    __device__ static uint32_t aux_soff(const GemvArgs&, int) { return 0; }
+    __device__ static Aux load_aux(const AuxRes&, uint32_t, uint32_t) { return Aux{}; }
 
     template <int MT>
     __device__ static void accumulate(u32x4 q, const Aux&, const X (&xc)[MT], float (&out)[MT]) {

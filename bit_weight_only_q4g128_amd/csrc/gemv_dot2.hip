@@ -34,7 +34,7 @@ template <> struct FmtTraits<FmtBf16> { static constexpr int base_cpl = 4; };
 // Per-task launch plan: lanes per row (log2), waves per row (S in 1, 2, 4),
 // row-loads per wave (R, a multiple of the in-flight batch U), first block.
 struct TaskPlan {
-    int lpr_log2, S, R, blk0;
+    int lpr_log2, S, R, blk0, staged;
 };
 
 struct TaskTable {
@@ -44,12 +44,27 @@ struct TaskTable {
     int count;
 };
 
-template <int CPL> struct Batch { static constexpr int U = (CPL >= 4) ? 1 : (CPL == 2 ? 2 : 4); };
+template <int CPL> struct Batch { static constexpr int U = (CPL >= 4) ? 1 : 2; };
 
-template <class F, int MT, int CPL>
+// Sum over aligned groups of 2^L lanes with L known at compile time.
+template <int L>
+__device__ __forceinline__ float group_sum_fixed(float v) {
+    if (L >= 1) v += dpp<0xB1>(v);
+    if (L >= 2) v += dpp<0x4E>(v);
+    if (L >= 3) v += dpp<0x141>(v);
+    if (L >= 4) v += dpp<0x140>(v);
+    if (L >= 5) v += dpp<0x142, 0xA>(v);
+    if (L >= 6) v += dpp<0x143, 0xC>(v);
+    return v;
+}
+
+// LPRT: log2(lanes per row) fixed at compile time, or 0 for "from the plan".
+template <class F, int MT, int CPL, int LPRT>
 __global__ __launch_bounds__(256) void gemv_dot2_kernel(TaskTable tt) {
     constexpr int U = Batch<CPL>::U;
     __shared__ float red[kWavesPerWG][kMaxR][MT];
+    // per wave, two batches of staged group parameters (ping-pong)
+    __shared__ __attribute__((aligned(16))) uint8_t stage[F::kStaged ? kWavesPerWG : 1][2][F::kStageBytes > 0 ? F::kStageBytes : 16];
 
     // which task owns this workgroup
     int t = 0;
@@ -57,11 +72,13 @@ __global__ __launch_bounds__(256) void gemv_dot2_kernel(TaskTable tt) {
     for (int i = 1; i < kMaxTasks; ++i) t += ((int)blockIdx.x >= tt.blk0[i]) ? 1 : 0;
     const GemvArgs a = tt.a[t];
     const TaskPlan tp = tt.p[t];
-    const int lpr_log2 = tp.lpr_log2, S = tp.S, R = tp.R;
+    const int lpr_log2 = LPRT > 0 ? LPRT : tp.lpr_log2;
+    const int S = tp.S, R = tp.R;
+    const bool staged = F::kStaged && tp.staged;
     const int blk = blockIdx.x - tp.blk0;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int LPR = 1 << lpr_log2;
     const int RPL = 64 >> lpr_log2;
     const int RG = kWavesPerWG / S;
@@ -70,52 +87,62 @@ __global__ __launch_bounds__(256) void gemv_dot2_kernel(TaskTable tt) {
     const int sub = lane >> lpr_log2;
     const int li = lane & (LPR - 1);
     const int C = a.K / F::WPC;
-    const size_t rowbytes = (size_t)C * 16;
+    const uint32_t rowbytes = (uint32_t)C * 16;
     const int rowbase = (blk * RG + rg) * R * RPL;
+    int nrows = a.N - rowbase;                    // rows of this wave that exist
+    nrows = nrows < 0 ? 0 : (nrows > R * RPL ? R * RPL : nrows);
+
+    // Buffer resources start at the wave's first row and end at its last
+    // existing row: lanes whose row is past N read zeros.
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)rowbase * rowbytes, (uint32_t)nrows * rowbytes);
+    const typename F::AuxRes rx = F::make_aux(a, rowbase, nrows);
 
     int ch[CPL];
     bool act[CPL];
+    uint32_t vw[CPL], vx[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = (j * S + s) * LPR + li;
         act[j] = c < C;
         ch[j] = act[j] ? c : C - 1;
+        vw[j] = (uint32_t)sub * rowbytes + (uint32_t)ch[j] * 16;
+        vx[j] = F::aux_voff(a, sub, ch[j]);
     }
 
-    auto load_batch = [&](int i0, u32x4 (&q)[U][CPL], typename F::Aux (&ax)[U][CPL], int (&rows)[U]) {
+    // The whole offset goes in the lane offset (which the range check covers);
+    // the scalar offset stays 0.
+    auto load = [&](int i0, u32x4 (&q)[U][CPL], typename F::Aux (&ax)[U][CPL], u32x4& stg) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            rows[u] = rowbase + (i0 + u) * RPL + sub;
-            const int rc = rows[u] < a.N ? rows[u] : a.N - 1;
+            const int r = (i0 + u) * RPL;
+            const uint32_t sw = (uint32_t)r * rowbytes;
+            const uint32_t sx = F::aux_soff(a, r);
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                q[u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.w + (size_t)rc * rowbytes + (size_t)ch[j] * 16));
-                ax[u][j] = F::load_aux(a, rc, ch[j]);
+                q[u][j] = buf_load16(rw, vw[j] + sw, 0);
+                if (!staged) ax[u][j] = F::load_aux(rx, vx[j] + sx, 0);
             }
         }
+        if (staged) stg = F::load_stage(a, rowbase + i0 * RPL, lane);
     };
 
-    // weights of the first batch go out before the activations
-    u32x4 q[U][CPL];
-    typename F::Aux ax[U][CPL];
-    int rows[U];
-    load_batch(0, q, ax, rows);
-
     typename F::X xc[CPL][MT];
+    auto compute = [&](int i0, int buf, const u32x4 (&q)[U][CPL], typename F::Aux (&ax)[U][CPL], const u32x4& stg) {
+        if (staged) {
+            // one wave writes and reads its own slot: LDS keeps a wave's
+            // accesses in order, so no barrier is needed
+            uint8_t* slot = stage[F::kStaged ? wave : 0][buf];
+            *reinterpret_cast<u32x4*>(slot + lane * 16) = stg;
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = 0; j < CPL; ++j)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            F::load_x(a.x + (size_t)(m < a.M ? m : 0) * a.K, ch[j] * F::WPC, act[j] && m < a.M, xc[j][m]);
-
-    for (int i0 = 0; i0 < R; i0 += U) {
-        u32x4 qn[U][CPL];
-        typename F::Aux axn[U][CPL];
-        int rowsn[U];
-        const bool more = i0 + U < R;
-        if (more) load_batch(i0 + U, qn, axn, rowsn);
+                for (int j = 0; j < CPL; ++j)
+                    ax[u][j] = F::read_stage(reinterpret_cast<const uint16_t*>(slot), a, u * RPL + sub, ch[j]);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int row = rowbase + (i0 + u) * RPL + sub;
             float out[MT];
 #pragma unroll
             for (int m = 0; m < MT; ++m) out[m] = 0.f;
@@ -124,24 +151,41 @@ __global__ __launch_bounds__(256) void gemv_dot2_kernel(TaskTable tt) {
                 if (act[j]) F::template accumulate<MT>(q[u][j], ax[u][j], xc[j], out);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const float v = group_sum(out[m], LPR);
+                const float v = LPRT > 0 ? group_sum_fixed<LPRT>(out[m]) : group_sum(out[m], LPR);
                 if (li == LPR - 1) {
                     if (S == 1) {
-                        if (rows[u] < a.N && m < a.M) a.y[(size_t)m * a.N + rows[u]] = f32_to_bf16(F::finish(a, v));
+                        if (row < a.N && m < a.M) a.y[(size_t)m * a.N + row] = f32_to_bf16(F::finish(a, v));
                     } else {
                         red[wave][i0 + u][m] = v;
                     }
                 }
             }
         }
-        if (more) {
+    };
+
+    // weights of the first batch go out before the activations
+    u32x4 qa[U][CPL], qb[U][CPL];
+    typename F::Aux aa[U][CPL], ab[U][CPL];
+    u32x4 sa, sb;
+    load(0, qa, aa, sa);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                rows[u] = rowsn[u];
+    for (int j = 0; j < CPL; ++j)
 #pragma unroll
-                for (int j = 0; j < CPL; ++j) { q[u][j] = qn[u][j]; ax[u][j] = axn[u][j]; }
-            }
-        }
+        for (int m = 0; m < MT; ++m)
+            F::load_x(a.x + (size_t)(m < a.M ? m : 0) * a.K, ch[j] * F::WPC, act[j] && m < a.M, xc[j][m]);
+
+    // ping-pong: the next batch is in flight while the current one is used
+    for (int i0 = 0;;) {
+        const bool nb = i0 + U < R;
+        if (nb) load(i0 + U, qb, ab, sb);
+        compute(i0, 0, qa, aa, sa);
+        if (!nb) break;
+        i0 += U;
+        const bool na = i0 + U < R;
+        if (na) load(i0 + U, qa, aa, sa);
+        compute(i0, 1, qb, ab, sb);
+        if (!na) break;
+        i0 += U;
     }
 
     if (S > 1) {
@@ -178,7 +222,7 @@ bool make_plan(int N, int K, TaskPlan& p, int& cpl_out, int& blocks) {
     while ((1 << lpr_log2) < lpr) ++lpr_log2;
     const int RPL = 64 / lpr;
     const int loads = (N + RPL - 1) / RPL;
-    const int U = (cpl >= 4) ? 1 : (cpl == 2 ? 2 : 4);
+    const int U = (cpl >= 4) ? 1 : 2;
     // Aim for ~8 waves per CU; small matrices get one batch per wave.
     const int target_waves = 2048;
     int R = (int)(((long)loads * S + target_waves - 1) / target_waves);
@@ -189,28 +233,31 @@ bool make_plan(int N, int K, TaskPlan& p, int& cpl_out, int& blocks) {
     p.lpr_log2 = lpr_log2;
     p.S = S;
     p.R = R;
+    p.staged = 0;
     cpl_out = cpl;
     blocks = (loads + R * RG - 1) / (R * RG);
     return true;
 }
 
 template <class F, int MT, int CPL>
-hipError_t launch_mt(const TaskTable& tt, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((gemv_dot2_kernel<F, MT, CPL>), dim3(grid), dim3(256), 0, st, tt);
-    return hipGetLastError();
+hipError_t launch_mt(const TaskTable& tt, int grid, bool lpr64, hipStream_t st) {
+    // rows of 64 lanes (K = 2048 / 8192 for the 4-bit formats) get the
+    // straight-line reduction; batch tiles above 4 rows share the generic one
+    if (lpr64 && MT <= 4) return launch_kernel(gemv_dot2_kernel<F, MT, CPL, 6>, dim3(grid), dim3(256), 0, st, tt);
+    return launch_kernel(gemv_dot2_kernel<F, MT, CPL, 0>, dim3(grid), dim3(256), 0, st, tt);
 }
 
 template <class F, int CPL>
-hipError_t launch_cpl(const TaskTable& tt, int M, int grid, hipStream_t st) {
+hipError_t launch_cpl(const TaskTable& tt, int M, int grid, bool lpr64, hipStream_t st) {
     switch (M) {
-        case 1: return launch_mt<F, 1, CPL>(tt, grid, st);
-        case 2: return launch_mt<F, 2, CPL>(tt, grid, st);
-        case 3: return launch_mt<F, 3, CPL>(tt, grid, st);
-        case 4: return launch_mt<F, 4, CPL>(tt, grid, st);
-        case 5: return launch_mt<F, 5, CPL>(tt, grid, st);
-        case 6: return launch_mt<F, 6, CPL>(tt, grid, st);
-        case 7: return launch_mt<F, 7, CPL>(tt, grid, st);
-        default: return launch_mt<F, 8, CPL>(tt, grid, st);
+        case 1: return launch_mt<F, 1, CPL>(tt, grid, lpr64, st);
+        case 2: return launch_mt<F, 2, CPL>(tt, grid, lpr64, st);
+        case 3: return launch_mt<F, 3, CPL>(tt, grid, lpr64, st);
+        case 4: return launch_mt<F, 4, CPL>(tt, grid, lpr64, st);
+        case 5: return launch_mt<F, 5, CPL>(tt, grid, lpr64, st);
+        case 6: return launch_mt<F, 6, CPL>(tt, grid, lpr64, st);
+        case 7: return launch_mt<F, 7, CPL>(tt, grid, lpr64, st);
+        default: return launch_mt<F, 8, CPL>(tt, grid, lpr64, st);
     }
 }
 
@@ -237,6 +284,10 @@ hipError_t launch_fmt(const GemvArgs* tasks, int count, hipStream_t st) {
                 a.x = tasks[i].x + (size_t)m0 * tasks[i].K;
                 a.y = tasks[i].y + (size_t)m0 * tasks[i].N;
                 p.blk0 = grid;
+                // int4 group parameters go through LDS when their 16-byte
+                // loads are aligned (see FmtQ4)
+                p.staged = (F::kStaged && (tasks[i].K % 1024) == 0 && (reinterpret_cast<uintptr_t>(tasks[i].scale) % 16) == 0 &&
+                            (reinterpret_cast<uintptr_t>(tasks[i].minv) % 16) == 0) ? 1 : 0;
                 tt.blk0[tt.count] = grid;
                 tt.a[tt.count] = a;
                 tt.p[tt.count] = p;
@@ -244,9 +295,11 @@ hipError_t launch_fmt(const GemvArgs* tasks, int count, hipStream_t st) {
                 grid += blocks;
             }
             if (tt.count == 0) break;
+            bool lpr64 = true;
+            for (int i = 0; i < tt.count; ++i) lpr64 = lpr64 && tt.p[i].lpr_log2 == 6;
             const int mt = (M - m0) < kMaxMT ? (M - m0) : kMaxMT;
-            hipError_t e = (pass == 0) ? launch_cpl<F, FmtTraits<F>::base_cpl>(tt, mt, grid, st)
-                                       : launch_cpl<F, 2 * FmtTraits<F>::base_cpl>(tt, mt, grid, st);
+            hipError_t e = (pass == 0) ? launch_cpl<F, FmtTraits<F>::base_cpl>(tt, mt, grid, lpr64, st)
+                                       : launch_cpl<F, 2 * FmtTraits<F>::base_cpl>(tt, mt, grid, lpr64, st);
             if (e != hipSuccess) return e;
         }
     }

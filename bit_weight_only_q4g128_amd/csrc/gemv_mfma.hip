@@ -360,17 +360,13 @@ hipError_t launch_one(Fmt fmt, const GemvArgs& a, hipStream_t st) {
     switch (fmt) {
         case kFmtQ4: {
             const size_t shmem = (size_t)(a.K >> 7) * 16 * RT * sizeof(uint32_t) + red_bytes;
-            hipLaunchKernelGGL((q4_mfma_kernel<MTILES, RT>), dim3(grid), dim3(256), shmem, st, a);
-            break;
+            return launch_kernel(q4_mfma_kernel<MTILES, RT>, dim3(grid), dim3(256), shmem, st, a);
         }
         case kFmtNvfp4:
-            hipLaunchKernelGGL((nvfp4_mfma_kernel<MTILES, RT>), dim3(grid), dim3(256), red_bytes, st, a);
-            break;
+            return launch_kernel(nvfp4_mfma_kernel<MTILES, RT>, dim3(grid), dim3(256), red_bytes, st, a);
         default:
-            hipLaunchKernelGGL((bf16_mfma_kernel<MTILES, RT>), dim3(grid), dim3(256), red_bytes, st, a);
-            break;
+            return launch_kernel(bf16_mfma_kernel<MTILES, RT>, dim3(grid), dim3(256), red_bytes, st, a);
     }
-    return hipGetLastError();
 }
 
 // Two row tiles per workgroup once that still leaves >= 256 workgroups (and

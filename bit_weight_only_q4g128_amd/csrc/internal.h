@@ -2,12 +2,33 @@
 // translation units.  Everything here assumes the arguments were validated.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "formats.h"
 
 namespace q4 {
+
+// Caller-owned events that the next kernel launch of the calling thread
+// records at its start and end (set through q4gemv_time_next_launch).
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& pending_launch_events();
+
+template <typename Kernel, typename... Args>
+hipError_t launch_kernel(Kernel k, dim3 grid, dim3 block, size_t shmem, hipStream_t st, Args... args) {
+    LaunchEvents& ev = pending_launch_events();
+    if (ev.start || ev.stop) {
+        const LaunchEvents e = ev;
+        ev = LaunchEvents{};
+        hipExtLaunchKernelGGL(k, grid, block, shmem, st, e.start, e.stop, 0, args...);
+    } else {
+        hipLaunchKernelGGL(k, grid, block, shmem, st, args...);
+    }
+    return hipGetLastError();
+}
 
 enum Fmt { kFmtQ4 = 0, kFmtNvfp4 = 1, kFmtBf16 = 2 };
 

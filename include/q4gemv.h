@@ -131,6 +131,15 @@ int q4g128_dequant_f32(const uint8_t* qweight, const uint16_t* scale, const uint
 int nvfp4g16_dequant_f32(const uint8_t* qweight, const uint8_t* scale_e4m3, float global_scale, int N, int K, float* w,
                          void* stream);
 
+/*
+ * Kernel timing without host gaps: the next kernel launched by the calling
+ * thread through this library records start_event when it begins executing
+ * and stop_event when it ends (hipExtLaunchKernel).  Both are caller-owned
+ * hipEvent_t handles (either may be NULL); they apply to one launch only, so
+ * time calls that launch one kernel.  Host only, always returns Q4_OK.
+ */
+int q4gemv_time_next_launch(void* start_event, void* stop_event);
+
 /* Name of the kernel a call would run ("dot2", "mfma"); host only, never fails. */
 const char* q4gemv_variant_name(int fmt, int variant, int M, int N, int K);
 

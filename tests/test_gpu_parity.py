@@ -316,3 +316,50 @@ def test_q4_grouped_mixed_k(q4):
         w32 = oracle.q4g128_dequant_f32(m[0].numpy(), synth.bits16(m[1]), synth.bits16(m[2]))
         xb = x_bits(x.cpu())
         check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"mixed N={N} K={K}")
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_q4_scale_arrays_only_2byte_aligned(q4, variant):
+    # scale/min as views one element into larger buffers: 2-byte but not
+    # 16-byte aligned, so the kernels must not assume wider alignment
+    N, K, M = 300, 2048, 2
+    qw, sc, mn = synth.q4_matrix(N, K, ("misaligned",))
+    big_s = torch.zeros(sc.numel() + 8, dtype=torch.float16, device="cuda")
+    big_m = torch.zeros(mn.numel() + 8, dtype=torch.float16, device="cuda")
+    big_s[1:1 + sc.numel()] = sc.flatten().cuda()
+    big_m[1:1 + mn.numel()] = mn.flatten().cuda()
+    s_view = big_s[1:1 + sc.numel()].view(N, K // 128)
+    m_view = big_m[1:1 + mn.numel()].view(N, K // 128)
+    assert s_view.data_ptr() % 16 != 0
+    x = gpu(synth.x_bf16(M, K, ("misaligned-x",)))
+    y = q4.q4g128_gemv(x, gpu(qw), s_view, m_view, variant=variant)
+    y_ref = q4.q4g128_gemv(x, gpu(qw), gpu(sc), gpu(mn), variant=variant)
+    assert torch.equal(y, y_ref)
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    xb = x_bits(x.cpu())
+    check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, "misaligned scales")
+
+
+def test_launch_timing_hook(q4):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    a, z = ctypes.c_void_p(), ctypes.c_void_p()
+    assert hip.hipEventCreate(ctypes.byref(a)) == 0 and hip.hipEventCreate(ctypes.byref(z)) == 0
+    qw, sc, mn = (gpu(t) for t in synth.q4_matrix(8192, 2048, ("timing",)))
+    x = gpu(synth.x_bf16(1, 2048, ("timing-x",)))
+    q4.q4g128_gemv(x, qw, sc, mn)
+    torch.cuda.synchronize()
+    assert q4.lib.q4gemv_time_next_launch(a, z) == 0
+    y = q4.q4g128_gemv(x, qw, sc, mn)
+    y2 = q4.q4g128_gemv(x, qw, sc, mn)     # not timed: the events are used once
+    torch.cuda.synchronize()
+    assert hip.hipEventSynchronize(z) == 0
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), a, z) == 0
+    assert 0.0 < ms.value < 5.0, ms.value
+    assert torch.equal(y, y2)
+    hip.hipEventDestroy(a)
+    hip.hipEventDestroy(z)
