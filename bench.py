@@ -230,11 +230,11 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_q4_grouped_M1_traffic.json"
 
 
 def csrc_digest():
-    """sha256 over the HIP sources and headers the measured kernel is built from."""
-    import glob
+    """sha256 over the sources the measured packed-dot kernel is built from."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "bit_weight_only_q4g128_amd", "csrc", "*")))
+    files = [os.path.join(ROOT, "bit_weight_only_q4g128_amd", "csrc", n)
+             for n in ("common.h", "formats.h", "internal.h", "gemv_dot2.hip")]
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
@@ -283,6 +283,8 @@ def main():
     ap.add_argument("--head", choices=("full", "slice"), default="full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
+    ap.add_argument("--modes", default="M1_grouped,M1_plain,M48_grouped,M48_plain",
+                    help="comma list of timed modes; M1_grouped is always timed (it is the headline value)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -300,9 +302,12 @@ def main():
         return
     wl = Workload(q4, synth, torch, head_rows)
 
+    modes = {"M1_grouped"} | set(m for m in args.modes.split(",") if m)
     res = {}
     for M in (1, 48):
         for mode in ("grouped", "plain"):
+            if f"M{M}_{mode}" not in modes:
+                continue
             ms, g = time_graph(torch, wl, M, args.steps, args.warmup, mode)
             by = wl.step_bytes(M)
             res[(M, mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(wl.launches(M, mode)))

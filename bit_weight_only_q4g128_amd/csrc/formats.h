@@ -80,11 +80,14 @@ struct FmtQ4 {
     // wave) cannot express without a readfirstlane loop.  With K % 1024 == 0
     // every array is a whole number of 16-byte pieces, so the bound check
     // per piece is exact.
-    __device__ static u32x4 load_stage(const GemvArgs& a, int row0, int lane) {
+    // rows: rows in the batch (the block is rows * K/128 fp16 per array).
+    __device__ static u32x4 load_stage(const GemvArgs& a, int row0, int rows, int lane) {
         const size_t G = (size_t)(a.K >> 7);
-        const size_t off = (size_t)row0 * G * 2 + (size_t)(lane & 31) * 16;
+        const uint32_t piece = (uint32_t)(lane & 31) * 16;
+        const size_t off = (size_t)row0 * G * 2 + piece;
         const uint8_t* base = reinterpret_cast<const uint8_t*>(lane < 32 ? a.scale : a.minv);
-        return off < (size_t)a.N * G * 2 ? *reinterpret_cast<const u32x4*>(base + off) : u32x4{0, 0, 0, 0};
+        const bool ok = piece < (uint32_t)rows * G * 2 && off < (size_t)a.N * G * 2;
+        return ok ? *reinterpret_cast<const u32x4*>(base + off) : u32x4{0, 0, 0, 0};
     }
     // row_in_batch: row offset inside the staged batch
     __device__ static Aux read_stage(const uint16_t* st, const GemvArgs& a, int row_in_batch, int chunk) {
@@ -165,7 +168,7 @@ struct FmtNvfp4 {
 
     static constexpr bool kStaged = false;
     static constexpr int kStageBytes = 0;
-    __device__ static u32x4 load_stage(const GemvArgs&, int, int) { return u32x4{0, 0, 0, 0}; }
+    __device__ static u32x4 load_stage(const GemvArgs&, int, int, int) { return u32x4{0, 0, 0, 0}; }
     __device__ static Aux read_stage(const uint16_t*, const GemvArgs&, int, int) { return Aux{}; }
 
     __device__ static AuxRes make_aux(const GemvArgs& a, int row0, int rows) {
@@ -228,7 +231,7 @@ struct FmtBf16 {
     }
     static constexpr bool kStaged = false;
     static constexpr int kStageBytes = 0;
-    __device__ static u32x4 load_stage(const GemvArgs&, int, int) { return u32x4{0, 0, 0, 0}; }
+    __device__ static u32x4 load_stage(const GemvArgs&, int, int, int) { return u32x4{0, 0, 0, 0}; }
     __device__ static Aux read_stage(const uint16_t*, const GemvArgs&, int, int) { return Aux{}; }
     __device__ static AuxRes make_aux(const GemvArgs&, int, int) { return AuxRes{}; }
     __device__ static uint32_t aux_voff(const GemvArgs&, int, int) { return 0; }

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void gemv_dot2_kernel(TaskTable tt) {
                 if (!staged) ax[u][j] = F::load_aux(rx, vx[j] + sx, 0);
             }
         }
-        if (staged) stg = F::load_stage(a, rowbase + i0 * RPL, lane);
+        if (staged) stg = F::load_stage(a, rowbase + i0 * RPL, U * RPL, lane);
     };
 
     typename F::X xc[CPL][MT];
