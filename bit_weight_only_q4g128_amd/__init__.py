@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib",
-    "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
+    "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4gemv.so")
@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with: python bit_weight_only_q4g128_amd/_build.py")
 lib = ctypes.CDLL(LIB_PATH)
 
-VARIANT_AUTO, VARIANT_DOT2, VARIANT_MFMA = 0, 1, 2
+VARIANT_AUTO, VARIANT_DOT2, VARIANT_MFMA, VARIANT_STREAM = 0, 1, 2, 3
 FMT_Q4G128, FMT_NVFP4G16, FMT_BF16 = 0, 1, 2
 
 _p, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float

@@ -35,20 +35,30 @@ int check_common(const void* x, int M, int K, int N, const void* y) {
     return Q4_OK;
 }
 
-bool variant_ok(int variant) { return variant == Q4_VARIANT_AUTO || variant == Q4_VARIANT_DOT2 || variant == Q4_VARIANT_MFMA; }
+bool variant_ok(int variant) {
+    return variant == Q4_VARIANT_AUTO || variant == Q4_VARIANT_DOT2 || variant == Q4_VARIANT_MFMA || variant == Q4_VARIANT_STREAM;
+}
 
-// Kernel choice for Q4_VARIANT_AUTO.  Small batches stream through the
-// packed-dot kernel; larger ones go to the matrix cores.
+// Kernel choice for Q4_VARIANT_AUTO.  Small batches on rows of 1-4 KB go to
+// the streaming kernel, other small batches to the packed-dot kernel, larger
+// batches to the matrix cores.
 int pick(Fmt fmt, int variant, int M, int K) {
     if (variant == Q4_VARIANT_DOT2) return q4::dot2_supported(fmt, K) ? Q4_VARIANT_DOT2 : -1;
     if (variant == Q4_VARIANT_MFMA) return Q4_VARIANT_MFMA;
+    if (variant == Q4_VARIANT_STREAM) return q4::stream_supported(fmt, M, K) ? Q4_VARIANT_STREAM : -1;
+    if (M <= 4 && q4::stream_supported(fmt, M, K)) return Q4_VARIANT_STREAM;
     if (M <= 4 && q4::dot2_supported(fmt, K)) return Q4_VARIANT_DOT2;
     return Q4_VARIANT_MFMA;
 }
 
 int run(Fmt fmt, int chosen, const GemvArgs* a, int count, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = (chosen == Q4_VARIANT_DOT2) ? q4::launch_dot2(fmt, a, count, s) : q4::launch_mfma(fmt, a, count, s);
+    hipError_t e;
+    switch (chosen) {
+        case Q4_VARIANT_DOT2: e = q4::launch_dot2(fmt, a, count, s); break;
+        case Q4_VARIANT_STREAM: e = q4::launch_stream(fmt, a, count, s); break;
+        default: e = q4::launch_mfma(fmt, a, count, s); break;
+    }
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 
@@ -111,15 +121,20 @@ int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant,
     if (!variant_ok(variant)) return Q4_EVARIANT;
     GemvArgs a[q4::kMaxTasks];
     Range in[q4::kMaxTasks][4], out[q4::kMaxTasks];
-    int chosen = -2;
+    // one kernel family for the whole group: the matrix cores if any task
+    // needs them, the streaming kernel if every task can use it, else the
+    // packed-dot kernel (or the matrix cores where that cannot run)
+    int n_mfma = 0, n_stream = 0;
     for (int i = 0; i < count; ++i) {
         const q4g128_task& t = tasks[i];
         int rc = check_q4(t.x, M, t.K, t.qweight, t.scale, t.minv, t.N, t.y, a[i], in[i], out[i]);
         if (rc) return rc;
         const int c = pick(q4::kFmtQ4, variant, M, t.K);
         if (c < 0) return Q4_EVARIANT;
-        if (chosen == -2 || c == Q4_VARIANT_MFMA) chosen = c;   // one kernel family for the whole group
+        n_mfma += c == Q4_VARIANT_MFMA;
+        n_stream += c == Q4_VARIANT_STREAM;
     }
+    int chosen = n_mfma ? Q4_VARIANT_MFMA : (n_stream == count ? Q4_VARIANT_STREAM : Q4_VARIANT_DOT2);
     if (chosen == Q4_VARIANT_DOT2) {
         for (int i = 0; i < count; ++i)
             if (!q4::dot2_supported(q4::kFmtQ4, tasks[i].K)) chosen = Q4_VARIANT_MFMA;
@@ -213,6 +228,7 @@ const char* q4gemv_variant_name(int fmt, int variant, int M, int N, int K) {
     const int c = pick(static_cast<Fmt>(fmt), variant, M, K);
     if (c == Q4_VARIANT_DOT2) return "dot2";
     if (c == Q4_VARIANT_MFMA) return "mfma";
+    if (c == Q4_VARIANT_STREAM) return "stream";
     return "invalid";
 }
 
@@ -229,6 +245,6 @@ const char* q4gemv_strerror(int status) {
     }
 }
 
-int q4gemv_version(void) { return 100; }
+int q4gemv_version(void) { return 110; }
 
 }  // extern "C"

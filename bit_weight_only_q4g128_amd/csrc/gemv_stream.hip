@@ -1,0 +1,298 @@
+// Streaming GEMV for decode batches M <= 4 (gfx950).
+//
+// Shaped like a plain streaming read: every lane issues all of its 16-byte
+// weight loads (4 per lane, 4 KB per wave) at once, right after two small
+// shared loads, and nothing on the weight path waits for anything else.
+//
+//   * A workgroup (4 waves) owns 16 / CPL consecutive rows, where CPL =
+//     chunks per lane = row bytes / 1 KB (1, 2 or 4: K = 2048, 4096, 8192 for
+//     the 4-bit formats).  A wave owns 4 / CPL whole rows; load i of a lane is
+//     chunk (i % CPL) * 64 + lane of row i / CPL, so every wave-wide load is
+//     1 KB of consecutive bytes.
+//   * The activations x[0..M) are loaded once per workgroup, turned into the
+//     operand layout the packed dot products need (plus per-chunk sums for
+//     int4) and kept in LDS; so are the group parameters of the workgroup's
+//     rows.  Both loads go out before the weight loads, so waiting for them
+//     does not wait for the weights.
+//   * Rows past N read zeros through buffer-resource range checks and are
+//     not stored.
+//
+// One launch serves up to kMaxTasks GEMVs of one format and batch size; the
+// workgroups of a launch are split between tasks by a prefix table.
+#include <type_traits>
+
+#include "internal.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kLoads = 4;    // 16-byte weight loads per lane
+constexpr int kWaves = 4;    // waves per workgroup
+
+struct StreamTable {
+    int blk0[kMaxTasks];     // first workgroup of each task (unused: INT_MAX)
+    int cpl_log2[kMaxTasks];
+    GemvArgs a[kMaxTasks];
+    int count;
+};
+
+template <class F> struct Stream;
+
+// int4 g128: LDS holds x as 128+code-matching BF16 pairs [M][K], the chunk
+// sums [M][K/32] (fp32) and the rows' (scale | min << 16) words [rows][K/128].
+template <> struct Stream<FmtQ4> {
+    static constexpr int kAuxPerThread = 1;   // (16 / CPL rows) * (16 * CPL groups) = 256 words
+    __host__ __device__ static int x_bytes(int MT, int K) { return MT * K * 2; }
+    __host__ __device__ static int sum_bytes(int MT, int K) { return MT * (K / 32) * 4; }
+    __host__ __device__ static int aux_bytes() { return 256 * 4; }
+};
+// NVFP4: x raw [M][K]; the rows' e4m3 scale bytes [rows][K/16].
+template <> struct Stream<FmtNvfp4> {
+    static constexpr int kAuxPerThread = 4;   // (16 / CPL rows) * (128 * CPL bytes) = 2048 bytes = 1024 halves
+    __host__ __device__ static int x_bytes(int MT, int K) { return MT * K * 2; }
+    __host__ __device__ static int sum_bytes(int, int) { return 0; }
+    __host__ __device__ static int aux_bytes() { return 1024 * 2; }
+};
+// BF16: x raw [M][K], nothing else.
+template <> struct Stream<FmtBf16> {
+    static constexpr int kAuxPerThread = 0;
+    __host__ __device__ static int x_bytes(int MT, int K) { return MT * K * 2; }
+    __host__ __device__ static int sum_bytes(int, int) { return 0; }
+    __host__ __device__ static int aux_bytes() { return 0; }
+};
+
+template <class F>
+__host__ __device__ inline int stream_shmem(int MT, int K) {
+    return Stream<F>::x_bytes(MT, K) + Stream<F>::sum_bytes(MT, K) + Stream<F>::aux_bytes();
+}
+
+// 16-byte x pieces per thread (x is MT*K*2 bytes over 256 threads)
+template <class F> __host__ __device__ inline int x_pieces(int MT, int K) { return (MT * K / 8 + 255) / 256; }
+
+template <class F, int MT>
+__global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int kXP = MT * 4;   // most x pieces a thread stages (K <= 8192 for the 4-bit formats)
+
+    int t = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxTasks; ++i) t += ((int)blockIdx.x >= tt.blk0[i]) ? 1 : 0;
+    const GemvArgs a = tt.a[t];
+    const int cl = tt.cpl_log2[t];
+    const int blk = blockIdx.x - tt.blk0[t];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int CPL = 1 << cl;
+    const int C = 64 << cl;                      // chunks per row
+    const uint32_t rowbytes = (uint32_t)C * 16;
+    const int rpw = kLoads >> cl;                // rows per wave
+    const int RW = kWaves * rpw;                 // rows per workgroup
+    const int row0 = blk * RW;
+    const int wrow0 = row0 + wave * rpw;
+    const int K = a.K;
+
+    // --- 1. shared inputs: x pieces and group parameters into registers
+    const int nxp = x_pieces<F>(MT, K);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(MT * K * 2));
+    u32x4 xr[kXP];
+#pragma unroll
+    for (int i = 0; i < kXP; ++i)
+        xr[i] = i < nxp ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (tid + 256 * i) * 16, 0, 0))
+                        : u32x4{0, 0, 0, 0};
+    int wg_rows = a.N - row0;
+    wg_rows = wg_rows < 0 ? 0 : (wg_rows > RW ? RW : wg_rows);
+    uint32_t auxr[Stream<F>::kAuxPerThread > 0 ? Stream<F>::kAuxPerThread : 1];
+    if constexpr (Stream<F>::kAuxPerThread > 0) {
+        if constexpr (std::is_same<F, FmtQ4>::value) {
+            const int G = K >> 7;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + (size_t)row0 * G, (uint32_t)(wg_rows * G * 2));
+            const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)(wg_rows * G * 2));
+            auxr[0] = (uint32_t)buf_load2(rs, tid * 2, 0) | ((uint32_t)buf_load2(rm, tid * 2, 0) << 16);
+        } else {
+            const int SB = K >> 4;   // scale bytes per row
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale8 + (size_t)row0 * SB, (uint32_t)(wg_rows * SB));
+#pragma unroll
+            for (int i = 0; i < Stream<F>::kAuxPerThread; ++i) auxr[i] = buf_load2(rs, (tid + 256 * i) * 2, 0);
+        }
+    }
+
+    // --- 2. the weights: all of this lane's loads at once
+    int nrows = a.N - wrow0;
+    nrows = nrows < 0 ? 0 : (nrows > rpw ? rpw : nrows);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)wrow0 * rowbytes, (uint32_t)nrows * rowbytes);
+    u32x4 q[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const uint32_t r = (uint32_t)(i >> cl), j = (uint32_t)(i & (CPL - 1));
+        q[i] = buf_load16(rw, r * rowbytes + (j * 64 + lane) * 16, 0);
+    }
+
+    // --- 3. stage x (and int4 chunk sums) and the group parameters in LDS
+    uint8_t* xs = lds;
+    float* sums = reinterpret_cast<float*>(lds + Stream<F>::x_bytes(MT, K));
+    uint8_t* auxs = lds + Stream<F>::x_bytes(MT, K) + Stream<F>::sum_bytes(MT, K);
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        if (i < nxp) {
+            const int p = tid + 256 * i;   // piece index over [MT][K/8]
+            const bool in = p < MT * K / 8;
+            if constexpr (std::is_same<F, FmtQ4>::value) {
+                uint32_t pr[4];
+                xq4_pairs(xr[i].x, xr[i].y, xr[i].z, xr[i].w, pr);
+                if (in) *reinterpret_cast<u32x4*>(xs + p * 16) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+                // chunk (32 activations) = 4 consecutive pieces = 4 consecutive lanes
+                float s = dot2(xr[i].x, 0x3F803F80u, 0.f);
+                s = dot2(xr[i].y, 0x3F803F80u, s);
+                s = dot2(xr[i].z, 0x3F803F80u, s);
+                s = dot2(xr[i].w, 0x3F803F80u, s);
+                s += dpp<0xB1>(s);
+                s += dpp<0x4E>(s);
+                if (in && (lane & 3) == 0) sums[p >> 2] = s;
+            } else {
+                if (in) *reinterpret_cast<u32x4*>(xs + p * 16) = xr[i];
+            }
+        }
+    }
+    if constexpr (std::is_same<F, FmtQ4>::value) {
+        reinterpret_cast<uint32_t*>(auxs)[tid] = auxr[0];
+    } else if constexpr (std::is_same<F, FmtNvfp4>::value) {
+#pragma unroll
+        for (int i = 0; i < Stream<F>::kAuxPerThread; ++i) reinterpret_cast<uint16_t*>(auxs)[tid + 256 * i] = (uint16_t)auxr[i];
+    }
+    __syncthreads();
+
+    // --- 4. rows
+    const uint16_t* aux16 = reinterpret_cast<const uint16_t*>(auxs);
+    auto read_x = [&](int c, typename F::X (&xc)[MT]) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if constexpr (std::is_same<F, FmtBf16>::value) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(xs + (size_t)m * K * 2 + c * 16);
+                xc[m].p[0] = v.x; xc[m].p[1] = v.y; xc[m].p[2] = v.z; xc[m].p[3] = v.w;
+            } else {
+                const u32x4* src = reinterpret_cast<const u32x4*>(xs + (size_t)m * K * 2 + c * 64);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const u32x4 v = src[d];
+                    xc[m].p[4 * d + 0] = v.x; xc[m].p[4 * d + 1] = v.y; xc[m].p[4 * d + 2] = v.z; xc[m].p[4 * d + 3] = v.w;
+                }
+                if constexpr (std::is_same<F, FmtQ4>::value) xc[m].sum = sums[m * (K / 32) + c];
+            }
+        }
+    };
+    auto read_aux = [&](int rl, int c) {
+        typename F::Aux ax{};
+        if constexpr (std::is_same<F, FmtQ4>::value) {
+            const uint32_t v = reinterpret_cast<const uint32_t*>(auxs)[rl * (K >> 7) + (c >> 2)];
+            ax.s = f16_to_f32((uint16_t)(v & 0xFFFFu));
+            ax.m = f16_to_f32((uint16_t)(v >> 16));
+        } else if constexpr (std::is_same<F, FmtNvfp4>::value) {
+            const uint32_t b = aux16[rl * (K >> 5) + c];
+            ax.s0 = e4m3_to_f32<0>(b);
+            ax.s1 = e4m3_to_f32<1>(b);
+        }
+        return ax;
+    };
+    auto finish_row = [&](int r, float (&out)[MT]) {
+        const int row = wrow0 + r;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float v = out[m];
+            v += dpp<0xB1>(v);
+            v += dpp<0x4E>(v);
+            v += dpp<0x141>(v);
+            v += dpp<0x140>(v);
+            v += dpp<0x142, 0xA>(v);
+            v += dpp<0x143, 0xC>(v);
+            if (lane == 63 && row < a.N) a.y[(size_t)m * a.N + row] = f32_to_bf16(F::finish(a, v));
+            out[m] = 0.f;
+        }
+    };
+
+    float out[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) out[m] = 0.f;
+    if (cl == 0) {
+        // one chunk per lane: the lane's activations are the same for every row
+        typename F::X xc[MT];
+        read_x(lane, xc);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            F::template accumulate<MT>(q[i], read_aux(wave * rpw + i, lane), xc, out);
+            finish_row(i, out);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int r = i >> cl, c = (i & (CPL - 1)) * 64 + lane;
+            typename F::X xc[MT];
+            read_x(c, xc);
+            F::template accumulate<MT>(q[i], read_aux(wave * rpw + r, c), xc, out);
+            if ((i & (CPL - 1)) == CPL - 1) finish_row(r, out);
+        }
+    }
+}
+
+template <class F> int chunk_log2(int K) {
+    const int wpc = F::WPC;
+    if (K % wpc) return -1;
+    const int C = K / wpc;
+    for (int l = 0; l <= 2; ++l)
+        if (C == (64 << l)) return l;
+    return -1;
+}
+
+template <class F, int MT>
+hipError_t launch_stream_mt(const GemvArgs* tasks, int count, hipStream_t st) {
+    StreamTable tt{};
+    for (int i = 0; i < kMaxTasks; ++i) tt.blk0[i] = 0x7fffffff;
+    int grid = 0, shmem = 0;
+    for (int i = 0; i < count; ++i) {
+        const int cl = chunk_log2<F>(tasks[i].K);
+        const int rw = kWaves * (kLoads >> cl);
+        tt.blk0[i] = grid;
+        tt.cpl_log2[i] = cl;
+        tt.a[i] = tasks[i];
+        grid += (tasks[i].N + rw - 1) / rw;
+        const int sh = stream_shmem<F>(MT, tasks[i].K);
+        shmem = sh > shmem ? sh : shmem;
+    }
+    tt.count = count;
+    return launch_kernel(gemv_stream_kernel<F, MT>, dim3(grid), dim3(256), (size_t)shmem, st, tt);
+}
+
+template <class F>
+hipError_t launch_stream_fmt(const GemvArgs* tasks, int count, hipStream_t st) {
+    switch (tasks[0].M) {
+        case 1: return launch_stream_mt<F, 1>(tasks, count, st);
+        case 2: return launch_stream_mt<F, 2>(tasks, count, st);
+        case 3: return launch_stream_mt<F, 3>(tasks, count, st);
+        default: return launch_stream_mt<F, 4>(tasks, count, st);
+    }
+}
+
+template <class F> bool stream_ok(int M, int K) {
+    return M >= 1 && M <= kStreamMaxM && chunk_log2<F>(K) >= 0 && stream_shmem<F>(M, K) <= kStreamMaxShmem;
+}
+
+}  // namespace
+
+bool stream_supported(Fmt fmt, int M, int K) {
+    switch (fmt) {
+        case kFmtQ4: return stream_ok<FmtQ4>(M, K);
+        case kFmtNvfp4: return stream_ok<FmtNvfp4>(M, K);
+        default: return stream_ok<FmtBf16>(M, K);
+    }
+}
+
+hipError_t launch_stream(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s) {
+    switch (fmt) {
+        case kFmtQ4: return launch_stream_fmt<FmtQ4>(tasks, count, s);
+        case kFmtNvfp4: return launch_stream_fmt<FmtNvfp4>(tasks, count, s);
+        default: return launch_stream_fmt<FmtBf16>(tasks, count, s);
+    }
+}
+
+}  // namespace q4

@@ -42,6 +42,14 @@ constexpr int kMaxTasks = 8;
 hipError_t launch_dot2(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
 bool dot2_supported(Fmt fmt, int K);
 
+// Streaming GEMV for M <= kStreamMaxM on rows of 1, 2 or 4 KB; up to
+// kMaxTasks GEMVs per launch.  stream_supported() says whether (fmt, M, K)
+// qualifies.
+constexpr int kStreamMaxM = 4;
+constexpr int kStreamMaxShmem = 64 * 1024;
+hipError_t launch_stream(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
+bool stream_supported(Fmt fmt, int M, int K);
+
 // 16x16x32 BF16 matrix-core GEMV (any M <= 64), one launch per task.
 hipError_t launch_mfma(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
 

@@ -51,6 +51,9 @@ extern "C" {
 #define Q4_VARIANT_AUTO 0 /* pick by (M, N, K) */
 #define Q4_VARIANT_DOT2 1 /* wave-per-row packed-BF16 dot products; batch tiles of <= 8 rows */
 #define Q4_VARIANT_MFMA 2 /* 16x16x32 BF16 matrix-core tiles, batch padded to 16 */
+#define Q4_VARIANT_STREAM 3 /* M <= 4, rows of exactly 1, 2 or 4 KB (int4/NVFP4 K = 2048, 4096, 8192;
+                               BF16 K = 512, 1024, 2048): every weight load issued at once, activations
+                               and group parameters shared through LDS */
 
 /* weight formats (q4gemv_variant_name) */
 #define Q4_FMT_Q4G128 0

@@ -54,7 +54,8 @@ def q4call(x=A, M=1, K=2048, qw=A + (1 << 24), sc=A + (2 << 24), mn=A + (3 << 24
     (dict(K=2048 + 64), ESHAPE), (dict(x=A + 2), EALIGN), (dict(qw=A + (1 << 24) + 8), EALIGN),
     (dict(sc=A + (2 << 24) + 1), EALIGN), (dict(y=A + (4 << 24) + 1), EALIGN),
     (dict(y=A + (1 << 24) + 64), EALIAS), (dict(y=A + 16), EALIAS), (dict(y=A + (3 << 24)), EALIAS),
-    (dict(variant=3), EVARIANT), (dict(variant=-1), EVARIANT),
+    (dict(variant=4), EVARIANT), (dict(variant=-1), EVARIANT), (dict(variant=3, M=5), EVARIANT),
+    (dict(variant=3, K=1024), EVARIANT),
 ])
 def test_q4_validation(kw, rc):
     assert q4call(**kw) == rc
@@ -94,7 +95,11 @@ def test_dequant_validation():
 
 
 def test_variant_names():
-    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 1, 2048, 2048) == "dot2"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 1, 2048, 2048) == "stream"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 2, 2048, 8192) == "stream"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 1, 256, 512) == "dot2"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_STREAM, 5, 2048, 2048) == "invalid"
+    assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 1, 16385, 2048) == "stream"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 2048) == "mfma"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_MFMA, 1, 2048, 2048) == "mfma"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_DOT2, 3, 16385, 2048) == "dot2"

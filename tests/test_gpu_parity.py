@@ -25,7 +25,13 @@ def q4():
 
 
 VARIANTS = [1, 2]  # dot2, mfma
-VNAME = {0: "auto", 1: "dot2", 2: "mfma"}
+VNAME = {0: "auto", 1: "dot2", 2: "mfma", 3: "stream"}
+FMT = {"q4": 0, "nv": 1, "bf": 2}
+
+
+def vlist(q4, fmt, M, K):
+    """auto, dot2 and mfma, plus the streaming kernel where it accepts (M, K)."""
+    return [0, 1, 2] + ([3] if q4.variant_name(FMT[fmt], 3, M, 1, K) == "stream" else [])
 
 
 # ----------------------------------------------------------------------------
@@ -111,6 +117,47 @@ def test_bf16_onehot_bitwise(q4, variant, M):
     assert np.array_equal(y.cpu().float().numpy(), w[:, ks].T.float().numpy()), (VNAME[variant], M)
 
 
+# the streaming kernel takes rows of 1, 2 or 4 KB only
+@pytest.mark.parametrize("K", [2048, 4096, 8192])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_q4_onehot_bitwise_stream(q4, K, M):
+    if q4.variant_name(0, 3, M, 1, K) != "stream":
+        pytest.skip("activations of this (M, K) exceed the streaming kernel's LDS budget")
+    N = 37   # rows past N in the last workgroup
+    qw, sc, mn = synth.q4_matrix(N, K, ("onehot-st", K, M))
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    ks = _onehot_ks(K, M, 300 + M)
+    y = q4.q4g128_gemv(gpu(onehot_x(K, ks)), gpu(qw), gpu(sc), gpu(mn), variant=3)
+    got = y.cpu().float().numpy()
+    exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(got, exp), (K, M, np.argwhere(got != exp)[:4])
+
+
+@pytest.mark.parametrize("K", [2048, 8192])
+@pytest.mark.parametrize("M", [1, 3, 4])
+def test_nvfp4_onehot_bitwise_stream(q4, K, M):
+    if q4.variant_name(1, 3, M, 1, K) != "stream":
+        pytest.skip("activations of this (M, K) exceed the streaming kernel's LDS budget")
+    N = 21
+    qw, s8, G = synth.nvfp4_matrix(N, K, ("onehot-nv-st", K, M))
+    w32 = oracle.nvfp4g16_dequant_f32(qw.numpy(), s8.numpy(), G)
+    ks = _onehot_ks(K, M, 400 + M)
+    y = q4.nvfp4g16_gemv(gpu(onehot_x(K, ks)), gpu(qw), gpu(s8), G, variant=3)
+    gotv = torch.from_numpy(synth.bits16(y.cpu()).view(np.int16)).view(torch.bfloat16).float().numpy()
+    expv = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(gotv, expv), (K, M)
+
+
+@pytest.mark.parametrize("K", [512, 2048])
+@pytest.mark.parametrize("M", [1, 3])
+def test_bf16_onehot_bitwise_stream(q4, K, M):
+    N = 70
+    w = synth.bf16_matrix(N, K, ("onehot-bf-st", K, M))
+    ks = _onehot_ks(K, M, 500 + M)
+    y = q4.bf16_gemv(gpu(onehot_x(K, ks)), gpu(w), variant=3)
+    assert np.array_equal(y.cpu().float().numpy(), w[:, ks].T.float().numpy()), (K, M)
+
+
 # ----------------------------------------------------------------------------
 # the pages' shapes, within tolerance
 # ----------------------------------------------------------------------------
@@ -142,7 +189,7 @@ def test_q4_layer(q4, proj, M):
     N, K = synth.LAYER_SHAPES[proj]
     x = synth.x_bf16(M, K, ("layer-x", proj))
     ref = oracle.gemv_f64(x_bits(x), w32[proj])
-    for v in (0, 1, 2):
+    for v in vlist(q4, "q4", M, K):
         y = q4.q4g128_gemv(gpu(x), gpu(qw), gpu(sc), gpu(mn), variant=v)
         check_gemv(y, ref, w32[proj], x_bits(x), f"{proj} M={M} {VNAME[v]}")
 
@@ -156,13 +203,13 @@ def test_nvfp4_layer(q4, proj, M):
         w = synth.bf16_matrix(N, K, ("nv-layer", proj))
         w32 = oracle.bf16_dequant_f32(synth.bits16(w))
         ref = oracle.gemv_f64(x_bits(x), w32)
-        for v in (0, 1, 2):
+        for v in vlist(q4, "bf", M, K):
             check_gemv(q4.bf16_gemv(gpu(x), gpu(w), variant=v), ref, w32, x_bits(x), f"bf16 {proj} M={M} {VNAME[v]}")
         return
     qw, s8, G = synth.nvfp4_matrix(N, K, ("nv-layer", proj))
     w32 = oracle.nvfp4g16_dequant_f32(qw.numpy(), s8.numpy(), G)
     ref = oracle.gemv_f64(x_bits(x), w32)
-    for v in (0, 1, 2):
+    for v in vlist(q4, "nv", M, K):
         y = q4.nvfp4g16_gemv(gpu(x), gpu(qw), gpu(s8), G, variant=v)
         check_gemv(y, ref, w32, x_bits(x), f"nvfp4 {proj} M={M} {VNAME[v]}")
 
@@ -175,52 +222,53 @@ def test_bf16_head(q4, shape, M):
     x = synth.x_bf16(M, K, ("head-x", N))
     w32 = oracle.bf16_dequant_f32(synth.bits16(w))
     ref = oracle.gemv_f64(x_bits(x), w32)
-    for v in (0, 1, 2):
+    for v in vlist(q4, "bf", M, K):
         check_gemv(q4.bf16_gemv(gpu(x), gpu(w), variant=v), ref, w32, x_bits(x), f"head {N} M={M} {VNAME[v]}")
 
 
 # ----------------------------------------------------------------------------
 # edge shapes: ragged N, short/odd K, every batch size
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("N,K", [(1, 128), (7, 256), (17, 384), (65, 1536), (130, 4096), (33, 11008), (5, 16384)])
+@pytest.mark.parametrize("N,K", [(1, 128), (7, 256), (17, 384), (65, 1536), (130, 4096), (33, 11008), (5, 16384),
+                                 (1, 2048), (23, 8192), (4097, 2048)])
 def test_q4_edge_shapes(q4, N, K):
     qw, sc, mn = synth.q4_matrix(N, K, ("edge", N, K))
     w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
     for M in (1, 2, 5, 8, 9, 16, 33, 64):
         x = synth.x_bf16(M, K, ("edge-x", N, K, M))
         ref = oracle.gemv_f64(x_bits(x), w32)
-        for v in (0, 1, 2):
+        for v in vlist(q4, "q4", M, K):
             y = q4.q4g128_gemv(gpu(x), gpu(qw), gpu(sc), gpu(mn), variant=v)
             check_gemv(y, ref, w32, x_bits(x), f"edge N={N} K={K} M={M} {VNAME[v]}")
 
 
-@pytest.mark.parametrize("N,K", [(1, 32), (9, 96), (31, 160), (66, 2080)])
+@pytest.mark.parametrize("N,K", [(1, 32), (9, 96), (31, 160), (66, 2080), (3, 2048), (45, 4096), (18, 8192)])
 def test_nvfp4_edge_shapes(q4, N, K):
     qw, s8, G = synth.nvfp4_matrix(N, K, ("edge-nv", N, K))
     w32 = oracle.nvfp4g16_dequant_f32(qw.numpy(), s8.numpy(), G)
     for M in (1, 3, 8, 12, 40):
         x = synth.x_bf16(M, K, ("edge-nv-x", N, K, M))
         ref = oracle.gemv_f64(x_bits(x), w32)
-        for v in (0, 1, 2):
+        for v in vlist(q4, "nv", M, K):
             check_gemv(q4.nvfp4g16_gemv(gpu(x), gpu(qw), gpu(s8), G, variant=v), ref, w32, x_bits(x),
                        f"nv edge N={N} K={K} M={M} {VNAME[v]}")
 
 
-@pytest.mark.parametrize("N,K", [(1, 8), (3, 24), (19, 136), (40, 1000), (129, 2056)])
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 24), (19, 136), (40, 1000), (129, 2056), (1, 512), (21, 1024), (257, 2048)])
 def test_bf16_edge_shapes(q4, N, K):
     w = synth.bf16_matrix(N, K, ("edge-bf", N, K))
     w32 = oracle.bf16_dequant_f32(synth.bits16(w))
     for M in (1, 2, 7, 16, 20):
         x = synth.x_bf16(M, K, ("edge-bf-x", N, K, M))
         ref = oracle.gemv_f64(x_bits(x), w32)
-        for v in (0, 1, 2):
+        for v in vlist(q4, "bf", M, K):
             check_gemv(q4.bf16_gemv(gpu(x), gpu(w), variant=v), ref, w32, x_bits(x), f"bf edge N={N} K={K} M={M} {VNAME[v]}")
 
 
 # ----------------------------------------------------------------------------
 # invariants
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS + [3])
 def test_q4_power_of_two_scaling_is_bitwise(q4, variant):
     N, K, M = 300, 2048, 4
     qw, sc, mn = (gpu(t) for t in synth.q4_matrix(N, K, ("pow2",)))
@@ -241,7 +289,7 @@ def test_q4_row_permutation_is_bitwise(q4, variant):
     assert torch.equal(y1[:, perm.cuda()], y2)
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS + [3])
 def test_q4_repeat_runs_are_bitwise_identical(q4, variant):
     N, K, M = 2048, 8192, 3
     qw, sc, mn = (gpu(t) for t in synth.q4_matrix(N, K, ("det",)))
@@ -297,7 +345,7 @@ def test_q4_grouped_equals_single_calls(q4, M):
     xs = {"q": xin, "k": xin, "v": xin, "gate": xin, "up": xin, "o": xat, "down": xff}
     dev = {p: tuple(gpu(t) for t in lay[p]) for p in synth.LAYER_ORDER}
     for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
-        for v in (0, 1, 2):
+        for v in [0, 1, 2] + ([3] if M <= 4 else []):
             outs = q4.q4g128_gemv_grouped([(xs[p], *dev[p], None) for p in stage], variant=v)
             for p, y in zip(stage, outs):
                 ys = q4.q4g128_gemv(xs[p], *dev[p], variant=v)
@@ -318,7 +366,7 @@ def test_q4_grouped_mixed_k(q4):
         check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"mixed N={N} K={K}")
 
 
-@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("variant", [1, 2, 3])
 def test_q4_scale_arrays_only_2byte_aligned(q4, variant):
     # scale/min as views one element into larger buffers: 2-byte but not
     # 16-byte aligned, so the kernels must not assume wider alignment
