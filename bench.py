@@ -64,6 +64,7 @@ class Workload:
         self.order = synth.LAYER_ORDER
         self.head_rows = head_rows
         self.io = {}
+        self.ws = {}
 
     def buffers(self, M):
         if M not in self.io:
@@ -101,9 +102,22 @@ class Workload:
                 for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
                     items = [(xs[p], *lay[p], ys[p]) for p in stage]
                     wb = sum(q4_wbytes(*self.shapes[p]) for p in stage)
-                    out.append((lambda items=items: q4.q4g128_gemv_grouped(items), wb, True))
+                    ws = self.workspace(M, items)
+                    out.append((lambda items=items, ws=ws: q4.q4g128_gemv_grouped(items, workspace=ws), wb, True))
         out.append((lambda: q4.bf16_gemv(xin, self.head, out=yh), self.head_rows * 2048 * 2, False))
         return out
+
+    def workspace(self, M, items):
+        """One split-K workspace per batch size (zero-filled once), shared by
+        every grouped call of the step (the calls run in stream order)."""
+        need = self.q4.q4g128_workspace_bytes(items)
+        if need == 0:
+            return None
+        ws = self.ws.get(M)
+        if ws is None or ws.numel() < need:
+            ws = self.torch.zeros(need, dtype=self.torch.uint8, device="cuda")
+            self.ws[M] = ws
+        return ws
 
     def step_bytes(self, M):
         """Algorithmic bytes of one step: packed weights + group scales, each

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib",
-    "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
+    "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4gemv.so")
@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with: python bit_weight_only_q4g128_amd/_build.py")
 lib = ctypes.CDLL(LIB_PATH)
 
-VARIANT_AUTO, VARIANT_DOT2, VARIANT_MFMA, VARIANT_STREAM = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_DOT2, VARIANT_MFMA, VARIANT_STREAM, VARIANT_TILED = 0, 1, 2, 3, 4
 FMT_Q4G128, FMT_NVFP4G16, FMT_BF16 = 0, 1, 2
 
 _p, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
@@ -56,6 +56,10 @@ class Q4Task(ctypes.Structure):
 
 lib.q4g128_gemv_grouped.argtypes = [ctypes.POINTER(Q4Task), _i, _i, _i, _p]
 lib.q4g128_gemv_grouped.restype = ctypes.c_int
+lib.q4g128_gemv_grouped_ws.argtypes = [ctypes.POINTER(Q4Task), _i, _i, _i, _p, ctypes.c_size_t, _p]
+lib.q4g128_gemv_grouped_ws.restype = ctypes.c_int
+lib.q4g128_workspace_bytes.argtypes = [ctypes.POINTER(Q4Task), _i, _i, ctypes.POINTER(ctypes.c_size_t)]
+lib.q4g128_workspace_bytes.restype = ctypes.c_int
 
 
 class Q4GemvError(ValueError):
@@ -124,10 +128,7 @@ def q4g128_gemv(x, qweight, scale, minv, out=None, variant: int = VARIANT_AUTO):
     return y
 
 
-def q4g128_gemv_grouped(items, variant: int = VARIANT_AUTO):
-    """Several independent int4 g128 GEMVs with one batch size, launched
-    together.  items: sequence of (x, qweight, scale, min, out-or-None).
-    Returns the list of outputs."""
+def _task_array(items):
     items = list(items)
     if not 1 <= len(items) <= 8:
         raise ValueError("1..8 tasks per call")
@@ -148,8 +149,34 @@ def q4g128_gemv_grouped(items, variant: int = VARIANT_AUTO):
         y = _out(out, (M, N), torch.bfloat16, x)
         outs.append(y)
         arr[i] = Q4Task(x.data_ptr(), qweight.data_ptr(), scale.data_ptr(), minv.data_ptr(), y.data_ptr(), N, K)
-    _raise(lib.q4g128_gemv_grouped(arr, len(items), M, int(variant), _stream(items[0][0])))
+    return items, arr, outs, M
+
+
+def q4g128_gemv_grouped(items, variant: int = VARIANT_AUTO, workspace=None):
+    """Several independent int4 g128 GEMVs with one batch size, launched
+    together.  items: sequence of (x, qweight, scale, min, out-or-None).
+    workspace: optional uint8 device tensor of at least
+    q4g128_workspace_bytes(items) bytes, zero-filled before its first use and
+    reusable afterwards without clearing (lets large batches split K).
+    Returns the list of outputs."""
+    items, arr, outs, M = _task_array(items)
+    st = _stream(items[0][0])
+    if workspace is None:
+        _raise(lib.q4g128_gemv_grouped(arr, len(items), M, int(variant), st))
+    else:
+        if workspace.device != items[0][0].device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the activations' device")
+        _raise(lib.q4g128_gemv_grouped_ws(arr, len(items), M, int(variant), workspace.data_ptr(), workspace.numel(), st))
     return outs
+
+
+def q4g128_workspace_bytes(items) -> int:
+    """Bytes of zero-filled workspace q4g128_gemv_grouped may use for these
+    tasks (0: it never splits them)."""
+    items, arr, _, M = _task_array(items)
+    n = ctypes.c_size_t(0)
+    _raise(lib.q4g128_workspace_bytes(arr, len(items), M, ctypes.byref(n)))
+    return int(n.value)
 
 
 def nvfp4g16_gemv(x, qweight, scale_e4m3, global_scale: float, out=None, variant: int = VARIANT_AUTO):

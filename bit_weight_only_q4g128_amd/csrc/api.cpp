@@ -36,27 +36,32 @@ int check_common(const void* x, int M, int K, int N, const void* y) {
 }
 
 bool variant_ok(int variant) {
-    return variant == Q4_VARIANT_AUTO || variant == Q4_VARIANT_DOT2 || variant == Q4_VARIANT_MFMA || variant == Q4_VARIANT_STREAM;
+    return variant == Q4_VARIANT_AUTO || variant == Q4_VARIANT_DOT2 || variant == Q4_VARIANT_MFMA || variant == Q4_VARIANT_STREAM ||
+           variant == Q4_VARIANT_TILED;
 }
 
 // Kernel choice for Q4_VARIANT_AUTO.  Small batches on rows of 1-4 KB go to
-// the streaming kernel, other small batches to the packed-dot kernel, larger
-// batches to the matrix cores.
-int pick(Fmt fmt, int variant, int M, int K) {
+// the streaming kernel, other small batches to the packed-dot kernel; larger
+// int4 batches to the tiled matrix-core kernel, other larger batches to the
+// per-task matrix-core kernel.  `split`: a workspace allows K splits.
+int pick(Fmt fmt, int variant, int M, int K, bool split = false) {
     if (variant == Q4_VARIANT_DOT2) return q4::dot2_supported(fmt, K) ? Q4_VARIANT_DOT2 : -1;
     if (variant == Q4_VARIANT_MFMA) return Q4_VARIANT_MFMA;
     if (variant == Q4_VARIANT_STREAM) return q4::stream_supported(fmt, M, K) ? Q4_VARIANT_STREAM : -1;
+    if (variant == Q4_VARIANT_TILED) return (fmt == q4::kFmtQ4 && q4::mm_supported(M, K, split)) ? Q4_VARIANT_TILED : -1;
     if (M <= 4 && q4::stream_supported(fmt, M, K)) return Q4_VARIANT_STREAM;
     if (M <= 4 && q4::dot2_supported(fmt, K)) return Q4_VARIANT_DOT2;
+    if (fmt == q4::kFmtQ4 && q4::mm_supported(M, K, split)) return Q4_VARIANT_TILED;
     return Q4_VARIANT_MFMA;
 }
 
-int run(Fmt fmt, int chosen, const GemvArgs* a, int count, void* stream) {
+int run(Fmt fmt, int chosen, const GemvArgs* a, int count, void* stream, void* ws = nullptr, size_t ws_bytes = 0) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     switch (chosen) {
         case Q4_VARIANT_DOT2: e = q4::launch_dot2(fmt, a, count, s); break;
         case Q4_VARIANT_STREAM: e = q4::launch_stream(fmt, a, count, s); break;
+        case Q4_VARIANT_TILED: e = q4::launch_mm(a, count, ws, ws_bytes, s); break;
         default: e = q4::launch_mfma(fmt, a, count, s); break;
     }
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
@@ -115,26 +120,29 @@ int q4g128_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweight,
     return run(q4::kFmtQ4, chosen, a, stream);
 }
 
-int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant, void* stream) {
+// Validates a group and picks one kernel family for it: the matrix cores if
+// any task needs them (the tiled kernel if every task can use it), the
+// streaming kernel if every task can use it, else the packed-dot kernel (or
+// the matrix cores where that cannot run).
+static int plan_group(const q4g128_task* tasks, int count, int M, int variant, bool split, GemvArgs* a, int* chosen_out) {
     if (!tasks) return Q4_EINVAL_PTR;
     if (count < 1 || count > q4::kMaxTasks) return Q4_EINVAL_SHAPE;
     if (!variant_ok(variant)) return Q4_EVARIANT;
-    GemvArgs a[q4::kMaxTasks];
     Range in[q4::kMaxTasks][4], out[q4::kMaxTasks];
-    // one kernel family for the whole group: the matrix cores if any task
-    // needs them, the streaming kernel if every task can use it, else the
-    // packed-dot kernel (or the matrix cores where that cannot run)
-    int n_mfma = 0, n_stream = 0;
+    int n_big = 0, n_tiled = 0, n_stream = 0;
     for (int i = 0; i < count; ++i) {
         const q4g128_task& t = tasks[i];
         int rc = check_q4(t.x, M, t.K, t.qweight, t.scale, t.minv, t.N, t.y, a[i], in[i], out[i]);
         if (rc) return rc;
-        const int c = pick(q4::kFmtQ4, variant, M, t.K);
+        const int c = pick(q4::kFmtQ4, variant, M, t.K, split);
         if (c < 0) return Q4_EVARIANT;
-        n_mfma += c == Q4_VARIANT_MFMA;
+        n_big += c == Q4_VARIANT_MFMA || c == Q4_VARIANT_TILED;
+        n_tiled += c == Q4_VARIANT_TILED;
         n_stream += c == Q4_VARIANT_STREAM;
     }
-    int chosen = n_mfma ? Q4_VARIANT_MFMA : (n_stream == count ? Q4_VARIANT_STREAM : Q4_VARIANT_DOT2);
+    int chosen;
+    if (n_big) chosen = n_tiled == count ? Q4_VARIANT_TILED : Q4_VARIANT_MFMA;
+    else chosen = n_stream == count ? Q4_VARIANT_STREAM : Q4_VARIANT_DOT2;
     if (chosen == Q4_VARIANT_DOT2) {
         for (int i = 0; i < count; ++i)
             if (!q4::dot2_supported(q4::kFmtQ4, tasks[i].K)) chosen = Q4_VARIANT_MFMA;
@@ -145,7 +153,41 @@ int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant,
                 if (overlaps(out[i], r)) return Q4_EALIAS;
             if (i != j && overlaps(out[i], out[j])) return Q4_EALIAS;
         }
-    return run(q4::kFmtQ4, chosen, a, count, stream);
+    *chosen_out = chosen;
+    return Q4_OK;
+}
+
+int q4g128_gemv_grouped_ws(const q4g128_task* tasks, int count, int M, int variant, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (workspace && !aligned(workspace, 256)) return Q4_EALIGN;
+    GemvArgs a[q4::kMaxTasks];
+    int chosen = 0;
+    const bool split = workspace != nullptr && workspace_bytes > 0;
+    int rc = plan_group(tasks, count, M, variant, split, a, &chosen);
+    if (rc) return rc;
+    if (chosen == Q4_VARIANT_TILED && split) {
+        // a workspace too small for the planned split runs unsplit, which
+        // every task must then allow
+        if (workspace_bytes < q4::mm_workspace_bytes(a, count)) {
+            for (int i = 0; i < count; ++i)
+                if (!q4::mm_supported(M, a[i].K, false)) return Q4_EVARIANT;
+        }
+    }
+    return run(q4::kFmtQ4, chosen, a, count, stream, workspace, workspace_bytes);
+}
+
+int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant, void* stream) {
+    return q4g128_gemv_grouped_ws(tasks, count, M, variant, nullptr, 0, stream);
+}
+
+int q4g128_workspace_bytes(const q4g128_task* tasks, int count, int M, size_t* bytes) {
+    if (!bytes) return Q4_EINVAL_PTR;
+    GemvArgs a[q4::kMaxTasks];
+    int chosen = 0;
+    int rc = plan_group(tasks, count, M, Q4_VARIANT_AUTO, true, a, &chosen);
+    if (rc) return rc;
+    *bytes = chosen == Q4_VARIANT_TILED ? q4::mm_workspace_bytes(a, count) : 0;
+    return Q4_OK;
 }
 
 int q4g128_gemv(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
@@ -229,6 +271,7 @@ const char* q4gemv_variant_name(int fmt, int variant, int M, int N, int K) {
     if (c == Q4_VARIANT_DOT2) return "dot2";
     if (c == Q4_VARIANT_MFMA) return "mfma";
     if (c == Q4_VARIANT_STREAM) return "stream";
+    if (c == Q4_VARIANT_TILED) return "tiled";
     return "invalid";
 }
 

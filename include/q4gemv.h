@@ -51,6 +51,9 @@ extern "C" {
 #define Q4_VARIANT_AUTO 0 /* pick by (M, N, K) */
 #define Q4_VARIANT_DOT2 1 /* wave-per-row packed-BF16 dot products; batch tiles of <= 8 rows */
 #define Q4_VARIANT_MFMA 2 /* 16x16x32 BF16 matrix-core tiles, batch padded to 16 */
+#define Q4_VARIANT_TILED 4  /* int4 only, 5 <= M <= 64: 64-row workgroups, matrix cores, activations staged
+                               in LDS per 128-column group; split over K when given a workspace
+                               (q4g128_gemv_grouped_ws) */
 #define Q4_VARIANT_STREAM 3 /* M <= 4, rows of exactly 1, 2 or 4 KB (int4/NVFP4 K = 2048, 4096, 8192;
                                BF16 K = 512, 1024, 2048): every weight load issued at once, activations
                                and group parameters shared through LDS */
@@ -97,6 +100,29 @@ typedef struct q4g128_task {
 } q4g128_task;
 
 int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant, void* stream);
+
+/*
+ * Same as q4g128_gemv_grouped, with a caller-owned device workspace that lets
+ * the Q4_VARIANT_TILED kernel split K over several workgroups when the rows
+ * alone cannot fill the GPU (the o/down stage of a decode layer at M = 48).
+ * The partial tiles are summed in a fixed order by whichever workgroup
+ * finishes a row block last, so results do not depend on timing and equal
+ * those of the unsplit kernel within fp32 rounding.
+ *   workspace        device memory, 256-byte aligned, ZERO-FILLED before its
+ *                    first use; it holds arrival counters, which every call
+ *                    leaves at zero, and partial tiles, which are scratch: the
+ *                    workspace can be reused without being cleared again
+ *   workspace_bytes  at least what q4g128_workspace_bytes reports for the same
+ *                    tasks and M; with less (or NULL) the call runs unsplit
+ * Calls that use one workspace must not overlap in time (same stream, or
+ * ordered by events).
+ */
+int q4g128_gemv_grouped_ws(const q4g128_task* tasks, int count, int M, int variant, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes q4g128_gemv_grouped_ws needs for these tasks (0 if no
+ * split is planned).  Validates like the GEMV call; *bytes is set on Q4_OK. */
+int q4g128_workspace_bytes(const q4g128_task* tasks, int count, int M, size_t* bytes);
 
 /*
  * NVFP4 weight-only weights.

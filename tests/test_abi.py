@@ -54,7 +54,8 @@ def q4call(x=A, M=1, K=2048, qw=A + (1 << 24), sc=A + (2 << 24), mn=A + (3 << 24
     (dict(K=2048 + 64), ESHAPE), (dict(x=A + 2), EALIGN), (dict(qw=A + (1 << 24) + 8), EALIGN),
     (dict(sc=A + (2 << 24) + 1), EALIGN), (dict(y=A + (4 << 24) + 1), EALIGN),
     (dict(y=A + (1 << 24) + 64), EALIAS), (dict(y=A + 16), EALIAS), (dict(y=A + (3 << 24)), EALIAS),
-    (dict(variant=4), EVARIANT), (dict(variant=-1), EVARIANT), (dict(variant=3, M=5), EVARIANT),
+    (dict(variant=5), EVARIANT), (dict(variant=-1), EVARIANT), (dict(variant=3, M=5), EVARIANT),
+    (dict(variant=4, M=64, K=8192), EVARIANT),
     (dict(variant=3, K=1024), EVARIANT),
 ])
 def test_q4_validation(kw, rc):
@@ -100,7 +101,8 @@ def test_variant_names():
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 1, 256, 512) == "dot2"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_STREAM, 5, 2048, 2048) == "invalid"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 1, 16385, 2048) == "stream"
-    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 2048) == "mfma"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 16384) == "mfma"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_MFMA, 1, 2048, 2048) == "mfma"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_DOT2, 3, 16385, 2048) == "dot2"
     assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2048) == "mfma"
@@ -128,7 +130,18 @@ def test_grouped_validation():
     assert lib.q4g128_gemv_grouped(arr, 0, 1, 0, None) == ESHAPE
     assert lib.q4g128_gemv_grouped(arr, 9, 1, 0, None) == ESHAPE
     assert lib.q4g128_gemv_grouped(arr, 3, 0, 0, None) == ESHAPE
-    assert lib.q4g128_gemv_grouped(arr, 3, 1, 4, None) == EVARIANT
+    assert lib.q4g128_gemv_grouped(arr, 3, 1, 5, None) == EVARIANT
+    assert lib.q4g128_gemv_grouped_ws(arr, 3, 1, 0, A + 1, 4096, None) == EALIGN
+    import ctypes
+    assert lib.q4g128_workspace_bytes(arr, 3, 48, None) == EPTR
+    def far(i):   # disjoint address ranges (nothing is launched)
+        b = A + (i << 29)
+        return T(x=b, qweight=b + (1 << 26), scale=b + (2 << 26), minv=b + (3 << 26), y=b + (4 << 26), N=2048, K=2048)
+    ok3 = (T * 3)(far(0), far(1), far(2))
+    nb = ctypes.c_size_t(123)
+    assert lib.q4g128_workspace_bytes(ok3, 3, 1, ctypes.byref(nb)) == OK and nb.value == 0   # M = 1 never splits
+    # three 2048-row tasks at M = 48: 96 row blocks, so K is split
+    assert lib.q4g128_workspace_bytes(ok3, 3, 48, ctypes.byref(nb)) == OK and nb.value > 0
     bad = (T * 2)(task(0), task(1, K=100))
     assert lib.q4g128_gemv_grouped(bad, 2, 1, 0, None) == ESHAPE
     # task 1 writes over task 0's weights

@@ -25,13 +25,14 @@ def q4():
 
 
 VARIANTS = [1, 2]  # dot2, mfma
-VNAME = {0: "auto", 1: "dot2", 2: "mfma", 3: "stream"}
+VNAME = {0: "auto", 1: "dot2", 2: "mfma", 3: "stream", 4: "tiled"}
 FMT = {"q4": 0, "nv": 1, "bf": 2}
 
 
 def vlist(q4, fmt, M, K):
-    """auto, dot2 and mfma, plus the streaming kernel where it accepts (M, K)."""
-    return [0, 1, 2] + ([3] if q4.variant_name(FMT[fmt], 3, M, 1, K) == "stream" else [])
+    """auto, dot2 and mfma, plus the streaming and tiled kernels where they accept (M, K)."""
+    return ([0, 1, 2] + ([3] if q4.variant_name(FMT[fmt], 3, M, 1, K) == "stream" else [])
+            + ([4] if q4.variant_name(FMT[fmt], 4, M, 1, K) == "tiled" else []))
 
 
 # ----------------------------------------------------------------------------
@@ -156,6 +157,23 @@ def test_bf16_onehot_bitwise_stream(q4, K, M):
     ks = _onehot_ks(K, M, 500 + M)
     y = q4.bf16_gemv(gpu(onehot_x(K, ks)), gpu(w), variant=3)
     assert np.array_equal(y.cpu().float().numpy(), w[:, ks].T.float().numpy()), (K, M)
+
+
+# the tiled matrix-core kernel (int4): ragged row blocks, groups past a round
+# of eight, every batch-tile count
+@pytest.mark.parametrize("K", [128, 1152, 2048, 8192])
+@pytest.mark.parametrize("M", [5, 16, 17, 33, 48, 64])
+def test_q4_onehot_bitwise_tiled(q4, K, M):
+    if q4.variant_name(0, 4, M, 1, K) != "tiled":
+        pytest.skip("group parameters of this K exceed the tiled kernel's LDS budget at this M")
+    N = 70
+    qw, sc, mn = synth.q4_matrix(N, K, ("onehot-tl", K, M))
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    ks = _onehot_ks(K, M, 600 + M)
+    y = q4.q4g128_gemv(gpu(onehot_x(K, ks)), gpu(qw), gpu(sc), gpu(mn), variant=4)
+    got = y.cpu().float().numpy()
+    exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(got, exp), (K, M, np.argwhere(got != exp)[:4])
 
 
 # ----------------------------------------------------------------------------
@@ -345,13 +363,51 @@ def test_q4_grouped_equals_single_calls(q4, M):
     xs = {"q": xin, "k": xin, "v": xin, "gate": xin, "up": xin, "o": xat, "down": xff}
     dev = {p: tuple(gpu(t) for t in lay[p]) for p in synth.LAYER_ORDER}
     for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
-        for v in [0, 1, 2] + ([3] if M <= 4 else []):
+        for v in [0, 1, 2] + ([3] if M <= 4 else [4]):
             outs = q4.q4g128_gemv_grouped([(xs[p], *dev[p], None) for p in stage], variant=v)
             for p, y in zip(stage, outs):
                 ys = q4.q4g128_gemv(xs[p], *dev[p], variant=v)
                 assert torch.equal(y, ys), (p, M, VNAME[v])
                 xb = x_bits(xs[p].cpu())
                 check_gemv(y, oracle.gemv_f64(xb, w32[p]), w32[p], xb, f"grouped {p} M={M} {VNAME[v]}")
+
+
+@pytest.mark.parametrize("M", [16, 48])
+def test_q4_grouped_split_k_workspace(q4, M):
+    # o and down alone are 64 row blocks, so with a workspace K is split over
+    # workgroups; the result must match the oracle and the unsplit call within
+    # tolerance and repeat bitwise on the same workspace without re-zeroing it
+    lay, w32 = _layer_q4()
+    xat = gpu(synth.x_bf16(M, 2048, ("split-xat", M)))
+    xff = gpu(synth.x_bf16(M, 8192, ("split-xff", M)))
+    items = [(xat, *(gpu(t) for t in lay["o"]), None), (xff, *(gpu(t) for t in lay["down"]), None)]
+    nbytes = q4.q4g128_workspace_bytes(items)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    outs = q4.q4g128_gemv_grouped(items, workspace=ws)
+    plain = q4.q4g128_gemv_grouped(items)
+    for p, x, y, yp in zip(("o", "down"), (xat, xff), outs, plain):
+        xb = x_bits(x.cpu())
+        ref = oracle.gemv_f64(xb, w32[p])
+        check_gemv(y, ref, w32[p], xb, f"split {p} M={M}")
+        check_gemv(yp, ref, w32[p], xb, f"unsplit {p} M={M}")
+    for _ in range(5):
+        again = q4.q4g128_gemv_grouped(items, workspace=ws)
+        assert all(torch.equal(a, b) for a, b in zip(again, outs))
+
+
+def test_q4_split_k_small_tasks(q4):
+    # a few short matrices: split into as many slices as K allows, one-hot exact
+    N, K, M = 100, 2048, 20
+    qw, sc, mn = synth.q4_matrix(N, K, ("split-small",))
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    ks = _onehot_ks(K, M, 77)
+    items = [(gpu(onehot_x(K, ks)), gpu(qw), gpu(sc), gpu(mn), None)]
+    ws = torch.zeros(q4.q4g128_workspace_bytes(items), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    y = q4.q4g128_gemv_grouped(items, workspace=ws)[0]
+    exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(y.cpu().float().numpy(), exp)
 
 
 def test_q4_grouped_mixed_k(q4):
