@@ -13,7 +13,7 @@
 //   * two loader waves that stream the activations of each 128-column group
 //     (MT*16 batch rows) from L2 into a double-buffered LDS ring, already in
 //     B-fragment order and in the column pairing of the weight operand, and
-//     compute SX on the way.
+//     compute SX on the way (each loader half of it).
 //
 // One barrier per group keeps the ring in step.  When K is split over several
 // workgroups, each writes its fp32 partial tile to a caller-provided
@@ -36,7 +36,7 @@ constexpr int kRows = 64;        // rows per workgroup
 constexpr int kCompute = 4;      // compute waves (one 16-row tile each)
 constexpr int kLoaders = 2;      // activation loader waves
 constexpr int kThreads = 64 * (kCompute + kLoaders);
-constexpr int kPre = 8;          // weight groups in flight per compute lane
+constexpr int kPre = 4;          // weight groups in flight per compute lane
 constexpr int kXPre = 2;         // activation groups in flight per loader lane (divides kPre)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -61,22 +61,58 @@ struct MmTable {
     MmTask t[kMaxTasks];
 };
 
+// Activation ring: NS slots of one 128-column group each, [MT][4 k-steps][64
+// lanes] x 16 bytes per slot in B-fragment order.  The loaders keep XD groups
+// of direct-to-LDS loads in flight beyond the group they are preparing.
+constexpr int kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
 template <int MT>
-__host__ __device__ constexpr int mm_xbuf_bytes() { return 2 * MT * 4 * 64 * 16; }
+__host__ __device__ constexpr int mm_ns() { return MT <= 3 ? 5 : 4; }
 template <int MT>
-__host__ __device__ constexpr int mm_sx_bytes() { return 2 * MT * 16 * 4; }
+__host__ __device__ constexpr int mm_xd() { return mm_ns<MT>() - 2; }
 template <int MT>
-__host__ __device__ inline int mm_shmem(int gps) { return mm_xbuf_bytes<MT>() + mm_sx_bytes<MT>() + gps * kRows * 8; }
-// most groups per slice whose parameters fit the 64 KB LDS budget
+__host__ __device__ constexpr int mm_slot_bytes() { return MT * 4 * 64 * 16; }
 template <int MT>
-constexpr int mm_max_gps() { return (65536 - mm_xbuf_bytes<MT>() - mm_sx_bytes<MT>()) / (kRows * 8); }
+__host__ __device__ constexpr int mm_sx_bytes() { return mm_ns<MT>() * kLoaders * MT * 16 * 4; }
+template <int MT>
+__host__ __device__ inline int mm_shmem(int gps) {
+    return mm_ns<MT>() * mm_slot_bytes<MT>() + mm_sx_bytes<MT>() + gps * kRows * 8;
+}
+// most groups per slice whose parameters fit the LDS budget
+template <int MT>
+constexpr int mm_max_gps() {
+    return (kLdsBudget - mm_ns<MT>() * mm_slot_bytes<MT>() - mm_sx_bytes<MT>()) / (kRows * 8);
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most the direct-to-
+// LDS loads of XD - 1 groups (2 * MT instructions each) are outstanding.
+template <int MT>
+constexpr int mm_wait_xd() {
+    constexpr int n = (mm_xd<MT>() - 1) * 2 * MT;
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+template <int MT>
+constexpr int kWaitXD = mm_wait_xd<MT>();
+
+// Workgroup barrier for the main loops: waits only for this wave's LDS
+// traffic (lgkmcnt) and fences the compiler, so vector-memory loads -- the
+// weight prefetch and the direct-to-LDS activation loads -- stay in flight
+// across it.  (__syncthreads would add a workgroup release fence, which waits
+// for every outstanding direct-to-LDS load.)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 template <int MT>
 __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
+    constexpr int NS = mm_ns<MT>();
+    constexpr int XD = mm_xd<MT>();
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    u32x4* xb = reinterpret_cast<u32x4*>(lds);                                        // [2][MT][4][64]
-    float* sxb = reinterpret_cast<float*>(lds + mm_xbuf_bytes<MT>());                 // [2][MT*16]
-    f32x2* smb = reinterpret_cast<f32x2*>(lds + mm_xbuf_bytes<MT>() + mm_sx_bytes<MT>());   // [gps][64]
+    u32x4* xb = reinterpret_cast<u32x4*>(lds);                                                  // [NS][MT][4][64]
+    float* sxb = reinterpret_cast<float*>(lds + NS * mm_slot_bytes<MT>());                      // [NS][kLoaders][MT*16]
+    f32x2* smb = reinterpret_cast<f32x2*>(lds + NS * mm_slot_bytes<MT>() + mm_sx_bytes<MT>());  // [gps][64]
 
     int ti = 0;
 #pragma unroll
@@ -94,10 +130,9 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
     ng = ng < gps ? ng : gps;                      // groups of this slice (>= 1 by construction)
     const int row0 = blk * kRows;
     const uint32_t rowbytes = (uint32_t)a.K >> 1;
-
-    // Groups are processed in rounds of kPre; past the slice's last group the
-    // loads re-read that group (so every load is unconditional and the wait
-    // counts stay exact) and the results are not accumulated.
+    // Groups run in rounds of kPre; past the slice's last group the loads
+    // re-read that group (every load is unconditional, so the wait counts
+    // stay exact) and the results are not accumulated.
     const int niter = ((ng + kPre - 1) / kPre) * kPre;
 
     f32x4 acc[MT];
@@ -108,87 +143,139 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
         // ------------------------------------------------------------ compute
         const int trow0 = row0 + 16 * wave;
         int nr = a.N - trow0;
-        nr = nr < 0 ? 0 : (nr > 16 ? 16 : nr);
+        // uniform; kept in a scalar register so the buffer resource is too
+        nr = __builtin_amdgcn_readfirstlane(nr < 0 ? 0 : (nr > 16 ? 16 : nr));
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)trow0 * rowbytes, (uint32_t)nr * rowbytes);
         const uint32_t avoff = (uint32_t)(lane & 15) * rowbytes + ((uint32_t)g0 << 6) + ((uint32_t)(lane >> 4) << 4);
         auto aload = [&](int j) { return buf_load16(rw, avoff + ((uint32_t)(j < ng ? j : ng - 1) << 6), 0); };
         u32x4 q[kPre];
 #pragma unroll
         for (int u = 0; u < kPre; ++u) q[u] = aload(u);
-        __syncthreads();   // parameters and activation group 0 staged
+        lds_barrier();     // parameters and activation group 0 ready
 
+        // Software pipeline: iteration j issues group j's MFMAs into Dc and
+        // folds group j - 1 (Dp, with its SX / scale / min read one iteration
+        // earlier) while those run.
+        f32x4 Dp[MT];
+        float sxp[MT];
+        f32x4 smp01 = {0.f, 0.f, 0.f, 0.f}, smp23 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) { Dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f}; sxp[mt] = 0.f; }
+        auto fold = [&](const f32x4 (&D)[MT], const float (&sx)[MT], f32x4 sm01, f32x4 sm23) {
+            const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
+            const float mn[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float t = fmaf(-128.f, sx[mt], D[mt][v]);
+                    acc[mt][v] = fmaf(mn[v], sx[mt], fmaf(sc[v], t, acc[mt][v]));
+                }
+        };
+        int slot0 = 0;                              // slot of group j0
         for (int j0 = 0; j0 < niter; j0 += kPre) {
 #pragma unroll
             for (int u = 0; u < kPre; ++u) {
                 const int j = j0 + u;
-                const int slot = j & 1;
+                int slot = slot0 + u;
+                slot = slot >= NS ? slot - NS : slot;
+                slot = slot >= NS ? slot - NS : slot;
+                slot = slot >= NS ? slot - NS : slot;
+                const u32x4* xs = xb + (size_t)slot * MT * 4 * 64 + lane;
+                float sxc[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    sxc[mt] = sxb[(slot * kLoaders + 0) * MT * 16 + mt * 16 + (lane & 15)] +
+                              sxb[(slot * kLoaders + 1) * MT * 16 + mt * 16 + (lane & 15)];
+                const int jc = j < ng ? j : ng - 1;
+                const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + jc * kRows + 16 * wave + 4 * (lane >> 4));
+                const f32x4 smc01 = sm4[0], smc23 = sm4[1];
+                // fold group j - 1 (its MFMAs ran during the previous iteration)
+                if (j >= 1 && j - 1 < ng) fold(Dp, sxp, smp01, smp23);
+                // group j: per k-step, three activation fragments and one weight operand
                 const u32x4 qa = q[u];
                 q[u] = aload(j + kPre);
                 const uint32_t qd[4] = {qa.x, qa.y, qa.z, qa.w};
-                f32x4 D[MT];
+                f32x4 Dc[MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) D[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int mt = 0; mt < MT; ++mt) Dc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    uint32_t p[4];
-                    q4_pairs(qd[s], p);
-                    const bf16x8_t A = as_bf16x8(p[0], p[1], p[2], p[3]);
+                    u32x4 B[MT];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const u32x4 bv = xb[((slot * MT + mt) * 4 + s) * 64 + lane];
-                        D[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(bv), D[mt], 0, 0, 0);
-                    }
+                    for (int mt = 0; mt < MT; ++mt) B[mt] = xs[(mt * 4 + s) * 64];
+                    uint32_t A[4];
+                    q4_pairs(qd[s], A);
+                    const bf16x8_t Av = as_bf16x8(A[0], A[1], A[2], A[3]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        Dc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, as_bf16x8(B[mt]), Dc[mt], 0, 0, 0);
                 }
-                if (j < ng) {
-                    const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + j * kRows + 16 * wave + 4 * (lane >> 4));
-                    const f32x4 sm01 = sm4[0], sm23 = sm4[1];
-                    const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
-                    const float mn[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const float sx = sxb[slot * MT * 16 + mt * 16 + (lane & 15)];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const float t = fmaf(-128.f, sx, D[mt][v]);
-                            acc[mt][v] = fmaf(mn[v], sx, fmaf(sc[v], t, acc[mt][v]));
-                        }
-                    }
-                }
-                __syncthreads();
+                for (int mt = 0; mt < MT; ++mt) { Dp[mt] = Dc[mt]; sxp[mt] = sxc[mt]; }
+                smp01 = smc01;
+                smp23 = smc23;
+                lds_barrier();
             }
+            slot0 += kPre % NS;
+            slot0 = slot0 >= NS ? slot0 - NS : slot0;
         }
+        if (niter - 1 < ng) fold(Dp, sxp, smp01, smp23);
     } else {
         // ------------------------------------------------------------- loader
+        // Loader L owns k-steps s = 2L, 2L + 1 of every batch tile.  For group
+        // j it issues, per (mt, s), one direct-to-LDS load in which lane l
+        // fetches the 8 activations of batch row 16 mt + l % 16 at group
+        // columns 32 (l / 16) + 8 s .. + 8, landing exactly where compute lane
+        // l reads them; once they have landed it re-pairs them in place to
+        // match the weight operand and sums them for SX.
         const int L = wave - kCompute;
         const int lt = tid - 64 * kCompute;   // 0 .. 64 * kLoaders - 1
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.M * a.K * 2));
-        const int kp = lane & 15;
-        auto xload = [&](int j, int i) {
-            const int m = 8 * i + 4 * L + (lane >> 4);
+        const uint16_t* xg = a.x;
+        auto issue = [&](int j) {
+            const int slot = j % NS;
             const int g = g0 + (j < ng ? j : ng - 1);
-            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((m * a.K + (g << 7) + 8 * kp) * 2), 0, 0));
-        };
-        auto stage = [&](int j, const u32x4 (&xr)[2 * MT]) {
-            const int slot = j & 1;
 #pragma unroll
             for (int i = 0; i < 2 * MT; ++i) {
-                const int m = 8 * i + 4 * L + (lane >> 4);
-                uint32_t p[4];
-                xq4_pairs(xr[i].x, xr[i].y, xr[i].z, xr[i].w, p);
-                xb[((slot * MT + (m >> 4)) * 4 + (kp & 3)) * 64 + (kp >> 2) * 16 + (m & 15)] = u32x4{p[0], p[1], p[2], p[3]};
-                float sx = dot2(xr[i].x, 0x3F803F80u, 0.f);
-                sx = dot2(xr[i].y, 0x3F803F80u, sx);
-                sx = dot2(xr[i].z, 0x3F803F80u, sx);
-                sx = dot2(xr[i].w, 0x3F803F80u, sx);
-                sx = group_sum(sx, 16);
-                if (kp == 0) sxb[slot * MT * 16 + m] = sx;
+                const int mt = i >> 1, s = 2 * L + (i & 1);
+                int m = 16 * mt + (lane & 15);
+                m = m < a.M ? m : a.M - 1;        // padding rows re-read a real row; their columns are dropped
+                const uint16_t* src = xg + (size_t)m * a.K + (g << 7) + 32 * (lane >> 4) + 8 * s;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                                 (__attribute__((address_space(3))) void*)(xb + ((size_t)slot * MT * 4 + mt * 4 + s) * 64),
+                                                 16, 0, 0);
             }
         };
-        u32x4 xr[kXPre][2 * MT];
+        auto prepare = [&](int j) {
+            const int slot = j % NS;
+            u32x4* base = xb + (size_t)slot * MT * 4 * 64 + lane;
+            u32x4 v[MT][2];
 #pragma unroll
-        for (int u = 0; u < kXPre; ++u)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 2 * MT; ++i) xr[u][i] = xload(u, i);
+                for (int h = 0; h < 2; ++h) v[mt][h] = base[(mt * 4 + 2 * L + h) * 64];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                float sx = 0.f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t pr[4];
+                    xq4_pairs(v[mt][h].x, v[mt][h].y, v[mt][h].z, v[mt][h].w, pr);
+                    base[(mt * 4 + 2 * L + h) * 64] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+                    sx = dot2(v[mt][h].x, 0x3F803F80u, sx);
+                    sx = dot2(v[mt][h].y, 0x3F803F80u, sx);
+                    sx = dot2(v[mt][h].z, 0x3F803F80u, sx);
+                    sx = dot2(v[mt][h].w, 0x3F803F80u, sx);
+                }
+                // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same batch row
+                sx += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, sx), 0x401F));
+                sx += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, sx)));
+                const int m = 16 * mt + lane;
+                if (lane < 16) sxb[(slot * kLoaders + L) * MT * 16 + mt * 16 + lane] = (m < a.M) ? sx : 0.f;
+            }
+        };
+#pragma unroll
+        for (int u = 0; u <= XD; ++u) issue(u);
 
         // group parameters of the block's rows for the slice, fp32 (scale, min) [group][row]
         if (tt.t[ti].sm16) {
@@ -196,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
             // the host sets sm16 when K/128, the slice start and length are
             // multiples of 8 and both arrays are 16-byte aligned
             int wg_rows = a.N - row0;
-            wg_rows = wg_rows > kRows ? kRows : wg_rows;
+            wg_rows = __builtin_amdgcn_readfirstlane(wg_rows > kRows ? kRows : wg_rows);
             const uint32_t rb = (uint32_t)G * 2;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + (size_t)row0 * G, (uint32_t)wg_rows * rb);
             const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)wg_rows * rb);
@@ -238,24 +325,24 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
             }
         }
 
-        stage(0, xr[0]);
-#pragma unroll
-        for (int i = 0; i < 2 * MT; ++i) xr[0][i] = xload(kXPre, i);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);
+        prepare(0);
+        lds_barrier();
 
-        // iteration j stages group j + 1, held in ring slot (j + 1) % kXPre
-        // (j0 is a multiple of kPre, itself a multiple of kXPre)
+        // iteration j prepares group j + 1 and issues group j + 1 + XD into
+        // the slot of group j - 1, which the compute waves finished before
+        // the previous barrier
         for (int j0 = 0; j0 < niter; j0 += kPre) {
 #pragma unroll
             for (int u = 0; u < kPre; ++u) {
                 const int j = j0 + u;
-                const int r = (u + 1) % kXPre;
-                stage(j + 1, xr[r]);
-#pragma unroll
-                for (int i = 0; i < 2 * MT; ++i) xr[r][i] = xload(j + 1 + kXPre, i);
-                __syncthreads();
+                __builtin_amdgcn_s_waitcnt(kWaitXD<MT>);   // group j + 1 has landed
+                prepare(j + 1);
+                issue(j + 1 + XD);
+                lds_barrier();
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);   // no direct-to-LDS load outlives the wave
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -318,6 +405,7 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
     }
     if (tid == 0) __hip_atomic_store(&cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
 
 // Split plan: no split while the row blocks alone give >= 256 workgroups;
 // otherwise enough slices to reach about 384 workgroups, each slice >= 4
@@ -392,6 +480,9 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         grid += blocks * ks[i];
         gmax = gps[i] > gmax ? gps[i] : gmax;
     }
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q4_mm_kernel<MT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
+    if (attr != hipSuccess) return attr;
     return launch_kernel(q4_mm_kernel<MT>, dim3(grid), dim3(kThreads), (size_t)mm_shmem<MT>(gmax), st, tt);
 }
 

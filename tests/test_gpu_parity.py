@@ -364,12 +364,19 @@ def test_q4_grouped_equals_single_calls(q4, M):
     dev = {p: tuple(gpu(t) for t in lay[p]) for p in synth.LAYER_ORDER}
     for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
         for v in [0, 1, 2] + ([3] if M <= 4 else [4]):
-            outs = q4.q4g128_gemv_grouped([(xs[p], *dev[p], None) for p in stage], variant=v)
+            try:
+                outs = q4.q4g128_gemv_grouped([(xs[p], *dev[p], None) for p in stage], variant=v)
+            except q4.Q4GemvError:
+                # a forced variant that some task of the stage cannot run
+                assert v != 0
+                continue
             for p, y in zip(stage, outs):
-                ys = q4.q4g128_gemv(xs[p], *dev[p], variant=v)
-                assert torch.equal(y, ys), (p, M, VNAME[v])
                 xb = x_bits(xs[p].cpu())
                 check_gemv(y, oracle.gemv_f64(xb, w32[p]), w32[p], xb, f"grouped {p} M={M} {VNAME[v]}")
+                if v != 0:
+                    # the same kernel: grouping must not change a single bit
+                    ys = q4.q4g128_gemv(xs[p], *dev[p], variant=v)
+                    assert torch.equal(y, ys), (p, M, VNAME[v])
 
 
 @pytest.mark.parametrize("M", [16, 48])
