@@ -166,9 +166,10 @@ int q4g128_gemv_grouped_ws(const q4g128_task* tasks, int count, int M, int varia
     int rc = plan_group(tasks, count, M, variant, split, a, &chosen);
     if (rc) return rc;
     if (chosen == Q4_VARIANT_TILED && split) {
-        // a workspace too small for the planned split runs unsplit, which
-        // every task must then allow
-        if (workspace_bytes < q4::mm_workspace_bytes(a, count)) {
+        // a workspace too small for the planned split (or a launch too large
+        // to split) runs unsplit, which every task must then allow
+        const size_t need = q4::mm_workspace_bytes(a, count);
+        if (need == 0 || workspace_bytes < need) {
             for (int i = 0; i < count; ++i)
                 if (!q4::mm_supported(M, a[i].K, false)) return Q4_EVARIANT;
         }

@@ -1,24 +1,27 @@
 // Matrix-core GEMV for batched decode, int4 g128 (gfx950, v_mfma_f32_16x16x32_bf16).
 //
 // A workgroup owns a block of 64 weight rows and one slice of K (the whole of
-// K unless the rows alone cannot fill the chip).  It runs six waves:
+// K unless the row blocks alone cannot fill the chip).  The slice is cut into
+// two halves that the workgroup walks side by side, and it runs six waves:
 //
-//   * four compute waves, one 16-row tile each.  A compute wave issues only
-//     weight loads (kPre 128-column groups ahead), so its in-order waits on
-//     the vector-memory counter never stall behind anything but its own
-//     weights.  Per group it turns its 16 bytes per lane into BF16 "128 + code"
-//     operands, runs 4 k-steps x MT batch tiles of MFMA with the activations as
-//     the B operand, and folds the group as
+//   * four compute waves, one per (32-row pair, K half).  A compute wave
+//     issues only weight loads (kPre 128-column groups ahead), so its in-order
+//     waits on the vector-memory counter never stall behind anything but its
+//     own weights.  Per group it turns its 2 x 16 bytes per lane into BF16
+//     "128 + code" operands for its two 16-row tiles, runs 4 k-steps x MT
+//     batch tiles x 2 row tiles of MFMA with the activations as the B operand
+//     (each activation fragment read from LDS once serves both row tiles), and
+//     folds the group as
 //         acc += scale * (D - 128 * SX) + min * SX,   SX = sum of x over the group;
-//   * two loader waves that stream the activations of each 128-column group
-//     (MT*16 batch rows) from L2 into a double-buffered LDS ring, already in
-//     B-fragment order and in the column pairing of the weight operand, and
-//     compute SX on the way (each loader half of it).
+//   * two loader waves, one per K half, that stream the activations of each
+//     128-column group (MT*16 batch rows) from L2 through registers into a
+//     double-buffered LDS ring, already in B-fragment order and in the column
+//     pairing of the weight operand, and compute SX on the way.
 //
-// One barrier per group keeps the ring in step.  When K is split over several
-// workgroups, each writes its fp32 partial tile to a caller-provided
-// workspace; the workgroup that arrives last at the block's counter (release /
-// acquire fences around one atomic) sums the partials in slice order, so the
+// One barrier per group step keeps the ring in step.  At the end the two K
+// halves meet in LDS.  When K is split over several workgroups, each writes
+// its fp32 partial tile to a caller-provided workspace; the workgroup that
+// arrives last at the block's counter sums the partials in slice order, so the
 // result does not depend on timing, writes y and resets the counter to zero.
 //
 // MFMA operand layout (16x16x32): lane l holds A row l % 16 and B column
@@ -33,11 +36,11 @@ namespace q4 {
 namespace {
 
 constexpr int kRows = 64;        // rows per workgroup
-constexpr int kCompute = 4;      // compute waves (one 16-row tile each)
-constexpr int kLoaders = 2;      // activation loader waves
+constexpr int kCompute = 4;      // compute waves: 2 row pairs x 2 K halves
+constexpr int kLoaders = 2;      // activation loader waves, one per K half
 constexpr int kThreads = 64 * (kCompute + kLoaders);
 constexpr int kPre = 4;          // weight groups in flight per compute lane
-constexpr int kXPre = 2;         // activation groups in flight per loader lane (divides kPre)
+constexpr int kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -52,7 +55,8 @@ struct MmTask {
     int ks;            // workgroups per row block (K slices)
     int gps;           // 128-column groups per slice
     int sm16;          // group parameters can be read as 16-byte pieces (see below)
-    float* part;       // partial tiles (ks > 1): [blocks][ks][4 waves][MT][64 lanes] x 4 floats
+    int y8;            // y rows can be written 8 bytes at a time (y 8-byte aligned, N % 4 == 0)
+    float* part;       // partial tiles (ks > 1): [blocks][ks][4 tiles][MT][64 lanes] x 4 floats
     unsigned* cnt;     // arrival counters (ks > 1): [blocks]
 };
 
@@ -61,43 +65,24 @@ struct MmTable {
     MmTask t[kMaxTasks];
 };
 
-// Activation ring: NS slots of one 128-column group each, [MT][4 k-steps][64
-// lanes] x 16 bytes per slot in B-fragment order.  The loaders keep XD groups
-// of direct-to-LDS loads in flight beyond the group they are preparing.
-constexpr int kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
+// activation groups a loader keeps in flight (registers: 4 * MT pieces each)
 template <int MT>
-__host__ __device__ constexpr int mm_ns() { return MT <= 3 ? 5 : 4; }
+__host__ __device__ constexpr int mm_xp() { return MT <= 2 ? 2 : 1; }
+// LDS: ring [2 slots][2 halves][MT][4 k-steps][64 lanes] x 16 bytes, group sums
+// [2][2][MT * 16] floats, group parameters [groups][64 rows] x (scale, min)
 template <int MT>
-__host__ __device__ constexpr int mm_xd() { return mm_ns<MT>() - 2; }
+__host__ __device__ constexpr int mm_ring_bytes() { return 2 * 2 * MT * 4 * 64 * 16; }
 template <int MT>
-__host__ __device__ constexpr int mm_slot_bytes() { return MT * 4 * 64 * 16; }
+__host__ __device__ constexpr int mm_sx_bytes() { return 2 * 2 * MT * 16 * 4; }
 template <int MT>
-__host__ __device__ constexpr int mm_sx_bytes() { return mm_ns<MT>() * kLoaders * MT * 16 * 4; }
-template <int MT>
-__host__ __device__ inline int mm_shmem(int gps) {
-    return mm_ns<MT>() * mm_slot_bytes<MT>() + mm_sx_bytes<MT>() + gps * kRows * 8;
-}
+__host__ __device__ inline int mm_shmem(int gps) { return mm_ring_bytes<MT>() + mm_sx_bytes<MT>() + gps * kRows * 8; }
 // most groups per slice whose parameters fit the LDS budget
 template <int MT>
-constexpr int mm_max_gps() {
-    return (kLdsBudget - mm_ns<MT>() * mm_slot_bytes<MT>() - mm_sx_bytes<MT>()) / (kRows * 8);
-}
-
-// s_waitcnt immediate (gfx9 encoding) that waits until at most the direct-to-
-// LDS loads of XD - 1 groups (2 * MT instructions each) are outstanding.
-template <int MT>
-constexpr int mm_wait_xd() {
-    constexpr int n = (mm_xd<MT>() - 1) * 2 * MT;
-    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
-template <int MT>
-constexpr int kWaitXD = mm_wait_xd<MT>();
+constexpr int mm_max_gps() { return (kLdsBudget - mm_ring_bytes<MT>() - mm_sx_bytes<MT>()) / (kRows * 8); }
 
 // Workgroup barrier for the main loops: waits only for this wave's LDS
-// traffic (lgkmcnt) and fences the compiler, so vector-memory loads -- the
-// weight prefetch and the direct-to-LDS activation loads -- stay in flight
-// across it.  (__syncthreads would add a workgroup release fence, which waits
-// for every outstanding direct-to-LDS load.)
+// traffic (lgkmcnt) and fences the compiler, so vector-memory loads (the
+// weight and activation prefetch) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt untouched
@@ -105,14 +90,57 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Workspace layout, the same for every call so that calls with different
+// tasks can share one workspace: the arrival counters of all split tasks of a
+// call in the first kCntBytes (every call leaves them zero), partial tiles
+// after them.
+constexpr size_t kCntBytes = 64 * 1024;
+constexpr int kCoherent = 16;   // buffer cache policy sc1: device-coherent, not held in the per-XCD L2
+
+// contributors whose partial tiles the reducing wave loads at once (8 * MT
+// registers per lane each)
+template <int MT>
+__host__ __device__ constexpr int mm_reduce_batch() { return MT <= 1 ? 4 : MT == 2 ? 3 : 2; }
+
+// Byte offset of a partial tile: row block blk, K slice ks of KS, row pair
+// rp, row tile t, batch tile mt, lane.
+template <int MT>
+__device__ __forceinline__ uint32_t part_off(int blk, int KS, int ks, int rp, int t, int mt, int lane) {
+    return (uint32_t)(((((blk * KS + ks) * 4 + rp * 2 + t) * MT + mt) * 64 + lane) * 16);
+}
+
+// y for the two 16-row tiles of a row pair: lane l holds rows
+// prow0 + 16 t + 4 (l / 16) + v (v = 0..3) of batch row 16 mt + l % 16.
+template <int MT>
+__device__ __forceinline__ void write_y(const GemvArgs& a, bool y8, int prow0, int lane, const f32x4 (&v)[2][MT]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = 16 * mt + (lane & 15);
+            const int row = prow0 + 16 * t + 4 * (lane >> 4);
+            if (m >= a.M || row >= a.N) continue;
+            uint16_t* dst = a.y + (size_t)m * a.N + row;
+            const f32x4 r = v[t][mt];
+            if (y8 && row + 3 < a.N) {
+                const uint32_t lo = (uint32_t)f32_to_bf16(r.x) | ((uint32_t)f32_to_bf16(r.y) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16(r.z) | ((uint32_t)f32_to_bf16(r.w) << 16);
+                *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (row + q < a.N) dst[q] = f32_to_bf16(r[q]);
+            }
+        }
+}
+
 template <int MT>
 __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
-    constexpr int NS = mm_ns<MT>();
-    constexpr int XD = mm_xd<MT>();
+    constexpr int XP = mm_xp<MT>();
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    u32x4* xb = reinterpret_cast<u32x4*>(lds);                                                  // [NS][MT][4][64]
-    float* sxb = reinterpret_cast<float*>(lds + NS * mm_slot_bytes<MT>());                      // [NS][kLoaders][MT*16]
-    f32x2* smb = reinterpret_cast<f32x2*>(lds + NS * mm_slot_bytes<MT>() + mm_sx_bytes<MT>());  // [gps][64]
+    u32x4* xb = reinterpret_cast<u32x4*>(lds);                                               // [2][2][MT][4][64]
+    float* sxb = reinterpret_cast<float*>(lds + mm_ring_bytes<MT>());                        // [2][2][MT*16]
+    f32x2* smb = reinterpret_cast<f32x2*>(lds + mm_ring_bytes<MT>() + mm_sx_bytes<MT>());    // [gps][64]
 
     int ti = 0;
 #pragma unroll
@@ -130,152 +158,177 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
     ng = ng < gps ? ng : gps;                      // groups of this slice (>= 1 by construction)
     const int row0 = blk * kRows;
     const uint32_t rowbytes = (uint32_t)a.K >> 1;
-    // Groups run in rounds of kPre; past the slice's last group the loads
-    // re-read that group (every load is unconditional, so the wait counts
-    // stay exact) and the results are not accumulated.
-    const int niter = ((ng + kPre - 1) / kPre) * kPre;
-
-    f32x4 acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the two halves of the slice: groups [0, h0) and [h0, ng)
+    const int h0 = (ng + 1) >> 1;
+    const int h1 = ng - h0;
+    // Group steps run in rounds of kPre; past a half's last group the loads
+    // re-read that group (every load is unconditional, so the wait counts stay
+    // exact) and the results are not accumulated.
+    const int niter = ((h0 + kPre - 1) / kPre) * kPre;
 
     if (wave < kCompute) {
         // ------------------------------------------------------------ compute
-        const int trow0 = row0 + 16 * wave;
-        int nr = a.N - trow0;
-        // uniform; kept in a scalar register so the buffer resource is too
-        nr = __builtin_amdgcn_readfirstlane(nr < 0 ? 0 : (nr > 16 ? 16 : nr));
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)trow0 * rowbytes, (uint32_t)nr * rowbytes);
-        const uint32_t avoff = (uint32_t)(lane & 15) * rowbytes + ((uint32_t)g0 << 6) + ((uint32_t)(lane >> 4) << 4);
-        auto aload = [&](int j) { return buf_load16(rw, avoff + ((uint32_t)(j < ng ? j : ng - 1) << 6), 0); };
-        u32x4 q[kPre];
-#pragma unroll
-        for (int u = 0; u < kPre; ++u) q[u] = aload(u);
-        lds_barrier();     // parameters and activation group 0 ready
-
-        // Software pipeline: iteration j issues group j's MFMAs into Dc and
-        // folds group j - 1 (Dp, with its SX / scale / min read one iteration
-        // earlier) while those run.
-        f32x4 Dp[MT];
-        float sxp[MT];
-        f32x4 smp01 = {0.f, 0.f, 0.f, 0.f}, smp23 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) { Dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f}; sxp[mt] = 0.f; }
-        auto fold = [&](const f32x4 (&D)[MT], const float (&sx)[MT], f32x4 sm01, f32x4 sm23) {
-            const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
-            const float mn[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float t = fmaf(-128.f, sx[mt], D[mt][v]);
-                    acc[mt][v] = fmaf(mn[v], sx[mt], fmaf(sc[v], t, acc[mt][v]));
-                }
+        const int rp = wave & 1, kh = wave >> 1;
+        const int hlen = kh == 0 ? h0 : h1;
+        const int hbase = kh == 0 ? 0 : h0;
+        const int hlast = hlen > 0 ? hlen - 1 : 0;
+        const int hb = hlen > 0 ? hbase : 0;
+        const int prow0 = row0 + 32 * rp;
+        int nr = a.N - prow0;
+        nr = __builtin_amdgcn_readfirstlane(nr < 0 ? 0 : (nr > 32 ? 32 : nr));
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)prow0 * rowbytes, (uint32_t)nr * rowbytes);
+        const uint32_t avoff = (uint32_t)(lane & 15) * rowbytes + ((uint32_t)(g0 + hb) << 6) + ((uint32_t)(lane >> 4) << 4);
+        auto aload = [&](int i, int t) {
+            return buf_load16(rw, avoff + (uint32_t)t * 16u * rowbytes + ((uint32_t)(i < hlast ? i : hlast) << 6), 0);
         };
-        int slot0 = 0;                              // slot of group j0
-        for (int j0 = 0; j0 < niter; j0 += kPre) {
+        u32x4 q[kPre][2];
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) { q[u][0] = aload(u, 0); q[u][1] = aload(u, 1); }
+
+        f32x4 acc[2][MT];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lds_barrier();     // parameters and activation step 0 ready
+
+        for (int i0 = 0; i0 < niter; i0 += kPre) {
 #pragma unroll
             for (int u = 0; u < kPre; ++u) {
-                const int j = j0 + u;
-                int slot = slot0 + u;
-                slot = slot >= NS ? slot - NS : slot;
-                slot = slot >= NS ? slot - NS : slot;
-                slot = slot >= NS ? slot - NS : slot;
-                const u32x4* xs = xb + (size_t)slot * MT * 4 * 64 + lane;
-                float sxc[MT];
+                const int i = i0 + u;
+                const int slot = i & 1;
+                const u32x4* xs = xb + (size_t)((slot * 2 + kh) * MT) * 4 * 64 + lane;
+                const u32x4 qa0 = q[u][0], qa1 = q[u][1];
+                q[u][0] = aload(i + kPre, 0);
+                q[u][1] = aload(i + kPre, 1);
+                const uint32_t qd[2][4] = {{qa0.x, qa0.y, qa0.z, qa0.w}, {qa1.x, qa1.y, qa1.z, qa1.w}};
+                f32x4 D[2][MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    sxc[mt] = sxb[(slot * kLoaders + 0) * MT * 16 + mt * 16 + (lane & 15)] +
-                              sxb[(slot * kLoaders + 1) * MT * 16 + mt * 16 + (lane & 15)];
-                const int jc = j < ng ? j : ng - 1;
-                const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + jc * kRows + 16 * wave + 4 * (lane >> 4));
-                const f32x4 smc01 = sm4[0], smc23 = sm4[1];
-                // fold group j - 1 (its MFMAs ran during the previous iteration)
-                if (j >= 1 && j - 1 < ng) fold(Dp, sxp, smp01, smp23);
-                // group j: per k-step, three activation fragments and one weight operand
-                const u32x4 qa = q[u];
-                q[u] = aload(j + kPre);
-                const uint32_t qd[4] = {qa.x, qa.y, qa.z, qa.w};
-                f32x4 Dc[MT];
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) Dc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int mt = 0; mt < MT; ++mt) D[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     u32x4 B[MT];
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) B[mt] = xs[(mt * 4 + s) * 64];
-                    uint32_t A[4];
-                    q4_pairs(qd[s], A);
-                    const bf16x8_t Av = as_bf16x8(A[0], A[1], A[2], A[3]);
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        Dc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, as_bf16x8(B[mt]), Dc[mt], 0, 0, 0);
+                    for (int t = 0; t < 2; ++t) {
+                        uint32_t A[4];
+                        q4_pairs(qd[t][s], A);
+                        const bf16x8_t Av = as_bf16x8(A[0], A[1], A[2], A[3]);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, as_bf16x8(B[mt]), D[t][mt], 0, 0, 0);
+                    }
                 }
+                if (i < hlen) {
+                    float sx[MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) { Dp[mt] = Dc[mt]; sxp[mt] = sxc[mt]; }
-                smp01 = smc01;
-                smp23 = smc23;
+                    for (int mt = 0; mt < MT; ++mt) sx[mt] = sxb[(slot * 2 + kh) * MT * 16 + mt * 16 + (lane & 15)];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + (hbase + i) * kRows + 32 * rp + 16 * t + 4 * (lane >> 4));
+                        const f32x4 sm01 = sm4[0], sm23 = sm4[1];
+                        const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
+                        const float mn[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const float tt0 = fmaf(-128.f, sx[mt], D[t][mt][v]);
+                                acc[t][mt][v] = fmaf(mn[v], sx[mt], fmaf(sc[v], tt0, acc[t][mt][v]));
+                            }
+                    }
+                }
                 lds_barrier();
             }
-            slot0 += kPre % NS;
-            slot0 = slot0 >= NS ? slot0 - NS : slot0;
         }
-        if (niter - 1 < ng) fold(Dp, sxp, smp01, smp23);
+
+        // the two K halves meet: half 1 hands its tiles to half 0 through LDS
+        // (the ring is free once every wave has passed the last barrier)
+        f32x4* red = reinterpret_cast<f32x4*>(lds);   // [2 row pairs][2 tiles][MT][64]
+        if (kh == 1) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) red[((rp * 2 + t) * MT + mt) * 64 + lane] = acc[t][mt];
+        }
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[t][mt] += red[((rp * 2 + t) * MT + mt) * 64 + lane];
+        }
+        // ------------------------------------------------------------ epilogue
+        if (KS == 1) {
+            __syncthreads();   // every wave meets the same barriers
+            if (kh == 0) write_y<MT>(a, tt.t[ti].y8 != 0, prow0, lane, acc);
+            return;
+        }
+        // split K: publish this slice's partial tile; the last slice to arrive
+        // reduces.  Partials are written and read with device-coherent 16-byte
+        // accesses (1 KB contiguous per instruction), which do not stop in the
+        // per-XCD L2, and every wave waits for its stores to complete before
+        // the barrier that precedes the block's counter update, so no
+        // cache-wide write-back or invalidate is needed.
+        if (kh == 0) {
+            const int blocks = (a.N + kRows - 1) / kRows;
+            const __amdgpu_buffer_rsrc_t rpart = make_rsrc(tt.t[ti].part, (uint32_t)blocks * KS * 4u * MT * 64u * 16u);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t][mt]), rpart,
+                                                           part_off<MT>(blk, KS, ks, rp, t, mt, lane), 0, kCoherent);
+        }
     } else {
         // ------------------------------------------------------------- loader
-        // Loader L owns k-steps s = 2L, 2L + 1 of every batch tile.  For group
-        // j it issues, per (mt, s), one direct-to-LDS load in which lane l
-        // fetches the 8 activations of batch row 16 mt + l % 16 at group
-        // columns 32 (l / 16) + 8 s .. + 8, landing exactly where compute lane
-        // l reads them; once they have landed it re-pairs them in place to
-        // match the weight operand and sums them for SX.
-        const int L = wave - kCompute;
-        const int lt = tid - 64 * kCompute;   // 0 .. 64 * kLoaders - 1
-        const uint16_t* xg = a.x;
-        auto issue = [&](int j) {
-            const int slot = j % NS;
-            const int g = g0 + (j < ng ? j : ng - 1);
-#pragma unroll
-            for (int i = 0; i < 2 * MT; ++i) {
-                const int mt = i >> 1, s = 2 * L + (i & 1);
-                int m = 16 * mt + (lane & 15);
-                m = m < a.M ? m : a.M - 1;        // padding rows re-read a real row; their columns are dropped
-                const uint16_t* src = xg + (size_t)m * a.K + (g << 7) + 32 * (lane >> 4) + 8 * s;
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                                 (__attribute__((address_space(3))) void*)(xb + ((size_t)slot * MT * 4 + mt * 4 + s) * 64),
-                                                 16, 0, 0);
-            }
+        const int L = wave - kCompute;          // the K half this loader feeds
+        const int lt = tid - 64 * kCompute;     // 0 .. 64 * kLoaders - 1
+        const int hlen = L == 0 ? h0 : h1;
+        const int hbase = L == 0 ? 0 : h0;
+        const int hlast = hlen > 0 ? hlen - 1 : 0;
+        const int hb = hlen > 0 ? hbase : 0;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.M * a.K * 2));
+        // piece (mt, s) of step i: lane l gets the 8 activations of batch row
+        // 16 mt + l % 16 at group columns 32 (l / 16) + 8 s .. + 8
+        auto xload = [&](int i, int p) {
+            const int mt = p >> 2, s = p & 3;
+            const int m = 16 * mt + (lane & 15);
+            const int g = g0 + hb + (i < hlast ? i : hlast);
+            const int k = (g << 7) + 32 * (lane >> 4) + 8 * s;
+            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((m * a.K + k) * 2), 0, 0));
         };
-        auto prepare = [&](int j) {
-            const int slot = j % NS;
-            u32x4* base = xb + (size_t)slot * MT * 4 * 64 + lane;
-            u32x4 v[MT][2];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) v[mt][h] = base[(mt * 4 + 2 * L + h) * 64];
+        auto stage = [&](int i, const u32x4 (&xr)[4 * MT]) {
+            const int slot = i & 1;
+            u32x4* dst = xb + (size_t)((slot * 2 + L) * MT) * 4 * 64 + lane;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 float sx = 0.f;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int s = 0; s < 4; ++s) {
+                    const u32x4 v = xr[mt * 4 + s];
                     uint32_t pr[4];
-                    xq4_pairs(v[mt][h].x, v[mt][h].y, v[mt][h].z, v[mt][h].w, pr);
-                    base[(mt * 4 + 2 * L + h) * 64] = u32x4{pr[0], pr[1], pr[2], pr[3]};
-                    sx = dot2(v[mt][h].x, 0x3F803F80u, sx);
-                    sx = dot2(v[mt][h].y, 0x3F803F80u, sx);
-                    sx = dot2(v[mt][h].z, 0x3F803F80u, sx);
-                    sx = dot2(v[mt][h].w, 0x3F803F80u, sx);
+                    xq4_pairs(v.x, v.y, v.z, v.w, pr);
+                    dst[(mt * 4 + s) * 64] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+                    sx = dot2(v.x, 0x3F803F80u, sx);
+                    sx = dot2(v.y, 0x3F803F80u, sx);
+                    sx = dot2(v.z, 0x3F803F80u, sx);
+                    sx = dot2(v.w, 0x3F803F80u, sx);
                 }
                 // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same batch row
                 sx += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, sx), 0x401F));
                 sx += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, sx)));
-                const int m = 16 * mt + lane;
-                if (lane < 16) sxb[(slot * kLoaders + L) * MT * 16 + mt * 16 + lane] = (m < a.M) ? sx : 0.f;
+                if (lane < 16) sxb[(slot * 2 + L) * MT * 16 + mt * 16 + lane] = sx;
             }
         };
+        u32x4 xr[XP][4 * MT];
 #pragma unroll
-        for (int u = 0; u <= XD; ++u) issue(u);
+        for (int u = 0; u < XP; ++u)
+#pragma unroll
+            for (int p = 0; p < 4 * MT; ++p) xr[u][p] = xload(u, p);
 
         // group parameters of the block's rows for the slice, fp32 (scale, min) [group][row]
         if (tt.t[ti].sm16) {
@@ -325,87 +378,75 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
             }
         }
 
-        __builtin_amdgcn_s_waitcnt(0);
-        prepare(0);
+        stage(0, xr[0]);
+#pragma unroll
+        for (int p = 0; p < 4 * MT; ++p) xr[0][p] = xload(XP, p);
         lds_barrier();
 
-        // iteration j prepares group j + 1 and issues group j + 1 + XD into
-        // the slot of group j - 1, which the compute waves finished before
-        // the previous barrier
-        for (int j0 = 0; j0 < niter; j0 += kPre) {
+        // step i stages step i + 1, held in ring entry (i + 1) % XP (i0 is a
+        // multiple of kPre, itself a multiple of XP)
+        for (int i0 = 0; i0 < niter; i0 += kPre) {
 #pragma unroll
             for (int u = 0; u < kPre; ++u) {
-                const int j = j0 + u;
-                __builtin_amdgcn_s_waitcnt(kWaitXD<MT>);   // group j + 1 has landed
-                prepare(j + 1);
-                issue(j + 1 + XD);
+                const int i = i0 + u;
+                const int r = (u + 1) % XP;
+                stage(i + 1, xr[r]);
+#pragma unroll
+                for (int p = 0; p < 4 * MT; ++p) xr[r][p] = xload(i + 1 + XP, p);
                 lds_barrier();
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);   // no direct-to-LDS load outlives the wave
+        // the compute waves' two barriers of the half merge and the epilogue
+        __syncthreads();
+        if (KS == 1) {
+            __syncthreads();
+            return;
+        }
     }
 
-    // ---------------------------------------------------------------- epilogue
-    if (KS == 1) {
-        if (wave < kCompute) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int m = 16 * mt + (lane & 15);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = row0 + 16 * wave + 4 * (lane >> 4) + v;
-                    if (m < a.M && row < a.N) a.y[(size_t)m * a.N + row] = f32_to_bf16(acc[mt][v]);
-                }
-            }
-        }
-        return;
-    }
-    // split K: publish this slice's partial tile; the last slice to arrive
-    // reduces.  Partials are written and read with device-coherent (agent
-    // scope) accesses, which do not stop in the per-XCD L2, and every wave
-    // waits for its stores to complete before the barrier that precedes the
-    // block's counter update, so no cache-wide write-back or invalidate is
-    // needed.
-    float* part = tt.t[ti].part;
+    // --------------------------------------------------- split-K completion
     unsigned* cnt = tt.t[ti].cnt;
-    if (wave < kCompute) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float* dst = part + ((((size_t)blk * KS + ks) * kCompute + wave) * MT * 64 + mt * 64 + lane) * 4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) __hip_atomic_store(dst + v, acc[mt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
     __syncthreads();
     __shared__ unsigned s_prev;
     if (tid == 0) s_prev = __hip_atomic_fetch_add(&cnt[blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_prev != (unsigned)(KS - 1)) return;
-    if (wave < kCompute) {
-        f32x4 sum[MT];
+    if (wave < kCompute && (wave >> 1) == 0) {
+        // sum the slices in order, the tiles of kRB slices in flight at once
+        constexpr int kRB = mm_reduce_batch<MT>();
+        const int rp = wave & 1;
+        const int blocks = (a.N + kRows - 1) / kRows;
+        const __amdgpu_buffer_rsrc_t rpart = make_rsrc(tt.t[ti].part, (uint32_t)blocks * KS * 4u * MT * 64u * 16u);
+        f32x4 sum[2][MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) sum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < KS; ++s)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const float* src = part + ((((size_t)blk * KS + s) * kCompute + wave) * MT * 64 + mt * 64 + lane) * 4;
+            for (int mt = 0; mt < MT; ++mt) sum[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < KS; s0 += kRB) {
+            u32x4 pv[kRB][2][MT];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) sum[mt][v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int k = 0; k < kRB; ++k)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = 16 * mt + (lane & 15);
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = row0 + 16 * wave + 4 * (lane >> 4) + v;
-                if (m < a.M && row < a.N) a.y[(size_t)m * a.N + row] = f32_to_bf16(sum[mt][v]);
-            }
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint32_t off = s0 + k < KS ? part_off<MT>(blk, KS, s0 + k, rp, t, mt, lane) : 0xFFFFFFF0u;
+                        pv[k][t][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rpart, off, 0, kCoherent));
+                    }
+#pragma unroll
+            for (int k = 0; k < kRB; ++k)
+                if (s0 + k < KS) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) sum[t][mt] += __builtin_bit_cast(f32x4, pv[k][t][mt]);
+                }
         }
+        write_y<MT>(a, tt.t[ti].y8 != 0, row0 + 32 * rp, lane, sum);
     }
     if (tid == 0) __hip_atomic_store(&cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
 
 // Split plan: no split while the row blocks alone give >= 256 workgroups;
 // otherwise enough slices to reach about 384 workgroups, each slice >= 4
@@ -439,28 +480,33 @@ void mm_plan(const GemvArgs* tasks, int count, bool can_split, int* ks, int* gps
     }
 }
 
+// Workspace a launch needs: 0 when no task is split, or when the counters of
+// the split tasks would not fit the counter region (the launch then runs
+// unsplit).
 template <int MT>
 size_t ws_bytes_mt(const GemvArgs* tasks, int count) {
     int ks[kMaxTasks], gps[kMaxTasks];
     mm_plan<MT>(tasks, count, true, ks, gps);
-    size_t bytes = 0;
+    size_t cnt = 0, part = 0;
     for (int i = 0; i < count; ++i) {
         if (ks[i] <= 1) continue;
         const size_t blocks = (tasks[i].N + kRows - 1) / kRows;
-        bytes += blocks * ks[i] * kCompute * MT * 64 * 16;
-        bytes += ((blocks * 4 + 255) / 256) * 256;
+        part += blocks * ks[i] * kCompute * MT * 64 * 16;
+        cnt += blocks * 4;
     }
-    return bytes;
+    return (part > 0 && cnt <= kCntBytes) ? kCntBytes + part : 0;
 }
 
 template <int MT>
 hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t st) {
     int ks[kMaxTasks], gps[kMaxTasks];
-    const bool split = ws != nullptr && ws_bytes >= ws_bytes_mt<MT>(tasks, count);
+    const size_t need = ws_bytes_mt<MT>(tasks, count);
+    const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
     mm_plan<MT>(tasks, count, split, ks, gps);
     MmTable tt{};
     for (int i = 0; i < kMaxTasks; ++i) tt.blk0[i] = 0x7fffffff;
-    uint8_t* p = static_cast<uint8_t*>(ws);
+    uint8_t* pc = static_cast<uint8_t*>(ws);
+    uint8_t* pp = pc + kCntBytes;
     int grid = 0, gmax = 0;
     for (int i = 0; i < count; ++i) {
         const int blocks = (tasks[i].N + kRows - 1) / kRows;
@@ -471,11 +517,12 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         const int G = tasks[i].K >> 7;
         tt.t[i].sm16 = (G % 8 == 0 && gps[i] % 8 == 0 && (reinterpret_cast<uintptr_t>(tasks[i].scale) % 16) == 0 &&
                         (reinterpret_cast<uintptr_t>(tasks[i].minv) % 16) == 0) ? 1 : 0;
+        tt.t[i].y8 = (reinterpret_cast<uintptr_t>(tasks[i].y) % 8 == 0 && tasks[i].N % 4 == 0) ? 1 : 0;
         if (ks[i] > 1) {
-            tt.t[i].part = reinterpret_cast<float*>(p);
-            p += (size_t)blocks * ks[i] * kCompute * MT * 64 * 16;
-            tt.t[i].cnt = reinterpret_cast<unsigned*>(p);
-            p += (((size_t)blocks * 4 + 255) / 256) * 256;
+            tt.t[i].cnt = reinterpret_cast<unsigned*>(pc);
+            pc += (size_t)blocks * 4;
+            tt.t[i].part = reinterpret_cast<float*>(pp);
+            pp += (size_t)blocks * ks[i] * kCompute * MT * 64 * 16;
         }
         grid += blocks * ks[i];
         gmax = gps[i] > gmax ? gps[i] : gmax;

@@ -103,17 +103,21 @@ int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant,
 
 /*
  * Same as q4g128_gemv_grouped, with a caller-owned device workspace that lets
- * the Q4_VARIANT_TILED kernel split K over several workgroups when the rows
- * alone cannot fill the GPU (the o/down stage of a decode layer at M = 48).
- * The partial tiles are summed in a fixed order by whichever workgroup
- * finishes a row block last, so results do not depend on timing and equal
- * those of the unsplit kernel within fp32 rounding.
+ * the Q4_VARIANT_TILED kernel deal the work of the launch (64-row blocks x
+ * 128-column groups) out to its workgroups in equal ranges, so that a row
+ * block may be split over K between neighbouring workgroups.  Their partial
+ * tiles are summed in a fixed order by whichever of them finishes last, so
+ * results do not depend on timing and equal those of the unsplit kernel
+ * within fp32 rounding.
  *   workspace        device memory, 256-byte aligned, ZERO-FILLED before its
- *                    first use; it holds arrival counters, which every call
- *                    leaves at zero, and partial tiles, which are scratch: the
- *                    workspace can be reused without being cleared again
+ *                    first use; its first 64 KiB hold arrival counters, which
+ *                    every call leaves at zero, the rest partial tiles, which
+ *                    are scratch: the workspace can be reused, also by calls
+ *                    with other tasks, without being cleared again
  *   workspace_bytes  at least what q4g128_workspace_bytes reports for the same
- *                    tasks and M; with less (or NULL) the call runs unsplit
+ *                    tasks and M (a workspace sized for the largest of several
+ *                    calls serves them all); with less (or NULL) the call runs
+ *                    unsplit
  * Calls that use one workspace must not overlap in time (same stream, or
  * ordered by events).
  */

@@ -55,7 +55,7 @@ def q4call(x=A, M=1, K=2048, qw=A + (1 << 24), sc=A + (2 << 24), mn=A + (3 << 24
     (dict(sc=A + (2 << 24) + 1), EALIGN), (dict(y=A + (4 << 24) + 1), EALIGN),
     (dict(y=A + (1 << 24) + 64), EALIAS), (dict(y=A + 16), EALIAS), (dict(y=A + (3 << 24)), EALIAS),
     (dict(variant=5), EVARIANT), (dict(variant=-1), EVARIANT), (dict(variant=3, M=5), EVARIANT),
-    (dict(variant=4, M=64, K=8192), EVARIANT),
+    (dict(variant=4, M=64, K=32768, N=64), EVARIANT),
     (dict(variant=3, K=1024), EVARIANT),
 ])
 def test_q4_validation(kw, rc):

@@ -403,6 +403,37 @@ def test_q4_grouped_split_k_workspace(q4, M):
         assert all(torch.equal(a, b) for a, b in zip(again, outs))
 
 
+def test_q4_workspace_shared_by_different_calls(q4):
+    # the two grouped calls of a decode layer (q/k/v/gate/up, then o/down) at
+    # M = 48 take turns on one workspace sized for the larger; every call must
+    # find its counters at zero, so each round matches the oracle and the
+    # first round bitwise
+    M = 48
+    lay, w32 = _layer_q4()
+    xin = gpu(synth.x_bf16(M, 2048, ("wsh-xin",)))
+    xat = gpu(synth.x_bf16(M, 2048, ("wsh-xat",)))
+    xff = gpu(synth.x_bf16(M, 8192, ("wsh-xff",)))
+    xs = {"q": xin, "k": xin, "v": xin, "gate": xin, "up": xin, "o": xat, "down": xff}
+    dev = {p: tuple(gpu(t) for t in lay[p]) for p in synth.LAYER_ORDER}
+    stages = [("q", "k", "v", "gate", "up"), ("o", "down")]
+    items = [[(xs[p], *dev[p], None) for p in st] for st in stages]
+    need = max(q4.q4g128_workspace_bytes(it) for it in items)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = None
+    for rnd in range(3):
+        outs = [q4.q4g128_gemv_grouped(it, workspace=ws) for it in items]
+        if first is None:
+            first = outs
+            for st, ys in zip(stages, outs):
+                for p, y in zip(st, ys):
+                    xb = x_bits(xs[p].cpu())
+                    check_gemv(y, oracle.gemv_f64(xb, w32[p]), w32[p], xb, f"shared ws {p}")
+        else:
+            for ys, y0 in zip(outs, first):
+                assert all(torch.equal(a, b) for a, b in zip(ys, y0)), rnd
+
+
 def test_q4_split_k_small_tasks(q4):
     # a few short matrices: split into as many slices as K allows, one-hot exact
     N, K, M = 100, 2048, 20
@@ -415,6 +446,42 @@ def test_q4_split_k_small_tasks(q4):
     y = q4.q4g128_gemv_grouped(items, workspace=ws)[0]
     exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
     assert np.array_equal(y.cpu().float().numpy(), exp)
+
+
+@pytest.mark.parametrize("M", [5, 20, 48, 64])
+def test_q4_split_k_mixed_tasks_onehot_and_random(q4, M):
+    # with a workspace, a launch whose row blocks cannot fill the GPU splits
+    # the tasks whose K allows it over several workgroups and runs the others
+    # (K = 128, 384, 1152) whole; one-hot activations must come out exact and
+    # random ones within tolerance, and repeat bitwise on the reused workspace
+    shapes = [(70, 128), (200, 1152), (130, 2048), (64, 4096), (1000, 384)]
+    mats = [synth.q4_matrix(N, K, ("sk", N, K)) for N, K in shapes]
+    w32s = [oracle.q4g128_dequant_f32(m[0].numpy(), synth.bits16(m[1]), synth.bits16(m[2])) for m in mats]
+    for kind in ("onehot", "random"):
+        xs, kss = [], []
+        for i, (N, K) in enumerate(shapes):
+            if kind == "onehot":
+                ks = _onehot_ks(K, M, 900 + 7 * i + M)
+                kss.append(ks)
+                xs.append(gpu(onehot_x(K, ks)))
+            else:
+                xs.append(gpu(synth.x_bf16(M, K, ("sk-x", K, M))))
+        items = [(x, *(gpu(t) for t in m), None) for x, m in zip(xs, mats)]
+        nbytes = q4.q4g128_workspace_bytes(items)
+        assert nbytes > 0
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        outs = q4.q4g128_gemv_grouped(items, variant=4, workspace=ws)
+        for i, ((N, K), w32, x, y) in enumerate(zip(shapes, w32s, xs, outs)):
+            if kind == "onehot":
+                exp = torch.from_numpy(rn_bf16_bits(w32[:, kss[i]].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+                got = y.cpu().float().numpy()
+                assert np.array_equal(got, exp), (N, K, M, np.argwhere(got != exp)[:4])
+            else:
+                xb = x_bits(x.cpu())
+                check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"stream-k N={N} K={K} M={M}")
+        for _ in range(3):
+            again = q4.q4g128_gemv_grouped(items, variant=4, workspace=ws)
+            assert all(torch.equal(a, b) for a, b in zip(again, outs))
 
 
 def test_q4_grouped_mixed_k(q4):
