@@ -103,12 +103,11 @@ int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant,
 
 /*
  * Same as q4g128_gemv_grouped, with a caller-owned device workspace that lets
- * the Q4_VARIANT_TILED kernel deal the work of the launch (64-row blocks x
- * 128-column groups) out to its workgroups in equal ranges, so that a row
- * block may be split over K between neighbouring workgroups.  Their partial
- * tiles are summed in a fixed order by whichever of them finishes last, so
- * results do not depend on timing and equal those of the unsplit kernel
- * within fp32 rounding.
+ * the Q4_VARIANT_TILED kernel split K over several workgroups when the row
+ * blocks of the launch alone cannot fill the GPU (the o/down stage of a decode
+ * layer at M = 48).  The partial tiles are summed in a fixed order by
+ * whichever workgroup finishes a row block last, so results do not depend on
+ * timing and equal those of the unsplit kernel within fp32 rounding.
  *   workspace        device memory, 256-byte aligned, ZERO-FILLED before its
  *                    first use; its first 64 KiB hold arrival counters, which
  *                    every call leaves at zero, the rest partial tiles, which
