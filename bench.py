@@ -10,9 +10,11 @@ scales + activations read + outputs written) per second at batch M = 1.  The
 same step at M = 48 is reported alongside.
 
 Also reported on the same JSON line:
-  * roofline: the int4 GEMV kernel used at M = 1, its algorithmic bytes per
-    launch over its average launch duration (HIP events around each launch
-    on the launch stream), against the 8 TB/s HBM peak;
+  * roofline: the int4 GEMV kernel used at M = 1 (the streaming kernel), its
+    algorithmic bytes per launch over its average launch duration (HIP events
+    around each launch on the launch stream), against the 8 TB/s HBM peak,
+    with the HBM bytes per launch measured by rocprofv3 counters; the same for
+    the matrix-core kernel at M = 48 under roofline_M48;
   * cpu_baseline: the CPU oracle (NumPy, fp64) timed on a bounded sample of
     the same workload on this host's cores.
 
@@ -240,42 +242,47 @@ def cpu_baseline(wl, budget_s=15.0):
                       f"{t_used:.1f} s"}
 
 
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_q4_grouped_M1_traffic.json")
+# per batch size: the kernel the grouped int4 launches run, the sources it is
+# built from, and the committed rocprofv3 traffic record for it
+KERNELS = {
+    1: ("gemv_stream_kernel<FmtQ4, 1>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
+        os.path.join(ROOT, "profiles", "gemv_stream_q4_M1_grouped_traffic.json")),
+    48: ("q4_mm_kernel<3>", ("common.h", "formats.h", "internal.h", "gemv_mm.hip"),
+         os.path.join(ROOT, "profiles", "q4_mm_M48_grouped_traffic.json")),
+}
 
 
-def csrc_digest():
-    """sha256 over the sources the measured packed-dot kernel is built from."""
+def csrc_digest(M):
+    """sha256 over the sources of the kernel the grouped launches run at M."""
     import hashlib
     h = hashlib.sha256()
-    files = [os.path.join(ROOT, "bit_weight_only_q4g128_amd", "csrc", n)
-             for n in ("common.h", "formats.h", "internal.h", "gemv_dot2.hip")]
-    for f in files:
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    for n in KERNELS[M][1]:
+        with open(os.path.join(ROOT, "bit_weight_only_q4g128_amd", "csrc", n), "rb") as fh:
+            h.update(n.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the M=1 grouped int4 GEMV from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None if the kernel sources
-    changed since those counters were taken."""
+def measured_traffic(M):
+    """HBM bytes per grouped int4 launch at M from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs, or None if the kernel sources changed since
+    those counters were taken."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(KERNELS[M][2]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("csrc_digest") != csrc_digest():
+    if rec.get("csrc_digest") != csrc_digest(M):
         return None
     return rec.get("traffic_bytes_per_launch")
 
 
-def counters_pass(q4, synth, torch, head_rows):
-    """Workload for hardware-counter runs (no timing): the M=1 grouped step
+def counters_pass(q4, synth, torch, head_rows, M):
+    """Workload for hardware-counter runs (no timing): the grouped step at M
     three times, eagerly, then a 256 MiB device-to-device copy whose byte
     count is known (the reference that scales FETCH_SIZE / WRITE_SIZE)."""
     wl = Workload(q4, synth, torch, head_rows)
-    calls = wl.launches(1, "grouped")
+    calls = wl.launches(M, "grouped")
     for _ in range(3):
         for f, _, _ in calls:
             f()
@@ -286,7 +293,7 @@ def counters_pass(q4, synth, torch, head_rows):
     torch.cuda.synchronize()
     b.copy_(a)
     torch.cuda.synchronize()
-    log(f"bench: counters pass done ({len(calls)} launches per step, csrc digest {csrc_digest()})")
+    log(f"bench: counters pass at M={M} done ({len(calls)} launches per step, csrc digest {csrc_digest(M)})")
 
 
 def main():
@@ -297,6 +304,7 @@ def main():
     ap.add_argument("--head", choices=("full", "slice"), default="full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
+    ap.add_argument("--counters-m", type=int, choices=(1, 48), default=1, help="batch size of the --counters workload")
     ap.add_argument("--modes", default="M1_grouped,M1_plain,M48_grouped,M48_plain",
                     help="comma list of timed modes; M1_grouped is always timed (it is the headline value)")
     args = ap.parse_args()
@@ -312,7 +320,7 @@ def main():
     torch.cuda.set_device(0)
     head_rows = synth.HEAD_FULL[0] if args.head == "full" else synth.HEAD_SLICE[0]
     if args.counters:
-        counters_pass(q4, synth, torch, head_rows)
+        counters_pass(q4, synth, torch, head_rows, args.counters_m)
         return
     wl = Workload(q4, synth, torch, head_rows)
 
@@ -328,10 +336,18 @@ def main():
             log(f"bench: M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(M, mode)]['gbs']:6.0f} GB/s, "
                 f"{1e3 / ms:6.0f} steps/s, {res[(M, mode)]['launches']} launches")
             del g
-    kms, kbytes = time_q4_launches(torch, q4, wl, 1, "grouped")
-    kname = f"gemv_dot2_kernel<FmtQ4, MT=1, CPL=1> ({q4.variant_name(q4.FMT_Q4G128, 0, 1, 2048, 2048)}), grouped launches"
-    achieved = kbytes / (kms * 1e-3) / 1e9
-    log(f"bench: int4 GEMV launches at M=1: avg {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
+    roof = {}
+    for M in (1, 48):
+        if M != 1 and f"M{M}_grouped" not in modes:
+            continue
+        kms, kbytes = time_q4_launches(torch, q4, wl, M, "grouped")
+        achieved = kbytes / (kms * 1e-3) / 1e9
+        vname = q4.variant_name(q4.FMT_Q4G128, 0, M, 2048, 2048)
+        log(f"bench: int4 GEMV launches at M={M} ({vname}): avg {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, "
+            f"{achieved:.0f} GB/s")
+        roof[M] = {"bound": "hbm", "kernel": f"{KERNELS[M][0]} ({vname}), M={M} grouped launches",
+                   "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                   "traffic": measured_traffic(M), "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)}
     head = res[(1, "grouped")]
 
     out = {
@@ -361,10 +377,10 @@ def main():
                                         "launches_per_step": r["launches"], "bytes_per_step": r["bytes"]}
                       for (M, mode), r in res.items()},
         },
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)},
+        "roofline": roof[1],
     }
+    if 48 in roof:
+        out["roofline_M48"] = roof[48]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
