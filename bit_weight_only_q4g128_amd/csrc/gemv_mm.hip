@@ -1,7 +1,8 @@
 // Matrix-core GEMV for batched decode, int4 g128 (gfx950, v_mfma_f32_16x16x32_bf16).
 //
 // A workgroup owns a block of 64 weight rows and one slice of K (the whole of
-// K unless the row blocks alone cannot fill the chip).  The slice is cut into
+// K unless the row blocks alone cannot give every CU the same work; see the
+// split plan).  The slice is cut into
 // two halves that the workgroup walks side by side, and it runs six waves:
 //
 //   * four compute waves, one per (32-row pair, K half).  A compute wave
@@ -43,6 +44,7 @@ constexpr int kPre = 4;          // weight groups in flight per compute lane
 constexpr int kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     u32x4 v = {a, b, c, d};
@@ -54,7 +56,7 @@ struct MmTask {
     GemvArgs a;
     int ks;            // workgroups per row block (K slices)
     int gps;           // 128-column groups per slice
-    int sm16;          // group parameters can be read as 16-byte pieces (see below)
+    int smw;           // group parameters can be read in pieces of smw (8 or 4) groups, 0: one by one
     int y8;            // y rows can be written 8 bytes at a time (y 8-byte aligned, N % 4 == 0)
     float* part;       // partial tiles (ks > 1): [blocks][ks][4 tiles][MT][64 lanes] x 4 floats
     unsigned* cnt;     // arrival counters (ks > 1): [blocks]
@@ -161,10 +163,10 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
     // the two halves of the slice: groups [0, h0) and [h0, ng)
     const int h0 = (ng + 1) >> 1;
     const int h1 = ng - h0;
-    // Group steps run in rounds of kPre; past a half's last group the loads
-    // re-read that group (every load is unconditional, so the wait counts stay
-    // exact) and the results are not accumulated.
-    const int niter = ((h0 + kPre - 1) / kPre) * kPre;
+    // One group step per barrier, h0 of them.  Past a half's last group the
+    // loads re-read that group (every load is unconditional, so the wait
+    // counts stay exact) and the results are not accumulated.
+    const int niter = h0;
 
     if (wave < kCompute) {
         // ------------------------------------------------------------ compute
@@ -181,6 +183,10 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
         auto aload = [&](int i, int t) {
             return buf_load16(rw, avoff + (uint32_t)t * 16u * rowbytes + ((uint32_t)(i < hlast ? i : hlast) << 6), 0);
         };
+        // the loaders' first activation and group-parameter loads go out
+        // before this workgroup's weight prefetch, so they do not queue
+        // behind it
+        lds_barrier();
         u32x4 q[kPre][2];
 #pragma unroll
         for (int u = 0; u < kPre; ++u) { q[u][0] = aload(u, 0); q[u][1] = aload(u, 1); }
@@ -196,6 +202,7 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
 #pragma unroll
             for (int u = 0; u < kPre; ++u) {
                 const int i = i0 + u;
+                if (i >= niter) break;
                 const int slot = i & 1;
                 const u32x4* xs = xb + (size_t)((slot * 2 + kh) * MT) * 4 * 64 + lane;
                 const u32x4 qa0 = q[u][0], qa1 = q[u][1];
@@ -330,27 +337,37 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
 #pragma unroll
             for (int p = 0; p < 4 * MT; ++p) xr[u][p] = xload(u, p);
 
-        // group parameters of the block's rows for the slice, fp32 (scale, min) [group][row]
-        if (tt.t[ti].sm16) {
-            // 16-byte pieces (8 groups of one row), all loads issued at once:
-            // the host sets sm16 when K/128, the slice start and length are
-            // multiples of 8 and both arrays are 16-byte aligned
+        // group parameters of the block's rows for the slice, fp32 (scale, min)
+        // [group][row], every load of a lane issued before the first is used
+        const int smw = tt.t[ti].smw;
+        if (smw != 0) {
+            // pieces of smw = 8 or 4 groups of one row (16 or 8 bytes): the
+            // host sets smw when K/128, the slice start and length are
+            // multiples of it and both arrays are aligned to the piece
             int wg_rows = a.N - row0;
             wg_rows = __builtin_amdgcn_readfirstlane(wg_rows > kRows ? kRows : wg_rows);
             const uint32_t rb = (uint32_t)G * 2;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + (size_t)row0 * G, (uint32_t)wg_rows * rb);
             const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)wg_rows * rb);
-            const int ppr = ng >> 3;                  // pieces per row
-            constexpr int kMaxP = 4;                  // 64 rows * 64 groups / 8 / 128 threads
+            const int ppr = ng / smw;                 // pieces per row
+            constexpr int kMaxP = 4;                  // 64 rows x (56 groups / 8 or 16 groups / 4) / 128 threads
             u32x4 ps[kMaxP], pm[kMaxP];
 #pragma unroll
             for (int i = 0; i < kMaxP; ++i) {
                 const int c = lt + 64 * kLoaders * i;
                 const int r = c / ppr, pc = c - r * ppr;
-                const uint32_t off = (c < kRows * ppr) ? (uint32_t)r * rb + (uint32_t)(g0 + 8 * pc) * 2 : 0xFFFFFFF0u;
-                ps[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-                pm[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, off, 0, 0));
+                const uint32_t off = (c < kRows * ppr) ? r * rb + (uint32_t)(g0 + smw * pc) * 2 : 0xFFFFFFF0u;
+                if (smw == 8) {
+                    ps[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                    pm[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, off, 0, 0));
+                } else {
+                    const u32x2 s2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+                    const u32x2 m2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, off, 0, 0));
+                    ps[i] = u32x4{s2.x, s2.y, 0u, 0u};
+                    pm[i] = u32x4{m2.x, m2.y, 0u, 0u};
+                }
             }
+            lds_barrier();   // releases the compute waves' weight prefetch
 #pragma unroll
             for (int i = 0; i < kMaxP; ++i) {
                 const int c = lt + 64 * kLoaders * i;
@@ -360,21 +377,36 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
                     const uint32_t mw[4] = {pm[i].x, pm[i].y, pm[i].z, pm[i].w};
 #pragma unroll
                     for (int h = 0; h < 8; ++h) {
+                        if (h >= smw) break;
                         const uint16_t sh = (uint16_t)(sw[h >> 1] >> (16 * (h & 1)));
                         const uint16_t mh = (uint16_t)(mw[h >> 1] >> (16 * (h & 1)));
-                        smb[(8 * pc + h) * kRows + r] = f32x2{f16_to_f32(sh), f16_to_f32(mh)};
+                        smb[(smw * pc + h) * kRows + r] = f32x2{f16_to_f32(sh), f16_to_f32(mh)};
                     }
                 }
             }
         } else {
-            for (int e = lt; e < kRows * ng; e += 64 * kLoaders) {
-                const int r = e / ng, g = e - r * ng;
-                f32x2 v = {0.f, 0.f};
-                if (row0 + r < a.N) {
-                    const size_t gi = (size_t)(row0 + r) * G + g0 + g;
-                    v = f32x2{f16_to_f32(a.scale[gi]), f16_to_f32(a.minv[gi])};
+            lds_barrier();   // releases the compute waves' weight prefetch
+            // single groups, in batches of 8 per lane
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale, (uint32_t)a.N * (uint32_t)G * 2u);
+            const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv, (uint32_t)a.N * (uint32_t)G * 2u);
+            for (int e0 = lt; e0 < kRows * ng; e0 += 8 * 64 * kLoaders) {
+                uint16_t sv[8], mv[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int e = e0 + 64 * kLoaders * k;
+                    const int r = e / ng, g = e - r * ng;
+                    const uint32_t off = e < kRows * ng ? ((uint32_t)(row0 + r) * (uint32_t)G + (uint32_t)(g0 + g)) * 2u : 0xFFFFFFF0u;
+                    sv[k] = buf_load2(rs, off, 0);
+                    mv[k] = buf_load2(rm, off, 0);
                 }
-                smb[g * kRows + r] = v;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int e = e0 + 64 * kLoaders * k;
+                    if (e < kRows * ng) {
+                        const int r = e / ng, g = e - r * ng;
+                        smb[g * kRows + r] = f32x2{f16_to_f32(sv[k]), f16_to_f32(mv[k])};
+                    }
+                }
             }
         }
 
@@ -389,6 +421,7 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
 #pragma unroll
             for (int u = 0; u < kPre; ++u) {
                 const int i = i0 + u;
+                if (i >= niter) break;
                 const int r = (u + 1) % XP;
                 stage(i + 1, xr[r]);
 #pragma unroll
@@ -448,36 +481,82 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
     if (tid == 0) __hip_atomic_store(&cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Split plan: no split while the row blocks alone give >= 256 workgroups;
-// otherwise enough slices to reach about 384 workgroups, each slice >= 4
-// groups.  Without a workspace every task runs unsplit (the caller has
-// checked that its groups fit LDS).
+constexpr int kCUs = 256;
+constexpr int kMinSlice = 4;     // fewest groups in a K slice (two steps of the two halves)
+
+// groups per slice when G groups are cut into k slices: multiples of 4 where
+// K allows (so group parameters load in 8-byte pieces)
+inline int slice_groups(int G, int k) {
+    int g = (G + k - 1) / k;
+    if (G % 4 == 0) g = ((g + 3) / 4) * 4;
+    return g;
+}
+
+// Split plan.  Each row block of a task is cut into ks[i] K slices of gps[i]
+// groups (ks = 1: unsplit).  No split without a workspace, nor when the row
+// blocks alone give two workgroups per CU.  Otherwise the tasks with the most
+// blocks stay unsplit, one block per CU (at most kCUs blocks), and the other
+// tasks are split so that their slices fill the remaining workgroup slots (two
+// per CU in all; kCUs when no task stays unsplit), the largest slice as short
+// as the slots allow: every CU then streams about the same weight bytes.
+// whole[i] says which tasks stayed unsplit by this rule.
 template <int MT>
-void mm_plan(const GemvArgs* tasks, int count, bool can_split, int* ks, int* gps) {
-    int blocks = 0;
-    for (int i = 0; i < count; ++i) blocks += (tasks[i].N + kRows - 1) / kRows;
-    int want = 1;
-    if (can_split && blocks < 256) want = (384 + blocks - 1) / blocks;
+void mm_plan(const GemvArgs* tasks, int count, bool can_split, int* ks, int* gps, bool* whole) {
+    int blocks[kMaxTasks], btot = 0;
     for (int i = 0; i < count; ++i) {
-        const int G = tasks[i].K >> 7;
-        if (!can_split) {
-            ks[i] = 1;
-            gps[i] = G;
-            continue;
-        }
-        // slices of 8 groups (a multiple of the weight prefetch round and of
-        // a 16-byte parameter piece) where K allows, at least 4 groups each
-        int k = want;
-        const int kmax = G >= 8 ? G / 8 : 1;
-        if (k > kmax) k = kmax;
-        if (k < 1) k = 1;
-        int g = (G + k - 1) / k;
-        if (G % 8 == 0) g = ((g + 7) / 8) * 8;
-        const int gmax = (mm_max_gps<MT>() / 8) * 8;
-        if (g > gmax) g = gmax;
-        ks[i] = (G + g - 1) / g;
-        gps[i] = g;
+        blocks[i] = (tasks[i].N + kRows - 1) / kRows;
+        btot += blocks[i];
+        ks[i] = 1;
+        gps[i] = tasks[i].K >> 7;
+        whole[i] = true;
     }
+    if (can_split && btot < 2 * kCUs) {
+        int cap = kCUs, used = 0;
+        for (int i = 0; i < count; ++i) whole[i] = false;
+        if (btot >= kCUs) {
+            // largest tasks first
+            int order[kMaxTasks];
+            for (int i = 0; i < count; ++i) order[i] = i;
+            for (int a = 0; a < count; ++a)
+                for (int b = a + 1; b < count; ++b)
+                    if (blocks[order[b]] > blocks[order[a]]) { const int t = order[a]; order[a] = order[b]; order[b] = t; }
+            for (int a = 0; a < count; ++a)
+                if (used + blocks[order[a]] <= kCUs) {
+                    whole[order[a]] = true;
+                    used += blocks[order[a]];
+                }
+            cap = 2 * kCUs - used;
+        }
+        int tot = 0;
+        for (int i = 0; i < count; ++i)
+            if (!whole[i]) tot += blocks[i];
+        // shorten the longest slice while the slots allow
+        while (tot <= cap) {
+            int w = -1;
+            for (int i = 0; i < count; ++i)
+                if (!whole[i] && (w < 0 || gps[i] > gps[w])) w = i;
+            if (w < 0) break;
+            const int G = tasks[w].K >> 7;
+            int k = ks[w] + 1;
+            while (k <= G && slice_groups(G, k) >= gps[w]) ++k;
+            if (k > G) break;
+            const int g = slice_groups(G, k);
+            if (g < kMinSlice) break;
+            const int kk = (G + g - 1) / g;
+            if (tot + blocks[w] * (kk - ks[w]) > cap) break;
+            tot += blocks[w] * (kk - ks[w]);
+            ks[w] = kk;
+            gps[w] = g;
+        }
+    }
+    // every slice's group parameters fit LDS
+    const int gmax = (mm_max_gps<MT>() / 4) * 4;
+    for (int i = 0; i < count; ++i)
+        if (gps[i] > gmax) {
+            const int G = tasks[i].K >> 7;
+            gps[i] = gmax;
+            ks[i] = (G + gmax - 1) / gmax;
+        }
 }
 
 // Workspace a launch needs: 0 when no task is split, or when the counters of
@@ -486,7 +565,8 @@ void mm_plan(const GemvArgs* tasks, int count, bool can_split, int* ks, int* gps
 template <int MT>
 size_t ws_bytes_mt(const GemvArgs* tasks, int count) {
     int ks[kMaxTasks], gps[kMaxTasks];
-    mm_plan<MT>(tasks, count, true, ks, gps);
+    bool whole[kMaxTasks];
+    mm_plan<MT>(tasks, count, true, ks, gps, whole);
     size_t cnt = 0, part = 0;
     for (int i = 0; i < count; ++i) {
         if (ks[i] <= 1) continue;
@@ -502,26 +582,40 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
     int ks[kMaxTasks], gps[kMaxTasks];
     const size_t need = ws_bytes_mt<MT>(tasks, count);
     const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
-    mm_plan<MT>(tasks, count, split, ks, gps);
+    bool whole[kMaxTasks];
+    mm_plan<MT>(tasks, count, split, ks, gps, whole);
+    // unsplit tasks take the first workgroups, so that the dispatcher spreads
+    // their blocks one per CU before the slices fill the second slots
+    int order[kMaxTasks], n = 0;
+    for (int i = 0; i < count; ++i)
+        if (whole[i]) order[n++] = i;
+    for (int i = 0; i < count; ++i)
+        if (!whole[i]) order[n++] = i;
     MmTable tt{};
     for (int i = 0; i < kMaxTasks; ++i) tt.blk0[i] = 0x7fffffff;
     uint8_t* pc = static_cast<uint8_t*>(ws);
     uint8_t* pp = pc + kCntBytes;
     int grid = 0, gmax = 0;
-    for (int i = 0; i < count; ++i) {
+    for (int j = 0; j < count; ++j) {
+        const int i = order[j];
         const int blocks = (tasks[i].N + kRows - 1) / kRows;
-        tt.blk0[i] = grid;
-        tt.t[i].a = tasks[i];
-        tt.t[i].ks = ks[i];
-        tt.t[i].gps = gps[i];
+        tt.blk0[j] = grid;
+        tt.t[j].a = tasks[i];
+        tt.t[j].ks = ks[i];
+        tt.t[j].gps = gps[i];
         const int G = tasks[i].K >> 7;
-        tt.t[i].sm16 = (G % 8 == 0 && gps[i] % 8 == 0 && (reinterpret_cast<uintptr_t>(tasks[i].scale) % 16) == 0 &&
-                        (reinterpret_cast<uintptr_t>(tasks[i].minv) % 16) == 0) ? 1 : 0;
-        tt.t[i].y8 = (reinterpret_cast<uintptr_t>(tasks[i].y) % 8 == 0 && tasks[i].N % 4 == 0) ? 1 : 0;
+        const uintptr_t sa = reinterpret_cast<uintptr_t>(tasks[i].scale), ma = reinterpret_cast<uintptr_t>(tasks[i].minv);
+        if (G % 8 == 0 && gps[i] % 8 == 0 && gps[i] <= 64 && sa % 16 == 0 && ma % 16 == 0)
+            tt.t[j].smw = 8;
+        else if (G % 4 == 0 && gps[i] % 4 == 0 && gps[i] <= 32 && sa % 8 == 0 && ma % 8 == 0)
+            tt.t[j].smw = 4;
+        else
+            tt.t[j].smw = 0;
+        tt.t[j].y8 = (reinterpret_cast<uintptr_t>(tasks[i].y) % 8 == 0 && tasks[i].N % 4 == 0) ? 1 : 0;
         if (ks[i] > 1) {
-            tt.t[i].cnt = reinterpret_cast<unsigned*>(pc);
+            tt.t[j].cnt = reinterpret_cast<unsigned*>(pc);
             pc += (size_t)blocks * 4;
-            tt.t[i].part = reinterpret_cast<float*>(pp);
+            tt.t[j].part = reinterpret_cast<float*>(pp);
             pp += (size_t)blocks * ks[i] * kCompute * MT * 64 * 16;
         }
         grid += blocks * ks[i];
