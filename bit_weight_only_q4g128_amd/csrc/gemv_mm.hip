@@ -40,7 +40,7 @@ constexpr int kRows = 64;        // rows per workgroup
 constexpr int kCompute = 4;      // compute waves: 2 row pairs x 2 K halves
 constexpr int kLoaders = 2;      // activation loader waves, one per K half
 constexpr int kThreads = 64 * (kCompute + kLoaders);
-constexpr int kPre = 4;          // weight groups in flight per compute lane
+constexpr int kPre = 2;          // weight groups in flight per compute lane
 constexpr int kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -67,6 +67,11 @@ struct MmTable {
     MmTask t[kMaxTasks];
 };
 
+// waves per SIMD the register budget is cut for: two 6-wave workgroups per
+// CU need four when their waves land unevenly on the SIMDs (up to three batch
+// tiles; four tiles fit one workgroup per CU)
+template <int MT>
+__host__ __device__ constexpr int mm_waves() { return MT <= 3 ? 4 : 2; }
 // activation groups a loader keeps in flight (registers: 4 * MT pieces each)
 template <int MT>
 __host__ __device__ constexpr int mm_xp() { return MT <= 2 ? 2 : 1; }
@@ -137,7 +142,7 @@ __device__ __forceinline__ void write_y(const GemvArgs& a, bool y8, int prow0, i
 }
 
 template <int MT>
-__global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves<MT>()))) void q4_mm_kernel(MmTable tt) {
     constexpr int XP = mm_xp<MT>();
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     u32x4* xb = reinterpret_cast<u32x4*>(lds);                                               // [2][2][MT][4][64]
@@ -163,10 +168,11 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
     // the two halves of the slice: groups [0, h0) and [h0, ng)
     const int h0 = (ng + 1) >> 1;
     const int h1 = ng - h0;
-    // One group step per barrier, h0 of them.  Past a half's last group the
-    // loads re-read that group (every load is unconditional, so the wait
-    // counts stay exact) and the results are not accumulated.
-    const int niter = h0;
+    // One group step per barrier, in rounds of kPre (h0 rounded up; the split
+    // plan's slices make h0 even).  Past a half's last group the loads re-read
+    // that group (every load is unconditional, so the wait counts stay exact)
+    // and the results are not accumulated.
+    const int niter = ((h0 + kPre - 1) / kPre) * kPre;
 
     if (wave < kCompute) {
         // ------------------------------------------------------------ compute
@@ -198,58 +204,60 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
             for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         lds_barrier();     // parameters and activation step 0 ready
 
+        // one group step; u = i % kPre is the prefetch ring entry
+        auto step = [&](const int i, const int u) {
+            const int slot = i & 1;
+            const u32x4* xs = xb + (size_t)((slot * 2 + kh) * MT) * 4 * 64 + lane;
+            const u32x4 qa0 = q[u][0], qa1 = q[u][1];
+            q[u][0] = aload(i + kPre, 0);
+            q[u][1] = aload(i + kPre, 1);
+            const uint32_t qd[2][4] = {{qa0.x, qa0.y, qa0.z, qa0.w}, {qa1.x, qa1.y, qa1.z, qa1.w}};
+            f32x4 D[2][MT];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) D[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                u32x4 B[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) B[mt] = xs[(mt * 4 + s) * 64];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    uint32_t A[4];
+                    q4_pairs(qd[t][s], A);
+                    const bf16x8_t Av = as_bf16x8(A[0], A[1], A[2], A[3]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, as_bf16x8(B[mt]), D[t][mt], 0, 0, 0);
+                }
+            }
+            if (i < hlen) {
+                float sx[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) sx[mt] = sxb[(slot * 2 + kh) * MT * 16 + mt * 16 + (lane & 15)];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + (hbase + i) * kRows + 32 * rp + 16 * t + 4 * (lane >> 4));
+                    const f32x4 sm01 = sm4[0], sm23 = sm4[1];
+                    const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
+                    const float mn[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float tt0 = fmaf(-128.f, sx[mt], D[t][mt][v]);
+                            acc[t][mt][v] = fmaf(mn[v], sx[mt], fmaf(sc[v], tt0, acc[t][mt][v]));
+                        }
+                }
+            }
+            lds_barrier();
+        };
+        // whole rounds of kPre steps (a fixed trip structure keeps the
+        // compiler's waits on the weight prefetch exact)
         for (int i0 = 0; i0 < niter; i0 += kPre) {
 #pragma unroll
-            for (int u = 0; u < kPre; ++u) {
-                const int i = i0 + u;
-                if (i >= niter) break;
-                const int slot = i & 1;
-                const u32x4* xs = xb + (size_t)((slot * 2 + kh) * MT) * 4 * 64 + lane;
-                const u32x4 qa0 = q[u][0], qa1 = q[u][1];
-                q[u][0] = aload(i + kPre, 0);
-                q[u][1] = aload(i + kPre, 1);
-                const uint32_t qd[2][4] = {{qa0.x, qa0.y, qa0.z, qa0.w}, {qa1.x, qa1.y, qa1.z, qa1.w}};
-                f32x4 D[2][MT];
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) D[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    u32x4 B[MT];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) B[mt] = xs[(mt * 4 + s) * 64];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        uint32_t A[4];
-                        q4_pairs(qd[t][s], A);
-                        const bf16x8_t Av = as_bf16x8(A[0], A[1], A[2], A[3]);
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, as_bf16x8(B[mt]), D[t][mt], 0, 0, 0);
-                    }
-                }
-                if (i < hlen) {
-                    float sx[MT];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) sx[mt] = sxb[(slot * 2 + kh) * MT * 16 + mt * 16 + (lane & 15)];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + (hbase + i) * kRows + 32 * rp + 16 * t + 4 * (lane >> 4));
-                        const f32x4 sm01 = sm4[0], sm23 = sm4[1];
-                        const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
-                        const float mn[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const float tt0 = fmaf(-128.f, sx[mt], D[t][mt][v]);
-                                acc[t][mt][v] = fmaf(mn[v], sx[mt], fmaf(sc[v], tt0, acc[t][mt][v]));
-                            }
-                    }
-                }
-                lds_barrier();
-            }
+            for (int u = 0; u < kPre; ++u) step(i0 + u, u);
         }
 
         // the two K halves meet: half 1 hands its tiles to half 0 through LDS
@@ -417,17 +425,16 @@ __global__ __launch_bounds__(kThreads) void q4_mm_kernel(MmTable tt) {
 
         // step i stages step i + 1, held in ring entry (i + 1) % XP (i0 is a
         // multiple of kPre, itself a multiple of XP)
+        auto lstep = [&](const int i, const int u) {
+            const int r = (u + 1) % XP;
+            stage(i + 1, xr[r]);
+#pragma unroll
+            for (int p = 0; p < 4 * MT; ++p) xr[r][p] = xload(i + 1 + XP, p);
+            lds_barrier();
+        };
         for (int i0 = 0; i0 < niter; i0 += kPre) {
 #pragma unroll
-            for (int u = 0; u < kPre; ++u) {
-                const int i = i0 + u;
-                if (i >= niter) break;
-                const int r = (u + 1) % XP;
-                stage(i + 1, xr[r]);
-#pragma unroll
-                for (int p = 0; p < 4 * MT; ++p) xr[r][p] = xload(i + 1 + XP, p);
-                lds_barrier();
-            }
+            for (int u = 0; u < kPre; ++u) lstep(i0 + u, u);
         }
         // the compute waves' two barriers of the half merge and the epilogue
         __syncthreads();
