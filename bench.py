@@ -132,6 +132,42 @@ class Workload:
         return w + N_LAYERS * (per_layer_x + per_layer_y) + head_io
 
 
+def weight_bytes(wl):
+    """Packed weights + group parameters of one step (the head's BF16 rows
+    included): the bytes the weight stream must read."""
+    return sum(b for _, b, _ in wl.launches(1, "plain"))
+
+
+def read_ceiling(torch, q4, wl, steps, warmup):
+    """Plain-read reference for the M=1 grouped step: the same 73 launches,
+    each replaced by the library's diagnostic stream_read over exactly the
+    weight buffers (codes, scales, mins; the head's BF16 rows) that GEMV launch
+    streams, captured and replayed like the step.  Returns ms per step."""
+    groups = []
+    for lay in wl.layers:
+        for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
+            groups.append([t for p in stage for t in lay[p]])
+    groups.append([wl.head])
+    sinks = [torch.empty(q4.stream_read_sink_words(g), dtype=torch.int32, device="cuda") for g in groups]
+    for g, k in zip(groups, sinks):
+        q4.stream_read(g, k)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for g, k in zip(groups, sinks):
+            q4.stream_read(g, k)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        graph.replay()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / steps
+
+
 def time_graph(torch, wl, M, steps, warmup, mode):
     calls = wl.launches(M, mode)
     for f, _, _ in calls:  # eager warm-up outside capture
@@ -349,6 +385,11 @@ def main():
                    "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                    "traffic": measured_traffic(M), "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)}
     head = res[(1, "grouped")]
+    wbytes = weight_bytes(wl)
+    ceil_ms = read_ceiling(torch, q4, wl, args.steps, args.warmup)
+    ceil_gbs = wbytes / (ceil_ms * 1e-3) / 1e9
+    log(f"bench: plain read of the step's weight buffers in the same 73 launches: {ceil_ms * 1e3:.1f} us, "
+        f"{ceil_gbs:.0f} GB/s")
 
     out = {
         "metric": METRIC,
@@ -371,7 +412,13 @@ def main():
             "steps_per_s": round(1e3 / head["ms"], 1),
             "pct_of_8TBps": round(100 * head["gbs"] / PEAK_GBS, 2),
             "launches_per_step": head["launches"],
+            "weight_bytes_per_step": wbytes,
+            "read_ceiling": {"what": "diagnostic plain read of the same weight buffers in the same 73 launches, hipGraph",
+                             "ms_per_step": round(ceil_ms, 5), "weight_GB_s": round(ceil_gbs, 1),
+                             "pct_of_8TBps": round(100 * ceil_gbs / PEAK_GBS, 2)},
             "modes": {f"M{M}_{mode}": {"ms_per_step": round(r["ms"], 5), "GB_s": round(r["gbs"], 1),
+                                        "weight_GB_s": round(wbytes / (r["ms"] * 1e-3) / 1e9, 1),
+                                        "pct_of_read_ceiling": round(100 * ceil_ms / r["ms"], 1),
                                         "pct_of_8TBps": round(100 * r["gbs"] / PEAK_GBS, 2),
                                         "steps_per_s": round(1e3 / r["ms"], 1), "tokens_per_s": round(M * 1e3 / r["ms"], 1),
                                         "launches_per_step": r["launches"], "bytes_per_step": r["bytes"]}

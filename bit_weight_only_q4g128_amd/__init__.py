@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
-    "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib",
+    "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
     "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
 
@@ -47,6 +47,10 @@ lib.q4gemv_time_next_launch.argtypes = [_p, _p]
 lib.q4gemv_time_next_launch.restype = ctypes.c_int
 lib.q4gemv_version.argtypes = []
 lib.q4gemv_version.restype = ctypes.c_int
+lib.q4gemv_stream_read.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(ctypes.c_size_t), _i, _p, ctypes.c_size_t, _p]
+lib.q4gemv_stream_read.restype = ctypes.c_int
+lib.q4gemv_stream_read_sink_words.argtypes = [ctypes.POINTER(ctypes.c_size_t), _i]
+lib.q4gemv_stream_read_sink_words.restype = ctypes.c_size_t
 
 
 class Q4Task(ctypes.Structure):
@@ -222,3 +226,28 @@ def nvfp4g16_dequant_f32(qweight, scale_e4m3, global_scale: float, out=None):
     _raise(lib.nvfp4g16_dequant_f32(qweight.data_ptr(), scale_e4m3.data_ptr(), float(global_scale), N, K, w.data_ptr(),
                                     _stream(qweight)))
     return w
+
+
+def _read_args(tensors):
+    n = len(tensors)
+    ptrs = (_p * n)(*[t.data_ptr() for t in tensors])
+    sizes = (ctypes.c_size_t * n)(*[t.numel() * t.element_size() for t in tensors])
+    return ptrs, sizes, n
+
+
+def stream_read_sink_words(tensors) -> int:
+    """Sink words stream_read needs for these device tensors (0: invalid)."""
+    _, sizes, n = _read_args(tensors)
+    return int(lib.q4gemv_stream_read_sink_words(sizes, n))
+
+
+def stream_read(tensors, sink):
+    """Diagnostic plain read of the bytes of up to 32 contiguous device tensors
+    in one launch (the reference a GEMV launch of the same bytes is compared
+    with); one XOR word per wave lands in the int32 device tensor `sink`."""
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("stream_read takes contiguous device tensors")
+    ptrs, sizes, n = _read_args(tensors)
+    _raise(lib.q4gemv_stream_read(ptrs, sizes, n, sink.data_ptr(), sink.numel(), _stream(sink)))
+    return sink

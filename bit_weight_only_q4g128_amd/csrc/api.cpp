@@ -265,6 +265,32 @@ int nvfp4g16_dequant_f32(const uint8_t* qweight, const uint8_t* scale_e4m3, floa
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 
+size_t q4gemv_stream_read_sink_words(const size_t* bytes, int count) {
+    if (!bytes || count < 1 || count > q4::kMaxReadBufs) return 0;
+    for (int i = 0; i < count; ++i)
+        if (bytes[i] < 16 || bytes[i] >= ((size_t)1 << 32)) return 0;
+    return q4::stream_read_sink_words(bytes, count);
+}
+
+int q4gemv_stream_read(const void* const* bufs, const size_t* bytes, int count, uint32_t* sink, size_t sink_words,
+                       void* stream) {
+    if (!bufs || !bytes || !sink) return Q4_EINVAL_PTR;
+    if (count < 1 || count > q4::kMaxReadBufs) return Q4_EINVAL_SHAPE;
+    for (int i = 0; i < count; ++i) {
+        if (!bufs[i]) return Q4_EINVAL_PTR;
+        if (bytes[i] < 16 || bytes[i] >= ((size_t)1 << 32)) return Q4_EINVAL_SHAPE;
+        if (!aligned(bufs[i], 4)) return Q4_EALIGN;
+    }
+    const size_t need = q4::stream_read_sink_words(bytes, count);
+    if (sink_words < need) return Q4_EINVAL_SHAPE;
+    if (!aligned(sink, 4)) return Q4_EALIGN;
+    const Range sr = range_of(sink, need * 4);
+    for (int i = 0; i < count; ++i)
+        if (overlaps(sr, range_of(bufs[i], bytes[i]))) return Q4_EALIAS;
+    hipError_t e = q4::launch_stream_read(bufs, bytes, count, sink, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
 const char* q4gemv_variant_name(int fmt, int variant, int M, int N, int K) {
     (void)N;
     if (fmt < Q4_FMT_Q4G128 || fmt > Q4_FMT_BF16 || !variant_ok(variant) || M < 1 || M > kMaxM || K < 1) return "invalid";

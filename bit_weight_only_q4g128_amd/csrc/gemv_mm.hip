@@ -11,9 +11,10 @@
 //     own weights.  Per group it turns its 2 x 16 bytes per lane into BF16
 //     "128 + code" operands for its two 16-row tiles, runs 4 k-steps x MT
 //     batch tiles x 2 row tiles of MFMA with the activations as the B operand
-//     (each activation fragment read from LDS once serves both row tiles), and
-//     folds the group as
-//         acc += scale * (D - 128 * SX) + min * SX,   SX = sum of x over the group;
+//     (each activation fragment read from LDS once serves both row tiles),
+//     each chain starting from -128 * SX (SX = sum of x over the group) so
+//     that D is the sum of code * x, and folds the group as
+//         acc += scale * D + min * SX   (min staged as -min / 128, exact);
 //   * two loader waves, one per K half, that stream the activations of each
 //     128-column group (MT*16 batch rows) from L2 through registers into a
 //     double-buffered LDS ring, already in B-fragment order and in the column
@@ -80,7 +81,7 @@ __host__ __device__ constexpr int mm_xp() { return MT <= 2 ? 2 : 1; }
 template <int MT>
 __host__ __device__ constexpr int mm_ring_bytes() { return 2 * 2 * MT * 4 * 64 * 16; }
 template <int MT>
-__host__ __device__ constexpr int mm_sx_bytes() { return 2 * 2 * MT * 16 * 4; }
+__host__ __device__ constexpr int mm_sx_bytes() { return 2 * 2 * MT * 16 * 16; }
 template <int MT>
 __host__ __device__ inline int mm_shmem(int gps) { return mm_ring_bytes<MT>() + mm_sx_bytes<MT>() + gps * kRows * 8; }
 // most groups per slice whose parameters fit the LDS budget
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
     constexpr int XP = mm_xp<MT>();
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     u32x4* xb = reinterpret_cast<u32x4*>(lds);                                               // [2][2][MT][4][64]
-    float* sxb = reinterpret_cast<float*>(lds + mm_ring_bytes<MT>());                        // [2][2][MT*16]
+    f32x4* sxb = reinterpret_cast<f32x4*>(lds + mm_ring_bytes<MT>());                        // [2][2][MT*16]
     f32x2* smb = reinterpret_cast<f32x2*>(lds + mm_ring_bytes<MT>() + mm_sx_bytes<MT>());    // [gps][64]
 
     int ti = 0;
@@ -212,11 +213,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
             q[u][0] = aload(i + kPre, 0);
             q[u][1] = aload(i + kPre, 1);
             const uint32_t qd[2][4] = {{qa0.x, qa0.y, qa0.z, qa0.w}, {qa1.x, qa1.y, qa1.z, qa1.w}};
+            // the MFMA chains start from -128 * SX, so D = sum of code * x
+            f32x4 cx[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) cx[mt] = sxb[(slot * 2 + kh) * MT * 16 + mt * 16 + (lane & 15)];
             f32x4 D[2][MT];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) D[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int mt = 0; mt < MT; ++mt) D[t][mt] = cx[mt];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 u32x4 B[MT];
@@ -233,22 +238,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                 }
             }
             if (i < hlen) {
-                float sx[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) sx[mt] = sxb[(slot * 2 + kh) * MT * 16 + mt * 16 + (lane & 15)];
+                // acc += scale * D + min * SX, with min staged as -min / 128
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + (hbase + i) * kRows + 32 * rp + 16 * t + 4 * (lane >> 4));
                     const f32x4 sm01 = sm4[0], sm23 = sm4[1];
                     const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
-                    const float mn[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
+                    const float mq[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const float tt0 = fmaf(-128.f, sx[mt], D[t][mt][v]);
-                            acc[t][mt][v] = fmaf(mn[v], sx[mt], fmaf(sc[v], tt0, acc[t][mt][v]));
-                        }
+                        for (int v = 0; v < 4; ++v)
+                            acc[t][mt][v] = fmaf(mq[v], cx[mt][v], fmaf(sc[v], D[t][mt][v], acc[t][mt][v]));
                 }
             }
             lds_barrier();
@@ -336,7 +337,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                 // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same batch row
                 sx += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, sx), 0x401F));
                 sx += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, sx)));
-                if (lane < 16) sxb[(slot * 2 + L) * MT * 16 + mt * 16 + lane] = sx;
+                if (lane < 16) {
+                    const float c = -128.f * sx;   // exact: a power-of-two scaling
+                    sxb[(slot * 2 + L) * MT * 16 + mt * 16 + lane] = f32x4{c, c, c, c};
+                }
             }
         };
         u32x4 xr[XP][4 * MT];
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                         if (h >= smw) break;
                         const uint16_t sh = (uint16_t)(sw[h >> 1] >> (16 * (h & 1)));
                         const uint16_t mh = (uint16_t)(mw[h >> 1] >> (16 * (h & 1)));
-                        smb[(smw * pc + h) * kRows + r] = f32x2{f16_to_f32(sh), f16_to_f32(mh)};
+                        smb[(smw * pc + h) * kRows + r] = f32x2{f16_to_f32(sh), -0.0078125f * f16_to_f32(mh)};
                     }
                 }
             }
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                     const int e = e0 + 64 * kLoaders * k;
                     if (e < kRows * ng) {
                         const int r = e / ng, g = e - r * ng;
-                        smb[g * kRows + r] = f32x2{f16_to_f32(sv[k]), f16_to_f32(mv[k])};
+                        smb[g * kRows + r] = f32x2{f16_to_f32(sv[k]), -0.0078125f * f16_to_f32(mv[k])};
                     }
                 }
             }

@@ -62,6 +62,12 @@ hipError_t launch_mm(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes
 // 16x16x32 BF16 matrix-core GEMV (any M <= 64), one launch per task.
 hipError_t launch_mfma(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
 
+// Diagnostic streaming read of up to kMaxReadBufs device buffers (each under
+// 4 GiB) in one launch; sink holds stream_read_sink_words() words.
+constexpr int kMaxReadBufs = 32;
+size_t stream_read_sink_words(const size_t* bytes, int count);
+hipError_t launch_stream_read(const void* const* bufs, const size_t* bytes, int count, uint32_t* sink, hipStream_t s);
+
 // Diagnostic dequantization to fp32 [N, K].
 hipError_t launch_q4_dequant(const uint8_t* qw, const uint16_t* sc, const uint16_t* mn, int N, int K, float* w, hipStream_t s);
 hipError_t launch_nvfp4_dequant(const uint8_t* qw, const uint8_t* sc, float G, int N, int K, float* w, hipStream_t s);

@@ -164,6 +164,21 @@ int nvfp4g16_dequant_f32(const uint8_t* qweight, const uint8_t* scale_e4m3, floa
                          void* stream);
 
 /*
+ * Diagnostic plain streaming read: the reference a GEMV launch of the same
+ * bytes is compared with.  Reads `count` (1..32) device buffers bufs[i] of
+ * bytes[i] bytes (each 4-byte aligned, 16 <= bytes[i] < 4 GiB) in one launch
+ * with 16-byte loads and writes one XOR word per wave to the device buffer
+ * `sink` of sink_words 32-bit words, which must be at least
+ * q4gemv_stream_read_sink_words() and must not overlap the buffers.
+ * Returns Q4_EINVAL_PTR, Q4_EINVAL_SHAPE, Q4_EALIGN or Q4_EALIAS before
+ * enqueueing anything; Q4_ELAUNCH if the launch fails.
+ */
+int q4gemv_stream_read(const void* const* bufs, const size_t* bytes, int count, uint32_t* sink, size_t sink_words,
+                       void* stream);
+/* Sink words q4gemv_stream_read needs for these sizes (0 on invalid input). */
+size_t q4gemv_stream_read_sink_words(const size_t* bytes, int count);
+
+/*
  * Kernel timing without host gaps: the next kernel launched by the calling
  * thread through this library records start_event when it begins executing
  * and stop_event when it ends (hipExtLaunchKernel).  Both are caller-owned

@@ -22,7 +22,7 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         src = open(h).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names += re.findall(r"^\s*(?:int|const\s+char\s*\*)\s+(\w+)\s*\(", src, flags=re.M)
+        names += re.findall(r"^\s*(?:int|size_t|const\s+char\s*\*)\s+(\w+)\s*\(", src, flags=re.M)
     return names
 
 
@@ -150,3 +150,30 @@ def test_grouped_validation():
     # two tasks share an output
     same = (T * 2)(task(0), task(1, y=A + (4 << 24)))
     assert lib.q4g128_gemv_grouped(same, 2, 1, 0, None) == EALIAS
+
+
+def test_stream_read_validation():
+    import ctypes
+    lib.q4gemv_stream_read.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.q4gemv_stream_read_sink_words.argtypes = [ctypes.POINTER(ctypes.c_size_t), ctypes.c_int]
+    lib.q4gemv_stream_read_sink_words.restype = ctypes.c_size_t
+    P, S = ctypes.c_void_p, ctypes.c_size_t
+    bufs = (P * 2)(A, A + (1 << 24))
+    sizes = (S * 2)(1 << 20, 4096)
+    # 16 KB per workgroup, 4 words per workgroup: 64 + 1 workgroups
+    need = lib.q4gemv_stream_read_sink_words(sizes, 2)
+    assert need == (64 + 1) * 4
+    assert lib.q4gemv_stream_read_sink_words(sizes, 0) == 0
+    assert lib.q4gemv_stream_read_sink_words((S * 1)(8), 1) == 0
+    sink = A + (2 << 24)
+    assert lib.q4gemv_stream_read(None, sizes, 2, sink, need, None) == EPTR
+    assert lib.q4gemv_stream_read(bufs, sizes, 2, None, need, None) == EPTR
+    assert lib.q4gemv_stream_read((P * 2)(A, None), sizes, 2, sink, need, None) == EPTR
+    assert lib.q4gemv_stream_read(bufs, sizes, 0, sink, need, None) == ESHAPE
+    assert lib.q4gemv_stream_read(bufs, sizes, 33, sink, need, None) == ESHAPE
+    assert lib.q4gemv_stream_read(bufs, (S * 2)(1 << 20, 8), 2, sink, need, None) == ESHAPE
+    assert lib.q4gemv_stream_read(bufs, sizes, 2, sink, need - 1, None) == ESHAPE
+    assert lib.q4gemv_stream_read((P * 2)(A + 2, A + (1 << 24)), sizes, 2, sink, need, None) == EALIGN
+    assert lib.q4gemv_stream_read(bufs, sizes, 2, sink + 2, need, None) == EALIGN
+    assert lib.q4gemv_stream_read(bufs, sizes, 2, A + 4096, need, None) == EALIAS

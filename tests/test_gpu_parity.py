@@ -541,3 +541,19 @@ def test_launch_timing_hook(q4):
     assert torch.equal(y, y2)
     hip.hipEventDestroy(a)
     hip.hipEventDestroy(z)
+
+
+def test_stream_read_touches_every_byte(q4):
+    # the diagnostic read XORs every 32-bit word of its buffers into the sink
+    g = torch.Generator().manual_seed(5)
+    bufs = [torch.randint(-2**31, 2**31 - 1, (n,), dtype=torch.int32, generator=g) for n in (4096 * 7 + 12, 4, 100000)]
+    dev = [b.cuda() for b in bufs]
+    words = q4.stream_read_sink_words(dev)
+    assert words > 0
+    sink = torch.full((words,), -1, dtype=torch.int32, device="cuda")
+    q4.stream_read(dev, sink)
+    expect = 0
+    for b in bufs:
+        expect ^= int(np.bitwise_xor.reduce(b.numpy().view(np.uint32)))
+    got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+    assert got == expect
