@@ -18,7 +18,8 @@
 //   * two loader waves, one per K half, that stream the activations of each
 //     128-column group (MT*16 batch rows) from L2 through registers into a
 //     double-buffered LDS ring, already in B-fragment order and in the column
-//     pairing of the weight operand, and compute SX on the way.
+//     pairing of the weight operand, and get -128 * SX on the way from MFMAs
+//     with an all -128 A operand.
 //
 // One barrier per group step keeps the ring in step.  At the end the two K
 // halves meet in LDS.  When K is split over several workgroups, each writes
@@ -320,27 +321,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         auto stage = [&](int i, const u32x4 (&xr)[4 * MT]) {
             const int slot = i & 1;
             u32x4* dst = xb + (size_t)((slot * 2 + L) * MT) * 4 * 64 + lane;
+            // -128 * SX from the matrix core: an A operand of all -128 against
+            // the pieces as loaded (the column order within a k-step does not
+            // matter to a sum) leaves -128 * SX of batch row l % 16 in all four
+            // results of lane l, the form the compute waves start from
+            const bf16x8_t neg128 = as_bf16x8(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                float sx = 0.f;
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const u32x4 v = xr[mt * 4 + s];
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, as_bf16x8(v), c, 0, 0, 0);
                     uint32_t pr[4];
                     xq4_pairs(v.x, v.y, v.z, v.w, pr);
                     dst[(mt * 4 + s) * 64] = u32x4{pr[0], pr[1], pr[2], pr[3]};
-                    sx = dot2(v.x, 0x3F803F80u, sx);
-                    sx = dot2(v.y, 0x3F803F80u, sx);
-                    sx = dot2(v.z, 0x3F803F80u, sx);
-                    sx = dot2(v.w, 0x3F803F80u, sx);
                 }
-                // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same batch row
-                sx += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, sx), 0x401F));
-                sx += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, sx)));
-                if (lane < 16) {
-                    const float c = -128.f * sx;   // exact: a power-of-two scaling
-                    sxb[(slot * 2 + L) * MT * 16 + mt * 16 + lane] = f32x4{c, c, c, c};
-                }
+                if (lane < 16) sxb[(slot * 2 + L) * MT * 16 + mt * 16 + lane] = c;
             }
         };
         u32x4 xr[XP][4 * MT];
