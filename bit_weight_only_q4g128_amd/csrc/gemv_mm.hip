@@ -106,10 +106,10 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr size_t kCntBytes = 64 * 1024;
 constexpr int kCoherent = 16;   // buffer cache policy sc1: device-coherent, not held in the per-XCD L2
 
-// contributors whose partial tiles the reducing wave loads at once (8 * MT
-// registers per lane each)
+// slices whose partial tile a reducing wave loads at once (4 * MT registers
+// per lane each)
 template <int MT>
-__host__ __device__ constexpr int mm_reduce_batch() { return MT <= 1 ? 4 : MT == 2 ? 3 : 2; }
+__host__ __device__ constexpr int mm_reduce_batch() { return 24 / MT; }
 
 // Byte offset of a partial tile: row block blk, K slice ks of KS, row pair
 // rp, row tile t, batch tile mt, lane.
@@ -118,29 +118,32 @@ __device__ __forceinline__ uint32_t part_off(int blk, int KS, int ks, int rp, in
     return (uint32_t)(((((blk * KS + ks) * 4 + rp * 2 + t) * MT + mt) * 64 + lane) * 16);
 }
 
-// y for the two 16-row tiles of a row pair: lane l holds rows
-// prow0 + 16 t + 4 (l / 16) + v (v = 0..3) of batch row 16 mt + l % 16.
+// y for one 16-row tile: lane l holds rows trow0 + 4 (l / 16) + v (v = 0..3)
+// of batch row 16 mt + l % 16; write_y does the two tiles of a row pair.
+template <int MT>
+__device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, int trow0, int lane, const f32x4 (&v)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + (lane & 15);
+        const int row = trow0 + 4 * (lane >> 4);
+        if (m >= a.M || row >= a.N) continue;
+        uint16_t* dst = a.y + (size_t)m * a.N + row;
+        const f32x4 r = v[mt];
+        if (y8 && row + 3 < a.N) {
+            const uint32_t lo = (uint32_t)f32_to_bf16(r.x) | ((uint32_t)f32_to_bf16(r.y) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(r.z) | ((uint32_t)f32_to_bf16(r.w) << 16);
+            *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (row + q < a.N) dst[q] = f32_to_bf16(r[q]);
+        }
+    }
+}
 template <int MT>
 __device__ __forceinline__ void write_y(const GemvArgs& a, bool y8, int prow0, int lane, const f32x4 (&v)[2][MT]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = 16 * mt + (lane & 15);
-            const int row = prow0 + 16 * t + 4 * (lane >> 4);
-            if (m >= a.M || row >= a.N) continue;
-            uint16_t* dst = a.y + (size_t)m * a.N + row;
-            const f32x4 r = v[t][mt];
-            if (y8 && row + 3 < a.N) {
-                const uint32_t lo = (uint32_t)f32_to_bf16(r.x) | ((uint32_t)f32_to_bf16(r.y) << 16);
-                const uint32_t hi = (uint32_t)f32_to_bf16(r.z) | ((uint32_t)f32_to_bf16(r.w) << 16);
-                *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (row + q < a.N) dst[q] = f32_to_bf16(r[q]);
-            }
-        }
+    write_y_tile<MT>(a, y8, prow0, lane, v[0]);
+    write_y_tile<MT>(a, y8, prow0 + 16, lane, v[1]);
 }
 
 template <int MT>
@@ -453,38 +456,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
     if (tid == 0) s_prev = __hip_atomic_fetch_add(&cnt[blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_prev != (unsigned)(KS - 1)) return;
-    if (wave < kCompute && (wave >> 1) == 0) {
-        // sum the slices in order, the tiles of kRB slices in flight at once
+    if (wave < kCompute) {
+        // each compute wave sums one 16-row tile over the slices, in slice
+        // order, with the partial tiles of kRB slices in flight at once
         constexpr int kRB = mm_reduce_batch<MT>();
-        const int rp = wave & 1;
+        const int rp = wave & 1, t = wave >> 1;
         const int blocks = (a.N + kRows - 1) / kRows;
         const __amdgpu_buffer_rsrc_t rpart = make_rsrc(tt.t[ti].part, (uint32_t)blocks * KS * 4u * MT * 64u * 16u);
-        f32x4 sum[2][MT];
+        f32x4 sum[MT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sum[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) sum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int s0 = 0; s0 < KS; s0 += kRB) {
-            u32x4 pv[kRB][2][MT];
+            u32x4 pv[kRB][MT];
 #pragma unroll
             for (int k = 0; k < kRB; ++k)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const uint32_t off = s0 + k < KS ? part_off<MT>(blk, KS, s0 + k, rp, t, mt, lane) : 0xFFFFFFF0u;
-                        pv[k][t][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rpart, off, 0, kCoherent));
-                    }
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint32_t off = s0 + k < KS ? part_off<MT>(blk, KS, s0 + k, rp, t, mt, lane) : 0xFFFFFFF0u;
+                    pv[k][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rpart, off, 0, kCoherent));
+                }
 #pragma unroll
             for (int k = 0; k < kRB; ++k)
                 if (s0 + k < KS) {
 #pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) sum[t][mt] += __builtin_bit_cast(f32x4, pv[k][t][mt]);
+                    for (int mt = 0; mt < MT; ++mt) sum[mt] += __builtin_bit_cast(f32x4, pv[k][mt]);
                 }
         }
-        write_y<MT>(a, tt.t[ti].y8 != 0, row0 + 32 * rp, lane, sum);
+        write_y_tile<MT>(a, tt.t[ti].y8 != 0, row0 + 32 * rp + 16 * t, lane, sum);
     }
     if (tid == 0) __hip_atomic_store(&cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
