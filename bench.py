@@ -132,6 +132,63 @@ class Workload:
         return w + N_LAYERS * (per_layer_x + per_layer_y) + head_io
 
 
+def nvfp4_wbytes(N, K):
+    """weight bytes of one NVFP4 matrix: E2M1 codes + e4m3 group-16 scales + the fp32 global scale."""
+    return N * K // 2 + N * (K // 16) + 4
+
+
+class Nvfp4Workload:
+    """The same decode step with NVFP4 weights: q, k, o, gate, up NVFP4 (E2M1
+    codes, e4m3 scales per 16 columns, one fp32 global scale) and v, down BF16,
+    as the VoxCPM2-NVFP4 card quantizes them; then the same BF16 head.  One
+    launch per projection (there is no grouped NVFP4 call)."""
+
+    def __init__(self, q4, synth, torch, int4_wl):
+        self.q4, self.torch = q4, torch
+        t0 = time.time()
+        self.layers = []
+        for i in range(N_LAYERS):
+            lay = {}
+            for p in synth.LAYER_ORDER:
+                N, K = synth.LAYER_SHAPES[p]
+                if p in synth.NVFP4_BF16_PROJ:
+                    lay[p] = synth.bf16_matrix(N, K, ("nvfp4-step-bf16", i, p), device="cuda")
+                else:
+                    lay[p] = synth.nvfp4_matrix(N, K, ("nvfp4-step", i, p), device="cuda")
+            self.layers.append(lay)
+        torch.cuda.synchronize()
+        log(f"bench: generated {N_LAYERS} NVFP4 layers (v, down BF16) in {time.time() - t0:.1f}s")
+        self.bf16_proj = synth.NVFP4_BF16_PROJ
+        self.int4 = int4_wl
+        self.shapes, self.order = synth.LAYER_SHAPES, synth.LAYER_ORDER
+
+    def weight_bytes_of(self, p):
+        N, K = self.shapes[p]
+        return N * K * 2 if p in self.bf16_proj else nvfp4_wbytes(N, K)
+
+    def launches(self, M, mode="plain"):
+        xs, ys, xin, yh = self.int4.buffers(M)
+        q4, out = self.q4, []
+        for lay in self.layers:
+            for p in self.order:
+                if p in self.bf16_proj:
+                    out.append((lambda x=xs[p], w=lay[p], y=ys[p]: q4.bf16_gemv(x, w, out=y), self.weight_bytes_of(p), False))
+                else:
+                    qw, s8, G = lay[p]
+                    out.append((lambda x=xs[p], qw=qw, s8=s8, G=G, y=ys[p]: q4.nvfp4g16_gemv(x, qw, s8, G, out=y),
+                                self.weight_bytes_of(p), True))
+        head = self.int4.head
+        out.append((lambda: q4.bf16_gemv(xin, head, out=yh), self.int4.head_rows * 2048 * 2, False))
+        return out
+
+    def step_bytes(self, M):
+        w = sum(b for _, b, _ in self.launches(M))
+        per_layer_x = (2048 + 2048 + 8192) * M * 2
+        per_layer_y = sum(self.shapes[p][0] for p in self.order) * M * 2
+        head_io = 2048 * M * 2 + self.int4.head_rows * M * 2
+        return w + N_LAYERS * (per_layer_x + per_layer_y) + head_io
+
+
 def weight_bytes(wl):
     """Packed weights + group parameters of one step (the head's BF16 rows
     included): the bytes the weight stream must read."""
@@ -249,6 +306,39 @@ def time_q4_launches(torch, q4, wl, M, mode, reps=3):
     return tot_ms / n, tot_bytes / n
 
 
+def time_nvfp4_launches(torch, q4, nv, M, reps=3):
+    """Average execution time of the NVFP4 GEMV launches of one NVFP4 step
+    (HIP events on the launch stream, as for the int4 launches) and their
+    average algorithmic bytes: weights + that projection's x and y."""
+    xs, ys, _, _ = nv.int4.buffers(M)
+    calls = []
+    all_calls = nv.launches(M)
+    k = 0
+    for li in range(N_LAYERS):
+        for p in nv.order:
+            f, b, is_nv = all_calls[k]
+            k += 1
+            if is_nv:
+                calls.append((f, b + xs[p].numel() * 2 + ys[p].numel() * 2))
+    he = HipEvents()
+    evs = [(he.create(), he.create()) for _ in calls]
+    tot_ms, tot_bytes, n = 0.0, 0, 0
+    for _ in range(reps):
+        for (f, b), (a, z) in zip(calls, evs):
+            q4.lib.q4gemv_time_next_launch(a, z)
+            f()
+        torch.cuda.synchronize()
+        he.sync(evs[-1][1])
+        for (f, b), (a, z) in zip(calls, evs):
+            tot_ms += he.elapsed_ms(a, z)
+            tot_bytes += b
+            n += 1
+    for a, z in evs:
+        he.destroy(a)
+        he.destroy(z)
+    return tot_ms / n, tot_bytes / n
+
+
 def cpu_baseline(wl, budget_s=15.0):
     """The oracle (plain NumPy, fp64 product) on whole layers of the step's
     weights, M = 1, until about budget_s seconds of CPU work."""
@@ -332,6 +422,27 @@ def counters_pass(q4, synth, torch, head_rows, M):
     log(f"bench: counters pass at M={M} done ({len(calls)} launches per step, csrc digest {csrc_digest(M)})")
 
 
+def mode_key(k):
+    M, mode = k
+    return f"{M}_{mode}" if isinstance(M, str) else f"M{M}_{mode}"
+
+
+def mode_record(k, r, int4_wbytes, ceil_ms):
+    """One timed mode: step time and rates; the int4 modes also against the
+    plain read of their weight buffers (the read ceiling)."""
+    M, _ = k
+    batch = int(M.split("_M")[1]) if isinstance(M, str) else M
+    wb = r.get("wbytes", int4_wbytes)
+    rec = {"ms_per_step": round(r["ms"], 5), "GB_s": round(r["gbs"], 1), "weight_GB_s": round(wb / (r["ms"] * 1e-3) / 1e9, 1),
+           "pct_of_8TBps": round(100 * r["gbs"] / PEAK_GBS, 2), "steps_per_s": round(1e3 / r["ms"], 1),
+           "tokens_per_s": round(batch * 1e3 / r["ms"], 1), "launches_per_step": r["launches"], "bytes_per_step": r["bytes"]}
+    if not isinstance(M, str):
+        rec["pct_of_read_ceiling"] = round(100 * ceil_ms / r["ms"], 1)
+    else:
+        rec["weight_bytes_per_step"] = wb
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -341,7 +452,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
     ap.add_argument("--counters-m", type=int, choices=(1, 48), default=1, help="batch size of the --counters workload")
-    ap.add_argument("--modes", default="M1_grouped,M1_plain,M48_grouped,M48_plain",
+    ap.add_argument("--modes", default="M1_grouped,M1_plain,M48_grouped,M48_plain,NVFP4_M1_plain,NVFP4_M48_plain",
                     help="comma list of timed modes; M1_grouped is always timed (it is the headline value)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -372,6 +483,19 @@ def main():
             log(f"bench: M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(M, mode)]['gbs']:6.0f} GB/s, "
                 f"{1e3 / ms:6.0f} steps/s, {res[(M, mode)]['launches']} launches")
             del g
+    nv = None
+    for M in (1, 48):
+        if f"NVFP4_M{M}_plain" not in modes:
+            continue
+        if nv is None:
+            nv = Nvfp4Workload(q4, synth, torch, wl)
+        ms, g = time_graph(torch, nv, M, args.steps, args.warmup, "plain")
+        by = nv.step_bytes(M)
+        res[(f"NVFP4_M{M}", "plain")] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(nv.launches(M)),
+                                             wbytes=sum(b for _, b, _ in nv.launches(M)))
+        log(f"bench: NVFP4 M={M} plain step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(f'NVFP4_M{M}', 'plain')]['gbs']:6.0f} GB/s, "
+            f"{1e3 / ms:6.0f} steps/s")
+        del g
     roof = {}
     for M in (1, 48):
         if M != 1 and f"M{M}_grouped" not in modes:
@@ -416,18 +540,21 @@ def main():
             "read_ceiling": {"what": "diagnostic plain read of the same weight buffers in the same 73 launches, hipGraph",
                              "ms_per_step": round(ceil_ms, 5), "weight_GB_s": round(ceil_gbs, 1),
                              "pct_of_8TBps": round(100 * ceil_gbs / PEAK_GBS, 2)},
-            "modes": {f"M{M}_{mode}": {"ms_per_step": round(r["ms"], 5), "GB_s": round(r["gbs"], 1),
-                                        "weight_GB_s": round(wbytes / (r["ms"] * 1e-3) / 1e9, 1),
-                                        "pct_of_read_ceiling": round(100 * ceil_ms / r["ms"], 1),
-                                        "pct_of_8TBps": round(100 * r["gbs"] / PEAK_GBS, 2),
-                                        "steps_per_s": round(1e3 / r["ms"], 1), "tokens_per_s": round(M * 1e3 / r["ms"], 1),
-                                        "launches_per_step": r["launches"], "bytes_per_step": r["bytes"]}
-                      for (M, mode), r in res.items()},
+            "modes": {mode_key(k): mode_record(k, r, wbytes, ceil_ms) for k, r in res.items()},
         },
         "roofline": roof[1],
     }
     if 48 in roof:
         out["roofline_M48"] = roof[48]
+    if nv is not None:
+        kms, kbytes = time_nvfp4_launches(torch, q4, nv, 1)
+        achieved = kbytes / (kms * 1e-3) / 1e9
+        vname = q4.variant_name(q4.FMT_NVFP4G16, 0, 1, 2048, 2048)
+        log(f"bench: NVFP4 GEMV launches at M=1 ({vname}): avg {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
+        out["roofline_nvfp4_M1"] = {"bound": "hbm", "kernel": f"gemv_stream_kernel<FmtNvfp4, 1> ({vname}), M=1 per-projection launches",
+                                    "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                                    "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
