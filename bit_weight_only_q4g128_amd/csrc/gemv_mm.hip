@@ -17,9 +17,11 @@
 //         acc += scale * D + min * SX   (min staged as -min / 128, exact);
 //   * two loader waves, one per K half, that stream the activations of each
 //     128-column group (MT*16 batch rows) from L2 through registers into a
-//     double-buffered LDS ring, already in B-fragment order and in the column
-//     pairing of the weight operand, and get -128 * SX on the way from MFMAs
-//     with an all -128 A operand.
+//     double-buffered LDS ring.  Each load reads four whole rows of the group
+//     (1 KB contiguous, so every load fills whole cache lines); the writes
+//     scatter them into B-fragment order, in the column pairing of the weight
+//     operand, and the loader reads the fragments back to get -128 * SX from
+//     MFMAs with an all -128 A operand.
 //
 // One barrier per group step keeps the ring in step.  At the end the two K
 // halves meet in LDS.  When K is split over several workgroups, each writes
@@ -98,6 +100,13 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+
+// LDS slot of fragment lane L in a k-step s fragment (1 KB, 64 slots of 16
+// bytes).  The loaders scatter whole activation rows into fragment order, 16
+// lanes of a write landing in four fragments; the XOR keeps those 16 lanes,
+// and any 16 consecutive lanes of a fragment read, on distinct 16-byte bank
+// groups.
+__device__ __forceinline__ int frag_slot(int L, int s) { return L ^ (4 * s + ((L >> 4) & 3)); }
 
 // Workspace layout, the same for every call so that calls with different
 // tasks can share one workspace: the arrival counters of all split tasks of a
@@ -187,6 +196,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         const int hlast = hlen > 0 ? hlen - 1 : 0;
         const int hb = hlen > 0 ? hbase : 0;
         const int prow0 = row0 + 32 * rp;
+        int fs[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) fs[s] = frag_slot(lane, s);
         int nr = a.N - prow0;
         nr = __builtin_amdgcn_readfirstlane(nr < 0 ? 0 : (nr > 32 ? 32 : nr));
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)prow0 * rowbytes, (uint32_t)nr * rowbytes);
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         // one group step; u = i % kPre is the prefetch ring entry
         auto step = [&](const int i, const int u) {
             const int slot = i & 1;
-            const u32x4* xs = xb + (size_t)((slot * 2 + kh) * MT) * 4 * 64 + lane;
+            const u32x4* xs = xb + (size_t)((slot * 2 + kh) * MT) * 4 * 64;
             const u32x4 qa0 = q[u][0], qa1 = q[u][1];
             q[u][0] = aload(i + kPre, 0);
             q[u][1] = aload(i + kPre, 1);
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
             for (int s = 0; s < 4; ++s) {
                 u32x4 B[MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) B[mt] = xs[(mt * 4 + s) * 64];
+                for (int mt = 0; mt < MT; ++mt) B[mt] = xs[(mt * 4 + s) * 64 + fs[s]];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     uint32_t A[4];
@@ -312,34 +324,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         const int hlast = hlen > 0 ? hlen - 1 : 0;
         const int hb = hlen > 0 ? hbase : 0;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.M * a.K * 2));
-        // piece (mt, s) of step i: lane l gets the 8 activations of batch row
-        // 16 mt + l % 16 at group columns 32 (l / 16) + 8 s .. + 8
+        // piece (mt, s) of step i: four whole batch rows 16 mt + 4 s + l / 16
+        // of the group, lane l holding columns 8 (l % 16) .. + 8 (1 KB
+        // contiguous per row quartet, so each load fills whole cache lines)
         auto xload = [&](int i, int p) {
             const int mt = p >> 2, s = p & 3;
-            const int m = 16 * mt + (lane & 15);
+            const int m = 16 * mt + 4 * s + (lane >> 4);
             const int g = g0 + hb + (i < hlast ? i : hlast);
-            const int k = (g << 7) + 32 * (lane >> 4) + 8 * s;
+            const int k = (g << 7) + 8 * (lane & 15);
             return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((m * a.K + k) * 2), 0, 0));
         };
+        // where lane l's piece (mt, s) goes: fragment (mt, k-step l % 4), lane
+        // 4 s + l / 16 + 16 ((l / 4) % 4) (its row within the tile plus 16 x
+        // its column quarter); fsl: this lane's slot in each k-step's fragment
+        const int sp = lane & 3;
+        const int fl0 = (lane >> 4) + 16 * ((lane >> 2) & 3);
+        int fsl[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) fsl[s] = frag_slot(lane, s);
         auto stage = [&](int i, const u32x4 (&xr)[4 * MT]) {
             const int slot = i & 1;
-            u32x4* dst = xb + (size_t)((slot * 2 + L) * MT) * 4 * 64 + lane;
+            u32x4* frag = xb + (size_t)((slot * 2 + L) * MT) * 4 * 64;
             // -128 * SX from the matrix core: an A operand of all -128 against
-            // the pieces as loaded (the column order within a k-step does not
-            // matter to a sum) leaves -128 * SX of batch row l % 16 in all four
-            // results of lane l, the form the compute waves start from
+            // the fragments (read back in fragment order; the column order
+            // within a k-step does not matter to a sum) leaves -128 * SX of
+            // batch row l % 16 in all four results of lane l, the form the
+            // compute waves start from
             const bf16x8_t neg128 = as_bf16x8(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const u32x4 v = xr[mt * 4 + s];
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, as_bf16x8(v), c, 0, 0, 0);
                     uint32_t pr[4];
                     xq4_pairs(v.x, v.y, v.z, v.w, pr);
-                    dst[(mt * 4 + s) * 64] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+                    frag[(mt * 4 + sp) * 64 + frag_slot(fl0 + 4 * s, sp)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
                 }
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, as_bf16x8(frag[(mt * 4 + s) * 64 + fsl[s]]), c, 0, 0, 0);
                 if (lane < 16) sxb[(slot * 2 + L) * MT * 16 + mt * 16 + lane] = c;
             }
         };
