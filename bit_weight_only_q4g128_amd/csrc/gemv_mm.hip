@@ -102,11 +102,11 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // LDS slot of fragment lane L in a k-step s fragment (1 KB, 64 slots of 16
-// bytes).  The loaders scatter whole activation rows into fragment order, 16
-// lanes of a write landing in four fragments; the XOR keeps those 16 lanes,
-// and any 16 consecutive lanes of a fragment read, on distinct 16-byte bank
-// groups.
-__device__ __forceinline__ int frag_slot(int L, int s) { return L ^ (4 * s + ((L >> 4) & 3)); }
+// bytes).  The loaders scatter whole activation rows into fragment order, 8
+// consecutive lanes of a write landing in four fragments; the XOR puts those 8
+// lanes, and any 8 consecutive lanes of a fragment read, on 8 distinct
+// 16-byte bank groups (of 128 bytes).
+__device__ __forceinline__ int frag_slot(int L, int s) { return L ^ (2 * s + ((L >> 4) & 1)); }
 
 // Workspace layout, the same for every call so that calls with different
 // tasks can share one workspace: the arrival counters of all split tasks of a
