@@ -9,20 +9,22 @@
 //     issues only weight loads (kPre 128-column groups ahead), so its in-order
 //     waits on the vector-memory counter never stall behind anything but its
 //     own weights.  Per group it turns its 2 x 16 bytes per lane into BF16
-//     "128 + code" operands for its two 16-row tiles, runs 4 k-steps x MT
+//     "128 + code" operands for its two 16-row tiles and runs 4 k-steps x MT
 //     batch tiles x 2 row tiles of MFMA with the activations as the B operand
 //     (each activation fragment read from LDS once serves both row tiles),
-//     each chain starting from -128 * SX (SX = sum of x over the group) so
-//     that D is the sum of code * x, and folds the group as
-//         acc += scale * D + min * SX   (min staged as -min / 128, exact);
+//     giving D = sum of (128 + code) * x; beside them one chain per batch tile
+//     with an all -128 A operand gives C = -128 * SX (SX = sum of x over the
+//     group), and the group folds as
+//         acc += scale * (D + C) + min * SX   (min staged as -min / 128),
+//     exact up to the fp32 rounding of D + C (exact when one product is
+//     nonzero);
 //   * two loader waves, one per K half, that stream the activations of each
 //     128-column group (MT*16 batch rows) from L2 through registers into a
 //     double-buffered LDS ring.  Each load reads four whole rows of the group
 //     (1 KB contiguous, so every load fills whole cache lines); the writes
 //     scatter them into B-fragment order, in the column pairing of the weight
-//     operand, and the loader reads the fragments back to get -128 * SX from
-//     MFMAs with an all -128 A operand.
-//
+//     operand.
+
 // One barrier per group step keeps the ring in step.  At the end the two K
 // halves meet in LDS.  When K is split over several workgroups, each writes
 // its fp32 partial tile to a caller-provided workspace; the workgroup that
@@ -78,18 +80,16 @@ template <int MT>
 __host__ __device__ constexpr int mm_waves() { return MT <= 3 ? 4 : 2; }
 // activation groups a loader keeps in flight (registers: 4 * MT pieces each)
 template <int MT>
-__host__ __device__ constexpr int mm_xp() { return MT <= 2 ? 2 : 1; }
-// LDS: ring [2 slots][2 halves][MT][4 k-steps][64 lanes] x 16 bytes, group sums
-// [2][2][MT * 16] floats, group parameters [groups][64 rows] x (scale, min)
+__host__ __device__ constexpr int mm_xp() { return MT <= 1 ? 2 : 1; }
+// LDS: ring [2 slots][2 halves][MT][4 k-steps][64 lanes] x 16 bytes, group
+// parameters [groups][64 rows] x (scale, min)
 template <int MT>
 __host__ __device__ constexpr int mm_ring_bytes() { return 2 * 2 * MT * 4 * 64 * 16; }
 template <int MT>
-__host__ __device__ constexpr int mm_sx_bytes() { return 2 * 2 * MT * 16 * 16; }
-template <int MT>
-__host__ __device__ inline int mm_shmem(int gps) { return mm_ring_bytes<MT>() + mm_sx_bytes<MT>() + gps * kRows * 8; }
+__host__ __device__ inline int mm_shmem(int gps) { return mm_ring_bytes<MT>() + gps * kRows * 8; }
 // most groups per slice whose parameters fit the LDS budget
 template <int MT>
-constexpr int mm_max_gps() { return (kLdsBudget - mm_ring_bytes<MT>() - mm_sx_bytes<MT>()) / (kRows * 8); }
+constexpr int mm_max_gps() { return (kLdsBudget - mm_ring_bytes<MT>()) / (kRows * 8); }
 
 // Workgroup barrier for the main loops: waits only for this wave's LDS
 // traffic (lgkmcnt) and fences the compiler, so vector-memory loads (the
@@ -160,8 +160,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
     constexpr int XP = mm_xp<MT>();
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     u32x4* xb = reinterpret_cast<u32x4*>(lds);                                               // [2][2][MT][4][64]
-    f32x4* sxb = reinterpret_cast<f32x4*>(lds + mm_ring_bytes<MT>());                        // [2][2][MT*16]
-    f32x2* smb = reinterpret_cast<f32x2*>(lds + mm_ring_bytes<MT>() + mm_sx_bytes<MT>());    // [gps][64]
+    f32x2* smb = reinterpret_cast<f32x2*>(lds + mm_ring_bytes<MT>());    // [gps][64]
 
     int ti = 0;
 #pragma unroll
@@ -196,6 +195,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         const int hlast = hlen > 0 ? hlen - 1 : 0;
         const int hb = hlen > 0 ? hbase : 0;
         const int prow0 = row0 + 32 * rp;
+        const bf16x8_t neg128 = as_bf16x8(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u);
         int fs[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) fs[s] = frag_slot(lane, s);
@@ -229,20 +229,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
             q[u][0] = aload(i + kPre, 0);
             q[u][1] = aload(i + kPre, 1);
             const uint32_t qd[2][4] = {{qa0.x, qa0.y, qa0.z, qa0.w}, {qa1.x, qa1.y, qa1.z, qa1.w}};
-            // the MFMA chains start from -128 * SX, so D = sum of code * x
-            f32x4 cx[MT];
+            // D = sum of (128 + code) * x and C = -128 * SX: an all -128 A
+            // operand against the same fragments leaves -128 * SX of batch row
+            // l % 16 in all four results of lane l
+            f32x4 cx[MT], D[2][MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) cx[mt] = sxb[(slot * 2 + kh) * MT * 16 + mt * 16 + (lane & 15)];
-            f32x4 D[2][MT];
+            for (int mt = 0; mt < MT; ++mt) cx[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) D[t][mt] = cx[mt];
+                for (int mt = 0; mt < MT; ++mt) D[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 u32x4 B[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) B[mt] = xs[(mt * 4 + s) * 64 + fs[s]];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) cx[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, as_bf16x8(B[mt]), cx[mt], 0, 0, 0);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     uint32_t A[4];
@@ -254,7 +257,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                 }
             }
             if (i < hlen) {
-                // acc += scale * D + min * SX, with min staged as -min / 128
+                // acc += scale * (D + C) + min * SX with min staged as -min / 128;
+                // D + C is the sum of code * x (exact when one product is nonzero)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + (hbase + i) * kRows + 32 * rp + 16 * t + 4 * (lane >> 4));
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
-                            acc[t][mt][v] = fmaf(mq[v], cx[mt][v], fmaf(sc[v], D[t][mt][v], acc[t][mt][v]));
+                            acc[t][mt][v] = fmaf(mq[v], cx[mt][v], fmaf(sc[v], D[t][mt][v] + cx[mt][v], acc[t][mt][v]));
                 }
             }
             lds_barrier();
@@ -336,23 +340,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         };
         // where lane l's piece (mt, s) goes: fragment (mt, k-step l % 4), lane
         // 4 s + l / 16 + 16 ((l / 4) % 4) (its row within the tile plus 16 x
-        // its column quarter); fsl: this lane's slot in each k-step's fragment
+        // its column quarter)
         const int sp = lane & 3;
         const int fl0 = (lane >> 4) + 16 * ((lane >> 2) & 3);
-        int fsl[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) fsl[s] = frag_slot(lane, s);
         auto stage = [&](int i, const u32x4 (&xr)[4 * MT]) {
             const int slot = i & 1;
             u32x4* frag = xb + (size_t)((slot * 2 + L) * MT) * 4 * 64;
-            // -128 * SX from the matrix core: an A operand of all -128 against
-            // the fragments (read back in fragment order; the column order
-            // within a k-step does not matter to a sum) leaves -128 * SX of
-            // batch row l % 16 in all four results of lane l, the form the
-            // compute waves start from
-            const bf16x8_t neg128 = as_bf16x8(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const u32x4 v = xr[mt * 4 + s];
@@ -360,12 +355,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                     xq4_pairs(v.x, v.y, v.z, v.w, pr);
                     frag[(mt * 4 + sp) * 64 + frag_slot(fl0 + 4 * s, sp)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
                 }
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, as_bf16x8(frag[(mt * 4 + s) * 64 + fsl[s]]), c, 0, 0, 0);
-                if (lane < 16) sxb[(slot * 2 + L) * MT * 16 + mt * 16 + lane] = c;
-            }
         };
         u32x4 xr[XP][4 * MT];
 #pragma unroll
