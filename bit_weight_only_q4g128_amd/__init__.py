@@ -15,6 +15,7 @@ import torch
 
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
+    "nvfp4g16_gemv_grouped", "nvfp4g16_workspace_bytes", "bf16_gemv_grouped", "bf16_workspace_bytes",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
     "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
@@ -64,6 +65,23 @@ lib.q4g128_gemv_grouped_ws.argtypes = [ctypes.POINTER(Q4Task), _i, _i, _i, _p, c
 lib.q4g128_gemv_grouped_ws.restype = ctypes.c_int
 lib.q4g128_workspace_bytes.argtypes = [ctypes.POINTER(Q4Task), _i, _i, ctypes.POINTER(ctypes.c_size_t)]
 lib.q4g128_workspace_bytes.restype = ctypes.c_int
+
+
+class NvTask(ctypes.Structure):
+    """Mirror of the C struct nvfp4g16_task."""
+    _fields_ = [("x", _p), ("qweight", _p), ("scale_e4m3", _p), ("global_scale", _f), ("y", _p), ("N", _i), ("K", _i)]
+
+
+class BfTask(ctypes.Structure):
+    """Mirror of the C struct bf16_task."""
+    _fields_ = [("x", _p), ("w", _p), ("y", _p), ("N", _i), ("K", _i)]
+
+
+for _name, _T in (("nvfp4g16", NvTask), ("bf16", BfTask)):
+    getattr(lib, f"{_name}_gemv_grouped_ws").argtypes = [ctypes.POINTER(_T), _i, _i, _i, _p, ctypes.c_size_t, _p]
+    getattr(lib, f"{_name}_gemv_grouped_ws").restype = ctypes.c_int
+    getattr(lib, f"{_name}_workspace_bytes").argtypes = [ctypes.POINTER(_T), _i, _i, ctypes.POINTER(ctypes.c_size_t)]
+    getattr(lib, f"{_name}_workspace_bytes").restype = ctypes.c_int
 
 
 class Q4GemvError(ValueError):
@@ -195,6 +213,90 @@ def nvfp4g16_gemv(x, qweight, scale_e4m3, global_scale: float, out=None, variant
     _raise(lib.nvfp4g16_gemv_variant(x.data_ptr(), M, K, qweight.data_ptr(), scale_e4m3.data_ptr(), float(global_scale), N,
                                      y.data_ptr(), int(variant), _stream(x)))
     return y
+
+
+def _nv_task_array(items):
+    items = list(items)
+    if not 1 <= len(items) <= 8:
+        raise ValueError("1..8 tasks per call")
+    arr = (NvTask * len(items))()
+    outs, M = [], None
+    for i, (x, qweight, scale_e4m3, global_scale, out) in enumerate(items):
+        _check(x, "x", _U16, 2); _check(qweight, "qweight", _U8, 2); _check(scale_e4m3, "scale_e4m3", _E4M3, 2)
+        m, K = x.shape
+        N = qweight.shape[0]
+        M = m if M is None else M
+        if m != M:
+            raise ValueError("all tasks must share the batch size M")
+        if qweight.shape[1] * 2 != K or tuple(scale_e4m3.shape) != (N, K // 16):
+            raise ValueError(f"task {i}: inconsistent shapes")
+        y = _out(out, (M, N), torch.bfloat16, x)
+        outs.append(y)
+        arr[i] = NvTask(x.data_ptr(), qweight.data_ptr(), scale_e4m3.data_ptr(), float(global_scale), y.data_ptr(), N, K)
+    return items, arr, outs, M
+
+
+def _bf_task_array(items):
+    items = list(items)
+    if not 1 <= len(items) <= 8:
+        raise ValueError("1..8 tasks per call")
+    arr = (BfTask * len(items))()
+    outs, M = [], None
+    for i, (x, w, out) in enumerate(items):
+        _check(x, "x", _U16, 2); _check(w, "w", _U16, 2)
+        m, K = x.shape
+        N = w.shape[0]
+        M = m if M is None else M
+        if m != M:
+            raise ValueError("all tasks must share the batch size M")
+        if w.shape[1] != K:
+            raise ValueError(f"task {i}: inconsistent shapes")
+        y = _out(out, (M, N), torch.bfloat16, x)
+        outs.append(y)
+        arr[i] = BfTask(x.data_ptr(), w.data_ptr(), y.data_ptr(), N, K)
+    return items, arr, outs, M
+
+
+def _grouped(fn, items, arr, M, variant, workspace):
+    st = _stream(items[0][0])
+    if workspace is None:
+        _raise(fn(arr, len(items), M, int(variant), None, 0, st))
+    else:
+        if workspace.device != items[0][0].device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the activations' device")
+        _raise(fn(arr, len(items), M, int(variant), workspace.data_ptr(), workspace.numel(), st))
+
+
+def nvfp4g16_gemv_grouped(items, variant: int = VARIANT_AUTO, workspace=None):
+    """Several independent NVFP4 GEMVs with one batch size, launched together.
+    items: sequence of (x, qweight, scale_e4m3, global_scale, out-or-None);
+    workspace as for q4g128_gemv_grouped.  Returns the list of outputs."""
+    items, arr, outs, M = _nv_task_array(items)
+    _grouped(lib.nvfp4g16_gemv_grouped_ws, items, arr, M, variant, workspace)
+    return outs
+
+
+def nvfp4g16_workspace_bytes(items) -> int:
+    items, arr, _, M = _nv_task_array(items)
+    n = ctypes.c_size_t(0)
+    _raise(lib.nvfp4g16_workspace_bytes(arr, len(items), M, ctypes.byref(n)))
+    return int(n.value)
+
+
+def bf16_gemv_grouped(items, variant: int = VARIANT_AUTO, workspace=None):
+    """Several independent BF16 GEMVs with one batch size, launched together.
+    items: sequence of (x, w, out-or-None); workspace as for
+    q4g128_gemv_grouped.  Returns the list of outputs."""
+    items, arr, outs, M = _bf_task_array(items)
+    _grouped(lib.bf16_gemv_grouped_ws, items, arr, M, variant, workspace)
+    return outs
+
+
+def bf16_workspace_bytes(items) -> int:
+    items, arr, _, M = _bf_task_array(items)
+    n = ctypes.c_size_t(0)
+    _raise(lib.bf16_workspace_bytes(arr, len(items), M, ctypes.byref(n)))
+    return int(n.value)
 
 
 def bf16_gemv(x, w, out=None, variant: int = VARIANT_AUTO):

@@ -42,16 +42,17 @@ bool variant_ok(int variant) {
 
 // Kernel choice for Q4_VARIANT_AUTO.  Small batches on rows of 1-4 KB go to
 // the streaming kernel, other small batches to the packed-dot kernel; larger
-// int4 batches to the tiled matrix-core kernel, other larger batches to the
-// per-task matrix-core kernel.  `split`: a workspace allows K splits.
+// batches to the tiled matrix-core kernel where K allows it (K % 128 == 0 and
+// the int4 group parameters fit LDS, or a split), else to the per-task
+// matrix-core kernel.  `split`: a workspace allows K splits.
 int pick(Fmt fmt, int variant, int M, int K, bool split = false) {
     if (variant == Q4_VARIANT_DOT2) return q4::dot2_supported(fmt, K) ? Q4_VARIANT_DOT2 : -1;
     if (variant == Q4_VARIANT_MFMA) return Q4_VARIANT_MFMA;
     if (variant == Q4_VARIANT_STREAM) return q4::stream_supported(fmt, M, K) ? Q4_VARIANT_STREAM : -1;
-    if (variant == Q4_VARIANT_TILED) return (fmt == q4::kFmtQ4 && q4::mm_supported(M, K, split)) ? Q4_VARIANT_TILED : -1;
+    if (variant == Q4_VARIANT_TILED) return q4::mm_supported(fmt, M, K, split) ? Q4_VARIANT_TILED : -1;
     if (M <= 4 && q4::stream_supported(fmt, M, K)) return Q4_VARIANT_STREAM;
     if (M <= 4 && q4::dot2_supported(fmt, K)) return Q4_VARIANT_DOT2;
-    if (fmt == q4::kFmtQ4 && q4::mm_supported(M, K, split)) return Q4_VARIANT_TILED;
+    if (q4::mm_supported(fmt, M, K, split)) return Q4_VARIANT_TILED;
     return Q4_VARIANT_MFMA;
 }
 
@@ -61,7 +62,7 @@ int run(Fmt fmt, int chosen, const GemvArgs* a, int count, void* stream, void* w
     switch (chosen) {
         case Q4_VARIANT_DOT2: e = q4::launch_dot2(fmt, a, count, s); break;
         case Q4_VARIANT_STREAM: e = q4::launch_stream(fmt, a, count, s); break;
-        case Q4_VARIANT_TILED: e = q4::launch_mm(a, count, ws, ws_bytes, s); break;
+        case Q4_VARIANT_TILED: e = q4::launch_mm(fmt, a, count, ws, ws_bytes, s); break;
         default: e = q4::launch_mfma(fmt, a, count, s); break;
     }
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
@@ -86,6 +87,86 @@ int check_q4(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint
     a = GemvArgs{};
     a.x = x; a.w = qweight; a.scale = scale; a.minv = minv; a.y = y; a.M = M; a.N = N; a.K = K;
     return Q4_OK;
+}
+
+// Validation of one NVFP4 task.
+int check_nv(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint8_t* scale_e4m3, float global_scale, int N,
+             uint16_t* y, GemvArgs& a, Range in[4], Range& out) {
+    int rc = check_common(x, M, K, N, y);
+    if (rc) return rc;
+    if (!qweight || !scale_e4m3) return Q4_EINVAL_PTR;
+    if (K % 32) return Q4_EINVAL_SHAPE;
+    if (!aligned(qweight, 16)) return Q4_EALIGN;
+    in[0] = range_of(x, (size_t)M * K * 2);
+    in[1] = range_of(qweight, (size_t)N * K / 2);
+    in[2] = range_of(scale_e4m3, (size_t)N * K / 16);
+    in[3] = Range{0, 0};
+    out = range_of(y, (size_t)M * N * 2);
+    a = GemvArgs{};
+    a.x = x; a.w = qweight; a.scale8 = scale_e4m3; a.gscale = global_scale; a.y = y; a.M = M; a.N = N; a.K = K;
+    return Q4_OK;
+}
+
+// Validation of one BF16 task.
+int check_bf(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* y, GemvArgs& a, Range in[4], Range& out) {
+    int rc = check_common(x, M, K, N, y);
+    if (rc) return rc;
+    if (!w) return Q4_EINVAL_PTR;
+    if (K % 8) return Q4_EINVAL_SHAPE;
+    if (!aligned(w, 16)) return Q4_EALIGN;
+    in[0] = range_of(x, (size_t)M * K * 2);
+    in[1] = range_of(w, (size_t)N * K * 2);
+    in[2] = in[3] = Range{0, 0};
+    out = range_of(y, (size_t)M * N * 2);
+    a = GemvArgs{};
+    a.x = x; a.w = reinterpret_cast<const uint8_t*>(w); a.y = y; a.M = M; a.N = N; a.K = K;
+    return Q4_OK;
+}
+
+// Kernel family for a validated group of one format: the matrix cores if any
+// task needs them (the tiled kernel if every task can use it), the streaming
+// kernel if every task can use it, else the packed-dot kernel (or the matrix
+// cores where that cannot run); then the alias checks across tasks.
+int plan_checked(Fmt fmt, const GemvArgs* a, const Range (*in)[4], const Range* out, int count, int M, int variant, bool split,
+                 int* chosen_out) {
+    int n_big = 0, n_tiled = 0, n_stream = 0;
+    for (int i = 0; i < count; ++i) {
+        const int c = pick(fmt, variant, M, a[i].K, split);
+        if (c < 0) return Q4_EVARIANT;
+        n_big += c == Q4_VARIANT_MFMA || c == Q4_VARIANT_TILED;
+        n_tiled += c == Q4_VARIANT_TILED;
+        n_stream += c == Q4_VARIANT_STREAM;
+    }
+    int chosen;
+    if (n_big) chosen = n_tiled == count ? Q4_VARIANT_TILED : Q4_VARIANT_MFMA;
+    else chosen = n_stream == count ? Q4_VARIANT_STREAM : Q4_VARIANT_DOT2;
+    if (chosen == Q4_VARIANT_DOT2) {
+        for (int i = 0; i < count; ++i)
+            if (!q4::dot2_supported(fmt, a[i].K)) chosen = Q4_VARIANT_MFMA;
+    }
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j) {
+            for (int r = 0; r < 4; ++r)
+                if (overlaps(out[i], in[j][r])) return Q4_EALIAS;
+            if (i != j && overlaps(out[i], out[j])) return Q4_EALIAS;
+        }
+    *chosen_out = chosen;
+    return Q4_OK;
+}
+
+// A grouped call of one format after validation: a workspace too small for
+// the planned split (or a launch too large to split) runs unsplit, which
+// every task must then allow.
+int run_grouped(Fmt fmt, int chosen, const GemvArgs* a, int count, int M, void* workspace, size_t workspace_bytes, void* stream) {
+    const bool split = workspace != nullptr && workspace_bytes > 0;
+    if (chosen == Q4_VARIANT_TILED && split) {
+        const size_t need = q4::mm_workspace_bytes(fmt, a, count);
+        if (need == 0 || workspace_bytes < need) {
+            for (int i = 0; i < count; ++i)
+                if (!q4::mm_supported(fmt, M, a[i].K, false)) return Q4_EVARIANT;
+        }
+    }
+    return run(fmt, chosen, a, count, stream, workspace, workspace_bytes);
 }
 
 }  // namespace
@@ -120,41 +201,18 @@ int q4g128_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweight,
     return run(q4::kFmtQ4, chosen, a, stream);
 }
 
-// Validates a group and picks one kernel family for it: the matrix cores if
-// any task needs them (the tiled kernel if every task can use it), the
-// streaming kernel if every task can use it, else the packed-dot kernel (or
-// the matrix cores where that cannot run).
+// Validates an int4 group and picks one kernel family for it.
 static int plan_group(const q4g128_task* tasks, int count, int M, int variant, bool split, GemvArgs* a, int* chosen_out) {
     if (!tasks) return Q4_EINVAL_PTR;
     if (count < 1 || count > q4::kMaxTasks) return Q4_EINVAL_SHAPE;
     if (!variant_ok(variant)) return Q4_EVARIANT;
     Range in[q4::kMaxTasks][4], out[q4::kMaxTasks];
-    int n_big = 0, n_tiled = 0, n_stream = 0;
     for (int i = 0; i < count; ++i) {
         const q4g128_task& t = tasks[i];
         int rc = check_q4(t.x, M, t.K, t.qweight, t.scale, t.minv, t.N, t.y, a[i], in[i], out[i]);
         if (rc) return rc;
-        const int c = pick(q4::kFmtQ4, variant, M, t.K, split);
-        if (c < 0) return Q4_EVARIANT;
-        n_big += c == Q4_VARIANT_MFMA || c == Q4_VARIANT_TILED;
-        n_tiled += c == Q4_VARIANT_TILED;
-        n_stream += c == Q4_VARIANT_STREAM;
     }
-    int chosen;
-    if (n_big) chosen = n_tiled == count ? Q4_VARIANT_TILED : Q4_VARIANT_MFMA;
-    else chosen = n_stream == count ? Q4_VARIANT_STREAM : Q4_VARIANT_DOT2;
-    if (chosen == Q4_VARIANT_DOT2) {
-        for (int i = 0; i < count; ++i)
-            if (!q4::dot2_supported(q4::kFmtQ4, tasks[i].K)) chosen = Q4_VARIANT_MFMA;
-    }
-    for (int i = 0; i < count; ++i)
-        for (int j = 0; j < count; ++j) {
-            for (const Range& r : in[j])
-                if (overlaps(out[i], r)) return Q4_EALIAS;
-            if (i != j && overlaps(out[i], out[j])) return Q4_EALIAS;
-        }
-    *chosen_out = chosen;
-    return Q4_OK;
+    return plan_checked(q4::kFmtQ4, a, in, out, count, M, variant, split, chosen_out);
 }
 
 int q4g128_gemv_grouped_ws(const q4g128_task* tasks, int count, int M, int variant, void* workspace, size_t workspace_bytes,
@@ -165,16 +223,7 @@ int q4g128_gemv_grouped_ws(const q4g128_task* tasks, int count, int M, int varia
     const bool split = workspace != nullptr && workspace_bytes > 0;
     int rc = plan_group(tasks, count, M, variant, split, a, &chosen);
     if (rc) return rc;
-    if (chosen == Q4_VARIANT_TILED && split) {
-        // a workspace too small for the planned split (or a launch too large
-        // to split) runs unsplit, which every task must then allow
-        const size_t need = q4::mm_workspace_bytes(a, count);
-        if (need == 0 || workspace_bytes < need) {
-            for (int i = 0; i < count; ++i)
-                if (!q4::mm_supported(M, a[i].K, false)) return Q4_EVARIANT;
-        }
-    }
-    return run(q4::kFmtQ4, chosen, a, count, stream, workspace, workspace_bytes);
+    return run_grouped(q4::kFmtQ4, chosen, a, count, M, workspace, workspace_bytes, stream);
 }
 
 int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant, void* stream) {
@@ -187,7 +236,7 @@ int q4g128_workspace_bytes(const q4g128_task* tasks, int count, int M, size_t* b
     int chosen = 0;
     int rc = plan_group(tasks, count, M, Q4_VARIANT_AUTO, true, a, &chosen);
     if (rc) return rc;
-    *bytes = chosen == Q4_VARIANT_TILED ? q4::mm_workspace_bytes(a, count) : 0;
+    *bytes = chosen == Q4_VARIANT_TILED ? q4::mm_workspace_bytes(q4::kFmtQ4, a, count) : 0;
     return Q4_OK;
 }
 
@@ -238,6 +287,72 @@ int bf16_gemv_variant(const uint16_t* x, int M, int K, const uint16_t* w, int N,
 
 int bf16_gemv(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* y, void* stream) {
     return bf16_gemv_variant(x, M, K, w, N, y, Q4_VARIANT_AUTO, stream);
+}
+
+static int plan_nv(const nvfp4g16_task* tasks, int count, int M, int variant, bool split, GemvArgs* a, int* chosen) {
+    if (!tasks) return Q4_EINVAL_PTR;
+    if (count < 1 || count > q4::kMaxTasks) return Q4_EINVAL_SHAPE;
+    if (!variant_ok(variant)) return Q4_EVARIANT;
+    Range in[q4::kMaxTasks][4], out[q4::kMaxTasks];
+    for (int i = 0; i < count; ++i) {
+        const nvfp4g16_task& t = tasks[i];
+        int rc = check_nv(t.x, M, t.K, t.qweight, t.scale_e4m3, t.global_scale, t.N, t.y, a[i], in[i], out[i]);
+        if (rc) return rc;
+    }
+    return plan_checked(q4::kFmtNvfp4, a, in, out, count, M, variant, split, chosen);
+}
+
+int nvfp4g16_gemv_grouped_ws(const nvfp4g16_task* tasks, int count, int M, int variant, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (workspace && !aligned(workspace, 256)) return Q4_EALIGN;
+    GemvArgs a[q4::kMaxTasks];
+    int chosen = 0;
+    int rc = plan_nv(tasks, count, M, variant, workspace != nullptr && workspace_bytes > 0, a, &chosen);
+    if (rc) return rc;
+    return run_grouped(q4::kFmtNvfp4, chosen, a, count, M, workspace, workspace_bytes, stream);
+}
+
+int nvfp4g16_workspace_bytes(const nvfp4g16_task* tasks, int count, int M, size_t* bytes) {
+    if (!bytes) return Q4_EINVAL_PTR;
+    GemvArgs a[q4::kMaxTasks];
+    int chosen = 0;
+    int rc = plan_nv(tasks, count, M, Q4_VARIANT_AUTO, true, a, &chosen);
+    if (rc) return rc;
+    *bytes = chosen == Q4_VARIANT_TILED ? q4::mm_workspace_bytes(q4::kFmtNvfp4, a, count) : 0;
+    return Q4_OK;
+}
+
+static int plan_bf(const bf16_task* tasks, int count, int M, int variant, bool split, GemvArgs* a, int* chosen) {
+    if (!tasks) return Q4_EINVAL_PTR;
+    if (count < 1 || count > q4::kMaxTasks) return Q4_EINVAL_SHAPE;
+    if (!variant_ok(variant)) return Q4_EVARIANT;
+    Range in[q4::kMaxTasks][4], out[q4::kMaxTasks];
+    for (int i = 0; i < count; ++i) {
+        const bf16_task& t = tasks[i];
+        int rc = check_bf(t.x, M, t.K, t.w, t.N, t.y, a[i], in[i], out[i]);
+        if (rc) return rc;
+    }
+    return plan_checked(q4::kFmtBf16, a, in, out, count, M, variant, split, chosen);
+}
+
+int bf16_gemv_grouped_ws(const bf16_task* tasks, int count, int M, int variant, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (workspace && !aligned(workspace, 256)) return Q4_EALIGN;
+    GemvArgs a[q4::kMaxTasks];
+    int chosen = 0;
+    int rc = plan_bf(tasks, count, M, variant, workspace != nullptr && workspace_bytes > 0, a, &chosen);
+    if (rc) return rc;
+    return run_grouped(q4::kFmtBf16, chosen, a, count, M, workspace, workspace_bytes, stream);
+}
+
+int bf16_workspace_bytes(const bf16_task* tasks, int count, int M, size_t* bytes) {
+    if (!bytes) return Q4_EINVAL_PTR;
+    GemvArgs a[q4::kMaxTasks];
+    int chosen = 0;
+    int rc = plan_bf(tasks, count, M, Q4_VARIANT_AUTO, true, a, &chosen);
+    if (rc) return rc;
+    *bytes = chosen == Q4_VARIANT_TILED ? q4::mm_workspace_bytes(q4::kFmtBf16, a, count) : 0;
+    return Q4_OK;
 }
 
 int q4g128_dequant_f32(const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N, int K, float* w, void* stream) {

@@ -50,6 +50,17 @@ __device__ __forceinline__ f32x2 e2m1x2_to_f32x2(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
 }
 
+// Two E2M1 codes (byte SEL of dw) times an e4m3 group scale s -> a BF16 pair,
+// exact: the product has at most 6 significant bits and lies in [2^-10, 2688].
+// (The hardware's scaled FP4 conversions apply only the exponent of their scale
+// operand, so the e4m3 factor is a separate fp32 multiply.)
+template <int SEL>
+__device__ __forceinline__ uint32_t nv_pair_scaled(uint32_t dw, float s) {
+    f32x2 v = e2m1x2_to_f32x2<SEL>(dw);
+    const float lo = v.x * s, hi = v.y * s;
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
 // ---------------------------------------------------------------------------
 // int4 nibbles -> BF16 pairs holding 128 + code (exact)
 //

@@ -213,12 +213,6 @@ __global__ __launch_bounds__(256) void q4_mfma_kernel(GemvArgs a) {
 // hardware's scaled FP4 conversions apply only the exponent of their scale
 // operand, so the e4m3 factor is a separate fp32 multiply.)
 // ---------------------------------------------------------------------------
-template <int SEL>
-__device__ __forceinline__ uint32_t nv_pair_scaled(uint32_t dw, float s) {
-    f32x2 v = e2m1x2_to_f32x2<SEL>(dw);
-    const float lo = v.x * s, hi = v.y * s;
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
 
 template <int MTILES, int RT>
 __global__ __launch_bounds__(256) void nvfp4_mfma_kernel(GemvArgs a) {

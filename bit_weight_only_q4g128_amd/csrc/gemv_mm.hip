@@ -36,6 +36,8 @@
 // the group (any fixed assignment works as long as A and B agree), so one
 // 16-byte load per lane fetches all four k-steps of a row's group.  D: lane l
 // holds rows 4 * (l / 16) + v (v = 0..3) of column l % 16.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace q4 {
@@ -46,7 +48,6 @@ constexpr int kRows = 64;        // rows per workgroup
 constexpr int kCompute = 4;      // compute waves: 2 row pairs x 2 K halves
 constexpr int kLoaders = 2;      // activation loader waves, one per K half
 constexpr int kThreads = 64 * (kCompute + kLoaders);
-constexpr int kPre = 2;          // weight groups in flight per compute lane
 constexpr int kLdsBudget = 80 * 1024;   // two workgroups per CU (160 KB of LDS)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -57,6 +58,16 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
     return __builtin_bit_cast(bf16x8_t, v);
 }
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Weight formats of the tiled kernel.  kLoads: 16-byte loads per lane for one
+// 16-row tile's 128-column group (the group is 64 bytes of a row for the
+// 4-bit formats, 256 for BF16); kPre: weight groups a compute lane keeps in
+// flight beyond the current one.
+template <class F> struct MmFmt;
+template <> struct MmFmt<FmtQ4> { static constexpr int kLoads = 1, kPre = 2; };
+template <> struct MmFmt<FmtNvfp4> { static constexpr int kLoads = 1, kPre = 2; };
+template <> struct MmFmt<FmtBf16> { static constexpr int kLoads = 4, kPre = 1; };
+template <class F> __host__ __device__ constexpr bool is_q4() { return std::is_same<F, FmtQ4>::value; }
 
 struct MmTask {
     GemvArgs a;
@@ -85,11 +96,12 @@ __host__ __device__ constexpr int mm_xp() { return MT <= 1 ? 2 : 1; }
 // parameters [groups][64 rows] x (scale, min)
 template <int MT>
 __host__ __device__ constexpr int mm_ring_bytes() { return 2 * 2 * MT * 4 * 64 * 16; }
-template <int MT>
-__host__ __device__ inline int mm_shmem(int gps) { return mm_ring_bytes<MT>() + gps * kRows * 8; }
-// most groups per slice whose parameters fit the LDS budget
-template <int MT>
-constexpr int mm_max_gps() { return (kLdsBudget - mm_ring_bytes<MT>()) / (kRows * 8); }
+template <class F, int MT>
+__host__ __device__ inline int mm_shmem(int gps) { return mm_ring_bytes<MT>() + (is_q4<F>() ? gps * kRows * 8 : 0); }
+// most groups per slice whose parameters fit the LDS budget (int4 only; the
+// NVFP4 scales go straight to registers)
+template <class F, int MT>
+constexpr int mm_max_gps() { return is_q4<F>() ? (kLdsBudget - mm_ring_bytes<MT>()) / (kRows * 8) : (1 << 20); }
 
 // Workgroup barrier for the main loops: waits only for this wave's LDS
 // traffic (lgkmcnt) and fences the compiler, so vector-memory loads (the
@@ -129,15 +141,16 @@ __device__ __forceinline__ uint32_t part_off(int blk, int KS, int ks, int rp, in
 
 // y for one 16-row tile: lane l holds rows trow0 + 4 (l / 16) + v (v = 0..3)
 // of batch row 16 mt + l % 16; write_y does the two tiles of a row pair.
+// (times gs: the NVFP4 global scale, 1 otherwise)
 template <int MT>
-__device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, int trow0, int lane, const f32x4 (&v)[MT]) {
+__device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, float gs, int trow0, int lane, const f32x4 (&v)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = 16 * mt + (lane & 15);
         const int row = trow0 + 4 * (lane >> 4);
         if (m >= a.M || row >= a.N) continue;
         uint16_t* dst = a.y + (size_t)m * a.N + row;
-        const f32x4 r = v[mt];
+        const f32x4 r = v[mt] * gs;
         if (y8 && row + 3 < a.N) {
             const uint32_t lo = (uint32_t)f32_to_bf16(r.x) | ((uint32_t)f32_to_bf16(r.y) << 16);
             const uint32_t hi = (uint32_t)f32_to_bf16(r.z) | ((uint32_t)f32_to_bf16(r.w) << 16);
@@ -150,14 +163,16 @@ __device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, int tro
     }
 }
 template <int MT>
-__device__ __forceinline__ void write_y(const GemvArgs& a, bool y8, int prow0, int lane, const f32x4 (&v)[2][MT]) {
-    write_y_tile<MT>(a, y8, prow0, lane, v[0]);
-    write_y_tile<MT>(a, y8, prow0 + 16, lane, v[1]);
+__device__ __forceinline__ void write_y(const GemvArgs& a, bool y8, float gs, int prow0, int lane, const f32x4 (&v)[2][MT]) {
+    write_y_tile<MT>(a, y8, gs, prow0, lane, v[0]);
+    write_y_tile<MT>(a, y8, gs, prow0 + 16, lane, v[1]);
 }
 
-template <int MT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves<MT>()))) void q4_mm_kernel(MmTable tt) {
-    constexpr int XP = mm_xp<MT>();
+template <class F, int MT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves<MT>()))) void tiled_mm_kernel(MmTable tt) {
+    constexpr int kPre = MmFmt<F>::kPre;
+    constexpr int kLoads = MmFmt<F>::kLoads;
+    constexpr int XP = mm_xp<MT>() < kPre ? mm_xp<MT>() : kPre;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     u32x4* xb = reinterpret_cast<u32x4*>(lds);                                               // [2][2][MT][4][64]
     f32x2* smb = reinterpret_cast<f32x2*>(lds + mm_ring_bytes<MT>());    // [gps][64]
@@ -177,7 +192,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
     int ng = G - g0;
     ng = ng < gps ? ng : gps;                      // groups of this slice (>= 1 by construction)
     const int row0 = blk * kRows;
-    const uint32_t rowbytes = (uint32_t)a.K >> 1;
+    const uint32_t rowbytes = std::is_same<F, FmtBf16>::value ? (uint32_t)a.K * 2u : (uint32_t)a.K >> 1;
+    const float gs = std::is_same<F, FmtNvfp4>::value ? a.gscale : 1.0f;
     // the two halves of the slice: groups [0, h0) and [h0, ng)
     const int h0 = (ng + 1) >> 1;
     const int h1 = ng - h0;
@@ -202,17 +218,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         int nr = a.N - prow0;
         nr = __builtin_amdgcn_readfirstlane(nr < 0 ? 0 : (nr > 32 ? 32 : nr));
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)prow0 * rowbytes, (uint32_t)nr * rowbytes);
-        const uint32_t avoff = (uint32_t)(lane & 15) * rowbytes + ((uint32_t)(g0 + hb) << 6) + ((uint32_t)(lane >> 4) << 4);
-        auto aload = [&](int i, int t) {
-            return buf_load16(rw, avoff + (uint32_t)t * 16u * rowbytes + ((uint32_t)(i < hlast ? i : hlast) << 6), 0);
+        // lane l: row l % 16 of the tile, columns 32 (l / 16) .. + 32 of the
+        // group (16 * kLoads bytes: one load per k-step for BF16)
+        constexpr uint32_t kGroupBytes = 64u * kLoads;
+        const uint32_t avoff = (uint32_t)(lane & 15) * rowbytes + (uint32_t)(g0 + hb) * kGroupBytes + (uint32_t)(lane >> 4) * 16u * kLoads;
+        auto aload = [&](int i, int t, int j) {
+            return buf_load16(rw, avoff + (uint32_t)t * 16u * rowbytes + (uint32_t)(i < hlast ? i : hlast) * kGroupBytes + 16u * j, 0);
+        };
+        // NVFP4: the lane's two e4m3 scales (its 32 columns are two 16-column groups)
+        const uint32_t sbytes = (uint32_t)a.K >> 4;
+        const __amdgpu_buffer_rsrc_t rsc = make_rsrc(std::is_same<F, FmtNvfp4>::value ? a.scale8 + (size_t)prow0 * sbytes : nullptr,
+                                                     std::is_same<F, FmtNvfp4>::value ? (uint32_t)nr * sbytes : 0u);
+        const uint32_t svoff = (uint32_t)(lane & 15) * sbytes + (uint32_t)(g0 + hb) * 8u + (uint32_t)(lane >> 4) * 2u;
+        auto sload = [&](int i, int t) -> uint32_t {
+            if constexpr (std::is_same<F, FmtNvfp4>::value)
+                return buf_load2(rsc, svoff + (uint32_t)t * 16u * sbytes + (uint32_t)(i < hlast ? i : hlast) * 8u, 0);
+            else
+                return 0u;
         };
         // the loaders' first activation and group-parameter loads go out
         // before this workgroup's weight prefetch, so they do not queue
         // behind it
         lds_barrier();
-        u32x4 q[kPre][2];
+        u32x4 q[kPre][2][kLoads];
+        uint32_t sq[kPre][2];
 #pragma unroll
-        for (int u = 0; u < kPre; ++u) { q[u][0] = aload(u, 0); q[u][1] = aload(u, 1); }
+        for (int u = 0; u < kPre; ++u)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int j = 0; j < kLoads; ++j) q[u][t][j] = aload(u, t, j);
+                sq[u][t] = sload(u, t);
+            }
 
         f32x4 acc[2][MT];
 #pragma unroll
@@ -225,13 +262,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         auto step = [&](const int i, const int u) {
             const int slot = i & 1;
             const u32x4* xs = xb + (size_t)((slot * 2 + kh) * MT) * 4 * 64;
-            const u32x4 qa0 = q[u][0], qa1 = q[u][1];
-            q[u][0] = aload(i + kPre, 0);
-            q[u][1] = aload(i + kPre, 1);
-            const uint32_t qd[2][4] = {{qa0.x, qa0.y, qa0.z, qa0.w}, {qa1.x, qa1.y, qa1.z, qa1.w}};
-            // D = sum of (128 + code) * x and C = -128 * SX: an all -128 A
-            // operand against the same fragments leaves -128 * SX of batch row
-            // l % 16 in all four results of lane l
+            u32x4 qa[2][kLoads];
+            uint32_t sa[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int j = 0; j < kLoads; ++j) {
+                    qa[t][j] = q[u][t][j];
+                    q[u][t][j] = aload(i + kPre, t, j);
+                }
+                sa[t] = sq[u][t];
+                sq[u][t] = sload(i + kPre, t);
+            }
+            // the A operand of k-step s for row tile t
+            auto a_op = [&](int t, int s) -> bf16x8_t {
+                if constexpr (std::is_same<F, FmtBf16>::value) {
+                    return as_bf16x8(qa[t][s]);
+                } else {
+                    const uint32_t w = qa[t][0][s];
+                    uint32_t A[4];
+                    if constexpr (is_q4<F>()) {
+                        q4_pairs(w, A);   // 128 + code, in the (c0,c4) (c1,c5) ... pairing
+                    } else {
+                        // e2m1 * e4m3, natural column order; k-steps 0-1 and
+                        // 2-3 lie in the lane's first and second 16-column group
+                        const float sc = s < 2 ? e4m3_to_f32<0>(sa[t]) : e4m3_to_f32<1>(sa[t]);
+                        A[0] = nv_pair_scaled<0>(w, sc);
+                        A[1] = nv_pair_scaled<1>(w, sc);
+                        A[2] = nv_pair_scaled<2>(w, sc);
+                        A[3] = nv_pair_scaled<3>(w, sc);
+                    }
+                    return as_bf16x8(A[0], A[1], A[2], A[3]);
+                }
+            };
+            // int4: D = sum of (128 + code) * x and C = -128 * SX (an all -128
+            // A operand against the same fragments leaves -128 * SX of batch
+            // row l % 16 in all four results of lane l); otherwise D = sum of
+            // w * x over the group
             f32x4 cx[MT], D[2][MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) cx[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -244,32 +311,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                 u32x4 B[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) B[mt] = xs[(mt * 4 + s) * 64 + fs[s]];
+                if constexpr (is_q4<F>()) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) cx[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, as_bf16x8(B[mt]), cx[mt], 0, 0, 0);
+                    for (int mt = 0; mt < MT; ++mt) cx[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, as_bf16x8(B[mt]), cx[mt], 0, 0, 0);
+                }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    uint32_t A[4];
-                    q4_pairs(qd[t][s], A);
-                    const bf16x8_t Av = as_bf16x8(A[0], A[1], A[2], A[3]);
+                    const bf16x8_t Av = a_op(t, s);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, as_bf16x8(B[mt]), D[t][mt], 0, 0, 0);
                 }
             }
             if (i < hlen) {
-                // acc += scale * (D + C) + min * SX with min staged as -min / 128;
-                // D + C is the sum of code * x (exact when one product is nonzero)
+                if constexpr (is_q4<F>()) {
+                    // acc += scale * (D + C) + min * SX with min staged as -min / 128;
+                    // D + C is the sum of code * x (exact when one product is nonzero)
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + (hbase + i) * kRows + 32 * rp + 16 * t + 4 * (lane >> 4));
-                    const f32x4 sm01 = sm4[0], sm23 = sm4[1];
-                    const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
-                    const float mq[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4* sm4 = reinterpret_cast<const f32x4*>(smb + (hbase + i) * kRows + 32 * rp + 16 * t + 4 * (lane >> 4));
+                        const f32x4 sm01 = sm4[0], sm23 = sm4[1];
+                        const float sc[4] = {sm01.x, sm01.z, sm23.x, sm23.z};
+                        const float mq[4] = {sm01.y, sm01.w, sm23.y, sm23.w};
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
+                        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            acc[t][mt][v] = fmaf(mq[v], cx[mt][v], fmaf(sc[v], D[t][mt][v] + cx[mt][v], acc[t][mt][v]));
+                            for (int v = 0; v < 4; ++v)
+                                acc[t][mt][v] = fmaf(mq[v], cx[mt][v], fmaf(sc[v], D[t][mt][v] + cx[mt][v], acc[t][mt][v]));
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc[t][mt] += D[t][mt];
                 }
             }
             lds_barrier();
@@ -300,7 +374,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         // ------------------------------------------------------------ epilogue
         if (KS == 1) {
             __syncthreads();   // every wave meets the same barriers
-            if (kh == 0) write_y<MT>(a, tt.t[ti].y8 != 0, prow0, lane, acc);
+            if (kh == 0) write_y<MT>(a, tt.t[ti].y8 != 0, gs, prow0, lane, acc);
             return;
         }
         // split K: publish this slice's partial tile; the last slice to arrive
@@ -351,9 +425,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const u32x4 v = xr[mt * 4 + s];
-                    uint32_t pr[4];
-                    xq4_pairs(v.x, v.y, v.z, v.w, pr);
-                    frag[(mt * 4 + sp) * 64 + frag_slot(fl0 + 4 * s, sp)] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+                    u32x4 w = v;
+                    if constexpr (is_q4<F>()) {
+                        uint32_t pr[4];
+                        xq4_pairs(v.x, v.y, v.z, v.w, pr);
+                        w = u32x4{pr[0], pr[1], pr[2], pr[3]};
+                    }
+                    frag[(mt * 4 + sp) * 64 + frag_slot(fl0 + 4 * s, sp)] = w;
                 }
         };
         u32x4 xr[XP][4 * MT];
@@ -364,75 +442,80 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
 
         // group parameters of the block's rows for the slice, fp32 (scale, min)
         // [group][row], every load of a lane issued before the first is used
-        const int smw = tt.t[ti].smw;
-        if (smw != 0) {
-            // pieces of smw = 8 or 4 groups of one row (16 or 8 bytes): the
-            // host sets smw when K/128, the slice start and length are
-            // multiples of it and both arrays are aligned to the piece
-            int wg_rows = a.N - row0;
-            wg_rows = __builtin_amdgcn_readfirstlane(wg_rows > kRows ? kRows : wg_rows);
-            const uint32_t rb = (uint32_t)G * 2;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + (size_t)row0 * G, (uint32_t)wg_rows * rb);
-            const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)wg_rows * rb);
-            const int ppr = ng / smw;                 // pieces per row
-            constexpr int kMaxP = 4;                  // 64 rows x (56 groups / 8 or 16 groups / 4) / 128 threads
-            u32x4 ps[kMaxP], pm[kMaxP];
-#pragma unroll
-            for (int i = 0; i < kMaxP; ++i) {
-                const int c = lt + 64 * kLoaders * i;
-                const int r = c / ppr, pc = c - r * ppr;
-                const uint32_t off = (c < kRows * ppr) ? r * rb + (uint32_t)(g0 + smw * pc) * 2 : 0xFFFFFFF0u;
-                if (smw == 8) {
-                    ps[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-                    pm[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, off, 0, 0));
-                } else {
-                    const u32x2 s2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
-                    const u32x2 m2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, off, 0, 0));
-                    ps[i] = u32x4{s2.x, s2.y, 0u, 0u};
-                    pm[i] = u32x4{m2.x, m2.y, 0u, 0u};
-                }
-            }
-            lds_barrier();   // releases the compute waves' weight prefetch
-#pragma unroll
-            for (int i = 0; i < kMaxP; ++i) {
-                const int c = lt + 64 * kLoaders * i;
-                if (c < kRows * ppr) {
+        if constexpr (is_q4<F>()) {
+            const int smw = tt.t[ti].smw;
+            if (smw != 0) {
+                // pieces of smw = 8 or 4 groups of one row (16 or 8 bytes): the
+                // host sets smw when K/128, the slice start and length are
+                // multiples of it and both arrays are aligned to the piece
+                int wg_rows = a.N - row0;
+                wg_rows = __builtin_amdgcn_readfirstlane(wg_rows > kRows ? kRows : wg_rows);
+                const uint32_t rb = (uint32_t)G * 2;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + (size_t)row0 * G, (uint32_t)wg_rows * rb);
+                const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)wg_rows * rb);
+                const int ppr = ng / smw;                 // pieces per row
+                constexpr int kMaxP = 4;                  // 64 rows x (56 groups / 8 or 16 groups / 4) / 128 threads
+                u32x4 ps[kMaxP], pm[kMaxP];
+    #pragma unroll
+                for (int i = 0; i < kMaxP; ++i) {
+                    const int c = lt + 64 * kLoaders * i;
                     const int r = c / ppr, pc = c - r * ppr;
-                    const uint32_t sw[4] = {ps[i].x, ps[i].y, ps[i].z, ps[i].w};
-                    const uint32_t mw[4] = {pm[i].x, pm[i].y, pm[i].z, pm[i].w};
-#pragma unroll
-                    for (int h = 0; h < 8; ++h) {
-                        if (h >= smw) break;
-                        const uint16_t sh = (uint16_t)(sw[h >> 1] >> (16 * (h & 1)));
-                        const uint16_t mh = (uint16_t)(mw[h >> 1] >> (16 * (h & 1)));
-                        smb[(smw * pc + h) * kRows + r] = f32x2{f16_to_f32(sh), -0.0078125f * f16_to_f32(mh)};
+                    const uint32_t off = (c < kRows * ppr) ? r * rb + (uint32_t)(g0 + smw * pc) * 2 : 0xFFFFFFF0u;
+                    if (smw == 8) {
+                        ps[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                        pm[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, off, 0, 0));
+                    } else {
+                        const u32x2 s2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+                        const u32x2 m2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, off, 0, 0));
+                        ps[i] = u32x4{s2.x, s2.y, 0u, 0u};
+                        pm[i] = u32x4{m2.x, m2.y, 0u, 0u};
+                    }
+                }
+                lds_barrier();   // releases the compute waves' weight prefetch
+    #pragma unroll
+                for (int i = 0; i < kMaxP; ++i) {
+                    const int c = lt + 64 * kLoaders * i;
+                    if (c < kRows * ppr) {
+                        const int r = c / ppr, pc = c - r * ppr;
+                        const uint32_t sw[4] = {ps[i].x, ps[i].y, ps[i].z, ps[i].w};
+                        const uint32_t mw[4] = {pm[i].x, pm[i].y, pm[i].z, pm[i].w};
+    #pragma unroll
+                        for (int h = 0; h < 8; ++h) {
+                            if (h >= smw) break;
+                            const uint16_t sh = (uint16_t)(sw[h >> 1] >> (16 * (h & 1)));
+                            const uint16_t mh = (uint16_t)(mw[h >> 1] >> (16 * (h & 1)));
+                            smb[(smw * pc + h) * kRows + r] = f32x2{f16_to_f32(sh), -0.0078125f * f16_to_f32(mh)};
+                        }
+                    }
+                }
+            } else {
+                lds_barrier();   // releases the compute waves' weight prefetch
+                // single groups, in batches of 8 per lane
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale, (uint32_t)a.N * (uint32_t)G * 2u);
+                const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv, (uint32_t)a.N * (uint32_t)G * 2u);
+                for (int e0 = lt; e0 < kRows * ng; e0 += 8 * 64 * kLoaders) {
+                    uint16_t sv[8], mv[8];
+    #pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int e = e0 + 64 * kLoaders * k;
+                        const int r = e / ng, g = e - r * ng;
+                        const uint32_t off = e < kRows * ng ? ((uint32_t)(row0 + r) * (uint32_t)G + (uint32_t)(g0 + g)) * 2u : 0xFFFFFFF0u;
+                        sv[k] = buf_load2(rs, off, 0);
+                        mv[k] = buf_load2(rm, off, 0);
+                    }
+    #pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int e = e0 + 64 * kLoaders * k;
+                        if (e < kRows * ng) {
+                            const int r = e / ng, g = e - r * ng;
+                            smb[g * kRows + r] = f32x2{f16_to_f32(sv[k]), -0.0078125f * f16_to_f32(mv[k])};
+                        }
                     }
                 }
             }
+
         } else {
             lds_barrier();   // releases the compute waves' weight prefetch
-            // single groups, in batches of 8 per lane
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale, (uint32_t)a.N * (uint32_t)G * 2u);
-            const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv, (uint32_t)a.N * (uint32_t)G * 2u);
-            for (int e0 = lt; e0 < kRows * ng; e0 += 8 * 64 * kLoaders) {
-                uint16_t sv[8], mv[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int e = e0 + 64 * kLoaders * k;
-                    const int r = e / ng, g = e - r * ng;
-                    const uint32_t off = e < kRows * ng ? ((uint32_t)(row0 + r) * (uint32_t)G + (uint32_t)(g0 + g)) * 2u : 0xFFFFFFF0u;
-                    sv[k] = buf_load2(rs, off, 0);
-                    mv[k] = buf_load2(rm, off, 0);
-                }
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int e = e0 + 64 * kLoaders * k;
-                    if (e < kRows * ng) {
-                        const int r = e / ng, g = e - r * ng;
-                        smb[g * kRows + r] = f32x2{f16_to_f32(sv[k]), -0.0078125f * f16_to_f32(mv[k])};
-                    }
-                }
-            }
         }
 
         stage(0, xr[0]);
@@ -495,7 +578,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                     for (int mt = 0; mt < MT; ++mt) sum[mt] += __builtin_bit_cast(f32x4, pv[k][mt]);
                 }
         }
-        write_y_tile<MT>(a, tt.t[ti].y8 != 0, row0 + 32 * rp + 16 * t, lane, sum);
+        write_y_tile<MT>(a, tt.t[ti].y8 != 0, gs, row0 + 32 * rp + 16 * t, lane, sum);
     }
     if (tid == 0) __hip_atomic_store(&cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -519,7 +602,7 @@ inline int slice_groups(int G, int k) {
 // per CU in all; kCUs when no task stays unsplit), the largest slice as short
 // as the slots allow: every CU then streams about the same weight bytes.
 // whole[i] says which tasks stayed unsplit by this rule.
-template <int MT>
+template <class F, int MT>
 void mm_plan(const GemvArgs* tasks, int count, bool can_split, int* ks, int* gps, bool* whole) {
     int blocks[kMaxTasks], btot = 0;
     for (int i = 0; i < count; ++i) {
@@ -569,7 +652,7 @@ void mm_plan(const GemvArgs* tasks, int count, bool can_split, int* ks, int* gps
         }
     }
     // every slice's group parameters fit LDS
-    const int gmax = (mm_max_gps<MT>() / 4) * 4;
+    const int gmax = (mm_max_gps<F, MT>() / 4) * 4;
     for (int i = 0; i < count; ++i)
         if (gps[i] > gmax) {
             const int G = tasks[i].K >> 7;
@@ -581,11 +664,11 @@ void mm_plan(const GemvArgs* tasks, int count, bool can_split, int* ks, int* gps
 // Workspace a launch needs: 0 when no task is split, or when the counters of
 // the split tasks would not fit the counter region (the launch then runs
 // unsplit).
-template <int MT>
+template <class F, int MT>
 size_t ws_bytes_mt(const GemvArgs* tasks, int count) {
     int ks[kMaxTasks], gps[kMaxTasks];
     bool whole[kMaxTasks];
-    mm_plan<MT>(tasks, count, true, ks, gps, whole);
+    mm_plan<F, MT>(tasks, count, true, ks, gps, whole);
     size_t cnt = 0, part = 0;
     for (int i = 0; i < count; ++i) {
         if (ks[i] <= 1) continue;
@@ -596,13 +679,13 @@ size_t ws_bytes_mt(const GemvArgs* tasks, int count) {
     return (part > 0 && cnt <= kCntBytes) ? kCntBytes + part : 0;
 }
 
-template <int MT>
+template <class F, int MT>
 hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t st) {
     int ks[kMaxTasks], gps[kMaxTasks];
-    const size_t need = ws_bytes_mt<MT>(tasks, count);
+    const size_t need = ws_bytes_mt<F, MT>(tasks, count);
     const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
     bool whole[kMaxTasks];
-    mm_plan<MT>(tasks, count, split, ks, gps, whole);
+    mm_plan<F, MT>(tasks, count, split, ks, gps, whole);
     // unsplit tasks take the first workgroups, so that the dispatcher spreads
     // their blocks one per CU before the slices fill the second slots
     int order[kMaxTasks], n = 0;
@@ -624,7 +707,9 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         tt.t[j].gps = gps[i];
         const int G = tasks[i].K >> 7;
         const uintptr_t sa = reinterpret_cast<uintptr_t>(tasks[i].scale), ma = reinterpret_cast<uintptr_t>(tasks[i].minv);
-        if (G % 8 == 0 && gps[i] % 8 == 0 && gps[i] <= 64 && sa % 16 == 0 && ma % 16 == 0)
+        if (!is_q4<F>())
+            tt.t[j].smw = 0;
+        else if (G % 8 == 0 && gps[i] % 8 == 0 && gps[i] <= 64 && sa % 16 == 0 && ma % 16 == 0)
             tt.t[j].smw = 8;
         else if (G % 4 == 0 && gps[i] % 4 == 0 && gps[i] <= 32 && sa % 8 == 0 && ma % 8 == 0)
             tt.t[j].smw = 4;
@@ -640,41 +725,68 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         grid += blocks * ks[i];
         gmax = gps[i] > gmax ? gps[i] : gmax;
     }
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q4_mm_kernel<MT>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(tiled_mm_kernel<F, MT>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
     if (attr != hipSuccess) return attr;
-    return launch_kernel(q4_mm_kernel<MT>, dim3(grid), dim3(kThreads), (size_t)mm_shmem<MT>(gmax), st, tt);
+    return launch_kernel(tiled_mm_kernel<F, MT>, dim3(grid), dim3(kThreads), (size_t)mm_shmem<F, MT>(gmax), st, tt);
 }
 
 }  // namespace
 
-bool mm_supported(int M, int K, bool split) {
+template <class F>
+bool mm_supported_f(int M, int K, bool split) {
     if (M < 1 || M > 64 || K % 128) return false;
     if (split) return true;
     const int G = K >> 7;
     switch ((M + 15) / 16) {
-        case 1: return G <= mm_max_gps<1>();
-        case 2: return G <= mm_max_gps<2>();
-        case 3: return G <= mm_max_gps<3>();
-        default: return G <= mm_max_gps<4>();
+        case 1: return G <= mm_max_gps<F, 1>();
+        case 2: return G <= mm_max_gps<F, 2>();
+        case 3: return G <= mm_max_gps<F, 3>();
+        default: return G <= mm_max_gps<F, 4>();
     }
 }
 
-size_t mm_workspace_bytes(const GemvArgs* tasks, int count) {
+template <class F>
+size_t mm_workspace_bytes_f(const GemvArgs* tasks, int count) {
     switch ((tasks[0].M + 15) / 16) {
-        case 1: return ws_bytes_mt<1>(tasks, count);
-        case 2: return ws_bytes_mt<2>(tasks, count);
-        case 3: return ws_bytes_mt<3>(tasks, count);
-        default: return ws_bytes_mt<4>(tasks, count);
+        case 1: return ws_bytes_mt<F, 1>(tasks, count);
+        case 2: return ws_bytes_mt<F, 2>(tasks, count);
+        case 3: return ws_bytes_mt<F, 3>(tasks, count);
+        default: return ws_bytes_mt<F, 4>(tasks, count);
     }
 }
 
-hipError_t launch_mm(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
+template <class F>
+hipError_t launch_mm_f(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
     switch ((tasks[0].M + 15) / 16) {
-        case 1: return launch_mm_mt<1>(tasks, count, ws, ws_bytes, s);
-        case 2: return launch_mm_mt<2>(tasks, count, ws, ws_bytes, s);
-        case 3: return launch_mm_mt<3>(tasks, count, ws, ws_bytes, s);
-        default: return launch_mm_mt<4>(tasks, count, ws, ws_bytes, s);
+        case 1: return launch_mm_mt<F, 1>(tasks, count, ws, ws_bytes, s);
+        case 2: return launch_mm_mt<F, 2>(tasks, count, ws, ws_bytes, s);
+        case 3: return launch_mm_mt<F, 3>(tasks, count, ws, ws_bytes, s);
+        default: return launch_mm_mt<F, 4>(tasks, count, ws, ws_bytes, s);
+    }
+}
+
+bool mm_supported(Fmt fmt, int M, int K, bool split) {
+    switch (fmt) {
+        case kFmtQ4: return mm_supported_f<FmtQ4>(M, K, split);
+        case kFmtNvfp4: return mm_supported_f<FmtNvfp4>(M, K, split);
+        default: return mm_supported_f<FmtBf16>(M, K, split);
+    }
+}
+
+size_t mm_workspace_bytes(Fmt fmt, const GemvArgs* tasks, int count) {
+    switch (fmt) {
+        case kFmtQ4: return mm_workspace_bytes_f<FmtQ4>(tasks, count);
+        case kFmtNvfp4: return mm_workspace_bytes_f<FmtNvfp4>(tasks, count);
+        default: return mm_workspace_bytes_f<FmtBf16>(tasks, count);
+    }
+}
+
+hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
+    switch (fmt) {
+        case kFmtQ4: return launch_mm_f<FmtQ4>(tasks, count, ws, ws_bytes, s);
+        case kFmtNvfp4: return launch_mm_f<FmtNvfp4>(tasks, count, ws, ws_bytes, s);
+        default: return launch_mm_f<FmtBf16>(tasks, count, ws, ws_bytes, s);
     }
 }
 

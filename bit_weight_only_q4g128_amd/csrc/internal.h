@@ -50,14 +50,15 @@ constexpr int kStreamMaxShmem = 64 * 1024;
 hipError_t launch_stream(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
 bool stream_supported(Fmt fmt, int M, int K);
 
-// int4 g128 matrix-core GEMV with staged activations (M <= 64), up to
-// kMaxTasks GEMVs per launch.  With a workspace of at least
-// mm_workspace_bytes() bytes (zero-filled before first use; its counters are
-// left at zero, the rest is scratch), K may be split over workgroups; without
-// one every task runs unsplit, which mm_supported(M, K, false) must allow.
-bool mm_supported(int M, int K, bool split);
-size_t mm_workspace_bytes(const GemvArgs* tasks, int count);
-hipError_t launch_mm(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
+// Tiled matrix-core GEMV with staged activations (M <= 64, K % 128 == 0) for
+// the three weight formats, up to kMaxTasks GEMVs of one format per launch.
+// With a workspace of at least mm_workspace_bytes() bytes (zero-filled before
+// first use; its counters are left at zero, the rest is scratch), K may be
+// split over workgroups; without one every task runs unsplit, which
+// mm_supported(fmt, M, K, false) must allow.
+bool mm_supported(Fmt fmt, int M, int K, bool split);
+size_t mm_workspace_bytes(Fmt fmt, const GemvArgs* tasks, int count);
+hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
 
 // 16x16x32 BF16 matrix-core GEMV (any M <= 64), one launch per task.
 hipError_t launch_mfma(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);

@@ -51,9 +51,9 @@ extern "C" {
 #define Q4_VARIANT_AUTO 0 /* pick by (M, N, K) */
 #define Q4_VARIANT_DOT2 1 /* wave-per-row packed-BF16 dot products; batch tiles of <= 8 rows */
 #define Q4_VARIANT_MFMA 2 /* 16x16x32 BF16 matrix-core tiles, batch padded to 16 */
-#define Q4_VARIANT_TILED 4  /* int4 only, 5 <= M <= 64: 64-row workgroups, matrix cores, activations staged
-                               in LDS per 128-column group; split over K when given a workspace
-                               (q4g128_gemv_grouped_ws) */
+#define Q4_VARIANT_TILED 4  /* K % 128 == 0: 64-row workgroups, matrix cores, activations staged in LDS
+                               per 128-column group; split over K when given a workspace
+                               (the *_grouped_ws calls); the default for M >= 5 */
 #define Q4_VARIANT_STREAM 3 /* M <= 4, rows of exactly 1, 2 or 4 KB (int4/NVFP4 K = 2048, 4096, 8192;
                                BF16 K = 512, 1024, 2048): every weight load issued at once, activations
                                and group parameters shared through LDS */
@@ -144,6 +144,29 @@ int nvfp4g16_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweigh
                           int N, uint16_t* y, int variant, void* stream);
 
 /*
+ * Up to 8 independent NVFP4 GEMVs of one batch size M in one launch (the
+ * NVFP4 q, k, gate, up projections of a decode layer read the same input;
+ * Rumik TTS Fast Inference post, section "What Made It Faster": packing
+ * projections that share an input).  Each task is validated as
+ * nvfp4g16_gemv; outputs must not overlap any task's inputs or each other.
+ * workspace / workspace_bytes: as for q4g128_gemv_grouped_ws (NULL / 0: no K
+ * split); nvfp4g16_workspace_bytes gives the size (0 if no split is planned).
+ */
+typedef struct nvfp4g16_task {
+    const uint16_t* x;          /* bf16 [M, K] */
+    const uint8_t* qweight;     /* uint8 [N, K/2] E2M1 */
+    const uint8_t* scale_e4m3;  /* uint8 [N, K/16] */
+    float global_scale;         /* multiplier G */
+    uint16_t* y;                /* bf16 [M, N] */
+    int N;
+    int K;
+} nvfp4g16_task;
+
+int nvfp4g16_gemv_grouped_ws(const nvfp4g16_task* tasks, int count, int M, int variant, void* workspace,
+                             size_t workspace_bytes, void* stream);
+int nvfp4g16_workspace_bytes(const nvfp4g16_task* tasks, int count, int M, size_t* bytes);
+
+/*
  * Dense BF16 weights (the audio head head.audio_weight [16385, 2048] of the
  * rumik-oss-1-int4 card, section "Format"; its 2049-row codebook slice from
  * the Rumik TTS Fast Inference post, section "What Made It Faster"; and the
@@ -152,6 +175,23 @@ int nvfp4g16_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweigh
  */
 int bf16_gemv(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* y, void* stream);
 int bf16_gemv_variant(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* y, int variant, void* stream);
+
+/*
+ * Up to 8 independent BF16 GEMVs of one batch size M in one launch, validated
+ * as bf16_gemv; workspace as for q4g128_gemv_grouped_ws, sized by
+ * bf16_workspace_bytes (0 if no split is planned).
+ */
+typedef struct bf16_task {
+    const uint16_t* x;  /* bf16 [M, K] */
+    const uint16_t* w;  /* bf16 [N, K] */
+    uint16_t* y;        /* bf16 [M, N] */
+    int N;
+    int K;
+} bf16_task;
+
+int bf16_gemv_grouped_ws(const bf16_task* tasks, int count, int M, int variant, void* workspace, size_t workspace_bytes,
+                         void* stream);
+int bf16_workspace_bytes(const bf16_task* tasks, int count, int M, size_t* bytes);
 
 /*
  * Diagnostic dequantization of a whole matrix to fp32 w [N, K] (16-byte

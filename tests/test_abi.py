@@ -105,7 +105,11 @@ def test_variant_names():
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 16384) == "mfma"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_MFMA, 1, 2048, 2048) == "mfma"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_DOT2, 3, 16385, 2048) == "dot2"
-    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2048) == "mfma"
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2080) == "mfma"   # K % 128 != 0
+    assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 48, 16385, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 48, 16385, 2056) == "mfma"
+    assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_TILED, 48, 16385, 2056) == "invalid"
     assert q4.variant_name(7, 0, 1, 1, 128) == "invalid"
     assert q4.variant_name(0, 0, 0, 1, 128) == "invalid"
 
@@ -150,6 +154,45 @@ def test_grouped_validation():
     # two tasks share an output
     same = (T * 2)(task(0), task(1, y=A + (4 << 24)))
     assert lib.q4g128_gemv_grouped(same, 2, 1, 0, None) == EALIAS
+
+
+def test_grouped_nvfp4_bf16_validation():
+    import ctypes
+    NT, BT = q4.NvTask, q4.BfTask
+    def nv(i, **kw):
+        b = A + (i << 29)
+        base = dict(x=b, qweight=b + (1 << 26), scale_e4m3=b + (2 << 26), global_scale=1.0, y=b + (4 << 26), N=2048, K=2048)
+        base.update(kw)
+        return NT(**base)
+    def bf(i, **kw):
+        b = A + (i << 29)
+        base = dict(x=b, w=b + (1 << 26), y=b + (4 << 26), N=2048, K=2048)
+        base.update(kw)
+        return BT(**base)
+    for fn, mk, T in ((lib.nvfp4g16_gemv_grouped_ws, nv, NT), (lib.bf16_gemv_grouped_ws, bf, BT)):
+        arr = (T * 2)(mk(0), mk(1))
+        assert fn(None, 1, 1, 0, None, 0, None) == EPTR
+        assert fn(arr, 0, 1, 0, None, 0, None) == ESHAPE
+        assert fn(arr, 9, 1, 0, None, 0, None) == ESHAPE
+        assert fn(arr, 2, 65, 0, None, 0, None) == ESHAPE
+        assert fn(arr, 2, 1, 7, None, 0, None) == EVARIANT
+        assert fn(arr, 2, 48, 4, A + 8, 4096, None) == EALIGN
+        assert fn((T * 2)(mk(0), mk(1, x=None)), 2, 1, 0, None, 0, None) == EPTR
+        same = (T * 2)(mk(0), mk(1, y=A + (4 << 26)))
+        assert fn(same, 2, 1, 0, None, 0, None) == EALIAS
+        over = (T * 2)(mk(0), mk(1, y=A + (1 << 26) + 64))   # task 1 writes over task 0's weights
+        assert fn(over, 2, 1, 0, None, 0, None) == EALIAS
+    assert lib.nvfp4g16_gemv_grouped_ws((NT * 1)(nv(0, K=48)), 1, 1, 0, None, 0, None) == ESHAPE
+    assert lib.nvfp4g16_gemv_grouped_ws((NT * 1)(nv(0, qweight=A + (1 << 26) + 8)), 1, 1, 0, None, 0, None) == EALIGN
+    assert lib.bf16_gemv_grouped_ws((BT * 1)(bf(0, K=12)), 1, 1, 0, None, 0, None) == ESHAPE
+    # the tiled kernel needs K % 128 == 0
+    assert lib.bf16_gemv_grouped_ws((BT * 1)(bf(0, K=2056)), 1, 48, 4, None, 0, None) == EVARIANT
+    nb = ctypes.c_size_t(123)
+    for fnb, mk, T in ((lib.nvfp4g16_workspace_bytes, nv, NT), (lib.bf16_workspace_bytes, bf, BT)):
+        arr = (T * 2)(mk(0), mk(1))
+        assert fnb(arr, 2, 48, None) == EPTR
+        assert fnb(arr, 2, 1, ctypes.byref(nb)) == OK and nb.value == 0     # M = 1 never splits
+        assert fnb(arr, 2, 48, ctypes.byref(nb)) == OK and nb.value > 0     # 64 row blocks: K is split
 
 
 def test_stream_read_validation():

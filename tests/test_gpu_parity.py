@@ -91,7 +91,7 @@ def test_q4_onehot_bitwise(q4, variant, M):
     assert np.array_equal(got, exp), (VNAME[variant], M, np.argwhere(got != exp)[:4])
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS + [4])
 @pytest.mark.parametrize("M", [1, 4, 17, 48])
 def test_nvfp4_onehot_bitwise(q4, variant, M):
     N, K = 150, 512
@@ -108,8 +108,8 @@ def test_nvfp4_onehot_bitwise(q4, variant, M):
     assert np.array_equal(gotv, expv), (VNAME[variant], M)
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
-@pytest.mark.parametrize("M", [1, 5, 32])
+@pytest.mark.parametrize("variant", VARIANTS + [4])
+@pytest.mark.parametrize("M", [1, 5, 32, 64])
 def test_bf16_onehot_bitwise(q4, variant, M):
     N, K = 77, 256
     w = synth.bf16_matrix(N, K, ("onehot-bf", M))
@@ -482,6 +482,78 @@ def test_q4_split_k_mixed_tasks_onehot_and_random(q4, M):
         for _ in range(3):
             again = q4.q4g128_gemv_grouped(items, variant=4, workspace=ws)
             assert all(torch.equal(a, b) for a, b in zip(again, outs))
+
+
+def _nv_mats(shapes, tag):
+    mats = [synth.nvfp4_matrix(N, K, (tag, N, K)) for N, K in shapes]
+    return mats, [oracle.nvfp4g16_dequant_f32(m[0].numpy(), m[1].numpy(), m[2]) for m in mats]
+
+
+def _bf_mats(shapes, tag):
+    mats = [synth.bf16_matrix(N, K, (tag, N, K)) for N, K in shapes]
+    return mats, [oracle.bf16_dequant_f32(synth.bits16(w)) for w in mats]
+
+
+@pytest.mark.parametrize("fmt", ["nv", "bf"])
+@pytest.mark.parametrize("M", [5, 20, 48, 64])
+def test_nvfp4_bf16_grouped_split_k_onehot_and_random(q4, fmt, M):
+    # the tiled kernel for NVFP4 and BF16 weights through the grouped calls:
+    # with a workspace the launch splits K; ragged N (rows past N in the last
+    # block), one-hot activations exact, random ones within tolerance, and
+    # repeats bitwise on the reused workspace
+    shapes = [(70, 512), (200, 1152), (130, 2048), (64, 4096), (33, 8192)]
+    mats, w32s = (_nv_mats if fmt == "nv" else _bf_mats)(shapes, "g" + fmt)
+    grouped = q4.nvfp4g16_gemv_grouped if fmt == "nv" else q4.bf16_gemv_grouped
+    wsbytes = q4.nvfp4g16_workspace_bytes if fmt == "nv" else q4.bf16_workspace_bytes
+    for kind in ("onehot", "random"):
+        xs, kss = [], []
+        for i, (N, K) in enumerate(shapes):
+            if kind == "onehot":
+                ks = _onehot_ks(K, M, 1300 + 7 * i + M)
+                kss.append(ks)
+                xs.append(gpu(onehot_x(K, ks)))
+            else:
+                xs.append(gpu(synth.x_bf16(M, K, ("g-x", fmt, K, M))))
+        if fmt == "nv":
+            items = [(x, gpu(m[0]), gpu(m[1]), m[2], None) for x, m in zip(xs, mats)]
+        else:
+            items = [(x, gpu(m), None) for x, m in zip(xs, mats)]
+        nbytes = wsbytes(items)
+        assert nbytes > 0
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        outs = grouped(items, variant=4, workspace=ws)
+        unsplit = grouped(items, variant=4)
+        for i, ((N, K), w32, x, y, y1) in enumerate(zip(shapes, w32s, xs, outs, unsplit)):
+            if kind == "onehot":
+                exp = torch.from_numpy(rn_bf16_bits(w32[:, kss[i]].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+                for got in (y.cpu().float().numpy(), y1.cpu().float().numpy()):
+                    assert np.array_equal(got, exp), (fmt, N, K, M, np.argwhere(got != exp)[:4])
+            else:
+                xb = x_bits(x.cpu())
+                ref = oracle.gemv_f64(xb, w32)
+                check_gemv(y, ref, w32, xb, f"{fmt} grouped split N={N} K={K} M={M}")
+                check_gemv(y1, ref, w32, xb, f"{fmt} grouped unsplit N={N} K={K} M={M}")
+        for _ in range(3):
+            again = grouped(items, variant=4, workspace=ws)
+            assert all(torch.equal(a, b) for a, b in zip(again, outs))
+
+
+@pytest.mark.parametrize("fmt", ["nv", "bf"])
+@pytest.mark.parametrize("M", [1, 3, 48])
+def test_nvfp4_bf16_grouped_equals_single_calls(q4, fmt, M):
+    # the automatic choice for a group (streaming kernel at M <= 4, tiled
+    # kernel above) against one call per task with the same kernel
+    shapes = [(512, 2048), (2048, 2048), (2049, 2048)]
+    mats, _ = (_nv_mats if fmt == "nv" else _bf_mats)(shapes, "ge" + fmt)
+    x = gpu(synth.x_bf16(M, 2048, ("ge-x", fmt, M)))
+    if fmt == "nv":
+        outs = q4.nvfp4g16_gemv_grouped([(x, gpu(m[0]), gpu(m[1]), m[2], None) for m in mats])
+        singles = [q4.nvfp4g16_gemv(x, gpu(m[0]), gpu(m[1]), m[2]) for m in mats]
+    else:
+        outs = q4.bf16_gemv_grouped([(x, gpu(m), None) for m in mats])
+        singles = [q4.bf16_gemv(x, gpu(m)) for m in mats]
+    for a, b in zip(outs, singles):
+        assert torch.equal(a, b)
 
 
 def test_q4_grouped_mixed_k(q4):
