@@ -140,8 +140,10 @@ def nvfp4_wbytes(N, K):
 class Nvfp4Workload:
     """The same decode step with NVFP4 weights: q, k, o, gate, up NVFP4 (E2M1
     codes, e4m3 scales per 16 columns, one fp32 global scale) and v, down BF16,
-    as the VoxCPM2-NVFP4 card quantizes them; then the same BF16 head.  One
-    launch per projection (there is no grouped NVFP4 call)."""
+    as the VoxCPM2-NVFP4 card quantizes them; then the same BF16 head.  plain:
+    one launch per projection; grouped: per layer the NVFP4 q, k, gate, up in
+    one launch, the BF16 v, the NVFP4 o and the BF16 down in one launch each
+    (a launch carries one weight format), then the head."""
 
     def __init__(self, q4, synth, torch, int4_wl):
         self.q4, self.torch = q4, torch
@@ -161,14 +163,45 @@ class Nvfp4Workload:
         self.bf16_proj = synth.NVFP4_BF16_PROJ
         self.int4 = int4_wl
         self.shapes, self.order = synth.LAYER_SHAPES, synth.LAYER_ORDER
+        self.ws = {}
 
     def weight_bytes_of(self, p):
         N, K = self.shapes[p]
         return N * K * 2 if p in self.bf16_proj else nvfp4_wbytes(N, K)
 
+    def workspace(self, M, need):
+        """One split-K workspace per batch size, shared by the step's grouped
+        calls of both formats (they run in stream order)."""
+        if need == 0:
+            return None
+        ws = self.ws.get(M)
+        if ws is None or ws.numel() < need:
+            ws = self.torch.zeros(need, dtype=self.torch.uint8, device="cuda")
+            self.ws[M] = ws
+        return ws
+
     def launches(self, M, mode="plain"):
         xs, ys, xin, yh = self.int4.buffers(M)
         q4, out = self.q4, []
+        if mode == "grouped":
+            # size the shared workspace for the largest call first
+            plan = []
+            for lay in self.layers:
+                for stage in (("q", "k", "gate", "up"), ("v",), ("o",), ("down",)):
+                    if stage[0] in self.bf16_proj:
+                        items = [(xs[p], lay[p], ys[p]) for p in stage]
+                        plan.append((q4.bf16_gemv_grouped, items, q4.bf16_workspace_bytes(items), stage))
+                    else:
+                        items = [(xs[p], *lay[p], ys[p]) for p in stage]
+                        plan.append((q4.nvfp4g16_gemv_grouped, items, q4.nvfp4g16_workspace_bytes(items), stage))
+            ws = self.workspace(M, max(n for _, _, n, _ in plan))
+            for fn, items, n, stage in plan:
+                wb = sum(self.weight_bytes_of(p) for p in stage)
+                out.append((lambda fn=fn, items=items, w=(ws if n else None): fn(items, workspace=w), wb,
+                            stage[0] not in self.bf16_proj))
+            head = self.int4.head
+            out.append((lambda: q4.bf16_gemv(xin, head, out=yh), self.int4.head_rows * 2048 * 2, False))
+            return out
         for lay in self.layers:
             for p in self.order:
                 if p in self.bf16_proj:
@@ -452,7 +485,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
     ap.add_argument("--counters-m", type=int, choices=(1, 48), default=1, help="batch size of the --counters workload")
-    ap.add_argument("--modes", default="M1_grouped,M1_plain,M48_grouped,M48_plain,NVFP4_M1_plain,NVFP4_M48_plain",
+    ap.add_argument("--modes", default="M1_grouped,M1_plain,M48_grouped,M48_plain,NVFP4_M1_grouped,NVFP4_M48_grouped,"
+                                       "NVFP4_M1_plain,NVFP4_M48_plain",
                     help="comma list of timed modes; M1_grouped is always timed (it is the headline value)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -485,17 +519,19 @@ def main():
             del g
     nv = None
     for M in (1, 48):
-        if f"NVFP4_M{M}_plain" not in modes:
-            continue
-        if nv is None:
-            nv = Nvfp4Workload(q4, synth, torch, wl)
-        ms, g = time_graph(torch, nv, M, args.steps, args.warmup, "plain")
-        by = nv.step_bytes(M)
-        res[(f"NVFP4_M{M}", "plain")] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(nv.launches(M)),
-                                             wbytes=sum(b for _, b, _ in nv.launches(M)))
-        log(f"bench: NVFP4 M={M} plain step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(f'NVFP4_M{M}', 'plain')]['gbs']:6.0f} GB/s, "
-            f"{1e3 / ms:6.0f} steps/s")
-        del g
+        for mode in ("grouped", "plain"):
+            if f"NVFP4_M{M}_{mode}" not in modes:
+                continue
+            if nv is None:
+                nv = Nvfp4Workload(q4, synth, torch, wl)
+            ms, g = time_graph(torch, nv, M, args.steps, args.warmup, mode)
+            by = nv.step_bytes(M)
+            calls = nv.launches(M, mode)
+            r = res[(f"NVFP4_M{M}", mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(calls),
+                                                  wbytes=sum(b for _, b, _ in calls))
+            log(f"bench: NVFP4 M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {r['gbs']:6.0f} GB/s, "
+                f"{1e3 / ms:6.0f} steps/s, {r['launches']} launches")
+            del g
     roof = {}
     for M in (1, 48):
         if M != 1 and f"M{M}_grouped" not in modes:

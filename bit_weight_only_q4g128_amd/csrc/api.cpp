@@ -44,15 +44,19 @@ bool variant_ok(int variant) {
 // the streaming kernel, other small batches to the packed-dot kernel; larger
 // batches to the tiled matrix-core kernel where K allows it (K % 128 == 0 and
 // the int4 group parameters fit LDS, or a split), else to the per-task
-// matrix-core kernel.  `split`: a workspace allows K splits.
-int pick(Fmt fmt, int variant, int M, int K, bool split = false) {
+// matrix-core kernel.  `split`: a workspace allows K splits.  Without one,
+// NVFP4 and BF16 matrices take the tiled kernel only when their 64-row blocks
+// alone fill the GPU (N >= 16384): with fewer rows the per-task kernel, which
+// splits K inside its workgroups, is faster for these formats (measured).
+constexpr int kTiledRowsAlone = 64 * 256;
+int pick(Fmt fmt, int variant, int M, int N, int K, bool split = false) {
     if (variant == Q4_VARIANT_DOT2) return q4::dot2_supported(fmt, K) ? Q4_VARIANT_DOT2 : -1;
     if (variant == Q4_VARIANT_MFMA) return Q4_VARIANT_MFMA;
     if (variant == Q4_VARIANT_STREAM) return q4::stream_supported(fmt, M, K) ? Q4_VARIANT_STREAM : -1;
     if (variant == Q4_VARIANT_TILED) return q4::mm_supported(fmt, M, K, split) ? Q4_VARIANT_TILED : -1;
     if (M <= 4 && q4::stream_supported(fmt, M, K)) return Q4_VARIANT_STREAM;
     if (M <= 4 && q4::dot2_supported(fmt, K)) return Q4_VARIANT_DOT2;
-    if (q4::mm_supported(fmt, M, K, split)) return Q4_VARIANT_TILED;
+    if (q4::mm_supported(fmt, M, K, split) && (fmt == q4::kFmtQ4 || split || N >= kTiledRowsAlone)) return Q4_VARIANT_TILED;
     return Q4_VARIANT_MFMA;
 }
 
@@ -131,7 +135,7 @@ int plan_checked(Fmt fmt, const GemvArgs* a, const Range (*in)[4], const Range* 
                  int* chosen_out) {
     int n_big = 0, n_tiled = 0, n_stream = 0;
     for (int i = 0; i < count; ++i) {
-        const int c = pick(fmt, variant, M, a[i].K, split);
+        const int c = pick(fmt, variant, M, a[i].N, a[i].K, split);
         if (c < 0) return Q4_EVARIANT;
         n_big += c == Q4_VARIANT_MFMA || c == Q4_VARIANT_TILED;
         n_tiled += c == Q4_VARIANT_TILED;
@@ -196,7 +200,7 @@ int q4g128_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweight,
     if (!variant_ok(variant)) return Q4_EVARIANT;
     for (const Range& r : in)
         if (overlaps(out, r)) return Q4_EALIAS;
-    const int chosen = pick(q4::kFmtQ4, variant, M, K);
+    const int chosen = pick(q4::kFmtQ4, variant, M, N, K);
     if (chosen < 0) return Q4_EVARIANT;
     return run(q4::kFmtQ4, chosen, a, stream);
 }
@@ -257,7 +261,7 @@ int nvfp4g16_gemv_variant(const uint16_t* x, int M, int K, const uint8_t* qweigh
     if (overlaps(yr, range_of(x, (size_t)M * K * 2)) || overlaps(yr, range_of(qweight, (size_t)N * K / 2)) ||
         overlaps(yr, range_of(scale_e4m3, (size_t)N * K / 16)))
         return Q4_EALIAS;
-    const int chosen = pick(q4::kFmtNvfp4, variant, M, K);
+    const int chosen = pick(q4::kFmtNvfp4, variant, M, N, K);
     if (chosen < 0) return Q4_EVARIANT;
     GemvArgs a{};
     a.x = x; a.w = qweight; a.scale8 = scale_e4m3; a.gscale = global_scale; a.y = y; a.M = M; a.N = N; a.K = K;
@@ -278,7 +282,7 @@ int bf16_gemv_variant(const uint16_t* x, int M, int K, const uint16_t* w, int N,
     if (!variant_ok(variant)) return Q4_EVARIANT;
     const Range yr = range_of(y, (size_t)M * N * 2);
     if (overlaps(yr, range_of(x, (size_t)M * K * 2)) || overlaps(yr, range_of(w, (size_t)N * K * 2))) return Q4_EALIAS;
-    const int chosen = pick(q4::kFmtBf16, variant, M, K);
+    const int chosen = pick(q4::kFmtBf16, variant, M, N, K);
     if (chosen < 0) return Q4_EVARIANT;
     GemvArgs a{};
     a.x = x; a.w = reinterpret_cast<const uint8_t*>(w); a.y = y; a.M = M; a.N = N; a.K = K;
@@ -407,9 +411,8 @@ int q4gemv_stream_read(const void* const* bufs, const size_t* bytes, int count, 
 }
 
 const char* q4gemv_variant_name(int fmt, int variant, int M, int N, int K) {
-    (void)N;
     if (fmt < Q4_FMT_Q4G128 || fmt > Q4_FMT_BF16 || !variant_ok(variant) || M < 1 || M > kMaxM || K < 1) return "invalid";
-    const int c = pick(static_cast<Fmt>(fmt), variant, M, K);
+    const int c = pick(static_cast<Fmt>(fmt), variant, M, N, K);
     if (c == Q4_VARIANT_DOT2) return "dot2";
     if (c == Q4_VARIANT_MFMA) return "mfma";
     if (c == Q4_VARIANT_STREAM) return "stream";

@@ -105,7 +105,9 @@ def test_variant_names():
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 16384) == "mfma"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_MFMA, 1, 2048, 2048) == "mfma"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_DOT2, 3, 16385, 2048) == "dot2"
-    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2048) == "mfma"    # no workspace: rows alone too few
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 16384, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_TILED, 48, 8192, 2048) == "tiled"
     assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2080) == "mfma"   # K % 128 != 0
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 48, 16385, 2048) == "tiled"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 48, 16385, 2056) == "mfma"
