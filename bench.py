@@ -406,8 +406,8 @@ def cpu_baseline(wl, budget_s=15.0):
 KERNELS = {
     1: ("gemv_stream_kernel<FmtQ4, 1>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
         os.path.join(ROOT, "profiles", "gemv_stream_q4_M1_grouped_traffic.json")),
-    48: ("q4_mm_kernel<3>", ("common.h", "formats.h", "internal.h", "gemv_mm.hip"),
-         os.path.join(ROOT, "profiles", "q4_mm_M48_grouped_traffic.json")),
+    48: ("tiled_mm_kernel<FmtQ4, 3>", ("common.h", "formats.h", "internal.h", "gemv_mm.hip"),
+         os.path.join(ROOT, "profiles", "tiled_mm_q4_M48_grouped_traffic.json")),
 }
 
 
