@@ -1,4 +1,6 @@
-// Matrix-core GEMV for batched decode, int4 g128 (gfx950, v_mfma_f32_16x16x32_bf16).
+// Tiled matrix-core GEMV for batched decode (gfx950, v_mfma_f32_16x16x32_bf16):
+// int4 g128 weights, and with the same structure NVFP4 and BF16 weights (see
+// the end of this comment).
 //
 // A workgroup owns a block of 64 weight rows and one slice of K (the whole of
 // K unless the row blocks alone cannot give every CU the same work; see the
@@ -30,6 +32,14 @@
 // its fp32 partial tile to a caller-provided workspace; the workgroup that
 // arrives last at the block's counter sums the partials in slice order, so the
 // result does not depend on timing, writes y and resets the counter to zero.
+//
+// NVFP4 (VoxCPM2-NVFP4 card, "What was quantized") and BF16 weights run the
+// same kernel: the A operand of a k-step is the lane's 8 E2M1 codes times the
+// e4m3 scale of their 16-column group, rounded to BF16 (exact: at most 6
+// significant bits), or the 16 bytes of BF16 weights themselves (one load per
+// k-step, one group in flight); the activations stay in natural column order,
+// D accumulates per group without a fold, and NVFP4 outputs are scaled by the
+// global scale G.
 //
 // MFMA operand layout (16x16x32): lane l holds A row l % 16 and B column
 // l % 16; for k-step s it holds the 8 columns 32 * (l / 16) + 8 * s .. + 8 of
