@@ -411,14 +411,24 @@ KERNELS = {
 }
 
 
+def _code_only(src):
+    """C++ source with comments and blank space removed (string literals in
+    these kernels hold no comment markers)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def csrc_digest(M):
-    """sha256 over the sources of the kernel the grouped launches run at M."""
+    """sha256 over the code (comments and layout removed) of the sources of
+    the kernel the grouped launches run at M."""
     import hashlib
     h = hashlib.sha256()
     for n in KERNELS[M][1]:
-        with open(os.path.join(ROOT, "bit_weight_only_q4g128_amd", "csrc", n), "rb") as fh:
+        with open(os.path.join(ROOT, "bit_weight_only_q4g128_amd", "csrc", n)) as fh:
             h.update(n.encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
