@@ -106,13 +106,20 @@ class Workload:
                     wb = sum(q4_wbytes(*self.shapes[p]) for p in stage)
                     ws = self.workspace(M, items)
                     out.append((lambda items=items, ws=ws: q4.q4g128_gemv_grouped(items, workspace=ws), wb, True))
-        out.append((lambda: q4.bf16_gemv(xin, self.head, out=yh), self.head_rows * 2048 * 2, False))
+        if mode == "grouped" and M > 4:
+            # the head as a one-task grouped call, so that it may split K
+            hitems = [(xin, self.head, yh)]
+            hws = self.workspace(M, hitems, self.q4.bf16_workspace_bytes(hitems))
+            out.append((lambda: q4.bf16_gemv_grouped(hitems, workspace=hws), self.head_rows * 2048 * 2, False))
+        else:
+            out.append((lambda: q4.bf16_gemv(xin, self.head, out=yh), self.head_rows * 2048 * 2, False))
         return out
 
-    def workspace(self, M, items):
+    def workspace(self, M, items, need=None):
         """One split-K workspace per batch size (zero-filled once), shared by
         every grouped call of the step (the calls run in stream order)."""
-        need = self.q4.q4g128_workspace_bytes(items)
+        if need is None:
+            need = self.q4.q4g128_workspace_bytes(items)
         if need == 0:
             return None
         ws = self.ws.get(M)
@@ -194,13 +201,16 @@ class Nvfp4Workload:
                     else:
                         items = [(xs[p], *lay[p], ys[p]) for p in stage]
                         plan.append((q4.nvfp4g16_gemv_grouped, items, q4.nvfp4g16_workspace_bytes(items), stage))
-            ws = self.workspace(M, max(n for _, _, n, _ in plan))
+            hitems = [(xin, self.int4.head, yh)]
+            hneed = q4.bf16_workspace_bytes(hitems) if M > 4 else 0
+            ws = self.workspace(M, max([n for _, _, n, _ in plan] + [hneed]))
             for fn, items, n, stage in plan:
                 wb = sum(self.weight_bytes_of(p) for p in stage)
                 out.append((lambda fn=fn, items=items, w=(ws if n else None): fn(items, workspace=w), wb,
                             stage[0] not in self.bf16_proj))
-            head = self.int4.head
-            out.append((lambda: q4.bf16_gemv(xin, head, out=yh), self.int4.head_rows * 2048 * 2, False))
+            # the head as a one-task grouped call, so that it may split K
+            out.append((lambda: q4.bf16_gemv_grouped(hitems, workspace=(ws if hneed else None)), self.int4.head_rows * 2048 * 2,
+                        False))
             return out
         for lay in self.layers:
             for p in self.order:
