@@ -13,7 +13,9 @@ What it computes, in plain NumPy:
     (VoxCPM2-NVFP4 card, section "What was quantized");
   * BF16 weights to fp32;
   * y = x . W^T with x widened from BF16 and the fp32 weights widened to fp64,
-    via an fp64 matrix product.
+    via an fp64 matrix product;
+  * the fused neighbours of the product: RN_bf16 from fp64, the SiLU-gated
+    activation h = RN_bf16(silu(g) * u), and the product plus a residual.
 
 Every function is pinned by tests against values fixed outside this module
 (hand-worked examples, closed forms, exhaustive comparison with numpy/torch
@@ -33,6 +35,9 @@ from .reference import (  # noqa: F401
     q4g128_gemv,
     nvfp4g16_gemv,
     bf16_gemv,
+    bf16_round_bits,
+    silu_mul_bf16,
+    gemv_residual_f64,
     GROUP_Q4,
     GROUP_NVFP4,
 )

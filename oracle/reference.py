@@ -15,6 +15,10 @@ Readings of points the pages leave open:
     fp32 once.
   * y = x . W^T with W stored [N, K] (the nn.Linear convention the per-module
     names imply); no bias.
+  * The MLP activation between the gate/up and down projections is SiLU
+    gating, h = silu(gate) * up (the pages name gate, up and down projections
+    but not the activation; SiLU gating is the one those three names go with),
+    rounded to BF16 once; residual adds round once with the product.
 """
 from __future__ import annotations
 
@@ -164,3 +168,62 @@ def nvfp4g16_gemv(x_bits, qweight, scale_bits, global_scale) -> np.ndarray:
 
 def bf16_gemv(x_bits, w_bits) -> np.ndarray:
     return gemv_f64(x_bits, bf16_dequant_f32(w_bits))
+
+
+# ----------------------------------------------------------------------------
+# the decode step's elementwise neighbours (Rumik TTS Fast Inference post,
+# "What Made It Faster": residual and normalization work fused around the
+# weight-only projections; the gated MLP activation between gate/up and down)
+# ----------------------------------------------------------------------------
+def bf16_round_bits(v) -> np.ndarray:
+    """fp64 values -> BF16 bit patterns, round to nearest with ties to even,
+    from the format's definition: 8 significant bits, fp32's exponent range,
+    subnormal step 2^-133, magnitudes that round past the largest finite
+    value -> infinity; NaN -> 0x7FC0."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))        # a = m 2^ex, m in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, -126)     # floor(log2 a), clamped to the normal range
+    step = np.ldexp(1.0, e - 7)
+    r = np.rint(a / step) * step                      # a / step is exact; rint ties to even
+    r = np.where(r >= 2.0 ** 128, np.inf, r)
+    with np.errstate(over="ignore"):
+        f = np.where(np.signbit(v), -r, r).astype(np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    return np.where(np.isnan(v), np.uint16(0x7FC0), bits)
+
+
+def _bf16_tie(a) -> np.ndarray:
+    """|a| lies exactly halfway between two neighbouring BF16 values."""
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    step = np.ldexp(1.0, np.maximum(ex.astype(np.int64) - 1, -126) - 7)
+    n = a / step
+    return (a > 0) & np.isfinite(a) & (n - np.floor(n) == 0.5)
+
+
+def silu_mul_bf16(g_bits, u_bits) -> np.ndarray:
+    """h = RN_bf16(silu(g) * u) with silu(g) = g / (1 + e^-g), for BF16 g and
+    u (bit patterns), rounded to BF16 once.
+
+    Written as P * sigma(g) with P = g * u, which is exact in fp64 (two 8-bit
+    significands), and sigma(g) = 1 / (1 + e^-g) in fp64.  For large g the
+    fp64 product equals P although the exact value is P (1 - sigma(-g)),
+    slightly smaller in magnitude; that only changes the rounding when P lies
+    exactly halfway between two BF16 values, and then the exact value rounds
+    to the neighbour nearer zero."""
+    g = bf16_value(g_bits)
+    u = bf16_value(u_bits)
+    P = g * u
+    with np.errstate(over="ignore"):
+        v = P / (1.0 + np.exp(-g))
+    lost = (g > 0) & (v == P) & _bf16_tie(P)
+    toward_zero = bf16_round_bits(P * (1.0 - 2.0 ** -40))
+    return np.where(lost, toward_zero, bf16_round_bits(v))
+
+
+def gemv_residual_f64(x_bits, w32, r_bits) -> np.ndarray:
+    """y = x . W^T + r in fp64, before its one rounding to BF16 (r BF16 bits
+    [M, N])."""
+    y = gemv_f64(x_bits, w32)
+    return y + bf16_value(r_bits).reshape(y.shape)

@@ -13,7 +13,9 @@ Sources of truth used here (never the oracle's own formulas):
   * exact rational arithmetic (fractions.Fraction) on tiny inputs;
   * integer-weight special cases where the product is exact in Python ints;
   * the nibble packer of the input generator (an independent implementation
-    of the inverse map).
+    of the inverse map);
+  * for the fused neighbours: torch's fp32 -> bf16 rounding, integer rounding
+    of exact rationals, and e^x from the decimal module at 60 digits.
 """
 from __future__ import annotations
 
@@ -295,6 +297,103 @@ def pin_integer_weights(O):
             assert y[m, n] == acc, (m, n, y[m, n], acc)
 
 
+# ----------------------------------------------------------------------------
+# fused neighbours: BF16 rounding from fp64, the SiLU-gated activation, the
+# product plus a residual
+# ----------------------------------------------------------------------------
+def _rn_bf16_exact(fr: Fraction) -> int:
+    """Exact rational -> BF16 bits by integer arithmetic, ties to even."""
+    sign = 0x8000 if fr < 0 else 0
+    a = abs(fr)
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    n = a / Fraction(2) ** (e - 7)
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    if fl == 256:
+        fl, e = 128, e + 1
+    if e > 127:
+        return sign | 0x7F80
+    if fl >= 128:
+        return sign | ((e + 127) << 7) | (fl - 128)
+    return sign | fl                       # subnormal (e == -126)
+
+
+def pin_bf16_round_library(O):
+    """fp32-representable inputs: RN_bf16 from fp64 must equal torch's fp32 ->
+    bf16 conversion (round to nearest even), ties and subnormals included."""
+    rng = np.random.default_rng(11)
+    v = (rng.standard_normal(60000) * np.exp2(rng.integers(-140, 120, 60000))).astype(np.float32)
+    b = rng.integers(0, 0x7F7F, 20000).astype(np.uint32) << 16          # BF16 values ...
+    ties = (b | 0x8000).view(np.float32)                                 # ... plus half a step: exact ties
+    near = (b | 0x7FFF).view(np.float32)                                 # just below the next tie
+    v = np.concatenate([v, ties, -ties, near, np.float32([0.0, -0.0, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134])])
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.bf16_round_bits(v.astype(np.float64))
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} mismatches, first {v[bad[0]]!r}: {got[bad[0]]:#06x} vs {want[bad[0]]:#06x}"
+
+
+def pin_bf16_round_exact(O):
+    """fp64 inputs between fp32 values: one rounding of the exact value (no
+    detour through fp32), checked by integer arithmetic."""
+    vals = []
+    for base in (1.0, 1.5, -3.25, 2.0 ** -120, 2.0 ** -130, 6.0e37):
+        step = 2.0 ** (math.floor(math.log2(abs(base))) - 7) if abs(base) >= 2.0 ** -126 else 2.0 ** -133
+        for frac in (0.5, 1.5):
+            for eps in (2.0 ** -30, -2.0 ** -30, 2.0 ** -45):
+                vals.append(base + (frac + eps) * step * (1 if base > 0 else -1))
+    got = O.bf16_round_bits(np.array(vals))
+    want = [_rn_bf16_exact(Fraction(v)) for v in vals]
+    assert [int(g) for g in got] == want, [(v, int(g), w) for v, g, w in zip(vals, got, want) if int(g) != w]
+
+
+def pin_silu_mul_decimal(O):
+    """h = RN_bf16(silu(g) * u) against an independent evaluation: e^-g by the
+    decimal module at 60 digits, exact rational product, integer rounding."""
+    import decimal
+    ctx = decimal.Context(prec=60)
+    rng = np.random.default_rng(12)
+    mags = np.exp2(rng.uniform(-12, 5.5, 1500))
+    g = np.concatenate([mags, -mags, [0.0, 1.0, -1.0, 20.0, -20.0, 88.0, -88.0]])
+    g_bits = torch.from_numpy(g.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for u in (1.0, -0.75, 3.5, 2.0 ** -20, 1000.0):
+        u_bits = np.full(g_bits.shape, torch.tensor(u, dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF, np.uint16)
+        got = O.silu_mul_bf16(g_bits, u_bits)
+        for gb, hb in zip(g_bits, got):
+            gv = Fraction(float(torch.tensor(int(gb), dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float()))
+            e = ctx.exp(ctx.minus(decimal.Decimal(gv.numerator) / decimal.Decimal(gv.denominator)))
+            s = gv / (1 + Fraction(e))
+            want = _rn_bf16_exact(s * Fraction(u))
+            if s == 0:   # an exact zero carries the IEEE sign of the product g * u
+                want = 0x8000 if (gb >> 15) ^ (u < 0) else 0
+            assert int(hb) == want, (float(gv), u, hex(int(hb)), hex(want))
+
+
+def pin_residual_exact(O):
+    """Integer weights, activations and residual: x . W^T + r is an exact
+    integer, which the oracle must return exactly, per element."""
+    rng = np.random.default_rng(13)
+    M, N, K = 3, 5, 256
+    codes = rng.integers(0, 16, size=(N, K))
+    x = rng.integers(-8, 9, size=(M, K))
+    r = rng.integers(-64, 65, size=(M, N))
+    w32 = codes.astype(np.float32)
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    rb = torch.from_numpy(r.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.gemv_residual_f64(xb, w32, rb)
+    want = [[sum(int(x[m, k]) * int(codes[n, k]) for k in range(K)) + int(r[m, n]) for n in range(N)] for m in range(M)]
+    assert got.shape == (M, N) and np.array_equal(got, np.array(want, dtype=np.float64))
+
+
 ALL_PINS = [
     pin_nibble_hand,
     pin_nibble_roundtrip,
@@ -311,4 +410,8 @@ ALL_PINS = [
     pin_nvfp4_gemv_exact,
     pin_bf16_gemv_library,
     pin_integer_weights,
+    pin_bf16_round_library,
+    pin_bf16_round_exact,
+    pin_silu_mul_decimal,
+    pin_residual_exact,
 ]

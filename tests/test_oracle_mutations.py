@@ -148,11 +148,52 @@ def _m_bf16_bias(O):
     O.bf16_value = lambda bits: orig(bits) * 2.0
 
 
+def _m_round_truncate(O):
+    # keep the upper half of the fp32 bits: rounds toward zero
+    O.bf16_round_bits = lambda v: (np.asarray(v, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _m_round_via_fp32(O):
+    orig = O.bf16_round_bits
+    O.bf16_round_bits = lambda v: orig(np.asarray(v, np.float64).astype(np.float32).astype(np.float64))
+
+
+def _m_round_ties_away(O):
+    orig = O.bf16_round_bits
+
+    def bf16_round_bits(v):
+        v = np.asarray(v, np.float64)
+        return orig(v + np.sign(v) * np.abs(v) * 2.0 ** -30)
+    O.bf16_round_bits = bf16_round_bits
+
+
+def _m_silu_no_gate(O):
+    def silu_mul_bf16(g_bits, u_bits):
+        g, u = O.bf16_value(g_bits), O.bf16_value(u_bits)
+        return O.bf16_round_bits(u / (1.0 + np.exp(-g)))
+    O.silu_mul_bf16 = silu_mul_bf16
+
+
+def _m_silu_sign(O):
+    def silu_mul_bf16(g_bits, u_bits):
+        g, u = O.bf16_value(g_bits), O.bf16_value(u_bits)
+        return O.bf16_round_bits(g / (1.0 + np.exp(g)) * u)
+    O.silu_mul_bf16 = silu_mul_bf16
+
+
+def _m_residual_transposed(O):
+    def gemv_residual_f64(x_bits, w32, r_bits):
+        y = O.gemv_f64(x_bits, w32)
+        return y + O.bf16_value(r_bits).reshape(y.shape[::-1]).T
+    O.gemv_residual_f64 = gemv_residual_f64
+
+
 MUTANTS = [
     _m_swap_nibbles, _m_drop_min, _m_negate_min, _m_group64, _m_group_index_mod,
     _m_fp16_bias, _m_fp16_ftz, _m_e4m3_bias8, _m_e4m3_no_nan, _m_e2m1_sub,
     _m_e2m1_nosign, _m_nvfp4_double_round, _m_gemv_drop_last_k, _m_gemv_transposed,
-    _m_gemv_fp32, _m_bf16_bias,
+    _m_gemv_fp32, _m_bf16_bias, _m_round_truncate, _m_round_via_fp32, _m_round_ties_away, _m_silu_no_gate,
+    _m_silu_sign, _m_residual_transposed,
 ]
 
 
