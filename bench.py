@@ -7,7 +7,10 @@ the BF16 audio-head GEMV (16385 x 2048).  Weights are seeded synthetic
 GPU and resident in HBM before timing.  The step is captured once into a HIP
 graph and replayed; `value` is total algorithmic bytes (packed weights + group
 scales + activations read + outputs written) per second at batch M = 1.  The
-same step at M = 48 is reported alongside.
+same step at M = 48 is reported alongside, and the step with the layer's
+second launch as one fused int4 call (o + residual; down of silu(gate) * up +
+residual), with per-call times of those fused calls against the same work
+unfused.
 
 Also reported on the same JSON line:
   * roofline: the int4 GEMV kernel used at M = 1 (the streaming kernel), its
@@ -66,6 +69,7 @@ class Workload:
         self.order = synth.LAYER_ORDER
         self.head_rows = head_rows
         self.io = {}
+        self.res = {}
         self.ws = {}
 
     def buffers(self, M):
@@ -80,6 +84,9 @@ class Workload:
             ys = {p: t.empty((M, self.shapes[p][0]), dtype=t.bfloat16, device="cuda") for p in self.order}
             yh = t.empty((M, self.head_rows), dtype=t.bfloat16, device="cuda")
             self.io[M] = (xs, ys, xin, yh)
+            # stand-in residual-stream inputs of the fused o and down calls
+            self.res[M] = (synth.x_bf16(M, 2048, ("bench-res-o", M), device="cuda"),
+                           synth.x_bf16(M, 2048, ("bench-res-down", M), device="cuda"))
         return self.io[M]
 
     def launches(self, M, mode="grouped"):
@@ -89,6 +96,9 @@ class Workload:
         grouped: per layer, q, k, v, gate, up (they read the same activations)
                  in one launch and o, down (independent of each other in a
                  parallel block) in another; then the head.
+        fused:   as grouped, but the o, down launch is one fused int4 call: o
+                 adds a residual, down reads silu(gate) * up -- the outputs of
+                 the layer's first launch -- and adds a residual.
         """
         xs, ys, xin, yh = self.buffers(M)
         out = []
@@ -102,11 +112,19 @@ class Workload:
                                 q4_wbytes(N, K), True))
             else:
                 for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
-                    items = [(xs[p], *lay[p], ys[p]) for p in stage]
                     wb = sum(q4_wbytes(*self.shapes[p]) for p in stage)
+                    if mode == "fused" and stage[0] == "o":
+                        ro, rd = self.res[M]
+                        fitems = [dict(x=xs["o"], qweight=lay["o"][0], scale=lay["o"][1], min=lay["o"][2], residual=ro, out=ys["o"]),
+                                  dict(x=ys["gate"], up=ys["up"], qweight=lay["down"][0], scale=lay["down"][1], min=lay["down"][2],
+                                       residual=rd, out=ys["down"])]
+                        ws = self.workspace(M, None, q4.q4g128_fused_workspace_bytes(fitems))
+                        out.append((lambda fitems=fitems, ws=ws: q4.q4g128_gemv_fused(fitems, workspace=ws), wb, True))
+                        continue
+                    items = [(xs[p], *lay[p], ys[p]) for p in stage]
                     ws = self.workspace(M, items)
                     out.append((lambda items=items, ws=ws: q4.q4g128_gemv_grouped(items, workspace=ws), wb, True))
-        if mode == "grouped" and M > 4:
+        if mode in ("grouped", "fused") and M > 4:
             # the head as a one-task grouped call, so that it may split K
             hitems = [(xin, self.head, yh)]
             hws = self.workspace(M, hitems, self.q4.bf16_workspace_bytes(hitems))
@@ -117,7 +135,9 @@ class Workload:
 
     def workspace(self, M, items, need=None):
         """One split-K workspace per batch size (zero-filled once), shared by
-        every grouped call of the step (the calls run in stream order)."""
+        every grouped and fused call of the step (the calls run in stream
+        order; a fused call's activation pass uses the space after its split-K
+        part)."""
         if need is None:
             need = self.q4.q4g128_workspace_bytes(items)
         if need == 0:
@@ -128,12 +148,14 @@ class Workload:
             self.ws[M] = ws
         return ws
 
-    def step_bytes(self, M):
+    def step_bytes(self, M, mode="grouped"):
         """Algorithmic bytes of one step: packed weights + group scales, each
         distinct activation vector read once (layer input, attention output,
-        FFN activation, head input), every output written once."""
+        FFN activation, head input), every output written once; the fused
+        step reads the gate and up outputs instead of the FFN activation,
+        plus two residuals per layer."""
         w = sum(b for _, b, _ in self.launches(M, "plain"))
-        per_layer_x = (2048 + 2048 + 8192) * M * 2
+        per_layer_x = (2048 + 2048 + (2 * 8192 + 2 * 2048 if mode == "fused" else 8192)) * M * 2
         per_layer_y = sum(self.shapes[p][0] for p in self.order) * M * 2
         head_io = 2048 * M * 2 + self.head_rows * M * 2
         return w + N_LAYERS * (per_layer_x + per_layer_y) + head_io
@@ -236,6 +258,70 @@ def weight_bytes(wl):
     """Packed weights + group parameters of one step (the head's BF16 rows
     included): the bytes the weight stream must read."""
     return sum(b for _, b, _ in wl.launches(1, "plain"))
+
+
+def graph_us(torch, fn, reps=20, iters=20):
+    """Microseconds per call of fn, captured `reps` times in one graph."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        g.replay()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / (iters * reps) * 1e3
+
+
+def fused_calls(torch, q4, synth, wl, M):
+    """The fused int4 calls of one layer against the same work unfused
+    (torch's silu, multiply and add around the plain grouped GEMV) and the
+    plain GEMV alone, microseconds per call in graphs; plus the fused down
+    call's algorithmic bytes per second (weights, gate and up, residual, y)."""
+    import torch.nn.functional as Fn
+    lay = wl.layers[0]
+    g = synth.x_bf16(M, 8192, ("bench-fz-g", M), device="cuda")
+    u = synth.x_bf16(M, 8192, ("bench-fz-u", M), device="cuda")
+    a = synth.x_bf16(M, 2048, ("bench-fz-a", M), device="cuda")
+    wl.buffers(M)
+    ro, rd = wl.res[M]
+    h = torch.empty_like(g)
+    yd = torch.empty((M, 2048), dtype=torch.bfloat16, device="cuda")
+    yo = torch.empty_like(yd)
+    d, o = lay["down"], lay["o"]
+    fd = [dict(x=g, up=u, qweight=d[0], scale=d[1], min=d[2], residual=rd, out=yd)]
+    fo = [dict(x=a, qweight=o[0], scale=o[1], min=o[2], residual=ro, out=yo)]
+    need = max(q4.q4g128_fused_workspace_bytes(fd), q4.q4g128_fused_workspace_bytes(fo),
+               q4.q4g128_workspace_bytes([(h, *d, yd)]), q4.q4g128_workspace_bytes([(a, *o, yo)]))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda") if need else None
+
+    def unfused_down():
+        h.copy_((Fn.silu(g.float()) * u.float()).to(torch.bfloat16))
+        q4.q4g128_gemv_grouped([(h, *d, yd)], workspace=ws)
+        yd.add_(rd)
+
+    def unfused_o():
+        q4.q4g128_gemv_grouped([(a, *o, yo)], workspace=ws)
+        yo.add_(ro)
+
+    rec = {}
+    for name, fused, unfused, plain in (
+            ("down_silu_up_residual", lambda: q4.q4g128_gemv_fused(fd, workspace=ws), unfused_down,
+             lambda: q4.q4g128_gemv_grouped([(h, *d, yd)], workspace=ws)),
+            ("o_residual", lambda: q4.q4g128_gemv_fused(fo, workspace=ws), unfused_o,
+             lambda: q4.q4g128_gemv_grouped([(a, *o, yo)], workspace=ws))):
+        rec[name] = {"fused_us": round(graph_us(torch, fused), 2), "unfused_us": round(graph_us(torch, unfused), 2),
+                     "plain_gemv_us": round(graph_us(torch, plain), 2)}
+    down_bytes = q4_wbytes(2048, 8192) + 2 * M * 8192 * 2 + 2 * M * 2048 * 2
+    rec["down_silu_up_residual"]["fused_GB_s"] = round(down_bytes / (rec["down_silu_up_residual"]["fused_us"] * 1e-6) / 1e9, 1)
+    return rec
 
 
 def read_ceiling(torch, q4, wl, steps, warmup):
@@ -505,7 +591,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
     ap.add_argument("--counters-m", type=int, choices=(1, 48), default=1, help="batch size of the --counters workload")
-    ap.add_argument("--modes", default="M1_grouped,M1_plain,M48_grouped,M48_plain,NVFP4_M1_grouped,NVFP4_M48_grouped,"
+    ap.add_argument("--modes", default="M1_grouped,M1_fused,M1_plain,M48_grouped,M48_fused,M48_plain,NVFP4_M1_grouped,NVFP4_M48_grouped,"
                                        "NVFP4_M1_plain,NVFP4_M48_plain",
                     help="comma list of timed modes; M1_grouped is always timed (it is the headline value)")
     args = ap.parse_args()
@@ -528,12 +614,14 @@ def main():
     modes = {"M1_grouped"} | set(m for m in args.modes.split(",") if m)
     res = {}
     for M in (1, 48):
-        for mode in ("grouped", "plain"):
+        for mode in ("grouped", "plain", "fused"):
             if f"M{M}_{mode}" not in modes:
                 continue
             ms, g = time_graph(torch, wl, M, args.steps, args.warmup, mode)
-            by = wl.step_bytes(M)
-            res[(M, mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(wl.launches(M, mode)))
+            by = wl.step_bytes(M, mode)
+            # a fused call on the tiled kernel forms silu(gate) * up in a pass of its own
+            extra = N_LAYERS if mode == "fused" and M > 4 else 0
+            res[(M, mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(wl.launches(M, mode)) + extra)
             log(f"bench: M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(M, mode)]['gbs']:6.0f} GB/s, "
                 f"{1e3 / ms:6.0f} steps/s, {res[(M, mode)]['launches']} launches")
             del g
@@ -564,6 +652,10 @@ def main():
         roof[M] = {"bound": "hbm", "kernel": f"{KERNELS[M][0]} ({vname}), M={M} grouped launches",
                    "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                    "traffic": measured_traffic(M), "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)}
+    fz = {f"M{M}": fused_calls(torch, q4, synth, wl, M) for M in (1, 48)}
+    for k, r in fz.items():
+        log(f"bench: fused calls {k}: " + ", ".join(f"{n} fused {v['fused_us']} us / unfused {v['unfused_us']} us / "
+                                                     f"plain GEMV {v['plain_gemv_us']} us" for n, v in r.items()))
     head = res[(1, "grouped")]
     wbytes = weight_bytes(wl)
     ceil_ms = read_ceiling(torch, q4, wl, args.steps, args.warmup)
@@ -597,6 +689,7 @@ def main():
                              "ms_per_step": round(ceil_ms, 5), "weight_GB_s": round(ceil_gbs, 1),
                              "pct_of_8TBps": round(100 * ceil_gbs / PEAK_GBS, 2)},
             "modes": {mode_key(k): mode_record(k, r, wbytes, ceil_ms) for k, r in res.items()},
+            "fused_calls": fz,
         },
         "roofline": roof[1],
     }

@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
     "nvfp4g16_gemv_grouped", "nvfp4g16_workspace_bytes", "bf16_gemv_grouped", "bf16_workspace_bytes",
+    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
     "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
@@ -82,6 +83,17 @@ for _name, _T in (("nvfp4g16", NvTask), ("bf16", BfTask)):
     getattr(lib, f"{_name}_gemv_grouped_ws").restype = ctypes.c_int
     getattr(lib, f"{_name}_workspace_bytes").argtypes = [ctypes.POINTER(_T), _i, _i, ctypes.POINTER(ctypes.c_size_t)]
     getattr(lib, f"{_name}_workspace_bytes").restype = ctypes.c_int
+
+
+class FusedTask(ctypes.Structure):
+    _fields_ = [("x", _p), ("up", _p), ("qweight", _p), ("scale", _p), ("minv", _p), ("residual", _p), ("y", _p),
+                ("N", _i), ("K", _i)]
+
+
+lib.q4g128_gemv_fused.argtypes = [ctypes.POINTER(FusedTask), _i, _i, _p, ctypes.c_size_t, _p]
+lib.q4g128_gemv_fused.restype = ctypes.c_int
+lib.q4g128_fused_workspace_bytes.argtypes = [ctypes.POINTER(FusedTask), _i, _i, ctypes.POINTER(ctypes.c_size_t)]
+lib.q4g128_fused_workspace_bytes.restype = ctypes.c_int
 
 
 class Q4GemvError(ValueError):
@@ -353,3 +365,61 @@ def stream_read(tensors, sink):
     ptrs, sizes, n = _read_args(tensors)
     _raise(lib.q4gemv_stream_read(ptrs, sizes, n, sink.data_ptr(), sink.numel(), _stream(sink)))
     return sink
+
+
+def _fused_task_array(items):
+    items = [dict(it) for it in items]
+    if not 1 <= len(items) <= 8:
+        raise ValueError("1..8 tasks per call")
+    arr = (FusedTask * len(items))()
+    outs, M = [], None
+    for i, it in enumerate(items):
+        x, qweight, scale, minv = it["x"], it["qweight"], it["scale"], it["min"]
+        up, res, out = it.get("up"), it.get("residual"), it.get("out")
+        _check(x, "x", _U16, 2); _check(qweight, "qweight", _U8, 2)
+        _check(scale, "scale", _F16, 2); _check(minv, "min", _F16, 2)
+        m, K = x.shape
+        N = qweight.shape[0]
+        M = m if M is None else M
+        if m != M:
+            raise ValueError("all tasks must share the batch size M")
+        if qweight.shape[1] * 2 != K or tuple(scale.shape) != (N, K // 128) or tuple(minv.shape) != (N, K // 128):
+            raise ValueError(f"task {i}: inconsistent shapes")
+        if up is not None:
+            _check(up, "up", _U16, 2)
+            if tuple(up.shape) != (M, K):
+                raise ValueError(f"task {i}: up must be [M, K]")
+        if res is not None:
+            _check(res, "residual", _U16, 2)
+            if tuple(res.shape) != (M, N):
+                raise ValueError(f"task {i}: residual must be [M, N]")
+        y = _out(out, (M, N), torch.bfloat16, x)
+        outs.append(y)
+        arr[i] = FusedTask(x.data_ptr(), up.data_ptr() if up is not None else None, qweight.data_ptr(), scale.data_ptr(),
+                           minv.data_ptr(), res.data_ptr() if res is not None else None, y.data_ptr(), N, K)
+    return items, arr, outs, M
+
+
+def q4g128_gemv_fused(items, workspace=None):
+    """int4 g128 GEMVs with the decode step's elementwise neighbours fused
+    (q4g128_gemv_fused in the C header).  items: sequence of dicts with keys
+    x, qweight, scale, min and optionally up (activations become
+    RN_bf16(silu(x) * up)), residual (added to the output before its
+    rounding; may be the out tensor itself) and out.  workspace as for
+    q4g128_gemv_grouped.  Returns the list of outputs."""
+    items, arr, outs, M = _fused_task_array(items)
+    st = _stream(items[0]["x"])
+    if workspace is None:
+        _raise(lib.q4g128_gemv_fused(arr, len(items), M, None, 0, st))
+    else:
+        if workspace.device != items[0]["x"].device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the activations' device")
+        _raise(lib.q4g128_gemv_fused(arr, len(items), M, workspace.data_ptr(), workspace.numel(), st))
+    return outs
+
+
+def q4g128_fused_workspace_bytes(items) -> int:
+    items, arr, _, M = _fused_task_array(items)
+    n = ctypes.c_size_t(0)
+    _raise(lib.q4g128_fused_workspace_bytes(arr, len(items), M, ctypes.byref(n)))
+    return int(n.value)

@@ -173,6 +173,43 @@ int run_grouped(Fmt fmt, int chosen, const GemvArgs* a, int count, int M, void* 
     return run(fmt, chosen, a, count, stream, workspace, workspace_bytes);
 }
 
+// Validation and kernel choice of a fused int4 call (see q4g128_fused_task):
+// fills a[] and *tiled (false: the streaming kernel).
+int check_fused(const q4g128_fused_task* tasks, int count, int M, bool split, GemvArgs* a, bool* tiled) {
+    if (!tasks) return Q4_EINVAL_PTR;
+    if (count < 1 || count > q4::kMaxTasks) return Q4_EINVAL_SHAPE;
+    Range in[q4::kMaxTasks][6], out[q4::kMaxTasks];
+    bool stream = true, mm = true;
+    for (int i = 0; i < count; ++i) {
+        const q4g128_fused_task& k = tasks[i];
+        int rc = check_q4(k.x, M, k.K, k.qweight, k.scale, k.minv, k.N, k.y, a[i], in[i], out[i]);
+        if (rc) return rc;
+        in[i][4] = in[i][5] = Range{0, 0};
+        if (k.up) {
+            if (!aligned(k.up, 16)) return Q4_EALIGN;
+            in[i][4] = range_of(k.up, (size_t)M * k.K * 2);
+        }
+        if (k.residual) {
+            if (!aligned(k.residual, 2)) return Q4_EALIGN;
+            // a residual that is exactly this task's y is read before each element is written
+            if (k.residual != k.y) in[i][5] = range_of(k.residual, (size_t)M * k.N * 2);
+        }
+        a[i].up = k.up;
+        a[i].resid = k.residual;
+        stream = stream && M <= 4 && q4::stream_supported(q4::kFmtQ4, M, k.K);
+        mm = mm && q4::mm_supported(q4::kFmtQ4, M, k.K, split);
+    }
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j) {
+            for (int r = 0; r < 6; ++r)
+                if (overlaps(out[i], in[j][r])) return Q4_EALIAS;
+            if (i != j && overlaps(out[i], out[j])) return Q4_EALIAS;
+        }
+    if (!stream && !mm) return Q4_EVARIANT;
+    *tiled = !stream;
+    return Q4_OK;
+}
+
 }  // namespace
 
 namespace q4 {
@@ -382,6 +419,76 @@ int nvfp4g16_dequant_f32(const uint8_t* qweight, const uint8_t* scale_e4m3, floa
         return Q4_EALIAS;
     hipError_t e = q4::launch_nvfp4_dequant(qweight, scale_e4m3, global_scale, N, K, w, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
+// Workspace of a fused tiled call: the split-K part, then (256-byte aligned)
+// one h buffer per gated task.
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t fused_h_bytes(const GemvArgs* a, int count) {
+    size_t n = 0;
+    for (int i = 0; i < count; ++i)
+        if (a[i].up) n += align256((size_t)a[i].M * a[i].K * 2);
+    return n;
+}
+
+int q4g128_gemv_fused(const q4g128_fused_task* tasks, int count, int M, void* workspace, size_t workspace_bytes, void* stream) {
+    GemvArgs a[q4::kMaxTasks];
+    bool tiled = false;
+    const bool split = workspace != nullptr && workspace_bytes > 0;
+    int rc = check_fused(tasks, count, M, split, a, &tiled);
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (!tiled) {
+        e = q4::launch_stream_fused(a, count, s);
+    } else {
+        const size_t need = q4::mm_workspace_bytes(q4::kFmtQ4, a, count);
+        const size_t h_off = align256(need), h_bytes = fused_h_bytes(a, count);
+        size_t mm_bytes = workspace_bytes;
+        if (split && h_bytes > 0 && workspace_bytes >= h_off + h_bytes) {
+            // h formed once into the workspace; the tiled kernel reads it as x
+            const uint16_t* g[q4::kMaxTasks];
+            const uint16_t* u[q4::kMaxTasks];
+            uint16_t* h[q4::kMaxTasks];
+            size_t n[q4::kMaxTasks];
+            int ng = 0;
+            uint8_t* p = static_cast<uint8_t*>(workspace) + h_off;
+            for (int i = 0; i < count; ++i) {
+                if (!a[i].up) continue;
+                g[ng] = a[i].x; u[ng] = a[i].up; h[ng] = reinterpret_cast<uint16_t*>(p);
+                n[ng] = (size_t)M * a[i].K;
+                a[i].x = h[ng];
+                a[i].up = nullptr;
+                p += align256(n[ng] * 2);
+                ++ng;
+            }
+            if (q4::launch_silu_mul(g, u, h, n, ng, s) != hipSuccess) return Q4_ELAUNCH;
+            mm_bytes = h_off;
+        }
+        if (split) {
+            if (need == 0 || mm_bytes < need) {
+                for (int i = 0; i < count; ++i)
+                    if (!q4::mm_supported(q4::kFmtQ4, M, a[i].K, false)) return Q4_EVARIANT;
+            }
+        }
+        e = q4::launch_mm_fused(a, count, workspace, mm_bytes, s);
+    }
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
+int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int M, size_t* bytes) {
+    if (!bytes) return Q4_EINVAL_PTR;
+    GemvArgs a[q4::kMaxTasks];
+    bool tiled = false;
+    int rc = check_fused(tasks, count, M, true, a, &tiled);
+    if (rc) return rc;
+    if (!tiled) {
+        *bytes = 0;
+        return Q4_OK;
+    }
+    const size_t h_bytes = fused_h_bytes(a, count);
+    *bytes = (h_bytes ? align256(q4::mm_workspace_bytes(q4::kFmtQ4, a, count)) : q4::mm_workspace_bytes(q4::kFmtQ4, a, count)) + h_bytes;
+    return Q4_OK;
 }
 
 size_t q4gemv_stream_read_sink_words(const size_t* bytes, int count) {

@@ -28,6 +28,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // fp16 bits -> fp32 (exact, subnormals kept).
+// RN_bf16(silu(g) * u) for the two BF16 values of each of g and u packed in
+// a dword (low half = first element); silu(g) = g / (1 + e^-g) evaluated in
+// fp32 with the hardware exp2 and reciprocal (a few fp32 ulps, far below one
+// BF16 step), then rounded to BF16 once.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-1.44269504088896341f * g);   // e^-g
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+__device__ __forceinline__ uint32_t silu_mul_bf16x2(uint32_t g, uint32_t u) {
+    const uint32_t lo = f32_to_bf16(silu_mul(bf16lo(g), bf16lo(u)));
+    const uint32_t hi = f32_to_bf16(silu_mul(bf16hi(g), bf16hi(u)));
+    return lo | (hi << 16);
+}
+
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }

@@ -21,6 +21,9 @@ struct GemvArgs {
     float gscale;            // nvfp4: per-matrix global scale (multiplier)
     uint16_t* y;             // [M, N] bf16
     int M, N, K;
+    // fused int4 calls only (kernels instantiated with kFused), else null:
+    const uint16_t* up;      // [M, K] bf16: the activations are RN_bf16(silu(x) * up)
+    const uint16_t* resid;   // [M, N] bf16: y = RN_bf16(x W^T + resid); may equal y
 };
 
 // ---------------------------------------------------------------------------

@@ -99,6 +99,10 @@ struct MmTable {
 // tiles; four tiles fit one workgroup per CU)
 template <int MT>
 __host__ __device__ constexpr int mm_waves() { return MT <= 3 ? 4 : 2; }
+// the fused instances' loaders also hold the up activations: 3 waves per
+// SIMD (168 registers) still keep two 6-wave workgroups per CU
+template <int MT, bool kFused>
+__host__ __device__ constexpr int mm_waves_f() { return kFused && MT <= 3 ? 3 : mm_waves<MT>(); }
 // activation groups a loader keeps in flight (registers: 4 * MT pieces each)
 template <int MT>
 __host__ __device__ constexpr int mm_xp() { return MT <= 1 ? 2 : 1; }
@@ -152,7 +156,9 @@ __device__ __forceinline__ uint32_t part_off(int blk, int KS, int ks, int rp, in
 // y for one 16-row tile: lane l holds rows trow0 + 4 (l / 16) + v (v = 0..3)
 // of batch row 16 mt + l % 16; write_y does the two tiles of a row pair.
 // (times gs: the NVFP4 global scale, 1 otherwise)
-template <int MT>
+// Fused instances add the residual (read by the lane that then writes the
+// same elements, so it may be y itself) before the one rounding.
+template <int MT, bool kFused = false>
 __device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, float gs, int trow0, int lane, const f32x4 (&v)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -160,7 +166,15 @@ __device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, float g
         const int row = trow0 + 4 * (lane >> 4);
         if (m >= a.M || row >= a.N) continue;
         uint16_t* dst = a.y + (size_t)m * a.N + row;
-        const f32x4 r = v[mt] * gs;
+        f32x4 r = v[mt] * gs;
+        if constexpr (kFused) {
+            if (a.resid != nullptr) {
+                const uint16_t* rs = a.resid + (size_t)m * a.N + row;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (row + q < a.N) r[q] += __builtin_bit_cast(float, (uint32_t)rs[q] << 16);
+            }
+        }
         if (y8 && row + 3 < a.N) {
             const uint32_t lo = (uint32_t)f32_to_bf16(r.x) | ((uint32_t)f32_to_bf16(r.y) << 16);
             const uint32_t hi = (uint32_t)f32_to_bf16(r.z) | ((uint32_t)f32_to_bf16(r.w) << 16);
@@ -172,14 +186,14 @@ __device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, float g
         }
     }
 }
-template <int MT>
+template <int MT, bool kFused = false>
 __device__ __forceinline__ void write_y(const GemvArgs& a, bool y8, float gs, int prow0, int lane, const f32x4 (&v)[2][MT]) {
-    write_y_tile<MT>(a, y8, gs, prow0, lane, v[0]);
-    write_y_tile<MT>(a, y8, gs, prow0 + 16, lane, v[1]);
+    write_y_tile<MT, kFused>(a, y8, gs, prow0, lane, v[0]);
+    write_y_tile<MT, kFused>(a, y8, gs, prow0 + 16, lane, v[1]);
 }
 
-template <class F, int MT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves<MT>()))) void tiled_mm_kernel(MmTable tt) {
+template <class F, int MT, bool kFused = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves_f<MT, kFused>()))) void tiled_mm_kernel(MmTable tt) {
     constexpr int kPre = MmFmt<F>::kPre;
     constexpr int kLoads = MmFmt<F>::kLoads;
     constexpr int XP = mm_xp<MT>() < kPre ? mm_xp<MT>() : kPre;
@@ -384,7 +398,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         // ------------------------------------------------------------ epilogue
         if (KS == 1) {
             __syncthreads();   // every wave meets the same barriers
-            if (kh == 0) write_y<MT>(a, tt.t[ti].y8 != 0, gs, prow0, lane, acc);
+            if (kh == 0) write_y<MT, kFused>(a, tt.t[ti].y8 != 0, gs, prow0, lane, acc);
             return;
         }
         // split K: publish this slice's partial tile; the last slice to arrive
@@ -415,26 +429,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
         // piece (mt, s) of step i: four whole batch rows 16 mt + 4 s + l / 16
         // of the group, lane l holding columns 8 (l % 16) .. + 8 (1 KB
         // contiguous per row quartet, so each load fills whole cache lines)
-        auto xload = [&](int i, int p) {
+        auto xoff = [&](int i, int p) {
             const int mt = p >> 2, s = p & 3;
             const int m = 16 * mt + 4 * s + (lane >> 4);
             const int g = g0 + hb + (i < hlast ? i : hlast);
             const int k = (g << 7) + 8 * (lane & 15);
-            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((m * a.K + k) * 2), 0, 0));
+            return (uint32_t)((m * a.K + k) * 2);
+        };
+        auto xload = [&](int i, int p) {
+            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff(i, p), 0, 0));
+        };
+        // fused: the up activations at the same places (an empty range when
+        // the task has none: the loads return zeros and are not used, and
+        // every load stays unconditional)
+        const bool gated = kFused && a.up != nullptr;
+        const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.up, gated ? (uint32_t)(a.M * a.K * 2) : 0u);
+        auto uload = [&](int i, int p) {
+            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, xoff(i, p), 0, 0));
         };
         // where lane l's piece (mt, s) goes: fragment (mt, k-step l % 4), lane
         // 4 s + l / 16 + 16 ((l / 4) % 4) (its row within the tile plus 16 x
         // its column quarter)
         const int sp = lane & 3;
         const int fl0 = (lane >> 4) + 16 * ((lane >> 2) & 3);
-        auto stage = [&](int i, const u32x4 (&xr)[4 * MT]) {
+        auto stage = [&](int i, const u32x4 (&xr)[4 * MT], const u32x4 (&ur)[kFused ? 4 * MT : 1]) {
             const int slot = i & 1;
             u32x4* frag = xb + (size_t)((slot * 2 + L) * MT) * 4 * 64;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const u32x4 v = xr[mt * 4 + s];
+                    u32x4 v = xr[mt * 4 + s];
+                    if constexpr (kFused) {
+                        if (gated) {
+                            const u32x4 u = ur[mt * 4 + s];
+                            v = u32x4{silu_mul_bf16x2(v.x, u.x), silu_mul_bf16x2(v.y, u.y), silu_mul_bf16x2(v.z, u.z),
+                                      silu_mul_bf16x2(v.w, u.w)};
+                        }
+                    }
                     u32x4 w = v;
                     if constexpr (is_q4<F>()) {
                         uint32_t pr[4];
@@ -445,10 +477,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                 }
         };
         u32x4 xr[XP][4 * MT];
+        u32x4 ur[XP][kFused ? 4 * MT : 1];
+        auto load_step = [&](int r, int i) {   // step i's x (and up) pieces into ring entry r
 #pragma unroll
-        for (int u = 0; u < XP; ++u)
+            for (int p = 0; p < 4 * MT; ++p) xr[r][p] = xload(i, p);
+            if constexpr (kFused) {
 #pragma unroll
-            for (int p = 0; p < 4 * MT; ++p) xr[u][p] = xload(u, p);
+                for (int p = 0; p < 4 * MT; ++p) ur[r][p] = uload(i, p);
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < XP; ++u) load_step(u, u);
 
         // group parameters of the block's rows for the slice, fp32 (scale, min)
         // [group][row], every load of a lane issued before the first is used
@@ -528,18 +567,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
             lds_barrier();   // releases the compute waves' weight prefetch
         }
 
-        stage(0, xr[0]);
-#pragma unroll
-        for (int p = 0; p < 4 * MT; ++p) xr[0][p] = xload(XP, p);
+        stage(0, xr[0], ur[0]);
+        load_step(0, XP);
         lds_barrier();
 
         // step i stages step i + 1, held in ring entry (i + 1) % XP (i0 is a
         // multiple of kPre, itself a multiple of XP)
         auto lstep = [&](const int i, const int u) {
             const int r = (u + 1) % XP;
-            stage(i + 1, xr[r]);
-#pragma unroll
-            for (int p = 0; p < 4 * MT; ++p) xr[r][p] = xload(i + 1 + XP, p);
+            stage(i + 1, xr[r], ur[r]);
+            load_step(r, i + 1 + XP);
             lds_barrier();
         };
         for (int i0 = 0; i0 < niter; i0 += kPre) {
@@ -588,7 +625,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
                     for (int mt = 0; mt < MT; ++mt) sum[mt] += __builtin_bit_cast(f32x4, pv[k][mt]);
                 }
         }
-        write_y_tile<MT>(a, tt.t[ti].y8 != 0, gs, row0 + 32 * rp + 16 * t, lane, sum);
+        write_y_tile<MT, kFused>(a, tt.t[ti].y8 != 0, gs, row0 + 32 * rp + 16 * t, lane, sum);
     }
     if (tid == 0) __hip_atomic_store(&cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -689,7 +726,7 @@ size_t ws_bytes_mt(const GemvArgs* tasks, int count) {
     return (part > 0 && cnt <= kCntBytes) ? kCntBytes + part : 0;
 }
 
-template <class F, int MT>
+template <class F, int MT, bool kFused = false>
 hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t st) {
     int ks[kMaxTasks], gps[kMaxTasks];
     const size_t need = ws_bytes_mt<F, MT>(tasks, count);
@@ -735,10 +772,10 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         grid += blocks * ks[i];
         gmax = gps[i] > gmax ? gps[i] : gmax;
     }
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(tiled_mm_kernel<F, MT>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(tiled_mm_kernel<F, MT, kFused>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
     if (attr != hipSuccess) return attr;
-    return launch_kernel(tiled_mm_kernel<F, MT>, dim3(grid), dim3(kThreads), (size_t)mm_shmem<F, MT>(gmax), st, tt);
+    return launch_kernel(tiled_mm_kernel<F, MT, kFused>, dim3(grid), dim3(kThreads), (size_t)mm_shmem<F, MT>(gmax), st, tt);
 }
 
 }  // namespace
@@ -766,13 +803,13 @@ size_t mm_workspace_bytes_f(const GemvArgs* tasks, int count) {
     }
 }
 
-template <class F>
+template <class F, bool kFused = false>
 hipError_t launch_mm_f(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
     switch ((tasks[0].M + 15) / 16) {
-        case 1: return launch_mm_mt<F, 1>(tasks, count, ws, ws_bytes, s);
-        case 2: return launch_mm_mt<F, 2>(tasks, count, ws, ws_bytes, s);
-        case 3: return launch_mm_mt<F, 3>(tasks, count, ws, ws_bytes, s);
-        default: return launch_mm_mt<F, 4>(tasks, count, ws, ws_bytes, s);
+        case 1: return launch_mm_mt<F, 1, kFused>(tasks, count, ws, ws_bytes, s);
+        case 2: return launch_mm_mt<F, 2, kFused>(tasks, count, ws, ws_bytes, s);
+        case 3: return launch_mm_mt<F, 3, kFused>(tasks, count, ws, ws_bytes, s);
+        default: return launch_mm_mt<F, 4, kFused>(tasks, count, ws, ws_bytes, s);
     }
 }
 
@@ -798,6 +835,10 @@ hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t
         case kFmtNvfp4: return launch_mm_f<FmtNvfp4>(tasks, count, ws, ws_bytes, s);
         default: return launch_mm_f<FmtBf16>(tasks, count, ws, ws_bytes, s);
     }
+}
+
+hipError_t launch_mm_fused(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
+    return launch_mm_f<FmtQ4, true>(tasks, count, ws, ws_bytes, s);
 }
 
 }  // namespace q4

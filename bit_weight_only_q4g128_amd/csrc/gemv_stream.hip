@@ -19,6 +19,12 @@
 //
 // One launch serves up to kMaxTasks GEMVs of one format and batch size; the
 // workgroups of a launch are split between tasks by a prefix table.
+//
+// Fused int4 instances (kFused) also take, per task, an optional second
+// activation array `up` -- the activations become RN_bf16(silu(x) * up),
+// formed while x is staged -- and an optional residual added to each output
+// before its one rounding (it may be the output array itself: each element
+// is read and then written by the same lane).
 #include <type_traits>
 
 #include "internal.h"
@@ -70,7 +76,7 @@ __host__ __device__ inline int stream_shmem(int MT, int K) {
 // 16-byte x pieces per thread (x is MT*K*2 bytes over 256 threads)
 template <class F> __host__ __device__ inline int x_pieces(int MT, int K) { return (MT * K / 8 + 255) / 256; }
 
-template <class F, int MT>
+template <class F, int MT, bool kFused>
 __global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int kXP = MT * 4;   // most x pieces a thread stages (K <= 8192 for the 4-bit formats)
@@ -101,6 +107,17 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
     for (int i = 0; i < kXP; ++i)
         xr[i] = i < nxp ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (tid + 256 * i) * 16, 0, 0))
                         : u32x4{0, 0, 0, 0};
+    const bool gated = kFused && a.up != nullptr;
+    u32x4 xu[kFused ? kXP : 1];
+    if constexpr (kFused) {
+        if (gated) {
+            const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.up, (uint32_t)(MT * K * 2));
+#pragma unroll
+            for (int i = 0; i < kXP; ++i)
+                xu[i] = i < nxp ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, (tid + 256 * i) * 16, 0, 0))
+                                : u32x4{0, 0, 0, 0};
+        }
+    }
     int wg_rows = a.N - row0;
     wg_rows = wg_rows < 0 ? 0 : (wg_rows > RW ? RW : wg_rows);
     uint32_t auxr[Stream<F>::kAuxPerThread > 0 ? Stream<F>::kAuxPerThread : 1];
@@ -128,6 +145,20 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
         const uint32_t r = (uint32_t)(i >> cl), j = (uint32_t)(i & (CPL - 1));
         q[i] = buf_load16(rw, r * rowbytes + (j * 64 + lane) * 16, 0);
     }
+    // fused: the residuals of the wave's rows (rows past N read as zero)
+    float res[kFused ? kLoads : 1][kFused ? MT : 1];
+    if constexpr (kFused) {
+        const bool has_res = a.resid != nullptr;
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.resid, has_res ? (uint32_t)(MT * a.N * 2) : 0u);
+#pragma unroll
+        for (int r = 0; r < kLoads; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int row = wrow0 + r;
+                const bool ok = has_res && r < rpw && row < a.N;
+                res[r][m] = ok ? __builtin_bit_cast(float, (uint32_t)buf_load2(rr, (uint32_t)(((size_t)m * a.N + row) * 2), 0) << 16) : 0.f;
+            }
+    }
 
     // --- 3. stage x (and int4 chunk sums) and the group parameters in LDS
     uint8_t* xs = lds;
@@ -139,6 +170,9 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
             const int p = tid + 256 * i;   // piece index over [MT][K/8]
             const bool in = p < MT * K / 8;
             if constexpr (std::is_same<F, FmtQ4>::value) {
+                if (gated)
+                    xr[i] = u32x4{silu_mul_bf16x2(xr[i].x, xu[i].x), silu_mul_bf16x2(xr[i].y, xu[i].y),
+                                  silu_mul_bf16x2(xr[i].z, xu[i].z), silu_mul_bf16x2(xr[i].w, xu[i].w)};
                 uint32_t pr[4];
                 xq4_pairs(xr[i].x, xr[i].y, xr[i].z, xr[i].w, pr);
                 if (in) *reinterpret_cast<u32x4*>(xs + p * 16) = u32x4{pr[0], pr[1], pr[2], pr[3]};
@@ -206,6 +240,7 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
             v += dpp<0x140>(v);
             v += dpp<0x142, 0xA>(v);
             v += dpp<0x143, 0xC>(v);
+            if constexpr (kFused) v += res[r][m];   // (F::finish is the identity for int4)
             if (lane == 63 && row < a.N) a.y[(size_t)m * a.N + row] = f32_to_bf16(F::finish(a, v));
             out[m] = 0.f;
         }
@@ -244,7 +279,7 @@ template <class F> int chunk_log2(int K) {
     return -1;
 }
 
-template <class F, int MT>
+template <class F, int MT, bool kFused>
 hipError_t launch_stream_mt(const GemvArgs* tasks, int count, hipStream_t st) {
     StreamTable tt{};
     for (int i = 0; i < kMaxTasks; ++i) tt.blk0[i] = 0x7fffffff;
@@ -260,16 +295,16 @@ hipError_t launch_stream_mt(const GemvArgs* tasks, int count, hipStream_t st) {
         shmem = sh > shmem ? sh : shmem;
     }
     tt.count = count;
-    return launch_kernel(gemv_stream_kernel<F, MT>, dim3(grid), dim3(256), (size_t)shmem, st, tt);
+    return launch_kernel(gemv_stream_kernel<F, MT, kFused>, dim3(grid), dim3(256), (size_t)shmem, st, tt);
 }
 
-template <class F>
+template <class F, bool kFused = false>
 hipError_t launch_stream_fmt(const GemvArgs* tasks, int count, hipStream_t st) {
     switch (tasks[0].M) {
-        case 1: return launch_stream_mt<F, 1>(tasks, count, st);
-        case 2: return launch_stream_mt<F, 2>(tasks, count, st);
-        case 3: return launch_stream_mt<F, 3>(tasks, count, st);
-        default: return launch_stream_mt<F, 4>(tasks, count, st);
+        case 1: return launch_stream_mt<F, 1, kFused>(tasks, count, st);
+        case 2: return launch_stream_mt<F, 2, kFused>(tasks, count, st);
+        case 3: return launch_stream_mt<F, 3, kFused>(tasks, count, st);
+        default: return launch_stream_mt<F, 4, kFused>(tasks, count, st);
     }
 }
 
@@ -293,6 +328,10 @@ hipError_t launch_stream(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t 
         case kFmtNvfp4: return launch_stream_fmt<FmtNvfp4>(tasks, count, s);
         default: return launch_stream_fmt<FmtBf16>(tasks, count, s);
     }
+}
+
+hipError_t launch_stream_fused(const GemvArgs* tasks, int count, hipStream_t s) {
+    return launch_stream_fmt<FmtQ4, true>(tasks, count, s);
 }
 
 }  // namespace q4

@@ -49,6 +49,9 @@ constexpr int kStreamMaxM = 4;
 constexpr int kStreamMaxShmem = 64 * 1024;
 hipError_t launch_stream(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
 bool stream_supported(Fmt fmt, int M, int K);
+// The int4 streaming kernel with the fused activation prologue and residual
+// epilogue (GemvArgs::up, GemvArgs::resid; either may be null).
+hipError_t launch_stream_fused(const GemvArgs* tasks, int count, hipStream_t s);
 
 // Tiled matrix-core GEMV with staged activations (M <= 64, K % 128 == 0) for
 // the three weight formats, up to kMaxTasks GEMVs of one format per launch.
@@ -59,6 +62,14 @@ bool stream_supported(Fmt fmt, int M, int K);
 bool mm_supported(Fmt fmt, int M, int K, bool split);
 size_t mm_workspace_bytes(Fmt fmt, const GemvArgs* tasks, int count);
 hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
+// The int4 tiled kernel with the fused activation prologue and residual
+// epilogue (GemvArgs::up, GemvArgs::resid; either may be null).
+hipError_t launch_mm_fused(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
+
+// h_i = RN_bf16(silu(g_i) * u_i) over values[i] elements (a multiple of 8;
+// every array 16-byte aligned) for count <= kMaxTasks segments, one launch.
+hipError_t launch_silu_mul(const uint16_t* const* g, const uint16_t* const* u, uint16_t* const* h, const size_t* values, int count,
+                           hipStream_t s);
 
 // 16x16x32 BF16 matrix-core GEMV (any M <= 64), one launch per task.
 hipError_t launch_mfma(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);

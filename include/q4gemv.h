@@ -194,6 +194,55 @@ int bf16_gemv_grouped_ws(const bf16_task* tasks, int count, int M, int variant, 
 int bf16_workspace_bytes(const bf16_task* tasks, int count, int M, size_t* bytes);
 
 /*
+ * Fused int4 GEMVs for the decode step's elementwise neighbours.  The Rumik
+ * TTS Fast Inference post ("What Made It Faster") fuses the residual and
+ * normalization operations around its weight-only projections so that their
+ * data movement disappears; here the two around the MLP and the residual
+ * stream of a decoder layer:
+ *
+ *   up != NULL:        the activations of the product are
+ *                          h[m, k] = RN_bf16(silu(x[m, k]) * up[m, k]),
+ *                      silu(g) = g / (1 + e^-g) -- the gated MLP's
+ *                      activation, formed while the activations are staged
+ *                      (x holds the gate projection's output): down(h) with
+ *                      no separate elementwise kernel and no h in memory;
+ *   residual != NULL:  y[m, n] = RN_bf16(sum_k h[m, k] w[n, k] + residual[m, n]),
+ *                      one rounding of the exact sum plus the residual (the
+ *                      o and down projections adding into the residual
+ *                      stream); residual may be y itself (in place).
+ *
+ * silu is evaluated in fp32 with the hardware exp2 and reciprocal (a few fp32
+ * ulps), so h can differ from the exactly rounded value by one BF16 step when
+ * the exact product lies within that error of a rounding boundary.  Kernels:
+ * the streaming kernel when every task allows it (M <= 4, K = 2048, 4096 or
+ * 8192), else the tiled kernel (K % 128 == 0); other shapes return
+ * Q4_EVARIANT.  Tasks obey the q4g128_gemv rules; up is bf16 [M, K], 16-byte
+ * aligned; residual is bf16 [M, N], 2-byte aligned; no y may overlap any
+ * input of any task or another y, except that a task's y may be exactly its
+ * own residual.  workspace / workspace_bytes as for q4g128_gemv_grouped_ws
+ * (q4g128_fused_workspace_bytes sizes it; NULL runs unsplit).  On the tiled
+ * kernel a workspace of that size also holds h: it is then formed once by a
+ * separate pass (one extra launch) instead of by the kernel's loader waves
+ * for every 64-row block -- same arithmetic, same result bit for bit, and at
+ * M = 48 about half the time (the loaders pace the tiled kernel's main loop).
+ */
+typedef struct q4g128_fused_task {
+    const uint16_t* x;         /* bf16 [M, K] (the gate activations when up is set) */
+    const uint16_t* up;        /* NULL, or bf16 [M, K] */
+    const uint8_t* qweight;    /* uint8 [N, K/2] */
+    const uint16_t* scale;     /* fp16 [N, K/128] */
+    const uint16_t* minv;      /* fp16 [N, K/128] */
+    const uint16_t* residual;  /* NULL, or bf16 [M, N] (may equal y) */
+    uint16_t* y;               /* bf16 [M, N] */
+    int N;
+    int K;
+} q4g128_fused_task;
+
+int q4g128_gemv_fused(const q4g128_fused_task* tasks, int count, int M, void* workspace, size_t workspace_bytes,
+                      void* stream);
+int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int M, size_t* bytes);
+
+/*
  * Diagnostic dequantization of a whole matrix to fp32 w [N, K] (16-byte
  * aligned).  Bitwise equal to the format definitions above: int4 rounds
  * code*scale+min once; NVFP4 rounds e2m1*e4m3*G once (the first product is

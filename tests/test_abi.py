@@ -197,6 +197,47 @@ def test_grouped_nvfp4_bf16_validation():
         assert fnb(arr, 2, 48, ctypes.byref(nb)) == OK and nb.value > 0     # 64 row blocks: K is split
 
 
+def test_fused_validation():
+    """q4g128_gemv_fused / q4g128_fused_workspace_bytes reject bad arguments
+    on the host (the size query never launches anything)."""
+    FT = q4.FusedTask
+
+    def ft(i, **kw):
+        b = A + (i << 29)
+        base = dict(x=b, up=b + (5 << 26), qweight=b + (1 << 26), scale=b + (2 << 26), minv=b + (3 << 26),
+                    residual=b + (6 << 26), y=b + (4 << 26), N=2048, K=2048)
+        base.update(kw)
+        return FT(**base)
+
+    nb = ctypes.c_size_t(123)
+
+    def size(tasks, M=1):
+        arr = (FT * len(tasks))(*tasks)
+        return lib.q4g128_fused_workspace_bytes(arr, len(tasks), M, ctypes.byref(nb))
+
+    def call(tasks, M=1):
+        arr = (FT * len(tasks))(*tasks)
+        return lib.q4g128_gemv_fused(arr, len(tasks), M, None, 0, None)
+
+    assert lib.q4g128_gemv_fused(None, 1, 1, None, 0, None) == EPTR
+    assert lib.q4g128_fused_workspace_bytes((FT * 1)(ft(0)), 1, 1, None) == EPTR
+    assert size([ft(0)]) == OK and nb.value == 0                       # M = 1: the streaming kernel, no split
+    assert size([ft(0), ft(1)], M=48) == OK and nb.value > 0            # M = 48: the tiled kernel splits K
+    assert size([ft(0, up=None, residual=None)]) == OK
+    assert size([ft(0, residual=A + (4 << 26))]) == OK                  # in place: residual is y
+    assert call([ft(i) for i in range(9)]) == ESHAPE
+    assert call([ft(0)], M=0) == ESHAPE
+    assert call([ft(0)], M=65) == ESHAPE
+    assert call([ft(0, x=None)]) == EPTR
+    assert call([ft(0, up=A + (5 << 26) + 8)]) == EALIGN
+    assert call([ft(0, residual=A + (6 << 26) + 1)]) == EALIGN
+    assert call([ft(0, y=A + (5 << 26) + 64)]) == EALIAS               # over its own up activations
+    assert call([ft(0, residual=A + (4 << 26) + 2)]) == EALIAS         # residual partly over y
+    assert call([ft(0), ft(1, y=A + (6 << 26))]) == EALIAS              # over another task's residual
+    assert call([ft(0), ft(1, y=A + (4 << 26))]) == EALIAS              # two tasks share an output
+    assert call([ft(0, K=32768, N=64)], M=64) == EVARIANT               # unsplit tiled kernel: too many groups
+
+
 def test_stream_read_validation():
     import ctypes
     lib.q4gemv_stream_read.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
