@@ -15,7 +15,9 @@ What it computes, in plain NumPy:
   * y = x . W^T with x widened from BF16 and the fp32 weights widened to fp64,
     via an fp64 matrix product;
   * the fused neighbours of the product: RN_bf16 from fp64, the SiLU-gated
-    activation h = RN_bf16(silu(g) * u), and the product plus a residual.
+    activation h = RN_bf16(silu(g) * u), and the product plus a residual;
+  * sampling from the head: top-k, softmax at a temperature, inverse-CDF draw
+    with a caller-supplied uniform.
 
 Every function is pinned by tests against values fixed outside this module
 (hand-worked examples, closed forms, exhaustive comparison with numpy/torch
@@ -38,6 +40,7 @@ from .reference import (  # noqa: F401
     bf16_round_bits,
     silu_mul_bf16,
     gemv_residual_f64,
+    sample_topk,
     GROUP_Q4,
     GROUP_NVFP4,
 )

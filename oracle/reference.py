@@ -15,6 +15,11 @@ Readings of points the pages leave open:
     fp32 once.
   * y = x . W^T with W stored [N, K] (the nn.Linear convention the per-module
     names imply); no bias.
+  * Sampling from the head (temperature 0.8, top-k 30 in the fast-inference
+    post): the k largest BF16 logits, ties to the lower index, in order of
+    (logit descending, index ascending); softmax of logit / T over those k;
+    the token is the first in that order whose cumulative probability
+    exceeds the caller's uniform u in [0, 1) (inverse CDF).
   * The MLP activation between the gate/up and down projections is SiLU
     gating, h = silu(gate) * up (the pages name gate, up and down projections
     but not the activation; SiLU gating is the one those three names go with),
@@ -227,3 +232,32 @@ def gemv_residual_f64(x_bits, w32, r_bits) -> np.ndarray:
     [M, N])."""
     y = gemv_f64(x_bits, w32)
     return y + bf16_value(r_bits).reshape(y.shape)
+
+
+# ----------------------------------------------------------------------------
+# sampling from the head (Rumik TTS Fast Inference post, "The Result":
+# temperature 0.8, top-k 30 over the audio-token head)
+# ----------------------------------------------------------------------------
+def sample_topk(logit_bits, temperature, top_k, u):
+    """Per batch row m of BF16 logits [M, V]: the top_k largest logits (ties
+    to the lower index), ordered by (logit descending, index ascending); their
+    probabilities softmax(logit / T) over those k, in fp64; the sampled token,
+    the first of that order whose cumulative probability exceeds u[m].
+    Returns (token [M] int64, index [M, k] int64, prob [M, k] fp64)."""
+    lg = bf16_value(logit_bits)
+    lg = lg.reshape(-1, lg.shape[-1])
+    M, V = lg.shape
+    assert 1 <= top_k <= V
+    u = np.asarray(u, dtype=np.float64).reshape(M)
+    index = np.empty((M, top_k), np.int64)
+    prob = np.empty((M, top_k), np.float64)
+    token = np.empty(M, np.int64)
+    for m in range(M):
+        order = np.lexsort((np.arange(V), -lg[m]))[:top_k]   # primary: logit descending; then index
+        z = lg[m, order] / temperature
+        e = np.exp(z - z[0])
+        p = e / e.sum()
+        c = np.cumsum(p)
+        pick = int(np.searchsorted(c, u[m], side="right"))
+        index[m], prob[m], token[m] = order, p, order[min(pick, top_k - 1)]
+    return token, index, prob

@@ -394,6 +394,73 @@ def pin_residual_exact(O):
     assert got.shape == (M, N) and np.array_equal(got, np.array(want, dtype=np.float64))
 
 
+# ----------------------------------------------------------------------------
+# sampling from the head
+# ----------------------------------------------------------------------------
+def _bf16_bits_of(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_sample_decimal(O):
+    """Top-k, softmax and the inverse-CDF draw against an independent
+    evaluation: Python's sorted() for the order, e^x from the decimal module
+    at 50 digits for the probabilities, an explicit walk for the draw."""
+    import decimal
+    ctx = decimal.Context(prec=50)
+    rng = np.random.default_rng(21)
+    V, k, T = 97, 30, 0.8
+    for trial in range(12):
+        vals = np.round(rng.standard_normal(V) * 3, 1)
+        vals[rng.integers(0, V, 6)] = vals[0]                  # ties
+        bits = _bf16_bits_of(vals.tolist())
+        lv = [float(torch.tensor(int(b), dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float()) for b in bits]
+        order = sorted(range(V), key=lambda i: (-lv[i], i))[:k]
+        dT = decimal.Decimal(repr(T))
+        z = [ctx.divide(decimal.Decimal(repr(lv[i])), dT) for i in order]
+        e = [ctx.exp(ctx.subtract(zi, z[0])) for zi in z]
+        s = sum(e, decimal.Decimal(0))
+        p = [float(ctx.divide(ei, s)) for ei in e]
+        us = rng.uniform(0, 1, 5)
+        tok, idx, prob = O.sample_topk(np.stack([bits] * 5), T, k, us)
+        for r in range(5):
+            assert list(idx[r]) == order, (trial, r)
+            assert np.allclose(prob[r], p, rtol=1e-12, atol=0)
+            acc, want = decimal.Decimal(0), order[-1]
+            for i, ei in zip(order, e):
+                acc += ctx.divide(ei, s)
+                if acc > decimal.Decimal(repr(float(us[r]))):
+                    want = i
+                    break
+            assert tok[r] == want, (trial, r)
+
+
+def pin_sample_invariants(O):
+    """k = 1 is the argmax (lowest index among equals) with probability 1;
+    adding a constant to every logit (exactly) changes nothing; the draw is
+    monotone in u; u on an exact CDF boundary is not exceeded by it."""
+    rng = np.random.default_rng(22)
+    vals = rng.integers(-40, 40, size=(3, 200)).astype(np.float64)
+    vals[1, 17] = vals[1, 150] = vals[1].max() + 3                # a tie at the top
+    bits = _bf16_bits_of(vals.tolist())
+    tok, idx, prob = O.sample_topk(bits, 0.8, 1, [0.3, 0.9, 0.999])
+    assert list(tok) == [int(np.argmax(vals[m])) for m in range(3)] and tok[1] == 17
+    assert np.all(prob == 1.0)
+    shifted = _bf16_bits_of((vals + 64).tolist())
+    for u in ([0.1, 0.5, 0.9], [0.0, 0.7, 0.99]):
+        a = O.sample_topk(bits, 0.8, 30, u)
+        b = O.sample_topk(shifted, 0.8, 30, u)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.allclose(a[2], b[2], rtol=1e-12)
+    us = np.linspace(0, 0.999, 40)
+    toks, idxs, _ = O.sample_topk(np.stack([bits[0]] * 40), 0.8, 30, us)
+    pos = [list(idxs[i]).index(toks[i]) for i in range(40)]
+    assert pos == sorted(pos) and pos[0] == 0
+    # two equal logits well above the rest: p = 1/2 each (to 1e-30); u = 1/2 is not exceeded by
+    # the first cumulative probability, so the second is drawn
+    two = _bf16_bits_of([[0.0] * 10 + [100.0, 100.0]])
+    assert O.sample_topk(two, 1.0, 2, [0.5])[0][0] == 11
+    assert O.sample_topk(two, 1.0, 2, [0.49])[0][0] == 10
+
+
 ALL_PINS = [
     pin_nibble_hand,
     pin_nibble_roundtrip,
@@ -414,4 +481,6 @@ ALL_PINS = [
     pin_bf16_round_exact,
     pin_silu_mul_decimal,
     pin_residual_exact,
+    pin_sample_decimal,
+    pin_sample_invariants,
 ]

@@ -188,12 +188,55 @@ def _m_residual_transposed(O):
     O.gemv_residual_f64 = gemv_residual_f64
 
 
+def _sample_mutant(O, order_fn=None, temp=None, side="right", over_all=False):
+    def sample_topk(logit_bits, temperature, top_k, u):
+        lg = O.bf16_value(logit_bits)
+        lg = lg.reshape(-1, lg.shape[-1])
+        M, V = lg.shape
+        u = np.asarray(u, dtype=np.float64).reshape(M)
+        index = np.empty((M, top_k), np.int64)
+        prob = np.empty((M, top_k), np.float64)
+        token = np.empty(M, np.int64)
+        T = temperature if temp is None else temp
+        for m in range(M):
+            order = (order_fn or (lambda v: np.lexsort((np.arange(V), -v))))(lg[m])[:top_k]
+            z = lg[m, order] / T
+            e = np.exp(z - z[0])
+            tot = np.exp(lg[m] / T - z[0]).sum() if over_all else e.sum()
+            p = e / tot
+            pick = int(np.searchsorted(np.cumsum(p), u[m], side=side))
+            index[m], prob[m], token[m] = order, p, order[min(pick, top_k - 1)]
+        return token, index, prob
+    O.sample_topk = sample_topk
+
+
+def _m_sample_ties_high(O):
+    _sample_mutant(O, order_fn=lambda v: np.lexsort((-np.arange(v.size), -v)))
+
+
+def _m_sample_smallest(O):
+    _sample_mutant(O, order_fn=lambda v: np.lexsort((np.arange(v.size), v)))
+
+
+def _m_sample_no_temperature(O):
+    _sample_mutant(O, temp=1.0)
+
+
+def _m_sample_cdf_at_least(O):
+    _sample_mutant(O, side="left")
+
+
+def _m_sample_softmax_over_all(O):
+    _sample_mutant(O, over_all=True)
+
+
 MUTANTS = [
     _m_swap_nibbles, _m_drop_min, _m_negate_min, _m_group64, _m_group_index_mod,
     _m_fp16_bias, _m_fp16_ftz, _m_e4m3_bias8, _m_e4m3_no_nan, _m_e2m1_sub,
     _m_e2m1_nosign, _m_nvfp4_double_round, _m_gemv_drop_last_k, _m_gemv_transposed,
     _m_gemv_fp32, _m_bf16_bias, _m_round_truncate, _m_round_via_fp32, _m_round_ties_away, _m_silu_no_gate,
-    _m_silu_sign, _m_residual_transposed,
+    _m_silu_sign, _m_residual_transposed, _m_sample_ties_high, _m_sample_smallest, _m_sample_no_temperature,
+    _m_sample_cdf_at_least, _m_sample_softmax_over_all,
 ]
 
 
