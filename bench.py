@@ -324,6 +324,22 @@ def fused_calls(torch, q4, synth, wl, M):
     return rec
 
 
+def head_sample_calls(torch, q4, synth, M):
+    """Sampling from the head at temperature 0.8, top-k 30 (caller-supplied
+    uniforms): the 2049-row head GEMV alone, GEMV + sampling in one call, and
+    the sampler alone on 2049 and 16385 logits; microseconds per call."""
+    rec = {}
+    x = synth.x_bf16(M, 2048, ("bench-hs-x", M), device="cuda")
+    u = torch.rand(M, generator=torch.Generator(device="cuda").manual_seed(M), device="cuda")
+    for N in (2049, 16385):
+        w = synth.bf16_matrix(N, 2048, ("bench-hs-w", N), device="cuda")
+        lg = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        rec[f"head{N}"] = {"gemv_us": round(graph_us(torch, lambda: q4.bf16_gemv(x, w, out=lg)), 2),
+                           "gemv_and_sample_us": round(graph_us(torch, lambda: q4.bf16_head_sample(x, w, u, logits=lg)), 2),
+                           "sample_only_us": round(graph_us(torch, lambda: q4.sample_topk(lg, u)), 2)}
+    return rec
+
+
 def read_ceiling(torch, q4, wl, steps, warmup):
     """Plain-read reference for the M=1 grouped step: the same 73 launches,
     each replaced by the library's diagnostic stream_read over exactly the
@@ -656,6 +672,10 @@ def main():
     for k, r in fz.items():
         log(f"bench: fused calls {k}: " + ", ".join(f"{n} fused {v['fused_us']} us / unfused {v['unfused_us']} us / "
                                                      f"plain GEMV {v['plain_gemv_us']} us" for n, v in r.items()))
+    hs = {f"M{M}": head_sample_calls(torch, q4, synth, M) for M in (1, 48)}
+    for k, r in hs.items():
+        log(f"bench: head + top-k sampling {k}: " + ", ".join(f"{n}: GEMV {v['gemv_us']} us, GEMV+sample {v['gemv_and_sample_us']} us, "
+                                                              f"sample alone {v['sample_only_us']} us" for n, v in r.items()))
     head = res[(1, "grouped")]
     wbytes = weight_bytes(wl)
     ceil_ms = read_ceiling(torch, q4, wl, args.steps, args.warmup)
@@ -690,6 +710,7 @@ def main():
                              "pct_of_8TBps": round(100 * ceil_gbs / PEAK_GBS, 2)},
             "modes": {mode_key(k): mode_record(k, r, wbytes, ceil_ms) for k, r in res.items()},
             "fused_calls": fz,
+            "head_sample": hs,
         },
         "roofline": roof[1],
     }

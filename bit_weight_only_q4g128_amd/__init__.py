@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
     "nvfp4g16_gemv_grouped", "nvfp4g16_workspace_bytes", "bf16_gemv_grouped", "bf16_workspace_bytes",
-    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes",
+    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
     "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
@@ -94,6 +94,12 @@ lib.q4g128_gemv_fused.argtypes = [ctypes.POINTER(FusedTask), _i, _i, _p, ctypes.
 lib.q4g128_gemv_fused.restype = ctypes.c_int
 lib.q4g128_fused_workspace_bytes.argtypes = [ctypes.POINTER(FusedTask), _i, _i, ctypes.POINTER(ctypes.c_size_t)]
 lib.q4g128_fused_workspace_bytes.restype = ctypes.c_int
+
+
+lib.q4_sample_topk.argtypes = [_p, _i, _i, _f, _i, _p, _p, _p, _p, _p]
+lib.q4_sample_topk.restype = ctypes.c_int
+lib.bf16_head_sample.argtypes = [_p, _i, _i, _p, _i, _p, _f, _i, _p, _p, _p, _p, _p]
+lib.bf16_head_sample.restype = ctypes.c_int
 
 
 class Q4GemvError(ValueError):
@@ -423,3 +429,43 @@ def q4g128_fused_workspace_bytes(items) -> int:
     n = ctypes.c_size_t(0)
     _raise(lib.q4g128_fused_workspace_bytes(arr, len(items), M, ctypes.byref(n)))
     return int(n.value)
+
+
+def _sample_outputs(M, top_k, like, want_topk):
+    tok = torch.empty(M, dtype=torch.int32, device=like.device)
+    if not want_topk:
+        return tok, None, None
+    return (tok, torch.empty((M, top_k), dtype=torch.int32, device=like.device),
+            torch.empty((M, top_k), dtype=torch.float32, device=like.device))
+
+
+def sample_topk(logits, u, temperature: float = 0.8, top_k: int = 30, return_topk: bool = False):
+    """Top-k sampling from BF16 logits [M, V] with the caller's uniforms u
+    (fp32 [M], in [0, 1)): returns token int32 [M], and with return_topk also
+    the top-k indices int32 [M, k] and probabilities fp32 [M, k]."""
+    _check(logits, "logits", _U16, 2); _check(u, "u", (torch.float32,), 1)
+    M, V = logits.shape
+    if u.shape[0] != M:
+        raise ValueError("u must hold one draw per batch row")
+    tok, ti, tp = _sample_outputs(M, top_k, logits, return_topk)
+    _raise(lib.q4_sample_topk(logits.data_ptr(), M, V, float(temperature), int(top_k), u.data_ptr(), tok.data_ptr(),
+                              ti.data_ptr() if ti is not None else None, tp.data_ptr() if tp is not None else None,
+                              _stream(logits)))
+    return (tok, ti, tp) if return_topk else tok
+
+
+def bf16_head_sample(x, w, u, temperature: float = 0.8, top_k: int = 30, logits=None, return_topk: bool = False):
+    """The BF16 head GEMV logits = x W^T followed by top-k sampling (two
+    launches).  Returns (token, logits) or (token, topk_index, topk_prob,
+    logits) with return_topk."""
+    _check(x, "x", _U16, 2); _check(w, "w", _U16, 2); _check(u, "u", (torch.float32,), 1)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or u.shape[0] != M:
+        raise ValueError("inconsistent shapes")
+    lg = _out(logits, (M, N), torch.bfloat16, x)
+    tok, ti, tp = _sample_outputs(M, top_k, x, return_topk)
+    _raise(lib.bf16_head_sample(x.data_ptr(), M, K, w.data_ptr(), N, lg.data_ptr(), float(temperature), int(top_k), u.data_ptr(),
+                                tok.data_ptr(), ti.data_ptr() if ti is not None else None, tp.data_ptr() if tp is not None else None,
+                                _stream(x)))
+    return (tok, ti, tp, lg) if return_topk else (tok, lg)

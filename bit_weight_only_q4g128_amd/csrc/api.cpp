@@ -210,6 +210,30 @@ int check_fused(const q4g128_fused_task* tasks, int count, int M, bool split, Ge
     return Q4_OK;
 }
 
+// Sampler arguments; `extra` are further input ranges the outputs must avoid.
+int check_sample(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, const int32_t* token,
+                 const int32_t* topk_index, const float* topk_prob, const Range* extra, int n_extra) {
+    if (!logits || !u || !token) return Q4_EINVAL_PTR;
+    if (M < 1 || M > 65535 || V < 1 || V > q4::kMaxVocab || top_k < 1 || top_k > q4::kMaxTopK || top_k > V)
+        return Q4_EINVAL_SHAPE;
+    if (!(temperature > 0.f) || !(temperature < __builtin_huge_valf())) return Q4_EINVAL_SHAPE;
+    if (!aligned(logits, 2) || !aligned(u, 4) || !aligned(token, 4) || (topk_index && !aligned(topk_index, 4)) ||
+        (topk_prob && !aligned(topk_prob, 4)))
+        return Q4_EALIGN;
+    const Range outs[3] = {range_of(token, (size_t)M * 4), topk_index ? range_of(topk_index, (size_t)M * top_k * 4) : Range{0, 0},
+                           topk_prob ? range_of(topk_prob, (size_t)M * top_k * 4) : Range{0, 0}};
+    const Range ins[2] = {range_of(logits, (size_t)M * V * 2), range_of(u, (size_t)M * 4)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 2; ++j)
+            if (overlaps(outs[i], ins[j])) return Q4_EALIAS;
+        for (int j = 0; j < n_extra; ++j)
+            if (overlaps(outs[i], extra[j])) return Q4_EALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], outs[j])) return Q4_EALIAS;
+    }
+    return Q4_OK;
+}
+
 }  // namespace
 
 namespace q4 {
@@ -489,6 +513,34 @@ int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int 
     const size_t h_bytes = fused_h_bytes(a, count);
     *bytes = (h_bytes ? align256(q4::mm_workspace_bytes(q4::kFmtQ4, a, count)) : q4::mm_workspace_bytes(q4::kFmtQ4, a, count)) + h_bytes;
     return Q4_OK;
+}
+
+int q4_sample_topk(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, int32_t* token,
+                   int32_t* topk_index, float* topk_prob, void* stream) {
+    int rc = check_sample(logits, M, V, temperature, top_k, u, token, topk_index, topk_prob, nullptr, 0);
+    if (rc) return rc;
+    hipError_t e = q4::launch_topk_sample(logits, M, V, temperature, top_k, u, token, topk_index, topk_prob,
+                                          reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
+int bf16_head_sample(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* logits, float temperature, int top_k,
+                     const float* u, int32_t* token, int32_t* topk_index, float* topk_prob, void* stream) {
+    GemvArgs a;
+    Range in[4], out;
+    int rc = check_bf(x, M, K, w, N, logits, a, in, out);
+    if (rc) return rc;
+    for (int r = 0; r < 2; ++r)
+        if (overlaps(out, in[r])) return Q4_EALIAS;
+    rc = check_sample(logits, M, N, temperature, top_k, u, token, topk_index, topk_prob, in, 2);
+    if (rc) return rc;
+    const int chosen = pick(q4::kFmtBf16, Q4_VARIANT_AUTO, M, N, K);
+    if (chosen < 0) return Q4_EVARIANT;
+    rc = run(q4::kFmtBf16, chosen, a, stream);
+    if (rc) return rc;
+    hipError_t e = q4::launch_topk_sample(logits, M, N, temperature, top_k, u, token, topk_index, topk_prob,
+                                          reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 
 size_t q4gemv_stream_read_sink_words(const size_t* bytes, int count) {

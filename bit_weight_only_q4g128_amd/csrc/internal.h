@@ -71,6 +71,13 @@ hipError_t launch_mm_fused(const GemvArgs* tasks, int count, void* ws, size_t ws
 hipError_t launch_silu_mul(const uint16_t* const* g, const uint16_t* const* u, uint16_t* const* h, const size_t* values, int count,
                            hipStream_t s);
 
+// Top-k sampling from BF16 logits [M, V], one workgroup per row (see
+// sample.hip); 1 <= top_k <= min(kMaxTopK, V), V <= kMaxVocab.
+constexpr int kMaxTopK = 64;
+constexpr int kMaxVocab = 30720;
+hipError_t launch_topk_sample(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, int32_t* token,
+                              int32_t* topk_index, float* topk_prob, hipStream_t s);
+
 // 16x16x32 BF16 matrix-core GEMV (any M <= 64), one launch per task.
 hipError_t launch_mfma(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
 

@@ -1,0 +1,196 @@
+// Top-k sampling from BF16 logits (the step after the head GEMV): the
+// Rumik TTS Fast Inference post samples audio tokens at temperature 0.8 with
+// top-k 30 ("The Result") from the head restricted to the current codebook
+// ("What Made It Faster").
+//
+// One workgroup per batch row:
+//   1. the row's logits go to LDS as order-preserving 16-bit keys (-0 taken
+//      as +0, so equal values tie);
+//   2. a two-pass 8-bit radix select finds the k-th largest key T;
+//   3. the keys above T are gathered, then the keys equal to T in index
+//      order (a block-wide prefix count) until there are k;
+//   4. one wave sorts the k entries by (logit descending, index ascending)
+//      with a bitonic network over its lanes;
+//   5. the lanes form e_i = exp(z_i - z_0), z = logit / T, and sum them in
+//      that order; the token is the first entry whose running sum exceeds
+//      u * S, and p_i = e_i / S.
+#include "internal.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t order_key(uint32_t bits) {
+    if (bits == 0x8000u) bits = 0;                      // -0 ties with +0
+    return (bits & 0x8000u) ? (~bits & 0xFFFFu) : (bits | 0x8000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+    const uint32_t bits = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+    return __builtin_bit_cast(float, bits << 16);
+}
+
+// Wave 0: the bin b (counting down from bin 255) where the running count
+// first reaches k; writes b and how many of bin b are still wanted.  Lane l
+// holds bins 4l .. 4l + 3; a shuffle suffix sum gives the count above its
+// bins, and the one lane whose bins cross k reports.
+__device__ void find_bin(const unsigned* hist, int k, int lane, int* s_bin, int* s_need) {
+    unsigned h[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = hist[4 * lane + j];
+    const unsigned mine = h[0] + h[1] + h[2] + h[3];
+    unsigned suf = mine;                                  // sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned o = __shfl_down(suf, off);
+        if (lane + off < 64) suf += o;
+    }
+    unsigned cum = suf - mine;                            // count in the bins above this lane's
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+        if (cum < (unsigned)k && cum + h[j] >= (unsigned)k) {
+            *s_bin = 4 * lane + j;
+            *s_need = k - (int)cum;
+        }
+        cum += h[j];
+    }
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ unsigned wave_scan(unsigned v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_sample_kernel(const uint16_t* __restrict__ logits, int V, float temperature, int k,
+                                                               const float* __restrict__ u, int32_t* __restrict__ token,
+                                                               int32_t* __restrict__ topk_index, float* __restrict__ topk_prob) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint16_t* keys = reinterpret_cast<uint16_t*>(lds);            // [V]
+    __shared__ unsigned hist[256];
+    __shared__ unsigned wsum[kThreads / 64];
+    __shared__ uint32_t list[64];
+    __shared__ int s_n, s_bin, s_need;
+
+    const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t* row = logits + (size_t)m * V;
+    const float um = u[m];                                        // loaded with the logits, used at the end
+
+    // logits to LDS keys, 16 independent loads in flight per thread
+    constexpr int kBatch = 16;
+    for (int i0 = tid; i0 < V; i0 += kBatch * kThreads) {
+        uint16_t v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int i = i0 + j * kThreads;
+            v[j] = i < V ? row[i] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int i = i0 + j * kThreads;
+            if (i < V) keys[i] = (uint16_t)order_key(v[j]);
+        }
+    }
+    hist[tid] = 0;
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+
+    // 2. radix select: high byte, then low byte within the chosen high byte
+    for (int i = tid; i < V; i += kThreads) atomicAdd(&hist[keys[i] >> 8], 1u);
+    __syncthreads();
+    if (wave == 0) find_bin(hist, k, lane, &s_bin, &s_need);
+    __syncthreads();
+    const int hi = s_bin, need_hi = s_need;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < V; i += kThreads)
+        if ((keys[i] >> 8) == hi) atomicAdd(&hist[keys[i] & 0xFF], 1u);
+    __syncthreads();
+    if (wave == 0) find_bin(hist, need_hi, lane, &s_bin, &s_need);
+    __syncthreads();
+    const uint32_t thr = ((uint32_t)hi << 8) | (uint32_t)s_bin;
+    const int need_eq = s_need;                                   // entries equal to thr to take
+
+    // 3. gather: contiguous index ranges per thread, so that equal keys can be
+    // ranked in index order by a prefix count over the threads
+    const int per = (V + kThreads - 1) / kThreads;
+    const int i0 = tid * per, i1 = (i0 + per < V) ? i0 + per : V;
+    unsigned n_eq = 0;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t key = keys[i];
+        if (key > thr) {
+            const int slot = atomicAdd(&s_n, 1);
+            list[slot] = (key << 16) | (0xFFFFu - (uint32_t)i);
+        }
+        n_eq += key == thr ? 1u : 0u;
+    }
+    const unsigned incl = wave_scan(n_eq, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    unsigned rank = incl - n_eq;                                  // equal keys before this thread's range
+    for (int w = 0; w < wave; ++w) rank += wsum[w];
+    const int n_gt = k - need_eq;
+    for (int i = i0; i < i1 && (int)rank < need_eq; ++i) {
+        if (keys[i] == thr) {
+            list[n_gt + rank] = (thr << 16) | (0xFFFFu - (uint32_t)i);
+            ++rank;
+        }
+    }
+    __syncthreads();
+
+    // 4. sort the k entries descending on (key, -index) in wave 0; an entry
+    // is key << 16 | (0xFFFF - index) (V <= 30720 fits 16 bits)
+    if (wave == 0) {
+        uint32_t v = lane < k ? list[lane] : 0u;                 // padding sorts last
+        for (int size = 2; size <= 64; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const uint32_t o = __shfl_xor(v, stride);
+                const bool up = ((lane & size) == 0);            // this half of the sequence descends
+                const bool lower = (lane & stride) == 0;
+                const bool keep_max = (up == lower);
+                v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+            }
+        }
+        // 5. probabilities and the draw: e_i in lane i; the sums run in entry
+        // order, one lane value at a time, identically on every lane
+        const float z = key_value(v >> 16) / temperature;
+        const float z0 = __shfl(z, 0);
+        const float e = lane < k ? expf(z - z0) : 0.f;
+        const int eb = __builtin_bit_cast(int, e);
+        float S = 0.f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i)
+            if (i < k) S += __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, i));
+        const float target = um * S;
+        int pick = k - 1;
+        float c = 0.f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+            if (i < k) {
+                c += __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, i));
+                if (c > target && pick == k - 1 && i < k - 1) pick = i;
+            }
+        }
+        const int index = (int)(0xFFFFu - (v & 0xFFFFu));
+        if (lane == pick) token[m] = index;
+        if (lane < k) {
+            if (topk_index) topk_index[(size_t)m * k + lane] = index;
+            if (topk_prob) topk_prob[(size_t)m * k + lane] = e / S;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk_sample(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, int32_t* token,
+                              int32_t* topk_index, float* topk_prob, hipStream_t s) {
+    return launch_kernel(topk_sample_kernel, dim3(M), dim3(kThreads), (size_t)V * 2, s, logits, V, temperature, top_k, u, token,
+                         topk_index, topk_prob);
+}
+
+}  // namespace q4

@@ -243,6 +243,36 @@ int q4g128_gemv_fused(const q4g128_fused_task* tasks, int count, int M, void* wo
 int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int M, size_t* bytes);
 
 /*
+ * Sampling from the head: the step after the path.  The Rumik TTS Fast
+ * Inference post samples each audio token at temperature 0.8 with top-k 30
+ * ("The Result") from the head restricted to the current codebook, 2049 rows
+ * ("What Made It Faster").  Per batch row m of BF16 logits [M, V]:
+ *   1. the top_k largest logits, equal logits ordered by lower index (-0 and
+ *      +0 are equal), in order of (logit descending, index ascending);
+ *   2. p_i = softmax(logit_i / temperature) over those top_k, in fp32;
+ *   3. token[m] = the first of that order whose running sum of p exceeds
+ *      u[m] (the caller's uniform draw in [0, 1); the library draws no
+ *      random numbers).
+ * Outputs: token [M] int32; optionally topk_index [M, top_k] int32 and
+ * topk_prob [M, top_k] fp32 (NULL to skip).  1 <= top_k <= 64 and
+ * top_k <= V <= 30720; temperature finite and > 0; logits must hold no NaN.
+ * The selection is exact; the probabilities and the draw are fp32 (a draw
+ * can differ from exact arithmetic only when u lies within fp32 rounding of a
+ * cumulative boundary).  Alignment: logits 2 bytes, u and the outputs 4 bytes;
+ * outputs must not overlap each other or the inputs.
+ *
+ * q4_sample_topk samples from logits already in memory (one launch);
+ * bf16_head_sample runs the BF16 head GEMV logits = x W^T (the bf16_gemv
+ * rules, N = V; logits is the caller's [M, N] buffer) and then samples (two
+ * launches).  Both return Q4_EINVAL_PTR / Q4_EINVAL_SHAPE / Q4_EALIGN /
+ * Q4_EALIAS before enqueueing anything, Q4_ELAUNCH on a launch failure.
+ */
+int q4_sample_topk(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, int32_t* token,
+                   int32_t* topk_index, float* topk_prob, void* stream);
+int bf16_head_sample(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* logits, float temperature, int top_k,
+                     const float* u, int32_t* token, int32_t* topk_index, float* topk_prob, void* stream);
+
+/*
  * Diagnostic dequantization of a whole matrix to fp32 w [N, K] (16-byte
  * aligned).  Bitwise equal to the format definitions above: int4 rounds
  * code*scale+min once; NVFP4 rounds e2m1*e4m3*G once (the first product is

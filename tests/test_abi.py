@@ -238,6 +238,35 @@ def test_fused_validation():
     assert call([ft(0, K=32768, N=64)], M=64) == EVARIANT               # unsplit tiled kernel: too many groups
 
 
+def test_sample_validation():
+    """q4_sample_topk / bf16_head_sample reject bad arguments before any launch."""
+    L, U, T = A, A + (1 << 26), A + (2 << 26)          # logits, u, token
+    TI, TP = A + (3 << 26), A + (4 << 26)
+    f = ctypes.c_float
+
+    def s(logits=L, M=1, V=2049, temp=0.8, k=30, u=U, tok=T, ti=TI, tp=TP):
+        return lib.q4_sample_topk(logits, M, V, f(temp), k, u, tok, ti, tp, None)
+
+    assert s(logits=None) == EPTR and s(u=None) == EPTR and s(tok=None) == EPTR
+    for kw in (dict(M=0), dict(V=0), dict(V=30721), dict(k=0), dict(k=65), dict(V=20, k=21), dict(temp=0.0), dict(temp=-1.0),
+               dict(temp=float("inf")), dict(temp=float("nan"))):
+        assert s(**kw) == ESHAPE, kw
+    assert s(logits=L + 1) == EALIGN and s(u=U + 2) == EALIGN and s(tok=T + 2) == EALIGN and s(tp=TP + 2) == EALIGN
+    assert s(tok=L + 64) == EALIAS            # token over the logits
+    assert s(ti=U) == EALIAS                  # indices over the draws
+    assert s(tp=T) == EALIAS                  # probabilities over the tokens
+    X, W, LG = A + (5 << 29), A + (6 << 29), A + (7 << 29)   # far apart: a 40000 x 2048 weight spans 164 MB
+
+    def h(x=X, w=W, lg=LG, tok=T, ti=None, tp=None, M=1, K=2048, N=2049, k=30):
+        return lib.bf16_head_sample(x, M, K, w, N, lg, f(0.8), k, U, tok, ti, tp, None)
+
+    assert h(x=None) == EPTR and h(lg=None) == EPTR
+    assert h(M=0) == ESHAPE and h(K=12) == ESHAPE and h(N=40000) == ESHAPE
+    assert h(lg=W + 64) == EALIAS             # logits over the weights
+    assert h(tok=X) == EALIAS                 # token over the activations
+    assert h(ti=W + 128) == EALIAS
+
+
 def test_stream_read_validation():
     import ctypes
     lib.q4gemv_stream_read.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
