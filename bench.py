@@ -340,6 +340,27 @@ def head_sample_calls(torch, q4, synth, M):
     return rec
 
 
+def prefill_calls(torch, q4, synth):
+    """The int4 prefill GEMM (q4g128_gemm) on the layer's projection shapes at
+    M = 1024 and 4096 tokens: microseconds and TFLOP/s against the 2.5 PFLOP/s
+    dense BF16 matrix-core peak, beside torch's BF16 GEMM (the vendor library)
+    on weights dequantized to BF16 beforehand."""
+    rec = {}
+    for (N, K) in ((2048, 2048), (8192, 2048), (2048, 8192)):
+        qd = tuple(t.cuda() for t in synth.q4_matrix(N, K, ("bench-prefill", N, K)))
+        wd = q4.q4g128_dequant_f32(*qd).to(torch.bfloat16)
+        for M in (1024, 4096):
+            x = synth.x_bf16(M, K, ("bench-prefill-x", M, K), device="cuda")
+            y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            us = graph_us(torch, lambda: q4.q4g128_gemm(x, *qd, out=y), reps=5, iters=10)
+            ub = graph_us(torch, lambda: torch.matmul(x, wd.t(), out=y), reps=5, iters=10)
+            fl = 2.0 * M * N * K
+            rec[f"N{N}_K{K}_M{M}"] = {"int4_us": round(us, 1), "int4_TFLOP_s": round(fl / us / 1e6, 1),
+                                      "frac_of_bf16_mfma_peak": round(fl / us / 1e6 / 2500.0, 3),
+                                      "bf16_library_on_dequantized_us": round(ub, 1)}
+    return rec
+
+
 def read_ceiling(torch, q4, wl, steps, warmup):
     """Plain-read reference for the M=1 grouped step: the same 73 launches,
     each replaced by the library's diagnostic stream_read over exactly the
@@ -676,6 +697,9 @@ def main():
     for k, r in hs.items():
         log(f"bench: head + top-k sampling {k}: " + ", ".join(f"{n}: GEMV {v['gemv_us']} us, GEMV+sample {v['gemv_and_sample_us']} us, "
                                                               f"sample alone {v['sample_only_us']} us" for n, v in r.items()))
+    pf = prefill_calls(torch, q4, synth)
+    log("bench: int4 prefill GEMM: " + ", ".join(f"{k} {v['int4_us']} us ({v['int4_TFLOP_s']} TFLOP/s; BF16 library on dequantized "
+                                                  f"weights {v['bf16_library_on_dequantized_us']} us)" for k, v in pf.items()))
     head = res[(1, "grouped")]
     wbytes = weight_bytes(wl)
     ceil_ms = read_ceiling(torch, q4, wl, args.steps, args.warmup)
@@ -711,6 +735,7 @@ def main():
             "modes": {mode_key(k): mode_record(k, r, wbytes, ceil_ms) for k, r in res.items()},
             "fused_calls": fz,
             "head_sample": hs,
+            "prefill": pf,
         },
         "roofline": roof[1],
     }

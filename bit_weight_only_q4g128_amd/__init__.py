@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
     "nvfp4g16_gemv_grouped", "nvfp4g16_workspace_bytes", "bf16_gemv_grouped", "bf16_workspace_bytes",
-    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample",
+    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample", "q4g128_gemm",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
     "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
@@ -96,6 +96,8 @@ lib.q4g128_fused_workspace_bytes.argtypes = [ctypes.POINTER(FusedTask), _i, _i, 
 lib.q4g128_fused_workspace_bytes.restype = ctypes.c_int
 
 
+lib.q4g128_gemm.argtypes = [_p, _i, _i, _p, _p, _p, _i, _p, _p]
+lib.q4g128_gemm.restype = ctypes.c_int
 lib.q4_sample_topk.argtypes = [_p, _i, _i, _f, _i, _p, _p, _p, _p, _p]
 lib.q4_sample_topk.restype = ctypes.c_int
 lib.bf16_head_sample.argtypes = [_p, _i, _i, _p, _i, _p, _f, _i, _p, _p, _p, _p, _p]
@@ -469,3 +471,17 @@ def bf16_head_sample(x, w, u, temperature: float = 0.8, top_k: int = 30, logits=
                                 tok.data_ptr(), ti.data_ptr() if ti is not None else None, tp.data_ptr() if tp is not None else None,
                                 _stream(x)))
     return (tok, ti, tp, lg) if return_topk else (tok, lg)
+
+
+def q4g128_gemm(x, qweight, scale, minv, out=None):
+    """Prefill GEMM y[M, N] = x[M, K] . W^T for int4 g128 weights, any M
+    (q4g128_gemm in the C header)."""
+    _check(x, "x", _U16, 2); _check(qweight, "qweight", _U8, 2)
+    _check(scale, "scale", _F16, 2); _check(minv, "min", _F16, 2)
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 2 != K or tuple(scale.shape) != (N, K // 128) or tuple(minv.shape) != (N, K // 128):
+        raise ValueError("inconsistent shapes")
+    y = _out(out, (M, N), torch.bfloat16, x)
+    _raise(lib.q4g128_gemm(x.data_ptr(), M, K, qweight.data_ptr(), scale.data_ptr(), minv.data_ptr(), N, y.data_ptr(), _stream(x)))
+    return y

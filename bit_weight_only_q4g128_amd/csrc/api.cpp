@@ -515,6 +515,24 @@ int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int 
     return Q4_OK;
 }
 
+int q4g128_gemm(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
+                uint16_t* y, void* stream) {
+    if (M >= 1 && M <= kMaxM) return q4g128_gemv_variant(x, M, K, qweight, scale, minv, N, y, Q4_VARIANT_AUTO, stream);
+    if (M < 1 || M > (1 << 19)) return Q4_EINVAL_SHAPE;
+    GemvArgs a;
+    Range in[4], out;
+    int rc = check_q4(x, 1, K, qweight, scale, minv, N, y, a, in, out);   // pointers, K, N, alignment
+    if (rc) return rc;
+    in[0] = range_of(x, (size_t)M * K * 2);
+    out = range_of(y, (size_t)M * N * 2);
+    for (int r = 0; r < 4; ++r)
+        if (overlaps(out, in[r])) return Q4_EALIAS;
+    if (!q4::mm_chunks_supported(K)) return Q4_EVARIANT;
+    a.M = M;
+    hipError_t e = q4::launch_mm_chunks(a, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
 int q4_sample_topk(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, int32_t* token,
                    int32_t* topk_index, float* topk_prob, void* stream) {
     int rc = check_sample(logits, M, V, temperature, top_k, u, token, topk_index, topk_prob, nullptr, 0);

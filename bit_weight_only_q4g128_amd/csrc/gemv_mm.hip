@@ -192,7 +192,21 @@ __device__ __forceinline__ void write_y(const GemvArgs& a, bool y8, float gs, in
     write_y_tile<MT, kFused>(a, y8, gs, prow0 + 16, lane, v[1]);
 }
 
-template <class F, int MT, bool kFused = false>
+// Batch chunking (kChunks, one unsplit task): block row y of the grid takes
+// batch rows [16 MT y, 16 MT (y + 1)) -- the prefill GEMM, M in the hundreds or
+// thousands, as independent 16 MT-row products over the same weights.
+template <bool kChunks, int MT>
+__device__ __forceinline__ GemvArgs chunk_args(GemvArgs a) {
+    if constexpr (kChunks) {
+        const int m0 = (int)blockIdx.y * 16 * MT;
+        a.x += (size_t)m0 * a.K;
+        a.y += (size_t)m0 * a.N;
+        a.M = a.M - m0 < 16 * MT ? a.M - m0 : 16 * MT;
+    }
+    return a;
+}
+
+template <class F, int MT, bool kFused = false, bool kChunks = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves_f<MT, kFused>()))) void tiled_mm_kernel(MmTable tt) {
     constexpr int kPre = MmFmt<F>::kPre;
     constexpr int kLoads = MmFmt<F>::kLoads;
@@ -204,7 +218,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
     int ti = 0;
 #pragma unroll
     for (int i = 1; i < kMaxTasks; ++i) ti += ((int)blockIdx.x >= tt.blk0[i]) ? 1 : 0;
-    const GemvArgs a = tt.t[ti].a;
+    const GemvArgs a = chunk_args<kChunks, MT>(tt.t[ti].a);
     const int KS = tt.t[ti].ks, gps = tt.t[ti].gps;
     const int local = blockIdx.x - tt.blk0[ti];
     const int blk = local / KS, ks = local - blk * KS;
@@ -726,6 +740,22 @@ size_t ws_bytes_mt(const GemvArgs* tasks, int count) {
     return (part > 0 && cnt <= kCntBytes) ? kCntBytes + part : 0;
 }
 
+// The task's int4 group-parameter load width (smw) and output store width (y8).
+template <class F>
+void fill_flags(MmTask& tk, const GemvArgs& a, int gps) {
+    const int G = a.K >> 7;
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(a.scale), ma = reinterpret_cast<uintptr_t>(a.minv);
+    if (!is_q4<F>())
+        tk.smw = 0;
+    else if (G % 8 == 0 && gps % 8 == 0 && gps <= 64 && sa % 16 == 0 && ma % 16 == 0)
+        tk.smw = 8;
+    else if (G % 4 == 0 && gps % 4 == 0 && gps <= 32 && sa % 8 == 0 && ma % 8 == 0)
+        tk.smw = 4;
+    else
+        tk.smw = 0;
+    tk.y8 = (reinterpret_cast<uintptr_t>(a.y) % 8 == 0 && a.N % 4 == 0) ? 1 : 0;
+}
+
 template <class F, int MT, bool kFused = false>
 hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t st) {
     int ks[kMaxTasks], gps[kMaxTasks];
@@ -752,17 +782,7 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         tt.t[j].a = tasks[i];
         tt.t[j].ks = ks[i];
         tt.t[j].gps = gps[i];
-        const int G = tasks[i].K >> 7;
-        const uintptr_t sa = reinterpret_cast<uintptr_t>(tasks[i].scale), ma = reinterpret_cast<uintptr_t>(tasks[i].minv);
-        if (!is_q4<F>())
-            tt.t[j].smw = 0;
-        else if (G % 8 == 0 && gps[i] % 8 == 0 && gps[i] <= 64 && sa % 16 == 0 && ma % 16 == 0)
-            tt.t[j].smw = 8;
-        else if (G % 4 == 0 && gps[i] % 4 == 0 && gps[i] <= 32 && sa % 8 == 0 && ma % 8 == 0)
-            tt.t[j].smw = 4;
-        else
-            tt.t[j].smw = 0;
-        tt.t[j].y8 = (reinterpret_cast<uintptr_t>(tasks[i].y) % 8 == 0 && tasks[i].N % 4 == 0) ? 1 : 0;
+        fill_flags<F>(tt.t[j], tasks[i], gps[i]);
         if (ks[i] > 1) {
             tt.t[j].cnt = reinterpret_cast<unsigned*>(pc);
             pc += (size_t)blocks * 4;
@@ -839,6 +859,47 @@ hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t
 
 hipError_t launch_mm_fused(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
     return launch_mm_f<FmtQ4, true>(tasks, count, ws, ws_bytes, s);
+}
+
+namespace {
+
+template <int MT>
+hipError_t launch_chunks_mt(const GemvArgs& a, hipStream_t st) {
+    MmTable tt{};
+    for (int i = 0; i < kMaxTasks; ++i) tt.blk0[i] = 0x7fffffff;
+    const int G = a.K >> 7;
+    tt.blk0[0] = 0;
+    tt.t[0].a = a;
+    tt.t[0].ks = 1;
+    tt.t[0].gps = G;
+    fill_flags<FmtQ4>(tt.t[0], a, G);
+    const dim3 grid((a.N + kRows - 1) / kRows, (a.M + 16 * MT - 1) / (16 * MT));
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(tiled_mm_kernel<FmtQ4, MT, false, true>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
+    if (attr != hipSuccess) return attr;
+    return launch_kernel(tiled_mm_kernel<FmtQ4, MT, false, true>, grid, dim3(kThreads), (size_t)mm_shmem<FmtQ4, MT>(G), st, tt);
+}
+
+// widest batch chunk whose group parameters fit LDS unsplit (0: none)
+int chunk_mt(int K) {
+    const int G = K >> 7;
+    if (K % 128) return 0;
+    if (G <= mm_max_gps<FmtQ4, 4>()) return 4;
+    if (G <= mm_max_gps<FmtQ4, 2>()) return 2;
+    if (G <= mm_max_gps<FmtQ4, 1>()) return 1;
+    return 0;
+}
+
+}  // namespace
+
+bool mm_chunks_supported(int K) { return chunk_mt(K) > 0; }
+
+hipError_t launch_mm_chunks(const GemvArgs& a, hipStream_t s) {
+    switch (chunk_mt(a.K)) {
+        case 4: return launch_chunks_mt<4>(a, s);
+        case 2: return launch_chunks_mt<2>(a, s);
+        default: return launch_chunks_mt<1>(a, s);
+    }
 }
 
 }  // namespace q4

@@ -62,6 +62,11 @@ hipError_t launch_stream_fused(const GemvArgs* tasks, int count, hipStream_t s);
 bool mm_supported(Fmt fmt, int M, int K, bool split);
 size_t mm_workspace_bytes(Fmt fmt, const GemvArgs* tasks, int count);
 hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
+// Prefill GEMM: the int4 tiled kernel over batch chunks of up to 64 rows
+// (grid rows), for any M, unsplit; K % 128 == 0 and the K's group
+// parameters within the kernel's LDS budget (K <= 16384).
+bool mm_chunks_supported(int K);
+hipError_t launch_mm_chunks(const GemvArgs& a, hipStream_t s);
 // The int4 tiled kernel with the fused activation prologue and residual
 // epilogue (GemvArgs::up, GemvArgs::resid; either may be null).
 hipError_t launch_mm_fused(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);

@@ -243,6 +243,21 @@ int q4g128_gemv_fused(const q4g128_fused_task* tasks, int count, int M, void* wo
 int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int M, size_t* bytes);
 
 /*
+ * Prefill GEMM: y[M, N] = x[M, K] . W^T for int4 g128 weights and any M >= 1
+ * (the prompt's tokens before the decode loop; the rumik-oss-1-int4 card's
+ * engine lists a 4-bit prefill matrix multiply beside its decode kernels,
+ * "Running it").  M <= 64 takes
+ * the q4g128_gemv choice; larger M runs the tiled matrix-core kernel over
+ * batch chunks of up to 64 rows in one launch, every chunk an unsplit
+ * product over the same weights (which stay in the memory-side cache across
+ * chunks).  Same layouts and rules as q4g128_gemv, with 1 <= M <= 524288;
+ * for M > 64, K % 128 == 0 and K <= 16384 (else Q4_EVARIANT; chunks of 64
+ * rows up to K = 4096, 32 rows up to 12288, 16 rows up to 16384).
+ */
+int q4g128_gemm(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
+                uint16_t* y, void* stream);
+
+/*
  * Sampling from the head: the step after the path.  The Rumik TTS Fast
  * Inference post samples each audio token at temperature 0.8 with top-k 30
  * ("The Result") from the head restricted to the current codebook, 2049 rows

@@ -1,0 +1,66 @@
+"""GPU parity of the int4 prefill GEMM (q4g128_gemm through the C ABI).
+
+Against the oracle within gpu_util.check_gemv's tolerance for M from 65 to
+517 (ragged last chunks) and the layer's K values; bitwise against the
+tiled decode kernel run on each batch chunk alone (the same arithmetic per
+chunk); M <= 64 equals the GEMV's automatic choice.
+"""
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_gemv, gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q4():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_weight_only_q4g128_amd as m
+    return m
+
+
+def mat(N, K, seed):
+    qw, sc, mn = synth.q4_matrix(N, K, seed)
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    return (gpu(qw), gpu(sc), gpu(mn)), w32
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 2048, 2048), (128, 300, 2048), (200, 2048, 8192), (517, 1000, 4096), (257, 130, 8192)])
+def test_gemm_against_oracle(q4, M, N, K):
+    dev, w32 = mat(N, K, ("gemm", N, K))
+    x = synth.x_bf16(M, K, ("gemm-x", M, K))
+    y = q4.q4g128_gemm(gpu(x), *dev)
+    xb = synth.bits16(x)
+    check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"gemm M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,K,chunk", [(192, 2048, 64), (200, 2048, 64), (100, 8192, 32), (70, 4096, 64)])
+def test_gemm_chunks_equal_tiled_decode_calls(q4, M, K, chunk):
+    dev, _ = mat(2048, K, ("gemm-chunks", K))
+    x = gpu(synth.x_bf16(M, K, ("gemm-chunks-x", M, K)))
+    y = q4.q4g128_gemm(x, *dev)
+    for m0 in range(0, M, chunk):
+        part = x[m0:m0 + chunk].contiguous()
+        ref = q4.q4g128_gemv(part, *dev, variant=q4.VARIANT_TILED)
+        assert torch.equal(y[m0:m0 + chunk].view(torch.int16), ref.view(torch.int16)), (M, K, m0)
+
+
+@pytest.mark.parametrize("M", [1, 4, 48, 64])
+def test_gemm_small_m_is_the_gemv(q4, M):
+    dev, _ = mat(2048, 2048, ("gemm-small",))
+    x = gpu(synth.x_bf16(M, 2048, ("gemm-small-x", M)))
+    assert torch.equal(q4.q4g128_gemm(x, *dev).view(torch.int16), q4.q4g128_gemv(x, *dev).view(torch.int16))
+
+
+def test_gemm_rejects(q4):
+    dev, _ = mat(64, 32768, ("gemm-bad",))
+    with pytest.raises(q4.Q4GemvError):          # K beyond the unsplit LDS budget
+        q4.q4g128_gemm(gpu(synth.x_bf16(100, 32768, "gemm-bad-x")), *dev)
+    d2, w2 = mat(64, 16384, ("gemm-16k",))       # the widest K: 16-row chunks
+    x2 = synth.x_bf16(70, 16384, "gemm-16k-x")
+    xb = synth.bits16(x2)
+    check_gemv(q4.q4g128_gemm(gpu(x2), *d2), oracle.gemv_f64(xb, w2), w2, xb, "gemm K=16384")
