@@ -537,9 +537,9 @@ def cpu_baseline(wl, budget_s=15.0):
 # per batch size: the kernel the grouped int4 launches run, the sources it is
 # built from, and the committed rocprofv3 traffic record for it
 KERNELS = {
-    1: ("gemv_stream_kernel<FmtQ4, 1>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
+    1: ("gemv_stream_kernel<FmtQ4, 1, false>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
         os.path.join(ROOT, "profiles", "gemv_stream_q4_M1_grouped_traffic.json")),
-    48: ("tiled_mm_kernel<FmtQ4, 3>", ("common.h", "formats.h", "internal.h", "gemv_mm.hip"),
+    48: ("tiled_mm_kernel<FmtQ4, 3, false, false>", ("common.h", "formats.h", "internal.h", "gemv_mm.hip"),
          os.path.join(ROOT, "profiles", "tiled_mm_q4_M48_grouped_traffic.json")),
 }
 
@@ -746,7 +746,7 @@ def main():
         achieved = kbytes / (kms * 1e-3) / 1e9
         vname = q4.variant_name(q4.FMT_NVFP4G16, 0, 1, 2048, 2048)
         log(f"bench: NVFP4 GEMV launches at M=1 ({vname}): avg {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
-        out["roofline_nvfp4_M1"] = {"bound": "hbm", "kernel": f"gemv_stream_kernel<FmtNvfp4, 1> ({vname}), M=1 per-projection launches",
+        out["roofline_nvfp4_M1"] = {"bound": "hbm", "kernel": f"gemv_stream_kernel<FmtNvfp4, 1, false> ({vname}), M=1 per-projection launches",
                                     "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
                                     "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)}
