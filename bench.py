@@ -170,9 +170,10 @@ class Nvfp4Workload:
     """The same decode step with NVFP4 weights: q, k, o, gate, up NVFP4 (E2M1
     codes, e4m3 scales per 16 columns, one fp32 global scale) and v, down BF16,
     as the VoxCPM2-NVFP4 card quantizes them; then the same BF16 head.  plain:
-    one launch per projection; grouped: per layer the NVFP4 q, k, gate, up in
-    one launch, the BF16 v, the NVFP4 o and the BF16 down in one launch each
-    (a launch carries one weight format), then the head."""
+    one launch per projection; grouped: per layer the NVFP4 q, k, gate, up with
+    the BF16 v in one mixed-format call (one launch at M <= 4, one per format
+    above), the NVFP4 o and the BF16 down (K = 8192, not a streaming shape) in
+    one launch each, then the head."""
 
     def __init__(self, q4, synth, torch, int4_wl):
         self.q4, self.torch = q4, torch
@@ -216,8 +217,13 @@ class Nvfp4Workload:
             # size the shared workspace for the largest call first
             plan = []
             for lay in self.layers:
-                for stage in (("q", "k", "gate", "up"), ("v",), ("o",), ("down",)):
-                    if stage[0] in self.bf16_proj:
+                for stage in (("q", "k", "gate", "up", "v"), ("o",), ("down",)):
+                    if "v" in stage:
+                        # NVFP4 q, k, gate, up with the BF16 v: one launch at M <= 4
+                        items = [("bf16", xs[p], lay[p], ys[p]) if p in self.bf16_proj else ("nvfp4g16", xs[p], *lay[p], ys[p])
+                                 for p in stage]
+                        plan.append((q4.gemv_grouped_mixed, items, q4.mixed_workspace_bytes(items), stage))
+                    elif stage[0] in self.bf16_proj:
                         items = [(xs[p], lay[p], ys[p]) for p in stage]
                         plan.append((q4.bf16_gemv_grouped, items, q4.bf16_workspace_bytes(items), stage))
                     else:
@@ -672,7 +678,9 @@ def main():
             ms, g = time_graph(torch, nv, M, args.steps, args.warmup, mode)
             by = nv.step_bytes(M)
             calls = nv.launches(M, mode)
-            r = res[(f"NVFP4_M{M}", mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(calls),
+            # above M = 4 the mixed-format call runs one launch per format
+            extra = N_LAYERS if mode == "grouped" and M > 4 else 0
+            r = res[(f"NVFP4_M{M}", mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(calls) + extra,
                                                   wbytes=sum(b for _, b, _ in calls))
             log(f"bench: NVFP4 M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {r['gbs']:6.0f} GB/s, "
                 f"{1e3 / ms:6.0f} steps/s, {r['launches']} launches")

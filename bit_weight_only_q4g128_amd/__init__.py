@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
     "nvfp4g16_gemv_grouped", "nvfp4g16_workspace_bytes", "bf16_gemv_grouped", "bf16_workspace_bytes",
-    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample", "q4g128_gemm",
+    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample", "q4g128_gemm", "gemv_grouped_mixed", "mixed_workspace_bytes",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
     "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
@@ -96,6 +96,15 @@ lib.q4g128_fused_workspace_bytes.argtypes = [ctypes.POINTER(FusedTask), _i, _i, 
 lib.q4g128_fused_workspace_bytes.restype = ctypes.c_int
 
 
+class MixedTask(ctypes.Structure):
+    _fields_ = [("format", _i), ("x", _p), ("weight", _p), ("scale", _p), ("minv", _p), ("global_scale", _f), ("y", _p),
+                ("N", _i), ("K", _i)]
+
+
+lib.q4gemv_grouped_mixed.argtypes = [ctypes.POINTER(MixedTask), _i, _i, _p, ctypes.c_size_t, _p]
+lib.q4gemv_grouped_mixed.restype = ctypes.c_int
+lib.q4gemv_mixed_workspace_bytes.argtypes = [ctypes.POINTER(MixedTask), _i, _i, ctypes.POINTER(ctypes.c_size_t)]
+lib.q4gemv_mixed_workspace_bytes.restype = ctypes.c_int
 lib.q4g128_gemm.argtypes = [_p, _i, _i, _p, _p, _p, _i, _p, _p]
 lib.q4g128_gemm.restype = ctypes.c_int
 lib.q4_sample_topk.argtypes = [_p, _i, _i, _f, _i, _p, _p, _p, _p, _p]
@@ -485,3 +494,68 @@ def q4g128_gemm(x, qweight, scale, minv, out=None):
     y = _out(out, (M, N), torch.bfloat16, x)
     _raise(lib.q4g128_gemm(x.data_ptr(), M, K, qweight.data_ptr(), scale.data_ptr(), minv.data_ptr(), N, y.data_ptr(), _stream(x)))
     return y
+
+
+def _mixed_task_array(items):
+    """Tagged task tuples -> (MixedTask array, outputs, M):
+      ("q4g128", x, qweight, scale, min, out), ("nvfp4g16", x, qweight,
+      scale_e4m3, global_scale, out), ("bf16", x, w, out); out may be None."""
+    items = list(items)
+    if not 1 <= len(items) <= 8:
+        raise ValueError("1..8 tasks per call")
+    arr = (MixedTask * len(items))()
+    outs, M = [], None
+    for i, it in enumerate(items):
+        kind = it[0]
+        if kind == "q4g128":
+            _, x, qw, sc, mn, out = it
+            _check(qw, "qweight", _U8, 2); _check(sc, "scale", _F16, 2); _check(mn, "min", _F16, 2)
+            fmt, w, G, N, K = FMT_Q4G128, qw, 0.0, qw.shape[0], qw.shape[1] * 2
+            if tuple(sc.shape) != (N, K // 128) or tuple(mn.shape) != (N, K // 128):
+                raise ValueError(f"task {i}: inconsistent shapes")
+        elif kind == "nvfp4g16":
+            _, x, qw, sc, G, out = it
+            _check(qw, "qweight", _U8, 2); _check(sc, "scale_e4m3", _E4M3, 2)
+            fmt, w, mn, N, K = FMT_NVFP4G16, qw, None, qw.shape[0], qw.shape[1] * 2
+            if tuple(sc.shape) != (N, K // 16):
+                raise ValueError(f"task {i}: inconsistent shapes")
+        elif kind == "bf16":
+            _, x, w, out = it
+            _check(w, "w", _U16, 2)
+            fmt, sc, mn, G, (N, K) = FMT_BF16, None, None, 0.0, w.shape
+        else:
+            raise ValueError(f"unknown task kind {kind!r} (q4g128, nvfp4g16, bf16)")
+        _check(x, "x", _U16, 2)
+        if x.shape[1] != K:
+            raise ValueError(f"task {i}: x has K = {x.shape[1]}, the weights {K}")
+        M = x.shape[0] if M is None else M
+        if x.shape[0] != M:
+            raise ValueError("all tasks must share the batch size M")
+        y = _out(out, (M, N), torch.bfloat16, x)
+        outs.append(y)
+        arr[i] = MixedTask(fmt, x.data_ptr(), w.data_ptr(), sc.data_ptr() if sc is not None else None,
+                           mn.data_ptr() if mn is not None else None, float(G), y.data_ptr(), N, K)
+    return items, arr, outs, M
+
+
+def gemv_grouped_mixed(items, workspace=None):
+    """Independent GEMVs of mixed weight formats with one batch size, in one
+    launch where the streaming kernel takes them all (M <= 4), else one
+    grouped launch per format (q4gemv_grouped_mixed in the C header).
+    Returns the list of outputs."""
+    items, arr, outs, M = _mixed_task_array(items)
+    st = _stream(items[0][1])
+    if workspace is None:
+        _raise(lib.q4gemv_grouped_mixed(arr, len(items), M, None, 0, st))
+    else:
+        if workspace.device != items[0][1].device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the activations' device")
+        _raise(lib.q4gemv_grouped_mixed(arr, len(items), M, workspace.data_ptr(), workspace.numel(), st))
+    return outs
+
+
+def mixed_workspace_bytes(items) -> int:
+    items, arr, _, M = _mixed_task_array(items)
+    n = ctypes.c_size_t(0)
+    _raise(lib.q4gemv_mixed_workspace_bytes(arr, len(items), M, ctypes.byref(n)))
+    return int(n.value)

@@ -173,6 +173,60 @@ int run_grouped(Fmt fmt, int chosen, const GemvArgs* a, int count, int M, void* 
     return run(fmt, chosen, a, count, stream, workspace, workspace_bytes);
 }
 
+// Validation of a mixed-format group: fills a[] and fmts[], checks every
+// output against every input and the other outputs.
+int check_mixed(const q4gemv_mixed_task* tasks, int count, int M, GemvArgs* a, Fmt* fmts, bool* one_launch) {
+    if (!tasks) return Q4_EINVAL_PTR;
+    if (count < 1 || count > q4::kMaxTasks) return Q4_EINVAL_SHAPE;
+    Range in[q4::kMaxTasks][4], out[q4::kMaxTasks];
+    bool stream = M <= 4;
+    for (int i = 0; i < count; ++i) {
+        const q4gemv_mixed_task& k = tasks[i];
+        int rc;
+        switch (k.format) {
+            case Q4_FMT_Q4G128:
+                rc = check_q4(k.x, M, k.K, static_cast<const uint8_t*>(k.weight), static_cast<const uint16_t*>(k.scale), k.minv, k.N,
+                              k.y, a[i], in[i], out[i]);
+                break;
+            case Q4_FMT_NVFP4G16:
+                rc = check_nv(k.x, M, k.K, static_cast<const uint8_t*>(k.weight), static_cast<const uint8_t*>(k.scale), k.global_scale,
+                              k.N, k.y, a[i], in[i], out[i]);
+                break;
+            case Q4_FMT_BF16:
+                rc = check_bf(k.x, M, k.K, static_cast<const uint16_t*>(k.weight), k.N, k.y, a[i], in[i], out[i]);
+                break;
+            default:
+                return Q4_EINVAL_SHAPE;
+        }
+        if (rc) return rc;
+        fmts[i] = static_cast<Fmt>(k.format);
+        stream = stream && q4::stream_supported(fmts[i], M, k.K);
+    }
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j) {
+            for (int r = 0; r < 4; ++r)
+                if (overlaps(out[i], in[j][r])) return Q4_EALIAS;
+            if (i != j && overlaps(out[i], out[j])) return Q4_EALIAS;
+        }
+    *one_launch = stream;
+    return Q4_OK;
+}
+
+// The tasks of format f, in order, and their variant under the automatic
+// choice (the grouped calls' rules).
+int mixed_subgroup(const GemvArgs* a, const Fmt* fmts, int count, Fmt f, int M, bool split, GemvArgs* sub, int* n, int* chosen) {
+    Range in[q4::kMaxTasks][4], out[q4::kMaxTasks];
+    *n = 0;
+    for (int i = 0; i < count; ++i)
+        if (fmts[i] == f) {
+            in[*n][0] = in[*n][1] = in[*n][2] = in[*n][3] = Range{0, 0};
+            out[*n] = Range{0, 0};   // aliasing was checked across all tasks already
+            sub[(*n)++] = a[i];
+        }
+    if (*n == 0) return Q4_OK;
+    return plan_checked(f, sub, in, out, *n, M, Q4_VARIANT_AUTO, split, chosen);
+}
+
 // Validation and kernel choice of a fused int4 call (see q4g128_fused_task):
 // fills a[] and *tiled (false: the streaming kernel).
 int check_fused(const q4g128_fused_task* tasks, int count, int M, bool split, GemvArgs* a, bool* tiled) {
@@ -453,6 +507,70 @@ size_t fused_h_bytes(const GemvArgs* a, int count) {
     for (int i = 0; i < count; ++i)
         if (a[i].up) n += align256((size_t)a[i].M * a[i].K * 2);
     return n;
+}
+
+int q4gemv_grouped_mixed(const q4gemv_mixed_task* tasks, int count, int M, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    GemvArgs a[q4::kMaxTasks];
+    Fmt fmts[q4::kMaxTasks];
+    bool one = false;
+    int rc = check_mixed(tasks, count, M, a, fmts, &one);
+    if (rc) return rc;
+    if (one) {
+        hipError_t e = q4::launch_stream_mixed(fmts, a, count, reinterpret_cast<hipStream_t>(stream));
+        return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+    }
+    // one grouped launch per format, in order of first appearance; every
+    // subgroup is planned before anything is enqueued
+    const bool split = workspace != nullptr && workspace_bytes > 0;
+    Fmt order[3];
+    int nf = 0;
+    for (int i = 0; i < count; ++i) {
+        bool seen = false;
+        for (int j = 0; j < nf; ++j) seen = seen || order[j] == fmts[i];
+        if (!seen) order[nf++] = fmts[i];
+    }
+    GemvArgs sub[3][q4::kMaxTasks];
+    int n[3], chosen[3];
+    for (int f = 0; f < nf; ++f) {
+        rc = mixed_subgroup(a, fmts, count, order[f], M, split, sub[f], &n[f], &chosen[f]);
+        if (rc) return rc;
+        if (chosen[f] == Q4_VARIANT_TILED && split) {
+            const size_t need = q4::mm_workspace_bytes(order[f], sub[f], n[f]);
+            if (need == 0 || workspace_bytes < need)
+                for (int i = 0; i < n[f]; ++i)
+                    if (!q4::mm_supported(order[f], M, sub[f][i].K, false)) return Q4_EVARIANT;
+        }
+    }
+    for (int f = 0; f < nf; ++f) {
+        rc = run_grouped(order[f], chosen[f], sub[f], n[f], M, workspace, workspace_bytes, stream);
+        if (rc) return rc;
+    }
+    return Q4_OK;
+}
+
+int q4gemv_mixed_workspace_bytes(const q4gemv_mixed_task* tasks, int count, int M, size_t* bytes) {
+    if (!bytes) return Q4_EINVAL_PTR;
+    GemvArgs a[q4::kMaxTasks];
+    Fmt fmts[q4::kMaxTasks];
+    bool one = false;
+    int rc = check_mixed(tasks, count, M, a, fmts, &one);
+    if (rc) return rc;
+    size_t need = 0;
+    if (!one) {
+        for (int f = 0; f < 3; ++f) {
+            GemvArgs sub[q4::kMaxTasks];
+            int n = 0, chosen = 0;
+            rc = mixed_subgroup(a, fmts, count, static_cast<Fmt>(f), M, true, sub, &n, &chosen);
+            if (rc) return rc;
+            if (n && chosen == Q4_VARIANT_TILED) {
+                const size_t b = q4::mm_workspace_bytes(static_cast<Fmt>(f), sub, n);
+                need = b > need ? b : need;
+            }
+        }
+    }
+    *bytes = need;
+    return Q4_OK;
 }
 
 int q4g128_gemv_fused(const q4g128_fused_task* tasks, int count, int M, void* workspace, size_t workspace_bytes, void* stream) {

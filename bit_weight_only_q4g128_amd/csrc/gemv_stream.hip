@@ -39,6 +39,7 @@ constexpr int kWaves = 4;    // waves per workgroup
 struct StreamTable {
     int blk0[kMaxTasks];     // first workgroup of each task (unused: INT_MAX)
     int cpl_log2[kMaxTasks];
+    int fmt[kMaxTasks];      // weight format of each task (the mixed-format kernel)
     GemvArgs a[kMaxTasks];
     int count;
 };
@@ -76,17 +77,17 @@ __host__ __device__ inline int stream_shmem(int MT, int K) {
 // 16-byte x pieces per thread (x is MT*K*2 bytes over 256 threads)
 template <class F> __host__ __device__ inline int x_pieces(int MT, int K) { return (MT * K / 8 + 255) / 256; }
 
-template <class F, int MT, bool kFused>
-__global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int kXP = MT * 4;   // most x pieces a thread stages (K <= 8192 for the 4-bit formats)
-
+__device__ __forceinline__ int stream_task(const StreamTable& tt) {
     int t = 0;
 #pragma unroll
     for (int i = 1; i < kMaxTasks; ++i) t += ((int)blockIdx.x >= tt.blk0[i]) ? 1 : 0;
-    const GemvArgs a = tt.a[t];
-    const int cl = tt.cpl_log2[t];
-    const int blk = blockIdx.x - tt.blk0[t];
+    return t;
+}
+
+// One workgroup block of task `a`: blk is the block's index within the task.
+template <class F, int MT, bool kFused>
+__device__ __forceinline__ void stream_block(const GemvArgs a, const int cl, const int blk, uint8_t* lds) {
+    constexpr int kXP = MT * 4;   // most x pieces a thread stages (K <= 8192 for the 4-bit formats)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -270,6 +271,28 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
     }
 }
 
+template <class F, int MT, bool kFused>
+__global__ __launch_bounds__(256) void gemv_stream_kernel(StreamTable tt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int t = stream_task(tt);
+    stream_block<F, MT, kFused>(tt.a[t], tt.cpl_log2[t], blockIdx.x - tt.blk0[t], lds);
+}
+
+// One launch over tasks of different weight formats (the NVFP4 decode step's
+// BF16 projections beside its NVFP4 ones): each workgroup runs its task's
+// format; the launch's registers are the widest format's.
+template <int MT>
+__global__ __launch_bounds__(256) void gemv_stream_mixed_kernel(StreamTable tt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int t = stream_task(tt);
+    const int blk = blockIdx.x - tt.blk0[t];
+    switch (tt.fmt[t]) {
+        case kFmtQ4: stream_block<FmtQ4, MT, false>(tt.a[t], tt.cpl_log2[t], blk, lds); break;
+        case kFmtNvfp4: stream_block<FmtNvfp4, MT, false>(tt.a[t], tt.cpl_log2[t], blk, lds); break;
+        default: stream_block<FmtBf16, MT, false>(tt.a[t], tt.cpl_log2[t], blk, lds); break;
+    }
+}
+
 template <class F> int chunk_log2(int K) {
     const int wpc = F::WPC;
     if (K % wpc) return -1;
@@ -332,6 +355,42 @@ hipError_t launch_stream(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t 
 
 hipError_t launch_stream_fused(const GemvArgs* tasks, int count, hipStream_t s) {
     return launch_stream_fmt<FmtQ4, true>(tasks, count, s);
+}
+
+namespace {
+
+template <int MT>
+hipError_t launch_stream_mixed_mt(const Fmt* fmts, const GemvArgs* tasks, int count, hipStream_t st) {
+    StreamTable tt{};
+    for (int i = 0; i < kMaxTasks; ++i) tt.blk0[i] = 0x7fffffff;
+    int grid = 0, shmem = 0;
+    for (int i = 0; i < count; ++i) {
+        const int K = tasks[i].K;
+        int cl, sh;
+        if (fmts[i] == kFmtQ4) { cl = chunk_log2<FmtQ4>(K); sh = stream_shmem<FmtQ4>(MT, K); }
+        else if (fmts[i] == kFmtNvfp4) { cl = chunk_log2<FmtNvfp4>(K); sh = stream_shmem<FmtNvfp4>(MT, K); }
+        else { cl = chunk_log2<FmtBf16>(K); sh = stream_shmem<FmtBf16>(MT, K); }
+        const int rw = kWaves * (kLoads >> cl);
+        tt.blk0[i] = grid;
+        tt.cpl_log2[i] = cl;
+        tt.fmt[i] = fmts[i];
+        tt.a[i] = tasks[i];
+        grid += (tasks[i].N + rw - 1) / rw;
+        shmem = sh > shmem ? sh : shmem;
+    }
+    tt.count = count;
+    return launch_kernel(gemv_stream_mixed_kernel<MT>, dim3(grid), dim3(256), (size_t)shmem, st, tt);
+}
+
+}  // namespace
+
+hipError_t launch_stream_mixed(const Fmt* fmts, const GemvArgs* tasks, int count, hipStream_t s) {
+    switch (tasks[0].M) {
+        case 1: return launch_stream_mixed_mt<1>(fmts, tasks, count, s);
+        case 2: return launch_stream_mixed_mt<2>(fmts, tasks, count, s);
+        case 3: return launch_stream_mixed_mt<3>(fmts, tasks, count, s);
+        default: return launch_stream_mixed_mt<4>(fmts, tasks, count, s);
+    }
 }
 
 }  // namespace q4

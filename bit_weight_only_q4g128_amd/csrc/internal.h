@@ -49,6 +49,9 @@ constexpr int kStreamMaxM = 4;
 constexpr int kStreamMaxShmem = 64 * 1024;
 hipError_t launch_stream(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);
 bool stream_supported(Fmt fmt, int M, int K);
+// The streaming kernel over tasks of several formats in one launch (fmts[i]
+// per task; every task stream_supported at the one batch size M).
+hipError_t launch_stream_mixed(const Fmt* fmts, const GemvArgs* tasks, int count, hipStream_t s);
 // The int4 streaming kernel with the fused activation prologue and residual
 // epilogue (GemvArgs::up, GemvArgs::resid; either may be null).
 hipError_t launch_stream_fused(const GemvArgs* tasks, int count, hipStream_t s);

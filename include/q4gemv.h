@@ -194,6 +194,35 @@ int bf16_gemv_grouped_ws(const bf16_task* tasks, int count, int M, int variant, 
 int bf16_workspace_bytes(const bf16_task* tasks, int count, int M, size_t* bytes);
 
 /*
+ * Grouped GEMVs of mixed weight formats: up to 8 independent GEMVs, each
+ * int4, NVFP4 or BF16, with one batch size M.  When M <= 4 and every task is
+ * a streaming shape (rows of 1, 2 or 4 KB: int4/NVFP4 K = 2048, 4096, 8192;
+ * BF16 K = 512, 1024, 2048) they run as ONE launch -- the NVFP4 decode step's
+ * BF16 v projection beside its NVFP4 q, k, gate, up (one launch per format
+ * would otherwise be needed).  Otherwise the tasks run as one grouped launch
+ * per format, in task order of first appearance, on the same stream (with
+ * the workspace, sized by q4gemv_mixed_workspace_bytes, shared by them).
+ * Results equal those of the single-format calls bit for bit.  Each task
+ * obeys its format's single-call rules; no task's y may overlap any task's
+ * inputs or another y.
+ */
+typedef struct q4gemv_mixed_task {
+    int format;              /* Q4_FMT_Q4G128, Q4_FMT_NVFP4G16 or Q4_FMT_BF16 */
+    const uint16_t* x;       /* bf16 [M, K], 16-byte aligned */
+    const void* weight;      /* int4/NVFP4: uint8 codes [N, K/2]; BF16: bf16 [N, K]; 16-byte aligned */
+    const void* scale;       /* int4: fp16 [N, K/128]; NVFP4: e4m3 bytes [N, K/16]; BF16: unused */
+    const uint16_t* minv;    /* int4: fp16 [N, K/128]; otherwise unused */
+    float global_scale;      /* NVFP4: per-matrix multiplier; otherwise unused */
+    uint16_t* y;             /* bf16 [M, N] */
+    int N;
+    int K;
+} q4gemv_mixed_task;
+
+int q4gemv_grouped_mixed(const q4gemv_mixed_task* tasks, int count, int M, void* workspace, size_t workspace_bytes,
+                         void* stream);
+int q4gemv_mixed_workspace_bytes(const q4gemv_mixed_task* tasks, int count, int M, size_t* bytes);
+
+/*
  * Fused int4 GEMVs for the decode step's elementwise neighbours.  The Rumik
  * TTS Fast Inference post ("What Made It Faster") fuses the residual and
  * normalization operations around its weight-only projections so that their

@@ -267,6 +267,40 @@ def test_sample_validation():
     assert h(ti=W + 128) == EALIAS
 
 
+def test_mixed_validation():
+    """q4gemv_grouped_mixed / q4gemv_mixed_workspace_bytes reject bad arguments
+    on the host (the size query never launches anything)."""
+    MT = q4.MixedTask
+    FQ, FN, FB = q4.FMT_Q4G128, q4.FMT_NVFP4G16, q4.FMT_BF16
+
+    def mt(i, fmt=FQ, **kw):
+        b = A + (i << 29)
+        base = dict(format=fmt, x=b, weight=b + (1 << 26), scale=b + (2 << 26), minv=b + (3 << 26), global_scale=1.0,
+                    y=b + (4 << 26), N=2048, K=2048)
+        base.update(kw)
+        return MT(**base)
+
+    nb = ctypes.c_size_t(7)
+
+    def size(tasks, M=1):
+        return lib.q4gemv_mixed_workspace_bytes((MT * len(tasks))(*tasks), len(tasks), M, ctypes.byref(nb))
+
+    def call(tasks, M=1):
+        return lib.q4gemv_grouped_mixed((MT * len(tasks))(*tasks), len(tasks), M, None, 0, None)
+
+    mixed = [mt(0, FN), mt(1, FB), mt(2, FQ)]
+    assert size(mixed) == OK and nb.value == 0                 # one streaming launch: no workspace
+    assert size(mixed, M=48) == OK and nb.value > 0            # one tiled launch per format, K splits
+    assert lib.q4gemv_grouped_mixed(None, 1, 1, None, 0, None) == EPTR
+    assert call([mt(i) for i in range(9)]) == ESHAPE
+    assert call([mt(0, fmt=5)]) == ESHAPE
+    assert call([mt(0, FN, scale=None)]) == EPTR
+    assert call([mt(0, FB, K=12)]) == ESHAPE
+    assert call([mt(0, FN, weight=A + (1 << 26) + 8)]) == EALIGN
+    assert call([mt(0, FN), mt(1, FB, y=A + (1 << 26) + 64)]) == EALIAS   # over another task's weights
+    assert call([mt(0, FN), mt(1, FB, y=A + (4 << 26))]) == EALIAS        # two tasks share an output
+
+
 def test_stream_read_validation():
     import ctypes
     lib.q4gemv_stream_read.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
