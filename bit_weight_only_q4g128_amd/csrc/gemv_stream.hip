@@ -74,6 +74,10 @@ __host__ __device__ inline int stream_shmem(int MT, int K) {
     return Stream<F>::x_bytes(MT, K) + Stream<F>::sum_bytes(MT, K) + Stream<F>::aux_bytes();
 }
 
+// rows a workgroup owns: 16 / CPL for rows up to 4 KB; one row per 4 / wpr
+// waves for the split BF16 rows of 8 and 16 KB
+__host__ __device__ inline int rows_per_wg(int cl) { return cl > 2 ? kWaves >> (cl - 2) : kWaves * (kLoads >> cl); }
+
 // 16-byte x pieces per thread (x is MT*K*2 bytes over 256 threads)
 template <class F> __host__ __device__ inline int x_pieces(int MT, int K) { return (MT * K / 8 + 255) / 256; }
 
@@ -94,10 +98,14 @@ __device__ __forceinline__ void stream_block(const GemvArgs a, const int cl, con
     const int CPL = 1 << cl;
     const int C = 64 << cl;                      // chunks per row
     const uint32_t rowbytes = (uint32_t)C * 16;
-    const int rpw = kLoads >> cl;                // rows per wave
-    const int RW = kWaves * rpw;                 // rows per workgroup
+    // BF16 rows of 8 or 16 KB (cl = 3, 4) are split over wpr = 2 or 4 waves,
+    // each taking the row's part-th quarter/half of its chunks
+    const int wpr = cl > 2 ? 1 << (cl - 2) : 1;  // waves per row
+    const int rpw = cl > 2 ? 1 : kLoads >> cl;   // rows per wave (a part of one row when wpr > 1)
+    const int RW = rows_per_wg(cl);              // rows per workgroup
     const int row0 = blk * RW;
-    const int wrow0 = row0 + wave * rpw;
+    const int wrow0 = row0 + (cl > 2 ? wave / wpr : wave * rpw);
+    const int part = cl > 2 ? wave % wpr : 0;
     const int K = a.K;
 
     // --- 1. shared inputs: x pieces and group parameters into registers
@@ -143,7 +151,7 @@ __device__ __forceinline__ void stream_block(const GemvArgs a, const int cl, con
     u32x4 q[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-        const uint32_t r = (uint32_t)(i >> cl), j = (uint32_t)(i & (CPL - 1));
+        const uint32_t r = (uint32_t)(i >> cl), j = (uint32_t)(i & (CPL - 1)) + (uint32_t)(part * kLoads);
         q[i] = buf_load16(rw, r * rowbytes + (j * 64 + lane) * 16, 0);
     }
     // fused: the residuals of the wave's rows (rows past N read as zero)
@@ -259,7 +267,7 @@ __device__ __forceinline__ void stream_block(const GemvArgs a, const int cl, con
             F::template accumulate<MT>(q[i], read_aux(wave * rpw + i, lane), xc, out);
             finish_row(i, out);
         }
-    } else {
+    } else if (cl <= 2) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
             const int r = i >> cl, c = (i & (CPL - 1)) * 64 + lane;
@@ -267,6 +275,37 @@ __device__ __forceinline__ void stream_block(const GemvArgs a, const int cl, con
             read_x(c, xc);
             F::template accumulate<MT>(q[i], read_aux(wave * rpw + r, c), xc, out);
             if ((i & (CPL - 1)) == CPL - 1) finish_row(r, out);
+            if constexpr (kFused) __builtin_amdgcn_sched_barrier(0);
+        }
+    } else if constexpr (std::is_same<F, FmtBf16>::value) {
+        // a part of one row: reduce it in the wave, add the parts of the row in
+        // wave order through LDS, and let the row's first wave store it
+        __shared__ float parts[kWaves][MT];
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            typename F::X xc[MT];
+            read_x((part * kLoads + i) * 64 + lane, xc);
+            F::template accumulate<MT>(q[i], read_aux(0, 0), xc, out);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float v = out[m];
+            v += dpp<0xB1>(v);
+            v += dpp<0x4E>(v);
+            v += dpp<0x141>(v);
+            v += dpp<0x140>(v);
+            v += dpp<0x142, 0xA>(v);
+            v += dpp<0x143, 0xC>(v);
+            if (lane == 63) parts[wave][m] = v;
+        }
+        __syncthreads();
+        if (part == 0 && lane == 63 && wrow0 < a.N) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                float v = parts[wave][m];
+                for (int p = 1; p < wpr; ++p) v += parts[wave + p][m];
+                a.y[(size_t)m * a.N + wrow0] = f32_to_bf16(F::finish(a, v));
+            }
         }
     }
 }
@@ -293,11 +332,14 @@ __global__ __launch_bounds__(256) void gemv_stream_mixed_kernel(StreamTable tt) 
     }
 }
 
+// rows of 1, 2 or 4 KB (64 << cl chunks); BF16 also 8 and 16 KB rows, split
+// over 2 or 4 waves
 template <class F> int chunk_log2(int K) {
     const int wpc = F::WPC;
     if (K % wpc) return -1;
     const int C = K / wpc;
-    for (int l = 0; l <= 2; ++l)
+    const int max_l = std::is_same<F, FmtBf16>::value ? 4 : 2;
+    for (int l = 0; l <= max_l; ++l)
         if (C == (64 << l)) return l;
     return -1;
 }
@@ -309,7 +351,7 @@ hipError_t launch_stream_mt(const GemvArgs* tasks, int count, hipStream_t st) {
     int grid = 0, shmem = 0;
     for (int i = 0; i < count; ++i) {
         const int cl = chunk_log2<F>(tasks[i].K);
-        const int rw = kWaves * (kLoads >> cl);
+        const int rw = rows_per_wg(cl);
         tt.blk0[i] = grid;
         tt.cpl_log2[i] = cl;
         tt.a[i] = tasks[i];
@@ -331,8 +373,9 @@ hipError_t launch_stream_fmt(const GemvArgs* tasks, int count, hipStream_t st) {
     }
 }
 
+// (256 bytes of margin for the kernel's own LDS: the split rows' partial sums)
 template <class F> bool stream_ok(int M, int K) {
-    return M >= 1 && M <= kStreamMaxM && chunk_log2<F>(K) >= 0 && stream_shmem<F>(M, K) <= kStreamMaxShmem;
+    return M >= 1 && M <= kStreamMaxM && chunk_log2<F>(K) >= 0 && stream_shmem<F>(M, K) + 256 <= kStreamMaxShmem;
 }
 
 }  // namespace
@@ -370,7 +413,7 @@ hipError_t launch_stream_mixed_mt(const Fmt* fmts, const GemvArgs* tasks, int co
         if (fmts[i] == kFmtQ4) { cl = chunk_log2<FmtQ4>(K); sh = stream_shmem<FmtQ4>(MT, K); }
         else if (fmts[i] == kFmtNvfp4) { cl = chunk_log2<FmtNvfp4>(K); sh = stream_shmem<FmtNvfp4>(MT, K); }
         else { cl = chunk_log2<FmtBf16>(K); sh = stream_shmem<FmtBf16>(MT, K); }
-        const int rw = kWaves * (kLoads >> cl);
+        const int rw = rows_per_wg(cl);
         tt.blk0[i] = grid;
         tt.cpl_log2[i] = cl;
         tt.fmt[i] = fmts[i];

@@ -149,7 +149,7 @@ def test_nvfp4_onehot_bitwise_stream(q4, K, M):
     assert np.array_equal(gotv, expv), (K, M)
 
 
-@pytest.mark.parametrize("K", [512, 2048])
+@pytest.mark.parametrize("K", [512, 2048, 4096, 8192])
 @pytest.mark.parametrize("M", [1, 3])
 def test_bf16_onehot_bitwise_stream(q4, K, M):
     N = 70
@@ -272,7 +272,8 @@ def test_nvfp4_edge_shapes(q4, N, K):
                        f"nv edge N={N} K={K} M={M} {VNAME[v]}")
 
 
-@pytest.mark.parametrize("N,K", [(1, 8), (3, 24), (19, 136), (40, 1000), (129, 2056), (1, 512), (21, 1024), (257, 2048)])
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 24), (19, 136), (40, 1000), (129, 2056), (1, 512), (21, 1024), (257, 2048),
+                                 (37, 4096), (65, 8192), (2, 8192)])
 def test_bf16_edge_shapes(q4, N, K):
     w = synth.bf16_matrix(N, K, ("edge-bf", N, K))
     w32 = oracle.bf16_dequant_f32(synth.bits16(w))
