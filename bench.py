@@ -367,6 +367,27 @@ def prefill_calls(torch, q4, synth):
     return rec
 
 
+def projection_calls(torch, q4, wl):
+    """Each projection alone (the automatic kernel choice) at M = 1, 3, 16, 48:
+    one launch per layer over the 36 layers' distinct copies, captured in one
+    graph and replayed, so gate, up and down (36 x 8.9 MB) overflow the
+    256 MB memory-side cache while q, o (80 MB) and k, v (20 MB) stay in it.
+    Microseconds and algorithmic GB/s per launch."""
+    rec = {}
+    for M in (1, 3, 16, 48):
+        x = {K: wl.torch.zeros((M, K), dtype=wl.torch.bfloat16, device="cuda").normal_() for K in (2048, 8192)}
+        for p in wl.order:
+            N, K = wl.shapes[p]
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            items = [[(x[K], *lay[p], y)] for lay in wl.layers]
+            ws = wl.workspace(M, items[0])
+            calls = [lambda it=it: q4.q4g128_gemv_grouped(it, workspace=ws) for it in items]
+            us = graph_us(torch, lambda: [c() for c in calls], reps=1, iters=20) / len(calls)
+            rec[f"{p}_M{M}"] = {"us": round(us, 2), "GB_s": round(q4_bytes(N, K, M) / (us * 1e-6) / 1e9, 1),
+                                "cached": q4_wbytes(N, K) * N_LAYERS < 256e6}
+    return rec
+
+
 def read_ceiling(torch, q4, wl, steps, warmup):
     """Plain-read reference for the M=1 grouped step: the same 73 launches,
     each replaced by the library's diagnostic stream_read over exactly the
@@ -535,9 +556,30 @@ def cpu_baseline(wl, budget_s=15.0):
         layers += 1
         if t_used >= budget_s:
             break
+    # the same on one thread, on one layer
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        host = {p: (t[0].cpu().numpy(), synth.bits16(t[1]), synth.bits16(t[2])) for p, t in wl.layers[0].items()}
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            b1 = 0
+            for p in wl.order:
+                N, K = wl.shapes[p]
+                oracle.q4g128_gemv(x[K], *host[p])
+                b1 += q4_bytes(N, K, 1)
+            one = round(b1 / (time.perf_counter() - t0) / 1e9, 4)
+    except Exception:
+        pass
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{layers} of {N_LAYERS} int4 layers (7 GEMVs each, M=1), NumPy dequant to fp32 + fp64 matmul, "
-                      f"{t_used:.1f} s"}
+                      f"{t_used:.1f} s", "value_1_thread": one, "cpu": model, "nproc": os.cpu_count()}
 
 
 # per batch size: the kernel the grouped int4 launches run, the sources it is
@@ -705,6 +747,9 @@ def main():
     for k, r in hs.items():
         log(f"bench: head + top-k sampling {k}: " + ", ".join(f"{n}: GEMV {v['gemv_us']} us, GEMV+sample {v['gemv_and_sample_us']} us, "
                                                               f"sample alone {v['sample_only_us']} us" for n, v in r.items()))
+    pj = projection_calls(torch, q4, wl)
+    log("bench: projections alone (36-copy rotation): " + ", ".join(f"{k} {v['us']} us {v['GB_s']} GB/s" for k, v in pj.items()
+                                                                    if k.startswith(("gate", "down"))))
     pf = prefill_calls(torch, q4, synth)
     log("bench: int4 prefill GEMM: " + ", ".join(f"{k} {v['int4_us']} us ({v['int4_TFLOP_s']} TFLOP/s; BF16 library on dequantized "
                                                   f"weights {v['bf16_library_on_dequantized_us']} us)" for k, v in pf.items()))
@@ -744,6 +789,7 @@ def main():
             "fused_calls": fz,
             "head_sample": hs,
             "prefill": pf,
+            "projections": pj,
         },
         "roofline": roof[1],
     }
