@@ -172,7 +172,8 @@ class Nvfp4Workload:
     as the VoxCPM2-NVFP4 card quantizes them; then the same BF16 head.  plain:
     one launch per projection; grouped: per layer the NVFP4 q, k, gate, up with
     the BF16 v in one mixed-format call and the NVFP4 o with the BF16 down in
-    another (one launch each at M <= 4, one per format above), then the head."""
+    another (one launch each: the streaming kernel at M <= 4, the tiled
+    matrix-core kernel above), then the head."""
 
     def __init__(self, q4, synth, torch, int4_wl):
         self.q4, self.torch = q4, torch
@@ -219,7 +220,7 @@ class Nvfp4Workload:
                 for stage in (("q", "k", "gate", "up", "v"), ("o", "down")):
                     if len(stage) > 1:
                         # NVFP4 q, k, gate, up with the BF16 v, and the NVFP4 o with the
-                        # BF16 down: one launch each at M <= 4
+                        # BF16 down: one launch each
                         items = [("bf16", xs[p], lay[p], ys[p]) if p in self.bf16_proj else ("nvfp4g16", xs[p], *lay[p], ys[p])
                                  for p in stage]
                         plan.append((q4.gemv_grouped_mixed, items, q4.mixed_workspace_bytes(items), stage))
@@ -720,9 +721,7 @@ def main():
             ms, g = time_graph(torch, nv, M, args.steps, args.warmup, mode)
             by = nv.step_bytes(M)
             calls = nv.launches(M, mode)
-            # above M = 4 each mixed-format call runs one launch per format
-            extra = 2 * N_LAYERS if mode == "grouped" and M > 4 else 0
-            r = res[(f"NVFP4_M{M}", mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(calls) + extra,
+            r = res[(f"NVFP4_M{M}", mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(calls),
                                                   wbytes=sum(b for _, b, _ in calls))
             log(f"bench: NVFP4 M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {r['gbs']:6.0f} GB/s, "
                 f"{1e3 / ms:6.0f} steps/s, {r['launches']} launches")

@@ -212,6 +212,15 @@ int check_mixed(const q4gemv_mixed_task* tasks, int count, int M, GemvArgs* a, F
     return Q4_OK;
 }
 
+// Every task NVFP4 or BF16 and on the tiled kernel (with K splits allowed):
+// the group can run as one mixed-format tiled launch.
+bool mixed_tiled(const GemvArgs* a, const Fmt* fmts, int count, int M) {
+    if (M <= 4) return false;
+    for (int i = 0; i < count; ++i)
+        if (fmts[i] == q4::kFmtQ4 || pick(fmts[i], Q4_VARIANT_AUTO, M, a[i].N, a[i].K, true) != Q4_VARIANT_TILED) return false;
+    return true;
+}
+
 // The tasks of format f, in order, and their variant under the automatic
 // choice (the grouped calls' rules).
 int mixed_subgroup(const GemvArgs* a, const Fmt* fmts, int count, Fmt f, int M, bool split, GemvArgs* sub, int* n, int* chosen) {
@@ -520,9 +529,16 @@ int q4gemv_grouped_mixed(const q4gemv_mixed_task* tasks, int count, int M, void*
         hipError_t e = q4::launch_stream_mixed(fmts, a, count, reinterpret_cast<hipStream_t>(stream));
         return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
     }
+    const bool split = workspace != nullptr && workspace_bytes > 0;
+    if (split && mixed_tiled(a, fmts, count, M)) {
+        const size_t need = q4::mm_workspace_bytes(q4::kFmtNvfp4, a, count);
+        if (need <= workspace_bytes) {
+            hipError_t e = q4::launch_mm_mixed(fmts, a, count, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+            return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+        }
+    }
     // one grouped launch per format, in order of first appearance; every
     // subgroup is planned before anything is enqueued
-    const bool split = workspace != nullptr && workspace_bytes > 0;
     Fmt order[3];
     int nf = 0;
     for (int i = 0; i < count; ++i) {
@@ -557,6 +573,7 @@ int q4gemv_mixed_workspace_bytes(const q4gemv_mixed_task* tasks, int count, int 
     int rc = check_mixed(tasks, count, M, a, fmts, &one);
     if (rc) return rc;
     size_t need = 0;
+    if (!one && mixed_tiled(a, fmts, count, M)) need = q4::mm_workspace_bytes(q4::kFmtNvfp4, a, count);
     if (!one) {
         for (int f = 0; f < 3; ++f) {
             GemvArgs sub[q4::kMaxTasks];

@@ -85,6 +85,7 @@ struct MmTask {
     int gps;           // 128-column groups per slice
     int smw;           // group parameters can be read in pieces of smw (8 or 4) groups, 0: one by one
     int y8;            // y rows can be written 8 bytes at a time (y 8-byte aligned, N % 4 == 0)
+    int fmt;           // weight format (the mixed-format kernel)
     float* part;       // partial tiles (ks > 1): [blocks][ks][4 tiles][MT][64 lanes] x 4 floats
     unsigned* cnt;     // arrival counters (ks > 1): [blocks]
 };
@@ -206,18 +207,22 @@ __device__ __forceinline__ GemvArgs chunk_args(GemvArgs a) {
     return a;
 }
 
-template <class F, int MT, bool kFused = false, bool kChunks = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves_f<MT, kFused>()))) void tiled_mm_kernel(MmTable tt) {
-    constexpr int kPre = MmFmt<F>::kPre;
-    constexpr int kLoads = MmFmt<F>::kLoads;
-    constexpr int XP = mm_xp<MT>() < kPre ? mm_xp<MT>() : kPre;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    u32x4* xb = reinterpret_cast<u32x4*>(lds);                                               // [2][2][MT][4][64]
-    f32x2* smb = reinterpret_cast<f32x2*>(lds + mm_ring_bytes<MT>());    // [gps][64]
-
+__device__ __forceinline__ int mm_task(const MmTable& tt) {
     int ti = 0;
 #pragma unroll
     for (int i = 1; i < kMaxTasks; ++i) ti += ((int)blockIdx.x >= tt.blk0[i]) ? 1 : 0;
+    return ti;
+}
+
+// One workgroup of task ti (a row block, or one K slice of it).
+template <class F, int MT, bool kFused, bool kChunks>
+__device__ __forceinline__ void tiled_body(const MmTable& tt, const int ti, uint8_t* lds) {
+    constexpr int kPre = MmFmt<F>::kPre;
+    constexpr int kLoads = MmFmt<F>::kLoads;
+    constexpr int XP = mm_xp<MT>() < kPre ? mm_xp<MT>() : kPre;
+    u32x4* xb = reinterpret_cast<u32x4*>(lds);                                               // [2][2][MT][4][64]
+    f32x2* smb = reinterpret_cast<f32x2*>(lds + mm_ring_bytes<MT>());    // [gps][64]
+
     const GemvArgs a = chunk_args<kChunks, MT>(tt.t[ti].a);
     const int KS = tt.t[ti].ks, gps = tt.t[ti].gps;
     const int local = blockIdx.x - tt.blk0[ti];
@@ -644,6 +649,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_wav
     if (tid == 0) __hip_atomic_store(&cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <class F, int MT, bool kFused = false, bool kChunks = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves_f<MT, kFused>()))) void tiled_mm_kernel(MmTable tt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    tiled_body<F, MT, kFused, kChunks>(tt, mm_task(tt), lds);
+}
+
+// One launch over NVFP4 and BF16 tasks (the NVFP4 decode step's BF16 v and down
+// beside its NVFP4 projections): each workgroup runs its task's format.  Both
+// formats use the same LDS layout (no staged group parameters) and planner.
+template <int MT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mm_waves<MT>()))) void tiled_mm_mixed_kernel(MmTable tt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int ti = mm_task(tt);
+    if (tt.t[ti].fmt == kFmtNvfp4) tiled_body<FmtNvfp4, MT, false, false>(tt, ti, lds);
+    else tiled_body<FmtBf16, MT, false, false>(tt, ti, lds);
+}
+
 constexpr int kCUs = 256;
 constexpr int kMinSlice = 4;     // fewest groups in a K slice (two steps of the two halves)
 
@@ -756,8 +778,10 @@ void fill_flags(MmTask& tk, const GemvArgs& a, int gps) {
     tk.y8 = (reinterpret_cast<uintptr_t>(a.y) % 8 == 0 && a.N % 4 == 0) ? 1 : 0;
 }
 
-template <class F, int MT, bool kFused = false>
-hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t st) {
+// The launch table of a tiled launch: plan the splits, order the tasks
+// (unsplit first), lay out the workspace; returns the grid and sets *gmax.
+template <class F, int MT>
+int build_table(const GemvArgs* tasks, const Fmt* fmts, int count, void* ws, size_t ws_bytes, MmTable& tt, int* gmax_out) {
     int ks[kMaxTasks], gps[kMaxTasks];
     const size_t need = ws_bytes_mt<F, MT>(tasks, count);
     const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
@@ -770,7 +794,6 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         if (whole[i]) order[n++] = i;
     for (int i = 0; i < count; ++i)
         if (!whole[i]) order[n++] = i;
-    MmTable tt{};
     for (int i = 0; i < kMaxTasks; ++i) tt.blk0[i] = 0x7fffffff;
     uint8_t* pc = static_cast<uint8_t*>(ws);
     uint8_t* pp = pc + kCntBytes;
@@ -783,6 +806,7 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         tt.t[j].ks = ks[i];
         tt.t[j].gps = gps[i];
         fill_flags<F>(tt.t[j], tasks[i], gps[i]);
+        tt.t[j].fmt = fmts ? fmts[i] : 0;
         if (ks[i] > 1) {
             tt.t[j].cnt = reinterpret_cast<unsigned*>(pc);
             pc += (size_t)blocks * 4;
@@ -792,11 +816,34 @@ hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_by
         grid += blocks * ks[i];
         gmax = gps[i] > gmax ? gps[i] : gmax;
     }
+    *gmax_out = gmax;
+    return grid;
+}
+
+template <class F, int MT, bool kFused = false>
+hipError_t launch_mm_mt(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t st) {
+    MmTable tt{};
+    int gmax = 0;
+    const int grid = build_table<F, MT>(tasks, nullptr, count, ws, ws_bytes, tt, &gmax);
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(tiled_mm_kernel<F, MT, kFused>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
     if (attr != hipSuccess) return attr;
     return launch_kernel(tiled_mm_kernel<F, MT, kFused>, dim3(grid), dim3(kThreads), (size_t)mm_shmem<F, MT>(gmax), st, tt);
 }
+
+// NVFP4 and BF16 tasks in one launch (fmts[i] per task), planned as NVFP4:
+// the two formats share the planner and the LDS layout.
+template <int MT>
+hipError_t launch_mm_mixed_mt(const Fmt* fmts, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t st) {
+    MmTable tt{};
+    int gmax = 0;
+    const int grid = build_table<FmtNvfp4, MT>(tasks, fmts, count, ws, ws_bytes, tt, &gmax);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(tiled_mm_mixed_kernel<MT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
+    if (attr != hipSuccess) return attr;
+    return launch_kernel(tiled_mm_mixed_kernel<MT>, dim3(grid), dim3(kThreads), (size_t)mm_shmem<FmtNvfp4, MT>(gmax), st, tt);
+}
+
 
 }  // namespace
 
@@ -899,6 +946,15 @@ hipError_t launch_mm_chunks(const GemvArgs& a, hipStream_t s) {
         case 4: return launch_chunks_mt<4>(a, s);
         case 2: return launch_chunks_mt<2>(a, s);
         default: return launch_chunks_mt<1>(a, s);
+    }
+}
+
+hipError_t launch_mm_mixed(const Fmt* fmts, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
+    switch ((tasks[0].M + 15) / 16) {
+        case 1: return launch_mm_mixed_mt<1>(fmts, tasks, count, ws, ws_bytes, s);
+        case 2: return launch_mm_mixed_mt<2>(fmts, tasks, count, ws, ws_bytes, s);
+        case 3: return launch_mm_mixed_mt<3>(fmts, tasks, count, ws, ws_bytes, s);
+        default: return launch_mm_mixed_mt<4>(fmts, tasks, count, ws, ws_bytes, s);
     }
 }
 

@@ -65,6 +65,10 @@ hipError_t launch_stream_fused(const GemvArgs* tasks, int count, hipStream_t s);
 bool mm_supported(Fmt fmt, int M, int K, bool split);
 size_t mm_workspace_bytes(Fmt fmt, const GemvArgs* tasks, int count);
 hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
+// The tiled kernel over NVFP4 and BF16 tasks in one launch (fmts[i] per
+// task), with the same workspace rules (sized by mm_workspace_bytes with
+// kFmtNvfp4).
+hipError_t launch_mm_mixed(const Fmt* fmts, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
 // Prefill GEMM: the int4 tiled kernel over batch chunks of up to 64 rows
 // (grid rows), for any M, unsplit; K % 128 == 0 and the K's group
 // parameters within the kernel's LDS budget (K <= 16384).

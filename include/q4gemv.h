@@ -199,9 +199,11 @@ int bf16_workspace_bytes(const bf16_task* tasks, int count, int M, size_t* bytes
  * a streaming shape (rows of 1, 2 or 4 KB: int4/NVFP4 K = 2048, 4096, 8192;
  * BF16 K = 512, 1024, 2048) they run as ONE launch -- the NVFP4 decode step's
  * BF16 v projection beside its NVFP4 q, k, gate, up (one launch per format
- * would otherwise be needed).  Otherwise the tasks run as one grouped launch
- * per format, in task order of first appearance, on the same stream (with
- * the workspace, sized by q4gemv_mixed_workspace_bytes, shared by them).
+ * would otherwise be needed).  Above M = 4, with a workspace of at least
+ * q4gemv_mixed_workspace_bytes, NVFP4 and BF16 tasks that all take the tiled
+ * matrix-core kernel also run as one launch.  Otherwise the tasks run as one
+ * grouped launch per format, in task order of first appearance, on the same
+ * stream (sharing the workspace).
  * Results equal those of the single-format calls bit for bit.  Each task
  * obeys its format's single-call rules; no task's y may overlap any task's
  * inputs or another y.

@@ -2,9 +2,9 @@
 
 At M <= 4 one streaming launch carries int4, NVFP4 and BF16 tasks: each
 output must equal the single-format streaming call bit for bit.  At larger M
-the call runs one grouped launch per format: bit for bit equal to the
-single-format grouped calls with the same workspace.  One case is also
-checked against the oracle.
+a group with int4 runs one grouped launch per format: bit for bit equal to
+the single-format grouped calls with the same workspace; NVFP4 and BF16 on
+the tiled kernel run as one launch, checked against the oracle.
 """
 import numpy as np
 import pytest
@@ -70,6 +70,32 @@ def test_mixed_per_format_launches_equal_grouped_calls(q4, M):
     ref_q = q4.q4g128_gemv_grouped([(items[2][1], *items[2][2:5], None)], workspace=ws)
     for y, r in zip([outs[0], outs[3], outs[1], outs[2]], ref_nv + ref_bf + ref_q):
         assert torch.equal(y.view(torch.int16), r.view(torch.int16)), M
+
+
+@pytest.mark.parametrize("M", [5, 48, 64])
+def test_mixed_tiled_one_launch_nvfp4_bf16(q4, M):
+    """NVFP4 and BF16 tasks on the tiled kernel run as one launch: each output
+    equal to the single-format grouped call with the same split plan (the plan
+    of the whole group), checked against the oracle, and equal to itself on a
+    second run (the workspace counters are left at zero)."""
+    n1 = synth.nvfp4_matrix(2048, 2048, ("mxt-nv",))
+    b = synth.bf16_matrix(512, 2048, ("mxt-bf",))
+    bd = synth.bf16_matrix(2048, 8192, ("mxt-bfd",))
+    x = synth.x_bf16(M, 2048, ("mxt-x", M))
+    xd = synth.x_bf16(M, 8192, ("mxt-xd", M))
+    items = [("nvfp4g16", gpu(x), gpu(n1[0]), gpu(n1[1]), n1[2], None), ("bf16", gpu(x), gpu(b), None),
+             ("bf16", gpu(xd), gpu(bd), None)]
+    ws = torch.zeros(q4.mixed_workspace_bytes(items), dtype=torch.uint8, device="cuda")
+    outs = q4.gemv_grouped_mixed(items, workspace=ws)
+    again = q4.gemv_grouped_mixed(items, workspace=ws)
+    for y, z in zip(outs, again):
+        assert torch.equal(y.view(torch.int16), z.view(torch.int16))
+    xb, xdb = synth.bits16(x), synth.bits16(xd)
+    w_n = oracle.nvfp4g16_dequant_f32(n1[0].numpy(), n1[1].numpy(), n1[2])
+    w_b = oracle.bf16_dequant_f32(synth.bits16(b))
+    w_d = oracle.bf16_dequant_f32(synth.bits16(bd))
+    for y, w, xx, name in ((outs[0], w_n, xb, "nvfp4"), (outs[1], w_b, xb, "bf16"), (outs[2], w_d, xdb, "bf16 K=8192")):
+        check_gemv(y, oracle.gemv_f64(xx, w), w, xx, f"mixed tiled {name} M={M}")
 
 
 def test_mixed_against_oracle(q4):
