@@ -348,10 +348,11 @@ def head_sample_calls(torch, q4, synth, M):
 
 
 def prefill_calls(torch, q4, synth):
-    """The int4 prefill GEMM (q4g128_gemm) on the layer's projection shapes at
-    M = 1024 and 4096 tokens: microseconds and TFLOP/s against the 2.5 PFLOP/s
-    dense BF16 matrix-core peak, beside torch's BF16 GEMM (the vendor library)
-    on weights dequantized to BF16 beforehand."""
+    """The int4 prefill GEMM (q4g128_gemm, the automatic kernel choice) on the
+    layer's projection shapes at M = 1024 and 4096 tokens: microseconds and
+    TFLOP/s against the 2.5 PFLOP/s dense BF16 matrix-core peak, beside the
+    tiled decode kernel over batch chunks (VARIANT_TILED) and torch's BF16 GEMM
+    (the vendor library) on weights dequantized to BF16 beforehand."""
     rec = {}
     for (N, K) in ((2048, 2048), (8192, 2048), (2048, 8192)):
         qd = tuple(t.cuda() for t in synth.q4_matrix(N, K, ("bench-prefill", N, K)))
@@ -360,10 +361,12 @@ def prefill_calls(torch, q4, synth):
             x = synth.x_bf16(M, K, ("bench-prefill-x", M, K), device="cuda")
             y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
             us = graph_us(torch, lambda: q4.q4g128_gemm(x, *qd, out=y), reps=5, iters=10)
+            uc = graph_us(torch, lambda: q4.q4g128_gemm(x, *qd, out=y, variant=q4.VARIANT_TILED), reps=5, iters=10)
             ub = graph_us(torch, lambda: torch.matmul(x, wd.t(), out=y), reps=5, iters=10)
             fl = 2.0 * M * N * K
             rec[f"N{N}_K{K}_M{M}"] = {"int4_us": round(us, 1), "int4_TFLOP_s": round(fl / us / 1e6, 1),
                                       "frac_of_bf16_mfma_peak": round(fl / us / 1e6 / 2500.0, 3),
+                                      "int4_batch_chunks_kernel_us": round(uc, 1),
                                       "bf16_library_on_dequantized_us": round(ub, 1)}
     return rec
 

@@ -18,7 +18,7 @@ __all__ = [
     "nvfp4g16_gemv_grouped", "nvfp4g16_workspace_bytes", "bf16_gemv_grouped", "bf16_workspace_bytes",
     "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample", "q4g128_gemm", "gemv_grouped_mixed", "mixed_workspace_bytes",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
-    "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
+    "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "VARIANT_GEMM", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4gemv.so")
@@ -26,11 +26,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with: python bit_weight_only_q4g128_amd/_build.py")
 lib = ctypes.CDLL(LIB_PATH)
 
-VARIANT_AUTO, VARIANT_DOT2, VARIANT_MFMA, VARIANT_STREAM, VARIANT_TILED = 0, 1, 2, 3, 4
+VARIANT_AUTO, VARIANT_DOT2, VARIANT_MFMA, VARIANT_STREAM, VARIANT_TILED, VARIANT_GEMM = 0, 1, 2, 3, 4, 5
 FMT_Q4G128, FMT_NVFP4G16, FMT_BF16 = 0, 1, 2
 
 _p, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 lib.q4g128_gemv_variant.argtypes = [_p, _i, _i, _p, _p, _p, _i, _p, _i, _p]
+lib.q4g128_gemm_variant.argtypes = [_p, _i, _i, _p, _p, _p, _i, _p, _i, _p]
 lib.nvfp4g16_gemv_variant.argtypes = [_p, _i, _i, _p, _p, _f, _i, _p, _i, _p]
 lib.bf16_gemv_variant.argtypes = [_p, _i, _i, _p, _i, _p, _i, _p]
 lib.q4g128_gemv.argtypes = [_p, _i, _i, _p, _p, _p, _i, _p, _p]
@@ -482,9 +483,11 @@ def bf16_head_sample(x, w, u, temperature: float = 0.8, top_k: int = 30, logits=
     return (tok, ti, tp, lg) if return_topk else (tok, lg)
 
 
-def q4g128_gemm(x, qweight, scale, minv, out=None):
+def q4g128_gemm(x, qweight, scale, minv, out=None, variant: int = VARIANT_AUTO):
     """Prefill GEMM y[M, N] = x[M, K] . W^T for int4 g128 weights, any M
-    (q4g128_gemm in the C header)."""
+    (q4g128_gemm_variant in the C header: VARIANT_AUTO, VARIANT_TILED for the
+    tiled decode kernel over batch chunks, VARIANT_GEMM for the large-tile
+    prefill kernel)."""
     _check(x, "x", _U16, 2); _check(qweight, "qweight", _U8, 2)
     _check(scale, "scale", _F16, 2); _check(minv, "min", _F16, 2)
     M, K = x.shape
@@ -492,7 +495,8 @@ def q4g128_gemm(x, qweight, scale, minv, out=None):
     if qweight.shape[1] * 2 != K or tuple(scale.shape) != (N, K // 128) or tuple(minv.shape) != (N, K // 128):
         raise ValueError("inconsistent shapes")
     y = _out(out, (M, N), torch.bfloat16, x)
-    _raise(lib.q4g128_gemm(x.data_ptr(), M, K, qweight.data_ptr(), scale.data_ptr(), minv.data_ptr(), N, y.data_ptr(), _stream(x)))
+    _raise(lib.q4g128_gemm_variant(x.data_ptr(), M, K, qweight.data_ptr(), scale.data_ptr(), minv.data_ptr(), N, y.data_ptr(),
+                                   variant, _stream(x)))
     return y
 
 

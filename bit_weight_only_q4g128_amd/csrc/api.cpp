@@ -49,6 +49,10 @@ bool variant_ok(int variant) {
 // alone fill the GPU (N >= 16384): with fewer rows the per-task kernel, which
 // splits K inside its workgroups, is faster for these formats (measured).
 constexpr int kTiledRowsAlone = 64 * 256;
+// Prefill above 64 batch rows: the large-tile GEMM kernel once its
+// 128 x 128 tiles number at least this many (one per CU), else the tiled
+// decode kernel over batch chunks, whose 64-row blocks occupy more CUs.
+constexpr long kGemmMinTiles = 256;
 int pick(Fmt fmt, int variant, int M, int N, int K, bool split = false) {
     if (variant == Q4_VARIANT_DOT2) return q4::dot2_supported(fmt, K) ? Q4_VARIANT_DOT2 : -1;
     if (variant == Q4_VARIANT_MFMA) return Q4_VARIANT_MFMA;
@@ -650,9 +654,11 @@ int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int 
     return Q4_OK;
 }
 
-int q4g128_gemm(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
-                uint16_t* y, void* stream) {
-    if (M >= 1 && M <= kMaxM) return q4g128_gemv_variant(x, M, K, qweight, scale, minv, N, y, Q4_VARIANT_AUTO, stream);
+int q4g128_gemm_variant(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv,
+                        int N, uint16_t* y, int variant, void* stream) {
+    if (variant != Q4_VARIANT_AUTO && variant != Q4_VARIANT_TILED && variant != Q4_VARIANT_GEMM) return Q4_EVARIANT;
+    if (variant == Q4_VARIANT_AUTO && M >= 1 && M <= kMaxM)
+        return q4g128_gemv_variant(x, M, K, qweight, scale, minv, N, y, Q4_VARIANT_AUTO, stream);
     if (M < 1 || M > (1 << 19)) return Q4_EINVAL_SHAPE;
     GemvArgs a;
     Range in[4], out;
@@ -662,10 +668,24 @@ int q4g128_gemm(const uint16_t* x, int M, int K, const uint8_t* qweight, const u
     out = range_of(y, (size_t)M * N * 2);
     for (int r = 0; r < 4; ++r)
         if (overlaps(out, in[r])) return Q4_EALIAS;
-    if (!q4::mm_chunks_supported(K)) return Q4_EVARIANT;
     a.M = M;
-    hipError_t e = q4::launch_mm_chunks(a, reinterpret_cast<hipStream_t>(stream));
+    int chosen = variant;
+    if (chosen == Q4_VARIANT_AUTO)
+        chosen = (q4::gemm_tiles(M, N, 2) >= kGemmMinTiles || !q4::mm_chunks_supported(K)) ? Q4_VARIANT_GEMM : Q4_VARIANT_TILED;
+    hipError_t e;
+    if (chosen == Q4_VARIANT_TILED) {
+        if (!q4::mm_chunks_supported(K)) return Q4_EVARIANT;
+        e = q4::launch_mm_chunks(a, reinterpret_cast<hipStream_t>(stream));
+    } else {
+        if (K >= (1 << 24)) return Q4_EVARIANT;
+        e = q4::launch_gemm(a, q4::gemm_tile_nt(M, N), reinterpret_cast<hipStream_t>(stream));
+    }
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
+int q4g128_gemm(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
+                uint16_t* y, void* stream) {
+    return q4g128_gemm_variant(x, M, K, qweight, scale, minv, N, y, Q4_VARIANT_AUTO, stream);
 }
 
 int q4_sample_topk(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, int32_t* token,

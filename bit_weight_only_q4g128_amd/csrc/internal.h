@@ -74,6 +74,12 @@ hipError_t launch_mm_mixed(const Fmt* fmts, const GemvArgs* tasks, int count, vo
 // parameters within the kernel's LDS budget (K <= 16384).
 bool mm_chunks_supported(int K);
 hipError_t launch_mm_chunks(const GemvArgs& a, hipStream_t s);
+// The prefill GEMM kernel (gemm.hip): workgroup tiles of 128 batch rows x
+// 64 * nt weight rows (nt = 2 or 4, gemm_tile_nt picks by shape), any M >= 1,
+// K % 128 == 0, K < 2^24.
+int gemm_tile_nt(int M, int N);
+long gemm_tiles(int M, int N, int nt);
+hipError_t launch_gemm(const GemvArgs& a, int nt, hipStream_t s);
 // The int4 tiled kernel with the fused activation prologue and residual
 // epilogue (GemvArgs::up, GemvArgs::resid; either may be null).
 hipError_t launch_mm_fused(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);

@@ -57,6 +57,9 @@ extern "C" {
 #define Q4_VARIANT_STREAM 3 /* M <= 4, rows of exactly 1, 2 or 4 KB (int4/NVFP4 K = 2048, 4096, 8192;
                                BF16 K = 512, 1024, 2048): every weight load issued at once, activations
                                and group parameters shared through LDS */
+#define Q4_VARIANT_GEMM 5   /* int4 prefill only (q4g128_gemm_variant): workgroup tiles of 128 batch
+                               rows x 128 or 256 weight rows over all of K, codes unpacked from LDS
+                               per wave, scale and min folded per 128-column group */
 
 /* weight formats (q4gemv_variant_name) */
 #define Q4_FMT_Q4G128 0
@@ -277,16 +280,25 @@ int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int 
  * Prefill GEMM: y[M, N] = x[M, K] . W^T for int4 g128 weights and any M >= 1
  * (the prompt's tokens before the decode loop; the rumik-oss-1-int4 card's
  * engine lists a 4-bit prefill matrix multiply beside its decode kernels,
- * "Running it").  M <= 64 takes
- * the q4g128_gemv choice; larger M runs the tiled matrix-core kernel over
- * batch chunks of up to 64 rows in one launch, every chunk an unsplit
- * product over the same weights (which stay in the memory-side cache across
- * chunks).  Same layouts and rules as q4g128_gemv, with 1 <= M <= 524288;
- * for M > 64, K % 128 == 0 and K <= 16384 (else Q4_EVARIANT; chunks of 64
- * rows up to K = 4096, 32 rows up to 12288, 16 rows up to 16384).
+ * "Running it").  M <= 64 takes the q4g128_gemv choice.  Larger M runs one
+ * of two kernels in one launch:
+ *   - Q4_VARIANT_GEMM: workgroup tiles of 128 batch rows x 128 or 256 weight
+ *     rows over all of K; the default once the 128 x 128 tiles number at
+ *     least 256 (one per CU), and for K > 16384;
+ *   - Q4_VARIANT_TILED: the tiled decode kernel over batch chunks of up to 64
+ *     rows, every chunk an unsplit product over the same weights (chunks of
+ *     64 rows up to K = 4096, 32 rows up to 12288, 16 rows up to 16384; above
+ *     that Q4_EVARIANT); the default for fewer tiles.
+ * Both compute sum over groups of scale * sum(code * x) + min * sum(x) in
+ * fp32 with every product exact, then round to BF16 once.  Same layouts and
+ * rules as q4g128_gemv, with 1 <= M <= 524288 and K % 128 == 0.
  */
 int q4g128_gemm(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv, int N,
                 uint16_t* y, void* stream);
+/* q4g128_gemm with an explicit variant: Q4_VARIANT_AUTO, Q4_VARIANT_TILED or
+ * Q4_VARIANT_GEMM (any M >= 1 for these two; else Q4_EVARIANT). */
+int q4g128_gemm_variant(const uint16_t* x, int M, int K, const uint8_t* qweight, const uint16_t* scale, const uint16_t* minv,
+                        int N, uint16_t* y, int variant, void* stream);
 
 /*
  * Sampling from the head: the step after the path.  The Rumik TTS Fast

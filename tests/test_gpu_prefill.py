@@ -1,10 +1,15 @@
 """GPU parity of the int4 prefill GEMM (q4g128_gemm through the C ABI).
 
-Against the oracle within gpu_util.check_gemv's tolerance for M from 65 to
-517 (ragged last chunks) and the layer's K values; bitwise against the
-tiled decode kernel run on each batch chunk alone (the same arithmetic per
-chunk); M <= 64 equals the GEMV's automatic choice.
+Both kernels (VARIANT_GEMM: 128-row batch tiles over all of K; VARIANT_TILED:
+the tiled decode kernel over batch chunks) against the oracle within
+gpu_util.check_gemv's tolerance for M from 65 to 517 (ragged last tiles and
+chunks), ragged N and the layer's K values; at the largest prefill shape the
+benchmark times (M = 4096, N = 8192, K = 2048) on sampled batch rows.  The
+chunked kernel bitwise against the tiled decode kernel run on each batch chunk
+alone (the same arithmetic per chunk); M <= 64 under the automatic choice
+equals the GEMV's.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -29,20 +34,46 @@ def mat(N, K, seed):
     return (gpu(qw), gpu(sc), gpu(mn)), w32
 
 
-@pytest.mark.parametrize("M,N,K", [(65, 2048, 2048), (128, 300, 2048), (200, 2048, 8192), (517, 1000, 4096), (257, 130, 8192)])
-def test_gemm_against_oracle(q4, M, N, K):
+@pytest.mark.parametrize("variant", ["GEMM", "TILED", "AUTO"])
+@pytest.mark.parametrize("M,N,K", [(65, 2048, 2048), (128, 300, 2048), (200, 2048, 8192), (517, 1000, 4096), (257, 130, 8192),
+                                   (300, 515, 2048)])
+def test_gemm_against_oracle(q4, M, N, K, variant):
     dev, w32 = mat(N, K, ("gemm", N, K))
     x = synth.x_bf16(M, K, ("gemm-x", M, K))
-    y = q4.q4g128_gemm(gpu(x), *dev)
+    y = q4.q4g128_gemm(gpu(x), *dev, variant=getattr(q4, "VARIANT_" + variant))
     xb = synth.bits16(x)
-    check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"gemm M={M} N={N} K={K}")
+    check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"gemm {variant} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N", [(1, 2048), (17, 64), (64, 2048)])
+def test_gemm_kernel_small_batches(q4, M, N):
+    """The large-tile kernel at batch sizes the automatic choice gives to the GEMV."""
+    dev, w32 = mat(N, 2048, ("gemm-smallb", N))
+    x = synth.x_bf16(M, 2048, ("gemm-smallb-x", M))
+    y = q4.q4g128_gemm(gpu(x), *dev, variant=q4.VARIANT_GEMM)
+    xb = synth.bits16(x)
+    check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"gemm kernel M={M} N={N}")
+
+
+def test_gemm_full_size_sampled_rows(q4):
+    """M = 4096, N = 8192, K = 2048 (256-row weight tiles, 1024 workgroups):
+    every output of 24 sampled batch rows (first, last, tile edges, random)
+    against the oracle; the whole output finite."""
+    M, N, K = 4096, 8192, 2048
+    dev, w32 = mat(N, K, ("gemm-full",))
+    x = synth.x_bf16(M, K, ("gemm-full-x",))
+    y = q4.q4g128_gemm(gpu(x), *dev)
+    assert torch.isfinite(y.float()).all()
+    rows = sorted({0, 1, 127, 128, 129, 2047, 2048, 4094, 4095} | set(int(r) for r in np.random.default_rng(7).choice(M, 15, replace=False)))
+    xb = synth.bits16(x)[rows]
+    check_gemv(y[rows], oracle.gemv_f64(xb, w32), w32, xb, "gemm M=4096 N=8192 K=2048 sampled rows")
 
 
 @pytest.mark.parametrize("M,K,chunk", [(192, 2048, 64), (200, 2048, 64), (100, 8192, 32), (70, 4096, 64)])
 def test_gemm_chunks_equal_tiled_decode_calls(q4, M, K, chunk):
     dev, _ = mat(2048, K, ("gemm-chunks", K))
     x = gpu(synth.x_bf16(M, K, ("gemm-chunks-x", M, K)))
-    y = q4.q4g128_gemm(x, *dev)
+    y = q4.q4g128_gemm(x, *dev, variant=q4.VARIANT_TILED)
     for m0 in range(0, M, chunk):
         part = x[m0:m0 + chunk].contiguous()
         ref = q4.q4g128_gemv(part, *dev, variant=q4.VARIANT_TILED)
@@ -57,9 +88,14 @@ def test_gemm_small_m_is_the_gemv(q4, M):
 
 
 def test_gemm_rejects(q4):
-    dev, _ = mat(64, 32768, ("gemm-bad",))
-    with pytest.raises(q4.Q4GemvError):          # K beyond the unsplit LDS budget
-        q4.q4g128_gemm(gpu(synth.x_bf16(100, 32768, "gemm-bad-x")), *dev)
+    dev, w32 = mat(64, 32768, ("gemm-bad",))
+    x = synth.x_bf16(100, 32768, "gemm-bad-x")
+    with pytest.raises(q4.Q4GemvError):          # K beyond the chunked kernel's unsplit LDS budget
+        q4.q4g128_gemm(gpu(x), *dev, variant=q4.VARIANT_TILED)
+    with pytest.raises(q4.Q4GemvError):          # not a prefill variant
+        q4.q4g128_gemm(gpu(x), *dev, variant=q4.VARIANT_STREAM)
+    xb = synth.bits16(x)                         # the automatic choice takes the large-tile kernel there
+    check_gemv(q4.q4g128_gemm(gpu(x), *dev), oracle.gemv_f64(xb, w32), w32, xb, "gemm K=32768")
     d2, w2 = mat(64, 16384, ("gemm-16k",))       # the widest K: 16-row chunks
     x2 = synth.x_bf16(70, 16384, "gemm-16k-x")
     xb = synth.bits16(x2)
