@@ -13,8 +13,10 @@
 //
 //   * activations: 128 rows x 128 columns of BF16, each 8-column chunk stored
 //     in the pair order (x0,x4)(x1,x5)(x2,x6)(x3,x7) that matches the nibble
-//     unpacking of the weights; rows padded to 272 bytes so that the 16 rows
-//     of one fragment read fall in 16 distinct 16-byte bank slots;
+//     unpacking of the weights; 16-byte chunk c of row r sits at chunk
+//     c ^ (r % 16) of its 256-byte row, so the 16 rows of one fragment read,
+//     and the 16 chunks of one row that 16 consecutive lanes stage, fall in
+//     16 distinct 16-byte bank slots;
 //   * weight codes stay packed in LDS (BN rows x 64 bytes, as four planes of
 //     16 bytes per row, one per 32-column k-step): each wave turns its lane's
 //     dword of 8 codes into the BF16 values 128 + code (exact) right before
@@ -25,9 +27,11 @@
 //     the threads that stage them).
 //
 // The MFMAs give D = sum over the group of (128 + code) * x per output (the
-// group's first k-step starts from zero), and the wave folds
-// y += s * D + m' * SX, which is sum (code * s + min) * x up to fp32 rounding
-// (every product in D is exact).
+// group's first k-step starts from zero), and the wave folds y += s * D; every
+// fourth group (and after the last) one fp32 MFMA per tile adds the term
+// sum over those groups of m' * SX (a 16 x 4 by 4 x 16 product: m' and SX
+// of the last groups stay in an eight-slot LDS ring).  The result is
+// sum (code * s + min) * x up to fp32 rounding (every product in D is exact).
 //
 // MFMA operand layout (16x16x32): lane l holds A row l % 16 (a weight row) and
 // B column l % 16 (a batch row), for k-step h the 8 columns 32 h + 8 (l / 16)
@@ -46,7 +50,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kBM = 128;                 // batch rows per workgroup
-constexpr int kXPitch = 272;             // LDS bytes per activation row (128 BF16 + 16 pad)
+constexpr int kXPitch = 256;             // LDS bytes per activation row (128 BF16, chunks swizzled)
 constexpr int kSuper = 8;                // batch blocks per super-row of the tile order
 constexpr uint32_t kOnes = 0x3F803F80u;  // BF16 pair (1, 1)
 
@@ -61,17 +65,18 @@ __device__ __forceinline__ float sum8(const u32x4& v, float acc) {
     return dot2(v.w, kOnes, dot2(v.z, kOnes, dot2(v.y, kOnes, dot2(v.x, kOnes, acc))));
 }
 
-// LDS layout of one group buffer (two of them)
+// LDS layout: two group buffers, then the rings of m' and SX
+constexpr int kRing = 8;
 template <int NT>
 struct GemmLayout {
     static constexpr int kBN = 64 * NT;
     static constexpr int kX = 0;                                // [kBM][kXPitch]
     static constexpr int kCodes = kX + kBM * kXPitch;            // [4 planes][kBN][16]
-    static constexpr int kSX = kCodes + kBN * 64;               // float [kBM]
-    static constexpr int kS = kSX + kBM * 4;                    // float [kBN]
-    static constexpr int kM = kS + kBN * 4;                     // float [kBN]
-    static constexpr int kBuf = kM + kBN * 4;
-    static constexpr int kBytes = 2 * kBuf;
+    static constexpr int kS = kCodes + kBN * 64;                // float [kBN]
+    static constexpr int kBuf = kS + kBN * 4;
+    static constexpr int kRingM = 2 * kBuf;                     // float [kRing][kBN]
+    static constexpr int kRingSX = kRingM + kRing * kBN * 4;    // float [kRing][kBM]
+    static constexpr int kBytes = kRingSX + kRing * kBM * 4;
 };
 
 template <int NT>
@@ -103,12 +108,12 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(scale + (size_t)n0 * G, (uint32_t)rows_n * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rn = make_rsrc(minv + (size_t)n0 * G, (uint32_t)rows_n * (uint32_t)G * 2u);
 
-    // loader roles per group: activation chunks xc and xc + 8 of rows xr and
-    // xr + 64; code chunks (planes) cp and cp + 2 of row cr for tid < 2 BN;
-    // the scale/min pair of row tid for tid < BN
-    const int xr = tid >> 3, xc = tid & 7;
+    // loader roles per group: activation chunk xc of rows xr + 32 i (i < 4);
+    // code chunks (planes) cp and cp + 2 of row cr for tid < 2 BN; the
+    // scale/min pair of row tid for tid < BN
+    const int xr = tid >> 4, xc = tid & 15;
     const uint32_t vx = (uint32_t)xr * (uint32_t)K * 2u + (uint32_t)xc * 16u;
-    const uint32_t vx64 = 64u * (uint32_t)K * 2u;
+    const uint32_t vx32 = 32u * (uint32_t)K * 2u;
     const int cr = tid >> 1, cp = tid & 1;
     const bool has_code = tid < 2 * BN, has_scale = tid < BN;
     const uint32_t vc = (uint32_t)cr * (uint32_t)(K >> 1) + (uint32_t)cp * 16u;
@@ -120,10 +125,8 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
 
     auto load = [&](int g) {
         const uint32_t sx0 = (uint32_t)g * 256u;
-        px[0] = ld16(rx, vx, sx0);
-        px[1] = ld16(rx, vx, sx0 + 128u);
-        px[2] = ld16(rx, vx + vx64, sx0);
-        px[3] = ld16(rx, vx + vx64, sx0 + 128u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) px[i] = ld16(rx, vx + (uint32_t)i * vx32, sx0);
         if (has_code) {
             pc[0] = ld16(rc, vc, (uint32_t)g * 64u);
             pc[1] = ld16(rc, vc, (uint32_t)g * 64u + 32u);
@@ -135,12 +138,14 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
     };
     auto store = [&](int g) {
         uint8_t* B = lds + (g & 1) * Lay::kBuf;
+        float* ringM = reinterpret_cast<float*>(lds + Lay::kRingM) + (g & (kRing - 1)) * BN;
+        float* ringSX = reinterpret_cast<float*>(lds + Lay::kRingSX) + (g & (kRing - 1)) * kBM;
         uint32_t p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             xq4_pairs(px[i].x, px[i].y, px[i].z, px[i].w, p);
-            const int row = xr + 64 * (i >> 1), col = xc + 8 * (i & 1);
-            *reinterpret_cast<u32x4*>(B + Lay::kX + row * kXPitch + col * 16) = u32x4{p[0], p[1], p[2], p[3]};
+            const int row = xr + 32 * i;
+            *reinterpret_cast<u32x4*>(B + Lay::kX + row * kXPitch + ((xc ^ (row & 15)) << 4)) = u32x4{p[0], p[1], p[2], p[3]};
         }
         if (has_code) {
             *reinterpret_cast<u32x4*>(B + Lay::kCodes + cp * BN * 16 + cr * 16) = pc[0];
@@ -149,13 +154,12 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
         if (has_scale) {
             const float s = f16_to_f32(ps);
             reinterpret_cast<float*>(B + Lay::kS)[tid] = s;
-            reinterpret_cast<float*>(B + Lay::kM)[tid] = __builtin_fmaf(-128.0f, s, f16_to_f32(pm));
+            ringM[tid] = __builtin_fmaf(-128.0f, s, f16_to_f32(pm));
         }
-        const float g0 = group_sum(sum8(px[1], sum8(px[0], 0.f)), 8);
-        const float g1 = group_sum(sum8(px[3], sum8(px[2], 0.f)), 8);
-        if (xc == 7) {
-            reinterpret_cast<float*>(B + Lay::kSX)[xr] = g0;
-            reinterpret_cast<float*>(B + Lay::kSX)[xr + 64] = g1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float gs = group_sum(sum8(px[i], 0.f), 16);
+            if (xc == 15) ringSX[xr + 32 * i] = gs;
         }
     };
 
@@ -169,7 +173,11 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
     store(0);
     __syncthreads();
 
-    const int xrow = (64 * wm + lr) * kXPitch + 16 * lq;
+    // row 64 wm + 16 u + lr (row % 16 == lr), chunk 4 h + lq, swizzled
+    const int xrow = (64 * wm + lr) * kXPitch;
+    int xoff[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) xoff[h] = xrow + (((4 * h + lq) ^ lr) << 4);
     const int crow = (16 * NT * wn + lr) * 16 + 4 * lq;
     for (int g = 0; g < G; ++g) {
         const bool more = g + 1 < G;
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
             bf16x8_g xf[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                xf[u] = *reinterpret_cast<const bf16x8_g*>(B + Lay::kX + xrow + 16 * u * kXPitch + 64 * h);
+                xf[u] = *reinterpret_cast<const bf16x8_g*>(B + Lay::kX + xoff[h] + 16 * u * kXPitch);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint32_t cw = *reinterpret_cast<const uint32_t*>(B + Lay::kCodes + h * BN * 16 + crow + 256 * t);
@@ -193,21 +201,32 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
             }
         }
         {
-            const float* SX = reinterpret_cast<const float*>(B + Lay::kSX);
             const float* S = reinterpret_cast<const float*>(B + Lay::kS);
-            const float* Mp = reinterpret_cast<const float*>(B + Lay::kM);
-            float sx[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) sx[u] = SX[64 * wm + 16 * u + lr];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const f32x4 s4 = *reinterpret_cast<const f32x4*>(S + 16 * NT * wn + 16 * t + 4 * lq);
-                const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mp + 16 * NT * wn + 16 * t + 4 * lq);
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) Y[t][u][v] = __builtin_fmaf(s4[v], D[t][u][v], __builtin_fmaf(m4[v], sx[u], Y[t][u][v]));
+                    for (int v = 0; v < 4; ++v) Y[t][u][v] = __builtin_fmaf(s4[v], D[t][u][v], Y[t][u][v]);
             }
+        }
+        if ((g & 3) == 3 || !more) {
+            // y += m' . SX over groups g0 .. g: lane l holds m' of weight row
+            // l % 16 and SX of batch row l % 16 for group g0 + l / 16
+            const int g0 = g & ~3, gl = g0 + lq;
+            const bool live = gl <= g;
+            const float* ringM = reinterpret_cast<const float*>(lds + Lay::kRingM) + (gl & (kRing - 1)) * BN;
+            const float* ringSX = reinterpret_cast<const float*>(lds + Lay::kRingSX) + (gl & (kRing - 1)) * kBM;
+            float am[NT], bs[4];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) am[t] = live ? ringM[16 * NT * wn + 16 * t + lr] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) bs[u] = live ? ringSX[64 * wm + 16 * u + lr] : 0.f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) Y[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[t], bs[u], Y[t][u], 0, 0, 0);
         }
         if (more) store(g + 1);
         __syncthreads();
