@@ -650,6 +650,19 @@ def counters_pass(q4, synth, torch, head_rows, M):
     log(f"bench: counters pass at M={M} done ({len(calls)} launches per step, csrc digest {csrc_digest(M)})")
 
 
+def counters_prefill(q4, synth, torch):
+    """Workload for hardware-counter runs of the prefill GEMM (no timing): the
+    large-tile kernel on the 8192 x 2048 projection at M = 4096, five times."""
+    N, K, M = 8192, 2048, 4096
+    qd = tuple(t.cuda() for t in synth.q4_matrix(N, K, ("bench-prefill", N, K)))
+    x = synth.x_bf16(M, K, ("bench-prefill-x", M, K), device="cuda")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        q4.q4g128_gemm(x, *qd, out=y, variant=q4.VARIANT_GEMM)
+    torch.cuda.synchronize()
+    log(f"bench: prefill counters pass done (N={N} K={K} M={M}, 5 launches)")
+
+
 def mode_key(k):
     M, mode = k
     return f"{M}_{mode}" if isinstance(M, str) else f"M{M}_{mode}"
@@ -680,6 +693,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
     ap.add_argument("--counters-m", type=int, choices=(1, 48), default=1, help="batch size of the --counters workload")
+    ap.add_argument("--counters-prefill", action="store_true",
+                    help="run the prefill GEMM (8192 x 2048, M = 4096) five times for rocprofv3 --pmc passes; no timing")
     ap.add_argument("--modes", default="M1_grouped,M1_fused,M1_plain,M48_grouped,M48_fused,M48_plain,NVFP4_M1_grouped,NVFP4_M48_grouped,"
                                        "NVFP4_M1_plain,NVFP4_M48_plain",
                     help="comma list of timed modes; M1_grouped is always timed (it is the headline value)")
@@ -695,6 +710,9 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     torch.cuda.set_device(0)
     head_rows = synth.HEAD_FULL[0] if args.head == "full" else synth.HEAD_SLICE[0]
+    if args.counters_prefill:
+        counters_prefill(q4, synth, torch)
+        return
     if args.counters:
         counters_pass(q4, synth, torch, head_rows, args.counters_m)
         return
