@@ -301,6 +301,33 @@ def test_mixed_validation():
     assert call([mt(0, FN), mt(1, FB, y=A + (4 << 26))]) == EALIAS        # two tasks share an output
 
 
+def test_gemm_validation():
+    """q4g128_gemm_variant rejects bad arguments on the host: the variant (only
+    AUTO, TILED and GEMM), M, K, pointers, alignment and aliasing; the chunked
+    kernel's K limit under an explicit TILED; M <= 64 under AUTO is the GEMV
+    (the GEMV's M limit does not apply to the prefill variants)."""
+    lib.q4g128_gemm_variant.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+
+    def call(x=A, M=1024, K=2048, qw=A + (1 << 28), sc=A + (2 << 28), mn=A + (3 << 28), N=2048, y=A + (4 << 28), variant=5):
+        return lib.q4g128_gemm_variant(x, M, K, qw, sc, mn, N, y, variant, None)
+
+    assert call(variant=1) == EVARIANT                     # a GEMV-only variant
+    assert call(variant=3) == EVARIANT
+    assert call(variant=9) == EVARIANT
+    assert call(M=0) == ESHAPE
+    assert call(M=(1 << 19) + 1) == ESHAPE
+    assert call(K=2000) == ESHAPE                          # K % 128
+    assert call(K=65536) == ESHAPE                         # beyond the library's K limit
+    assert call(x=None) == EPTR
+    assert call(mn=None) == EPTR
+    assert call(qw=A + (1 << 28) + 8) == EALIGN
+    assert call(y=A + (1 << 21)) == EALIAS                 # y [1024, 2048] overlaps x [1024, 2048] (4 MiB)
+    assert call(K=32768, variant=4) == EVARIANT            # the chunked kernel's LDS limit
+    assert call(M=65, variant=0, x=None) == EPTR           # AUTO above 64 rows: prefill checks
+    assert call(M=1, variant=0, K=2000) == ESHAPE          # AUTO at M <= 64: the GEMV's checks
+
+
 def test_stream_read_validation():
     import ctypes
     lib.q4gemv_stream_read.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
