@@ -55,6 +55,18 @@ def test_gemm_kernel_small_batches(q4, M, N):
     check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"gemm kernel M={M} N={N}")
 
 
+@pytest.mark.parametrize("M,N,K", [(130, 37, 128), (129, 6, 640), (1, 1, 128), (77, 260, 384), (300, 515, 1152)])
+def test_gemm_kernel_odd_shapes(q4, M, N, K):
+    """The large-tile kernel where the min term's four-group sets end early
+    (K / 128 = 1, 3, 5, 9 groups), N is not a multiple of 4 or below one
+    16-row tile, and M ends inside a 16-row batch tile."""
+    dev, w32 = mat(N, K, ("gemm-odd", N, K))
+    x = synth.x_bf16(M, K, ("gemm-odd-x", M, K))
+    y = q4.q4g128_gemm(gpu(x), *dev, variant=q4.VARIANT_GEMM)
+    xb = synth.bits16(x)
+    check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"gemm kernel M={M} N={N} K={K}")
+
+
 def test_gemm_full_size_sampled_rows(q4):
     """M = 4096, N = 8192, K = 2048 (256-row weight tiles, 1024 workgroups):
     every output of 24 sampled batch rows (first, last, tile edges, random)
