@@ -185,19 +185,20 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
         const uint8_t* B = lds + (g & 1) * Lay::kBuf;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            bf16x8_g xf[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                xf[u] = *reinterpret_cast<const bf16x8_g*>(B + Lay::kX + xoff[h] + 16 * u * kXPitch);
+            bf16x8_g a[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint32_t cw = *reinterpret_cast<const uint32_t*>(B + Lay::kCodes + h * BN * 16 + crow + 256 * t);
                 uint32_t p[4];
                 q4_pairs(cw, p);
-                const bf16x8_g a = __builtin_bit_cast(bf16x8_g, u32x4{p[0], p[1], p[2], p[3]});
+                a[t] = __builtin_bit_cast(bf16x8_g, u32x4{p[0], p[1], p[2], p[3]});
+            }
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    D[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xf[u], h == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][u], 0, 0, 0);
+            for (int u = 0; u < 4; ++u) {
+                const bf16x8_g xf = *reinterpret_cast<const bf16x8_g*>(B + Lay::kX + xoff[h] + 16 * u * kXPitch);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    D[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], xf, h == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : D[t][u], 0, 0, 0);
             }
         }
         {
