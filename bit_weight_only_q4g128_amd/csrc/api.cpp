@@ -162,13 +162,19 @@ int plan_checked(Fmt fmt, const GemvArgs* a, const Range (*in)[4], const Range* 
     return Q4_OK;
 }
 
+// Workspace a planned grouped launch can use (0: no K split planned).
+size_t grouped_ws_bytes(Fmt fmt, int chosen, const GemvArgs* a, int count) {
+    if (chosen == Q4_VARIANT_TILED) return q4::mm_workspace_bytes(fmt, a, count);
+    return 0;
+}
+
 // A grouped call of one format after validation: a workspace too small for
 // the planned split (or a launch too large to split) runs unsplit, which
 // every task must then allow.
 int run_grouped(Fmt fmt, int chosen, const GemvArgs* a, int count, int M, void* workspace, size_t workspace_bytes, void* stream) {
     const bool split = workspace != nullptr && workspace_bytes > 0;
     if (chosen == Q4_VARIANT_TILED && split) {
-        const size_t need = q4::mm_workspace_bytes(fmt, a, count);
+        const size_t need = grouped_ws_bytes(fmt, chosen, a, count);
         if (need == 0 || workspace_bytes < need) {
             for (int i = 0; i < count; ++i)
                 if (!q4::mm_supported(fmt, M, a[i].K, false)) return Q4_EVARIANT;
@@ -368,7 +374,7 @@ int q4g128_workspace_bytes(const q4g128_task* tasks, int count, int M, size_t* b
     int chosen = 0;
     int rc = plan_group(tasks, count, M, Q4_VARIANT_AUTO, true, a, &chosen);
     if (rc) return rc;
-    *bytes = chosen == Q4_VARIANT_TILED ? q4::mm_workspace_bytes(q4::kFmtQ4, a, count) : 0;
+    *bytes = grouped_ws_bytes(q4::kFmtQ4, chosen, a, count);
     return Q4_OK;
 }
 
@@ -515,6 +521,8 @@ int nvfp4g16_dequant_f32(const uint8_t* qweight, const uint8_t* scale_e4m3, floa
 // Workspace of a fused tiled call: the split-K part, then (256-byte aligned)
 // one h buffer per gated task.
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+// h starts after the split-K part, and in any case past the arrival counters
+size_t fused_h_offset(size_t need) { return align256(need > q4::kWsCounterBytes ? need : q4::kWsCounterBytes); }
 size_t fused_h_bytes(const GemvArgs* a, int count) {
     size_t n = 0;
     for (int i = 0; i < count; ++i)
@@ -556,7 +564,7 @@ int q4gemv_grouped_mixed(const q4gemv_mixed_task* tasks, int count, int M, void*
         rc = mixed_subgroup(a, fmts, count, order[f], M, split, sub[f], &n[f], &chosen[f]);
         if (rc) return rc;
         if (chosen[f] == Q4_VARIANT_TILED && split) {
-            const size_t need = q4::mm_workspace_bytes(order[f], sub[f], n[f]);
+            const size_t need = grouped_ws_bytes(order[f], chosen[f], sub[f], n[f]);
             if (need == 0 || workspace_bytes < need)
                 for (int i = 0; i < n[f]; ++i)
                     if (!q4::mm_supported(order[f], M, sub[f][i].K, false)) return Q4_EVARIANT;
@@ -584,8 +592,8 @@ int q4gemv_mixed_workspace_bytes(const q4gemv_mixed_task* tasks, int count, int 
             int n = 0, chosen = 0;
             rc = mixed_subgroup(a, fmts, count, static_cast<Fmt>(f), M, true, sub, &n, &chosen);
             if (rc) return rc;
-            if (n && chosen == Q4_VARIANT_TILED) {
-                const size_t b = q4::mm_workspace_bytes(static_cast<Fmt>(f), sub, n);
+            if (n) {
+                const size_t b = grouped_ws_bytes(static_cast<Fmt>(f), chosen, sub, n);
                 need = b > need ? b : need;
             }
         }
@@ -598,44 +606,46 @@ int q4g128_gemv_fused(const q4g128_fused_task* tasks, int count, int M, void* wo
     GemvArgs a[q4::kMaxTasks];
     bool tiled = false;
     const bool split = workspace != nullptr && workspace_bytes > 0;
+    if (workspace && !aligned(workspace, 256)) return Q4_EALIGN;
     int rc = check_fused(tasks, count, M, split, a, &tiled);
     if (rc) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (!tiled) {
         e = q4::launch_stream_fused(a, count, s);
-    } else {
-        const size_t need = q4::mm_workspace_bytes(q4::kFmtQ4, a, count);
-        const size_t h_off = align256(need), h_bytes = fused_h_bytes(a, count);
-        size_t mm_bytes = workspace_bytes;
-        if (split && h_bytes > 0 && workspace_bytes >= h_off + h_bytes) {
-            // h formed once into the workspace; the tiled kernel reads it as x
-            const uint16_t* g[q4::kMaxTasks];
-            const uint16_t* u[q4::kMaxTasks];
-            uint16_t* h[q4::kMaxTasks];
-            size_t n[q4::kMaxTasks];
-            int ng = 0;
-            uint8_t* p = static_cast<uint8_t*>(workspace) + h_off;
-            for (int i = 0; i < count; ++i) {
-                if (!a[i].up) continue;
-                g[ng] = a[i].x; u[ng] = a[i].up; h[ng] = reinterpret_cast<uint16_t*>(p);
-                n[ng] = (size_t)M * a[i].K;
-                a[i].x = h[ng];
-                a[i].up = nullptr;
-                p += align256(n[ng] * 2);
-                ++ng;
-            }
-            if (q4::launch_silu_mul(g, u, h, n, ng, s) != hipSuccess) return Q4_ELAUNCH;
-            mm_bytes = h_off;
-        }
-        if (split) {
-            if (need == 0 || mm_bytes < need) {
-                for (int i = 0; i < count; ++i)
-                    if (!q4::mm_supported(q4::kFmtQ4, M, a[i].K, false)) return Q4_EVARIANT;
-            }
-        }
-        e = q4::launch_mm_fused(a, count, workspace, mm_bytes, s);
+        return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
     }
+    // Everything is planned and checked before the first enqueue.  The h
+    // buffers start past the split-K part and never below the counter region,
+    // which other calls on the same workspace rely on staying zero.
+    const size_t need = q4::mm_workspace_bytes(q4::kFmtQ4, a, count);
+    const size_t h_off = fused_h_offset(need), h_bytes = fused_h_bytes(a, count);
+    const bool form_h = split && h_bytes > 0 && workspace_bytes >= h_off + h_bytes;
+    const size_t mm_bytes = form_h ? h_off : workspace_bytes;
+    if (split && (need == 0 || mm_bytes < need)) {
+        for (int i = 0; i < count; ++i)
+            if (!q4::mm_supported(q4::kFmtQ4, M, a[i].K, false)) return Q4_EVARIANT;
+    }
+    if (form_h) {
+        // h formed once into the workspace; the tiled kernel reads it as x
+        const uint16_t* g[q4::kMaxTasks];
+        const uint16_t* u[q4::kMaxTasks];
+        uint16_t* h[q4::kMaxTasks];
+        size_t n[q4::kMaxTasks];
+        int ng = 0;
+        uint8_t* p = static_cast<uint8_t*>(workspace) + h_off;
+        for (int i = 0; i < count; ++i) {
+            if (!a[i].up) continue;
+            g[ng] = a[i].x; u[ng] = a[i].up; h[ng] = reinterpret_cast<uint16_t*>(p);
+            n[ng] = (size_t)M * a[i].K;
+            a[i].x = h[ng];
+            a[i].up = nullptr;
+            p += align256(n[ng] * 2);
+            ++ng;
+        }
+        if (q4::launch_silu_mul(g, u, h, n, ng, s) != hipSuccess) return Q4_ELAUNCH;
+    }
+    e = q4::launch_mm_fused(a, count, workspace, mm_bytes, s);
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 
@@ -649,8 +659,9 @@ int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int 
         *bytes = 0;
         return Q4_OK;
     }
+    const size_t need = q4::mm_workspace_bytes(q4::kFmtQ4, a, count);
     const size_t h_bytes = fused_h_bytes(a, count);
-    *bytes = (h_bytes ? align256(q4::mm_workspace_bytes(q4::kFmtQ4, a, count)) : q4::mm_workspace_bytes(q4::kFmtQ4, a, count)) + h_bytes;
+    *bytes = h_bytes ? fused_h_offset(need) + h_bytes : need;
     return Q4_OK;
 }
 
@@ -705,6 +716,8 @@ int bf16_head_sample(const uint16_t* x, int M, int K, const uint16_t* w, int N, 
     if (rc) return rc;
     for (int r = 0; r < 2; ++r)
         if (overlaps(out, in[r])) return Q4_EALIAS;
+    // the GEMV writes the logits before the sampler reads u
+    if (u && overlaps(out, range_of(u, (size_t)M * 4))) return Q4_EALIAS;
     rc = check_sample(logits, M, N, temperature, top_k, u, token, topk_index, topk_prob, in, 2);
     if (rc) return rc;
     const int chosen = pick(q4::kFmtBf16, Q4_VARIANT_AUTO, M, N, K);

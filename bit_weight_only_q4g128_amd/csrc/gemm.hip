@@ -234,7 +234,9 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
     }
 
     // y: lane holds weight rows n .. n + 3 of batch row m for each (t, u)
-    const bool vec = (N & 3) == 0;
+    // 8-byte stores only where every row start is 8-byte aligned (y itself
+    // need only be 2-byte aligned)
+    const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int m = m0 + 64 * wm + 16 * u + lr;

@@ -139,7 +139,7 @@ __device__ __forceinline__ int frag_slot(int L, int s) { return L ^ (2 * s + ((L
 // tasks can share one workspace: the arrival counters of all split tasks of a
 // call in the first kCntBytes (every call leaves them zero), partial tiles
 // after them.
-constexpr size_t kCntBytes = 64 * 1024;
+constexpr size_t kCntBytes = kWsCounterBytes;
 constexpr int kCoherent = 16;   // buffer cache policy sc1: device-coherent, not held in the per-XCD L2
 
 // slices whose partial tile a reducing wave loads at once (4 * MT registers
@@ -611,11 +611,17 @@ __device__ __forceinline__ void tiled_body(const MmTable& tt, const int ti, uint
     }
 
     // --------------------------------------------------- split-K completion
+    // Each wave waits for its partial stores; the barrier orders them before
+    // the counter update, an acquire-release read-modify-write at device
+    // (agent) scope: its release publishes every store that happens before
+    // it (the other waves' through the barrier), and in the last slice to
+    // arrive its acquire orders the other slices' partials before the reads
+    // below (the other waves' through the second barrier).
     unsigned* cnt = tt.t[ti].cnt;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __shared__ unsigned s_prev;
-    if (tid == 0) s_prev = __hip_atomic_fetch_add(&cnt[blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) s_prev = __hip_atomic_fetch_add(&cnt[blk], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_prev != (unsigned)(KS - 1)) return;
     if (wave < kCompute) {

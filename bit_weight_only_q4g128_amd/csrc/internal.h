@@ -63,6 +63,9 @@ hipError_t launch_stream_fused(const GemvArgs* tasks, int count, hipStream_t s);
 // split over workgroups; without one every task runs unsplit, which
 // mm_supported(fmt, M, K, false) must allow.
 bool mm_supported(Fmt fmt, int M, int K, bool split);
+// Every workspace starts with this many bytes of arrival counters that each
+// call leaves at zero; scratch lies after them.
+constexpr size_t kWsCounterBytes = 64 * 1024;
 size_t mm_workspace_bytes(Fmt fmt, const GemvArgs* tasks, int count);
 hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
 // The tiled kernel over NVFP4 and BF16 tasks in one launch (fmts[i] per

@@ -233,6 +233,10 @@ def test_fused_validation():
     assert call([ft(0, residual=A + (6 << 26) + 1)]) == EALIGN
     assert call([ft(0, y=A + (5 << 26) + 64)]) == EALIAS               # over its own up activations
     assert call([ft(0, residual=A + (4 << 26) + 2)]) == EALIAS         # residual partly over y
+    # a workspace must be 256-byte aligned (rejected before anything is planned)
+    assert lib.q4g128_gemv_fused((FT * 1)(ft(0)), 1, 48, A + (7 << 26) + 16, 1 << 20, None) == EALIGN
+    # the h buffers never start inside the 64 KiB counter region, also when no K split is planned
+    assert size([ft(0, K=512, N=256, residual=None)], M=16) == OK and nb.value >= 64 * 1024 + 16 * 512 * 2
     assert call([ft(0), ft(1, y=A + (6 << 26))]) == EALIAS              # over another task's residual
     assert call([ft(0), ft(1, y=A + (4 << 26))]) == EALIAS              # two tasks share an output
     assert call([ft(0, K=32768, N=64)], M=64) == EVARIANT               # unsplit tiled kernel: too many groups
@@ -265,6 +269,7 @@ def test_sample_validation():
     assert h(lg=W + 64) == EALIAS             # logits over the weights
     assert h(tok=X) == EALIAS                 # token over the activations
     assert h(ti=W + 128) == EALIAS
+    assert h(lg=U - 64) == EALIAS             # logits written over the uniforms before they are read
 
 
 def test_mixed_validation():

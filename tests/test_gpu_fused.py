@@ -197,3 +197,29 @@ def test_fused_rejects_and_odd_shapes(q4):
     x2 = gpu(synth.x_bf16(1, 1152, "fz-odd-x"))
     (y,) = q4.q4g128_gemv_fused([task(d2, x2)])
     assert torch.equal(y.view(torch.int16), q4.q4g128_gemv(x2, *d2, variant=q4.VARIANT_TILED).view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [16, 48])
+def test_fused_unsplit_then_split_call_share_workspace(q4, M):
+    """A gated call whose tiled plan needs no K split (K = 512) keeps its h
+    past the arrival counters; a split call on the same workspace afterwards
+    must then find the counters at zero and produce the oracle's result."""
+    d1, w1 = mat(256, 512, ("fz-ws-a", M))
+    g, u = synth.x_bf16(M, 512, ("fz-ws-g", M)), synth.x_bf16(M, 512, ("fz-ws-u", M))
+    items = [task(d1, gpu(g), up=gpu(u))]
+    d2, w2 = mat(2048, 8192, ("fz-ws-b",))
+    x2 = synth.x_bf16(M, 8192, ("fz-ws-x2", M))
+    grouped = [(gpu(x2), *d2, None)]
+    n = max(q4.q4g128_fused_workspace_bytes(items), q4.q4g128_workspace_bytes(grouped))
+    assert q4.q4g128_workspace_bytes(grouped) > 0, "the second call must plan a K split"
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    (y1,) = q4.q4g128_gemv_fused(items, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:64 * 1024].count_nonzero()) == 0, "counter region written by the fused call"
+    (y2,) = q4.q4g128_gemv_grouped(grouped, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:64 * 1024].count_nonzero()) == 0
+    hb = oracle.silu_mul_bf16(bits(g), bits(u))
+    check_gemv(y1, oracle.gemv_f64(hb, w1), w1, hb, f"fused K=512 M={M}")
+    xb = bits(x2)
+    check_gemv(y2, oracle.gemv_f64(xb, w2), w2, xb, f"split after fused M={M}")

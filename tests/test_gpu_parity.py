@@ -630,3 +630,21 @@ def test_stream_read_touches_every_byte(q4):
         expect ^= int(np.bitwise_xor.reduce(b.numpy().view(np.uint32)))
     got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
     assert got == expect
+
+
+# the down projection's shape at M = 4, where the automatic choice is the
+# packed-dot kernel (the streaming kernel's LDS budget excludes K = 8192 at
+# this M): one-hot bitwise and the synthetic layer weights within tolerance
+def test_q4_down_shape_M4_auto(q4):
+    N, K, M = 2048, 8192, 4
+    name = q4.variant_name(0, 0, M, N, K)
+    lay, w32 = _layer_q4()
+    qw, sc, mn = lay["down"]
+    ks = _onehot_ks(K, M, 700)
+    y = q4.q4g128_gemv(gpu(onehot_x(K, ks)), gpu(qw), gpu(sc), gpu(mn))
+    got = y.cpu().float().numpy()
+    exp = torch.from_numpy(rn_bf16_bits(w32["down"][:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(got, exp), (name, np.argwhere(got != exp)[:4])
+    x = synth.x_bf16(M, K, ("down-M4-x",))
+    ref = oracle.gemv_f64(x_bits(x), w32["down"])
+    check_gemv(q4.q4g128_gemv(gpu(x), gpu(qw), gpu(sc), gpu(mn)), ref, w32["down"], x_bits(x), f"down M=4 {name}")

@@ -112,3 +112,18 @@ def test_gemm_rejects(q4):
     x2 = synth.x_bf16(70, 16384, "gemm-16k-x")
     xb = synth.bits16(x2)
     check_gemv(q4.q4g128_gemm(gpu(x2), *d2), oracle.gemv_f64(xb, w2), w2, xb, "gemm K=16384")
+
+
+def test_gemm_kernel_output_only_2_byte_aligned(q4):
+    """y need only be 2-byte aligned: an output view 2 bytes into a buffer
+    (N % 4 == 0, where aligned rows take 8-byte stores) must get the same
+    values as an aligned output."""
+    M, N, K = 130, 256, 2048
+    dev, w32 = mat(N, K, ("gemm-misal", N, K))
+    x = gpu(synth.x_bf16(M, K, ("gemm-misal-x",)))
+    y_al = q4.q4g128_gemm(x, *dev, variant=q4.VARIANT_GEMM)
+    buf = torch.full((M * N + 8,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y_mis = buf[1:1 + M * N].view(M, N)
+    q4.q4g128_gemm(x, *dev, out=y_mis, variant=q4.VARIANT_GEMM)
+    assert torch.equal(y_mis.view(torch.int16), y_al.view(torch.int16))
+    assert bool(torch.isnan(buf[0].float())) and bool(torch.isnan(buf[1 + M * N:].float()).all())
