@@ -37,7 +37,7 @@ int check_common(const void* x, int M, int K, int N, const void* y) {
 
 bool variant_ok(int variant) {
     return variant == Q4_VARIANT_AUTO || variant == Q4_VARIANT_DOT2 || variant == Q4_VARIANT_MFMA || variant == Q4_VARIANT_STREAM ||
-           variant == Q4_VARIANT_TILED;
+           variant == Q4_VARIANT_TILED || variant == Q4_VARIANT_SKINNY;
 }
 
 // Kernel choice for Q4_VARIANT_AUTO.  Small batches on rows of 1-4 KB go to
@@ -58,8 +58,10 @@ int pick(Fmt fmt, int variant, int M, int N, int K, bool split = false) {
     if (variant == Q4_VARIANT_MFMA) return Q4_VARIANT_MFMA;
     if (variant == Q4_VARIANT_STREAM) return q4::stream_supported(fmt, M, K) ? Q4_VARIANT_STREAM : -1;
     if (variant == Q4_VARIANT_TILED) return q4::mm_supported(fmt, M, K, split) ? Q4_VARIANT_TILED : -1;
+    if (variant == Q4_VARIANT_SKINNY) return fmt == q4::kFmtQ4 && q4::skinny_supported(M, K, split) ? Q4_VARIANT_SKINNY : -1;
     if (M <= 4 && q4::stream_supported(fmt, M, K)) return Q4_VARIANT_STREAM;
     if (M <= 4 && q4::dot2_supported(fmt, K)) return Q4_VARIANT_DOT2;
+    if (fmt == q4::kFmtQ4 && q4::skinny_supported(M, K, split)) return Q4_VARIANT_SKINNY;
     if (q4::mm_supported(fmt, M, K, split) && (fmt == q4::kFmtQ4 || split || N >= kTiledRowsAlone)) return Q4_VARIANT_TILED;
     return Q4_VARIANT_MFMA;
 }
@@ -71,6 +73,7 @@ int run(Fmt fmt, int chosen, const GemvArgs* a, int count, void* stream, void* w
         case Q4_VARIANT_DOT2: e = q4::launch_dot2(fmt, a, count, s); break;
         case Q4_VARIANT_STREAM: e = q4::launch_stream(fmt, a, count, s); break;
         case Q4_VARIANT_TILED: e = q4::launch_mm(fmt, a, count, ws, ws_bytes, s); break;
+        case Q4_VARIANT_SKINNY: e = q4::launch_skinny(a, count, ws, ws_bytes, s); break;
         default: e = q4::launch_mfma(fmt, a, count, s); break;
     }
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
@@ -137,16 +140,19 @@ int check_bf(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t
 // cores where that cannot run); then the alias checks across tasks.
 int plan_checked(Fmt fmt, const GemvArgs* a, const Range (*in)[4], const Range* out, int count, int M, int variant, bool split,
                  int* chosen_out) {
-    int n_big = 0, n_tiled = 0, n_stream = 0;
+    int n_big = 0, n_tiled = 0, n_stream = 0, n_skinny = 0, n_tiled_ok = 0;
     for (int i = 0; i < count; ++i) {
         const int c = pick(fmt, variant, M, a[i].N, a[i].K, split);
         if (c < 0) return Q4_EVARIANT;
-        n_big += c == Q4_VARIANT_MFMA || c == Q4_VARIANT_TILED;
+        n_big += c == Q4_VARIANT_MFMA || c == Q4_VARIANT_TILED || c == Q4_VARIANT_SKINNY;
         n_tiled += c == Q4_VARIANT_TILED;
         n_stream += c == Q4_VARIANT_STREAM;
+        n_skinny += c == Q4_VARIANT_SKINNY;
+        n_tiled_ok += q4::mm_supported(fmt, M, a[i].K, split);
     }
     int chosen;
-    if (n_big) chosen = n_tiled == count ? Q4_VARIANT_TILED : Q4_VARIANT_MFMA;
+    if (n_skinny == count) chosen = Q4_VARIANT_SKINNY;
+    else if (n_big) chosen = (n_tiled + n_skinny == count && n_tiled_ok == count) ? Q4_VARIANT_TILED : Q4_VARIANT_MFMA;
     else chosen = n_stream == count ? Q4_VARIANT_STREAM : Q4_VARIANT_DOT2;
     if (chosen == Q4_VARIANT_DOT2) {
         for (int i = 0; i < count; ++i)
@@ -165,6 +171,7 @@ int plan_checked(Fmt fmt, const GemvArgs* a, const Range (*in)[4], const Range* 
 // Workspace a planned grouped launch can use (0: no K split planned).
 size_t grouped_ws_bytes(Fmt fmt, int chosen, const GemvArgs* a, int count) {
     if (chosen == Q4_VARIANT_TILED) return q4::mm_workspace_bytes(fmt, a, count);
+    if (chosen == Q4_VARIANT_SKINNY) return q4::skinny_workspace_bytes(a, count);
     return 0;
 }
 
@@ -173,11 +180,12 @@ size_t grouped_ws_bytes(Fmt fmt, int chosen, const GemvArgs* a, int count) {
 // every task must then allow.
 int run_grouped(Fmt fmt, int chosen, const GemvArgs* a, int count, int M, void* workspace, size_t workspace_bytes, void* stream) {
     const bool split = workspace != nullptr && workspace_bytes > 0;
-    if (chosen == Q4_VARIANT_TILED && split) {
+    if ((chosen == Q4_VARIANT_TILED || chosen == Q4_VARIANT_SKINNY) && split) {
         const size_t need = grouped_ws_bytes(fmt, chosen, a, count);
         if (need == 0 || workspace_bytes < need) {
             for (int i = 0; i < count; ++i)
-                if (!q4::mm_supported(fmt, M, a[i].K, false)) return Q4_EVARIANT;
+                if (chosen == Q4_VARIANT_TILED ? !q4::mm_supported(fmt, M, a[i].K, false) : !q4::skinny_supported(M, a[i].K, false))
+                    return Q4_EVARIANT;
         }
     }
     return run(fmt, chosen, a, count, stream, workspace, workspace_bytes);
@@ -563,11 +571,13 @@ int q4gemv_grouped_mixed(const q4gemv_mixed_task* tasks, int count, int M, void*
     for (int f = 0; f < nf; ++f) {
         rc = mixed_subgroup(a, fmts, count, order[f], M, split, sub[f], &n[f], &chosen[f]);
         if (rc) return rc;
-        if (chosen[f] == Q4_VARIANT_TILED && split) {
+        if ((chosen[f] == Q4_VARIANT_TILED || chosen[f] == Q4_VARIANT_SKINNY) && split) {
             const size_t need = grouped_ws_bytes(order[f], chosen[f], sub[f], n[f]);
             if (need == 0 || workspace_bytes < need)
                 for (int i = 0; i < n[f]; ++i)
-                    if (!q4::mm_supported(order[f], M, sub[f][i].K, false)) return Q4_EVARIANT;
+                    if (chosen[f] == Q4_VARIANT_TILED ? !q4::mm_supported(order[f], M, sub[f][i].K, false)
+                                                      : !q4::skinny_supported(M, sub[f][i].K, false))
+                        return Q4_EVARIANT;
         }
     }
     for (int f = 0; f < nf; ++f) {
@@ -762,6 +772,7 @@ const char* q4gemv_variant_name(int fmt, int variant, int M, int N, int K) {
     if (c == Q4_VARIANT_MFMA) return "mfma";
     if (c == Q4_VARIANT_STREAM) return "stream";
     if (c == Q4_VARIANT_TILED) return "tiled";
+    if (c == Q4_VARIANT_SKINNY) return "skinny";
     return "invalid";
 }
 

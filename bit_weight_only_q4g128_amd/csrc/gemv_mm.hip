@@ -611,19 +611,24 @@ __device__ __forceinline__ void tiled_body(const MmTable& tt, const int ti, uint
     }
 
     // --------------------------------------------------- split-K completion
-    // Each wave waits for its partial stores; the barrier orders them before
-    // the counter update, an acquire-release read-modify-write at device
-    // (agent) scope: its release publishes every store that happens before
-    // it (the other waves' through the barrier), and in the last slice to
-    // arrive its acquire orders the other slices' partials before the reads
-    // below (the other waves' through the second barrier).
+    // The hand-over rests on the device-coherent (sc1) partial accesses, not
+    // on agent-scope fences (whose L2 write-back and invalidate cost more
+    // than the split saves, and whose invalidate evicts the activations the
+    // other workgroups on the XCD are reading): a wave's sc1 stores are
+    // acknowledged only once they reach the device's coherence point, the
+    // wave waits for those acknowledgements (vmcnt(0)) before the barrier
+    // that precedes the counter update, and the last slice's sc1 loads are
+    // issued only after its update returned and read at that point.  The
+    // asm memory clobbers keep the compiler from moving accesses across.
     unsigned* cnt = tt.t[ti].cnt;
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __shared__ unsigned s_prev;
-    if (tid == 0) s_prev = __hip_atomic_fetch_add(&cnt[blk], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) s_prev = __hip_atomic_fetch_add(&cnt[blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_prev != (unsigned)(KS - 1)) return;
+    asm volatile("" ::: "memory");
     if (wave < kCompute) {
         // each compute wave sums one 16-row tile over the slices, in slice
         // order, with the partial tiles of kRB slices in flight at once

@@ -57,6 +57,10 @@ extern "C" {
 #define Q4_VARIANT_STREAM 3 /* M <= 4, rows of exactly 1, 2 or 4 KB (int4/NVFP4 K = 2048, 4096, 8192;
                                BF16 K = 512, 1024, 2048): every weight load issued at once, activations
                                and group parameters shared through LDS */
+#define Q4_VARIANT_SKINNY 6 /* int4, 5 <= M <= 48, K % 128 == 0: workgroups of up to 80 rows over a slice of at
+                               most 16 groups of K, each wave loading its own weights and activation fragments
+                               straight into registers (no per-group barriers); split over K when given a
+                               workspace, else K <= 2048; the default for int4 at 5 <= M <= 48 */
 #define Q4_VARIANT_GEMM 5   /* int4 prefill only (q4g128_gemm_variant): workgroup tiles of 128 batch
                                rows x 128 or 256 weight rows over all of K, codes unpacked from LDS
                                per wave, scale and min folded per 128-column group */

@@ -101,7 +101,13 @@ def test_variant_names():
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 1, 256, 512) == "dot2"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_STREAM, 5, 2048, 2048) == "invalid"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 1, 16385, 2048) == "stream"
-    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 2048) == "skinny"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 5, 2048, 2048) == "skinny"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 49, 2048, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 8192) == "tiled"     # no workspace: K > 16 groups
+    assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_TILED, 48, 2048, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_Q4G128, 6, 4, 2048, 2048) == "invalid"                   # skinny: M >= 5
+    assert q4.variant_name(q4.FMT_NVFP4G16, 6, 48, 2048, 2048) == "invalid"                # skinny: int4 only
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 16384) == "mfma"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_MFMA, 1, 2048, 2048) == "mfma"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_DOT2, 3, 16385, 2048) == "dot2"
@@ -146,8 +152,14 @@ def test_grouped_validation():
     ok3 = (T * 3)(far(0), far(1), far(2))
     nb = ctypes.c_size_t(123)
     assert lib.q4g128_workspace_bytes(ok3, 3, 1, ctypes.byref(nb)) == OK and nb.value == 0   # M = 1 never splits
-    # three 2048-row tasks at M = 48: 96 row blocks, so K is split
-    assert lib.q4g128_workspace_bytes(ok3, 3, 48, ctypes.byref(nb)) == OK and nb.value > 0
+    # three 2048-row tasks at M = 48, K = 2048: the skinny kernel's 32-row
+    # blocks fill the GPU whole (192 workgroups), no split
+    assert lib.q4g128_workspace_bytes(ok3, 3, 48, ctypes.byref(nb)) == OK and nb.value == 0
+    # K = 8192 exceeds one workgroup slice: split with a workspace
+    ok3k = (T * 3)(*[T(x=t.x, qweight=t.qweight, scale=t.scale, minv=t.minv, y=t.y, N=2048, K=8192) for t in ok3])
+    assert lib.q4g128_workspace_bytes(ok3k, 3, 48, ctypes.byref(nb)) == OK and nb.value > 64 * 1024
+    # the tiled kernel (M = 64) splits the 2048-column tasks
+    assert lib.q4g128_workspace_bytes(ok3, 3, 64, ctypes.byref(nb)) == OK and nb.value > 0
     bad = (T * 2)(task(0), task(1, K=100))
     assert lib.q4g128_gemv_grouped(bad, 2, 1, 0, None) == ESHAPE
     # task 1 writes over task 0's weights

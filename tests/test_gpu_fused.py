@@ -158,7 +158,8 @@ def test_fused_tiled_prologue_pass_equals_loader_path(q4, M):
     r = gpu(synth.x_bf16(M, 2048, ("fz-pass-r", M)))
     items = [task(dev, g, up=u, residual=r)]
     full = q4.q4g128_fused_workspace_bytes(items)
-    split_only = q4.q4g128_workspace_bytes([(g, *dev, None)])
+    # the same call without up: just the split-K part of the same plan
+    split_only = q4.q4g128_fused_workspace_bytes([task(dev, g, residual=r)])
     assert full > split_only
     (y_pass,) = q4.q4g128_gemv_fused(items, workspace=torch.zeros(full, dtype=torch.uint8, device="cuda"))
     ws2 = torch.zeros(max(split_only, 256), dtype=torch.uint8, device="cuda")

@@ -25,14 +25,15 @@ def q4():
 
 
 VARIANTS = [1, 2]  # dot2, mfma
-VNAME = {0: "auto", 1: "dot2", 2: "mfma", 3: "stream", 4: "tiled"}
+VNAME = {0: "auto", 1: "dot2", 2: "mfma", 3: "stream", 4: "tiled", 6: "skinny"}
 FMT = {"q4": 0, "nv": 1, "bf": 2}
 
 
 def vlist(q4, fmt, M, K):
-    """auto, dot2 and mfma, plus the streaming and tiled kernels where they accept (M, K)."""
+    """auto, dot2 and mfma, plus the streaming, tiled and skinny kernels where they accept (M, K)."""
     return ([0, 1, 2] + ([3] if q4.variant_name(FMT[fmt], 3, M, 1, K) == "stream" else [])
-            + ([4] if q4.variant_name(FMT[fmt], 4, M, 1, K) == "tiled" else []))
+            + ([4] if q4.variant_name(FMT[fmt], 4, M, 1, K) == "tiled" else [])
+            + ([6] if q4.variant_name(FMT[fmt], 6, M, 1, K) == "skinny" else []))
 
 
 # ----------------------------------------------------------------------------
@@ -297,7 +298,7 @@ def test_q4_power_of_two_scaling_is_bitwise(q4, variant):
     assert torch.equal((y1.float() * 8).to(torch.bfloat16), y2)
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS + [6])
 def test_q4_row_permutation_is_bitwise(q4, variant):
     N, K, M = 256, 2048, 16
     qw, sc, mn = synth.q4_matrix(N, K, ("perm",))
@@ -364,7 +365,7 @@ def test_q4_grouped_equals_single_calls(q4, M):
     xs = {"q": xin, "k": xin, "v": xin, "gate": xin, "up": xin, "o": xat, "down": xff}
     dev = {p: tuple(gpu(t) for t in lay[p]) for p in synth.LAYER_ORDER}
     for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
-        for v in [0, 1, 2] + ([3] if M <= 4 else [4]):
+        for v in [0, 1, 2] + ([3] if M <= 4 else [4, 6]):
             try:
                 outs = q4.q4g128_gemv_grouped([(xs[p], *dev[p], None) for p in stage], variant=v)
             except q4.Q4GemvError:
@@ -442,11 +443,13 @@ def test_q4_split_k_small_tasks(q4):
     w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
     ks = _onehot_ks(K, M, 77)
     items = [(gpu(onehot_x(K, ks)), gpu(qw), gpu(sc), gpu(mn), None)]
-    ws = torch.zeros(q4.q4g128_workspace_bytes(items), dtype=torch.uint8, device="cuda")
-    assert ws.numel() > 0
-    y = q4.q4g128_gemv_grouped(items, workspace=ws)[0]
+    # a workspace larger than any plan needs: the tiled kernel splits K, the
+    # skinny kernel's plan for this shape stays unsplit
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
     exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
-    assert np.array_equal(y.cpu().float().numpy(), exp)
+    for v in (4, 6, 0):
+        y = q4.q4g128_gemv_grouped(items, variant=v, workspace=ws)[0]
+        assert np.array_equal(y.cpu().float().numpy(), exp), VNAME[v]
 
 
 @pytest.mark.parametrize("M", [5, 20, 48, 64])
@@ -648,3 +651,80 @@ def test_q4_down_shape_M4_auto(q4):
     x = synth.x_bf16(M, K, ("down-M4-x",))
     ref = oracle.gemv_f64(x_bits(x), w32["down"])
     check_gemv(q4.q4g128_gemv(gpu(x), gpu(qw), gpu(sc), gpu(mn)), ref, w32["down"], x_bits(x), f"down M=4 {name}")
+
+
+# the skinny matrix-core kernel (int4, 5 <= M <= 48): the planner's row-block
+# height follows the row count (N about 4000, 8000, 12000, 20000 at K = 2048
+# give 16, 32, 48 and 80 rows per workgroup), N ragged against every block and
+# not a multiple of 4 (element stores); one-hot bitwise, random activations
+# within tolerance
+@pytest.mark.parametrize("N", [4001, 8003, 12005, 20007])
+@pytest.mark.parametrize("M", [5, 16, 33, 48])
+def test_q4_skinny_row_blocks(q4, N, M):
+    K = 2048
+    assert q4.variant_name(0, 0, M, N, K) == "skinny"
+    qw, sc, mn = synth.q4_matrix(N, K, ("skinny-rb", N))
+    w32 = _w32_cached(("skinny-rb", N), qw, sc, mn)
+    dev = (gpu(qw), gpu(sc), gpu(mn))
+    ks = _onehot_ks(K, M, 800 + M)
+    y = q4.q4g128_gemv(gpu(onehot_x(K, ks)), *dev, variant=6)
+    got = y.cpu().float().numpy()
+    exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(got, exp), (N, M, np.argwhere(got != exp)[:4])
+    x = synth.x_bf16(M, K, ("skinny-rb-x", N, M))
+    check_gemv(q4.q4g128_gemv(gpu(x), *dev, variant=6), oracle.gemv_f64(x_bits(x), w32), w32, x_bits(x), f"skinny N={N} M={M}")
+
+
+_W32 = {}
+
+
+def _w32_cached(key, qw, sc, mn):
+    if key not in _W32:
+        _W32[key] = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    return _W32[key]
+
+
+# K beyond one workgroup slice (16 groups) needs a workspace: slices of 8 or
+# 16 groups, a ragged last slice (K = 11008: 86 groups), and K below a slice
+@pytest.mark.parametrize("K", [128, 1152, 4096, 8192, 11008, 16384])
+@pytest.mark.parametrize("M", [5, 17, 48])
+def test_q4_skinny_split_k_onehot_and_random(q4, K, M):
+    N = 300
+    qw, sc, mn = synth.q4_matrix(N, K, ("skinny-sk", K))
+    w32 = _w32_cached(("skinny-sk", K), qw, sc, mn)
+    dev = (gpu(qw), gpu(sc), gpu(mn))
+    ks = _onehot_ks(K, M, 850 + M)
+    for kind in ("onehot", "random"):
+        x = gpu(onehot_x(K, ks)) if kind == "onehot" else gpu(synth.x_bf16(M, K, ("skinny-sk-x", K, M)))
+        items = [(x, *dev, None)]
+        need = q4.q4g128_workspace_bytes(items)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+        (y,) = q4.q4g128_gemv_grouped(items, variant=6, workspace=ws)
+        (y2,) = q4.q4g128_gemv_grouped(items, variant=6, workspace=ws)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "repeat on the reused workspace"
+        assert int(ws[:64 * 1024].count_nonzero()) == 0
+        if kind == "onehot":
+            exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+            got = y.cpu().float().numpy()
+            assert np.array_equal(got, exp), (K, M, np.argwhere(got != exp)[:4])
+        else:
+            xb = x_bits(x.cpu())
+            check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"skinny split K={K} M={M}")
+
+
+def test_q4_skinny_misaligned_params_and_output(q4):
+    """Group parameters only 2-byte aligned (element loads instead of 16-byte
+    pieces) and an output that is only 2-byte aligned (element stores)."""
+    N, K, M = 260, 2048, 48
+    qw, sc, mn = synth.q4_matrix(N, K, ("skinny-mis",))
+    w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
+    scb = torch.zeros(N * (K // 128) + 1, dtype=torch.float16, device="cuda")
+    mnb = torch.zeros_like(scb)
+    scv, mnv = scb[1:].view(N, K // 128), mnb[1:].view(N, K // 128)
+    scv.copy_(gpu(sc)); mnv.copy_(gpu(mn))
+    yb = torch.full((M * N + 1,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = yb[1:].view(M, N)
+    x = synth.x_bf16(M, K, ("skinny-mis-x",))
+    q4.q4g128_gemv(gpu(x), gpu(qw), scv, mnv, out=y, variant=6)
+    check_gemv(y, oracle.gemv_f64(x_bits(x), w32), w32, x_bits(x), "skinny misaligned")
+    assert bool(torch.isnan(yb[0].float()))
