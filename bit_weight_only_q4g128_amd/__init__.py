@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = [
-    "q4g128_gemv", "q4g128_gemv_grouped", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
+    "q4g128_gemv", "q4g128_gemv_grouped", "q4g128_gemv_grouped_noalloc", "NOALLOC_SCRATCH_BYTES", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
     "nvfp4g16_gemv_grouped", "nvfp4g16_workspace_bytes", "bf16_gemv_grouped", "bf16_workspace_bytes",
     "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample", "q4g128_gemm", "gemv_grouped_mixed", "mixed_workspace_bytes",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
@@ -66,6 +66,9 @@ lib.q4g128_gemv_grouped.restype = ctypes.c_int
 lib.q4g128_gemv_grouped_ws.argtypes = [ctypes.POINTER(Q4Task), _i, _i, _i, _p, ctypes.c_size_t, _p]
 lib.q4g128_gemv_grouped_ws.restype = ctypes.c_int
 lib.q4g128_workspace_bytes.argtypes = [ctypes.POINTER(Q4Task), _i, _i, ctypes.POINTER(ctypes.c_size_t)]
+lib.q4g128_gemv_grouped_noalloc.argtypes = [ctypes.POINTER(Q4Task), _i, _i, _i, _p]
+lib.q4g128_gemv_grouped_noalloc.restype = ctypes.c_int
+NOALLOC_SCRATCH_BYTES = 8 << 20
 lib.q4g128_workspace_bytes.restype = ctypes.c_int
 
 
@@ -219,6 +222,16 @@ def q4g128_gemv_grouped(items, variant: int = VARIANT_AUTO, workspace=None):
         if workspace.device != items[0][0].device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the activations' device")
         _raise(lib.q4g128_gemv_grouped_ws(arr, len(items), M, int(variant), workspace.data_ptr(), workspace.numel(), st))
+    return outs
+
+
+def q4g128_gemv_grouped_noalloc(items, variant: int = VARIANT_AUTO):
+    """q4g128_gemv_grouped with the library's built-in split-K scratch instead
+    of a workspace (q4g128_gemv_grouped_noalloc in the C header: nothing is
+    allocated; calls on one GPU must not overlap in time).  items as for
+    q4g128_gemv_grouped.  Returns the list of outputs."""
+    items, arr, outs, M = _task_array(items)
+    _raise(lib.q4g128_gemv_grouped_noalloc(arr, len(items), M, int(variant), _stream(items[0][0])))
     return outs
 
 

@@ -12,6 +12,7 @@ using q4::GemvArgs;
 namespace {
 
 constexpr int kMaxM = 64;
+static_assert(Q4GEMV_NOALLOC_SCRATCH_BYTES == q4::kNoAllocScratchBytes, "header and library disagree on the built-in scratch");
 constexpr long kMaxK = 32768;
 constexpr long kMaxN = 1L << 24;
 
@@ -370,6 +371,18 @@ int q4g128_gemv_grouped_ws(const q4g128_task* tasks, int count, int M, int varia
     int rc = plan_group(tasks, count, M, variant, split, a, &chosen);
     if (rc) return rc;
     return run_grouped(q4::kFmtQ4, chosen, a, count, M, workspace, workspace_bytes, stream);
+}
+
+int q4g128_gemv_grouped_noalloc(const q4g128_task* tasks, int count, int M, int variant, void* stream) {
+    GemvArgs a[q4::kMaxTasks];
+    int chosen = 0;
+    int rc = plan_group(tasks, count, M, variant, true, a, &chosen);
+    if (rc) return rc;
+    const size_t need = grouped_ws_bytes(q4::kFmtQ4, chosen, a, count);
+    if (need > q4::kNoAllocScratchBytes) return Q4_ESCRATCH;
+    void* ws = nullptr;
+    if (need > 0 && q4::noalloc_scratch(reinterpret_cast<hipStream_t>(stream), &ws) != hipSuccess) return Q4_ELAUNCH;
+    return run_grouped(q4::kFmtQ4, chosen, a, count, M, ws, ws ? q4::kNoAllocScratchBytes : 0, stream);
 }
 
 int q4g128_gemv_grouped(const q4g128_task* tasks, int count, int M, int variant, void* stream) {
@@ -785,6 +798,7 @@ const char* q4gemv_strerror(int status) {
         case Q4_EALIAS: return "output overlaps an input";
         case Q4_ELAUNCH: return "kernel launch failed";
         case Q4_EVARIANT: return "unknown variant or variant cannot run this shape";
+        case Q4_ESCRATCH: return "the call needs more split-K scratch than the built-in array holds";
         default: return "unknown status";
     }
 }

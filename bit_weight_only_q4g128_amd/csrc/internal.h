@@ -66,6 +66,11 @@ bool mm_supported(Fmt fmt, int M, int K, bool split);
 // Every workspace starts with this many bytes of arrival counters that each
 // call leaves at zero; scratch lies after them.
 constexpr size_t kWsCounterBytes = 64 * 1024;
+// The built-in scratch of the allocation-free entry point (noalloc.hip): its
+// size, and its device address on the stream's device (set up on first use:
+// address lookup, counters cleared on stream s).
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+hipError_t noalloc_scratch(hipStream_t s, void** out);
 size_t mm_workspace_bytes(Fmt fmt, const GemvArgs* tasks, int count);
 hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
 // Skinny matrix-core GEMV (gemv_skinny.hip): int4, 5 <= M <= kSkinnyMaxM,

@@ -46,6 +46,7 @@ extern "C" {
 #define Q4_EALIAS (-4)       /* the output overlaps an input */
 #define Q4_ELAUNCH (-5)      /* the HIP runtime refused a kernel launch */
 #define Q4_EVARIANT (-6)     /* unknown variant, or the variant cannot run this shape */
+#define Q4_ESCRATCH (-7)     /* the call needs more split-K scratch than the built-in array holds */
 
 /* kernel variants (the *_gemv_variant entry points) */
 #define Q4_VARIANT_AUTO 0 /* pick by (M, N, K) */
@@ -133,6 +134,22 @@ int q4g128_gemv_grouped_ws(const q4g128_task* tasks, int count, int M, int varia
 /* Workspace bytes q4g128_gemv_grouped_ws needs for these tasks (0 if no
  * split is planned).  Validates like the GEMV call; *bytes is set on Q4_OK. */
 int q4g128_workspace_bytes(const q4g128_task* tasks, int count, int M, size_t* bytes);
+
+/*
+ * q4g128_gemv_grouped_ws without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The split-K scratch is a built-in device array of 8 MiB per
+ * GPU (Q4GEMV_NOALLOC_SCRATCH_BYTES), set up on the first call on a device
+ * and held until the process ends; calls whose plan needs more than that
+ * (q4g128_workspace_bytes > 8 MiB; no decode-layer shape at M <= 64 does)
+ * return Q4_ESCRATCH before anything is enqueued.  Same kernels, plan and
+ * results as q4g128_gemv_grouped_ws with a workspace of at least that size.
+ * Every call on one GPU shares that GPU's array: calls on one GPU must not
+ * overlap in time (same stream, or ordered by events), or they race.
+ */
+#define Q4GEMV_NOALLOC_SCRATCH_BYTES (8u << 20)
+int q4g128_gemv_grouped_noalloc(const q4g128_task* tasks, int count, int M, int variant, void* stream);
 
 /*
  * NVFP4 weight-only weights.
