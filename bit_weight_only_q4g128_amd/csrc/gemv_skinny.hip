@@ -3,38 +3,48 @@
 //
 // The decode batch shares one read of the weights: at M = 48 every weight byte
 // feeds 48 products ("rumik-oss-1-nvfp4-vllm" card, "Concurrent request
-// throughput": one weight read serves many sequences).  The work is cut so
-// that a workgroup (eight waves) owns R 16-row tiles over a slice of at most
-// 16 groups of K (the whole of K for the hidden-2048 projections), and every
-// wave owns distinct groups of that slice: group g0 + 8 r + w for round r of
-// wave w.  A wave therefore needs only its own data, and issues all of it at
-// once when it starts -- per round the activation fragments of its group (MT
-// batch tiles x 4 k-steps, 16 bytes a lane each, from L2) and the group's
-// 64 bytes of each of its R x 16 weight rows (one 16-byte load a lane per
-// tile, from HBM) -- so a workgroup's whole input is one memory round trip,
-// the waves never wait for each other until the end, and each activation byte
-// is read once per workgroup.  The group parameters of the workgroup's rows
-// are staged in LDS once (one barrier), as fp32 (scale, min - 128 scale).
+// throughput": one weight read serves many sequences).  A workgroup (eight
+// waves) owns R 16-row tiles over a slice of at most 16 groups of K (the whole
+// of K for the hidden-2048 projections); each wave owns one or two adjacent
+// groups of the slice (its rounds) for all R tiles, so a wave needs only its
+// own data and the waves meet only once, at the end.
 //
-// Per round a wave pairs its activations to match the nibble unpack
-// (x0,x4) (x1,x5) (x2,x6) (x3,x7), forms SX (the sum of the group's
-// activations per batch row) with an all-ones A operand, and per tile turns
-// each lane's 8 codes per k-step into BF16 "128 + code" (v_perm_b32 on the
-// 0x43 exponent byte) and accumulates D = sum of (128 + code) * x over the
-// group; the group folds as
-//     acc += scale * D + (min - 128 scale) * SX,
-// exact up to the fp32 roundings (both products and the fold are exact for a
-// one-hot x).  The eight waves' partial tiles meet in LDS in a fixed order;
-// when K is split over workgroups, each writes its fp32 tile to the caller's
-// workspace and the workgroup that arrives last at the row block's counter
-// sums the slices in slice order, writes y and resets the counter.
+// Memory.  A wave issues everything it will need as soon as it starts: the
+// weights of all its rounds (16 bytes a lane per tile and round, straight into
+// registers), its rows' scales and mins, and the first round's activations
+// (MT x 16 batch rows x 256 bytes) -- the last two straight into LDS with
+// buffer_load ... lds, in whole cache lines (each instruction reads four
+// activation rows), into a region of its own, so no barrier is involved.  The
+// second round's activations follow once the first round's are read out.
+// Every buffer offset is scalar plus one per-lane base, so the address
+// arithmetic costs no vector instructions.
+//
+// Arithmetic per round: the activation fragments are read from LDS (an XOR
+// swizzle of the 16-byte chunks by row makes every read conflict-free) and
+// paired as (x0,x4) (x1,x5) (x2,x6) (x3,x7) to match the nibble unpack; an
+// all-ones B operand gives SX (the group's activation sum per batch row); per
+// tile each lane's 8 codes per k-step become BF16 "128 + code" (v_perm_b32 on
+// the 0x43 exponent byte) and the MFMAs accumulate D = sum of (128 + code) * x
+// with the activations as the A operand, so a lane's four results share one
+// weight row; the round folds as acc += scale * D (one FMA per result).  The
+// remaining term, sum over groups of (min - 128 scale) * SX, is a product of
+// a [batch x groups] and a [groups x rows] matrix: it is formed once per
+// workgroup, after the waves meet, with fp32 MFMAs (v_mfma_f32_16x16x4f32)
+// from the SX and group parameters left in LDS.  Every product is exact, and
+// for a one-hot x so is every sum.
+//
+// The eight waves' tiles meet in LDS and are summed in wave order; when K is
+// split over workgroups, each adds its min term and writes its fp32 tiles to
+// the caller's workspace, and the workgroup that arrives last at the row
+// block's counter sums the slices in slice order, writes y and resets the
+// counter.
 //
 // MFMA operand layout (16x16x32): lane l holds A row l % 16 and B column
 // l % 16, k-values 8 (l / 16) .. + 8 of the k-step.  For k-step s of a group,
 // lane l's k-values are the 8 columns 32 (l / 16) + 8 s .. + 8 of the group
 // (in the pairing order): dword s of the lane's 16 weight bytes, and the
 // activations at the same columns.  D: lane l holds rows 4 (l / 16) + v
-// (v = 0..3) of column l % 16.
+// (v = 0..3; here batch rows) of column l % 16 (here a weight row).
 #include "internal.h"
 
 namespace q4 {
@@ -47,6 +57,7 @@ constexpr int kSkMaxGroups = 16;   // groups per workgroup slice: two rounds of 
 constexpr int kSkCoherent = 16;    // buffer cache policy sc1: device-coherent, not held in the per-XCD L2
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x8_t as_b8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -63,9 +74,26 @@ struct SkTable {
     SkTask t[kMaxTasks];
 };
 
-// LDS: the eight waves' partial tiles [8][R * MT][64 lanes] x 16 bytes
+// LDS layout (bytes):
+//   [0, kArea)           per wave: one round of activations, MT * 16 rows x
+//                        256 bytes; after the rounds, the eight waves' result
+//                        tiles [8][R * MT][64 lanes] x 16 bytes (the larger)
+//   [kArea, + kPar)      per wave: scales then mins of its 16 R rows for its
+//                        two group slots, [2][16 R][2] dwords holding the fp16
+//                        value in the low half (a 2-byte load to LDS writes one
+//                        zero-extended dword per lane), each array padded to
+//                        whole 64-lane loads
+//   [.., + kSx)          SX per group of the slice and batch row, fp32 [16][16 MT]
 template <int MT, int R>
-__host__ __device__ constexpr int sk_lds_bytes() { return kSkWaves * R * MT * 64 * 16; }
+struct SkLds {
+    static constexpr int kX = MT * 16 * 256;
+    static constexpr int kRed = kSkWaves * R * MT * 1024;
+    static constexpr int kArea = (kSkWaves * kX > kRed) ? kSkWaves * kX : kRed;
+    static constexpr int kParArr = ((32 * R + 63) / 64) * 64;   // dwords per (wave, array), whole 64-lane loads
+    static constexpr int kPar = kSkWaves * 2 * kParArr * 4;
+    static constexpr int kSx = kSkMaxGroups * 16 * MT * 4;
+    static constexpr int kBytes = kArea + kPar + kSx;
+};
 
 // Workgroup barrier that waits only for this wave's LDS traffic, so the
 // vector-memory loads in flight stay in flight across it.
@@ -75,6 +103,10 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) only, lgkmcnt(0) only
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kLgkm0 = 0xC07F;
 
 // One result tile (16 weight rows x 16 batch rows) to y: lane l holds batch
 // rows 16 mt + 4 (l / 16) + v (v = 0..3) of weight row trow + l % 16; the
@@ -98,6 +130,7 @@ __device__ __forceinline__ void sk_write_tile(const SkTask& tk, int trow, int mt
 
 template <int MT, int R>
 __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
+    using L = SkLds<MT, R>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int ti = 0;
 #pragma unroll
@@ -116,60 +149,96 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t rowbytes = (uint32_t)a.K >> 1;
-    f32x4* red = reinterpret_cast<f32x4*>(lds);   // [8 waves][R * MT][64 lanes]
+    const int nv = ng - nr * wave;                       // this wave's valid rounds (may be <= 0)
 
-    // ---- 1. this wave's loads, all at once.  Round r is group g0 + nr w + r
-    // (a wave's groups are adjacent, so its weight bytes of a row are whole
-    // cache lines).  Per round: the activation fragments (MT x 4 k-steps),
-    // then per tile the lane's 16 weight bytes and its row's scale and min
-    // (the lane's results share one weight row: row l % 16 of the tile).
-    // Loads of a round past the slice fall outside the buffer ranges and
-    // read zero, so the wait counts are the same on every path.
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.K * 2u);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)row0 * rowbytes, (uint32_t)nrows * rowbytes);
+    uint8_t* xbuf = lds + wave * L::kX;
+    uint32_t* par = reinterpret_cast<uint32_t*>(lds + L::kArea);     // [8][2][kParArr]
+    float* sxt = reinterpret_cast<float*>(lds + L::kArea + L::kPar);  // [16][16 MT]
+
+    // ---- 1. issue: group parameters (to LDS), round-0 activations (to LDS),
+    // all weights (to registers).  Out-of-range offsets read zero.
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + (size_t)row0 * G, (uint32_t)nrows * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)nrows * (uint32_t)G * 2u);
-    const uint32_t xoff0 = ((uint32_t)(lane & 15) * (uint32_t)a.K + 32u * (uint32_t)(lane >> 4)) * 2u;
-    const uint32_t woff0 = (uint32_t)(lane & 15) * rowbytes + 16u * (uint32_t)(lane >> 4);
-    const uint32_t poff0 = (uint32_t)(lane & 15) * (uint32_t)G * 2u;
-    u32x4 X[2][MT][4];
-    u32x4 W[2][R];
-    uint16_t S16[2][R], M16[2][R];
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.K * 2u);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)row0 * rowbytes, (uint32_t)nrows * rowbytes);
+    // parameters: element e = 64 i + lane is (row e / 2, slot e % 2) -> group g0 + nr w + slot
+    {
+        constexpr int kPI = (16 * R * 2 + 63) / 64;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int gl = nr * wave + r;          // group within the slice
-        const bool valid = r < nr && gl < ng;
-        const uint32_t g = (uint32_t)(g0 + gl);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint32_t off = valid ? xoff0 + ((uint32_t)(16 * mt) * (uint32_t)a.K + 128u * g + 8u * s) * 2u : 0xFFFFFFF0u;
-                X[r][mt][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-            }
-#pragma unroll
-        for (int t = 0; t < R; ++t) {
-            const uint32_t off = valid ? woff0 + (uint32_t)(16 * t) * rowbytes + 64u * g : 0xFFFFFFF0u;
-            W[r][t] = buf_load16(rw, off, 0);
-            const uint32_t po = valid ? poff0 + ((uint32_t)(16 * t) * (uint32_t)G + g) * 2u : 0xFFFFFFF0u;
-            S16[r][t] = buf_load2(rs, po, 0);
-            M16[r][t] = buf_load2(rm, po, 0);
+        for (int i = 0; i < kPI; ++i) {
+            const int e = 64 * i + lane;
+            const int row = e >> 1, slot = e & 1;
+            const bool ok = row < 16 * R && slot < nv;
+            const uint32_t off = ok ? ((uint32_t)row * (uint32_t)G + (uint32_t)(g0 + nr * wave + slot)) * 2u : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(par + (wave * 2 + 0) * L::kParArr + 64 * i), 2, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(par + (wave * 2 + 1) * L::kParArr + 64 * i), 2, off, 0, 0, 0);
         }
     }
+    // activations of round r: instruction i covers batch rows 4 i .. 4 i + 3;
+    // lane l writes position p = l % 16 of row m = 4 i + l / 16 and fetches
+    // the row's 16-byte chunk p ^ (m % 16) of the group
+    const int xm_l = lane >> 4, xp = lane & 15;
+    auto issue_x = [&](int r) {
+        const bool ok = r < nv;
+        const uint32_t gcol = (uint32_t)(g0 + nr * wave + r) * 128u;
+#pragma unroll
+        for (int i = 0; i < 4 * MT; ++i) {
+            const int m = 4 * i + xm_l;
+            const uint32_t off = ok ? ((uint32_t)m * (uint32_t)a.K + gcol + 8u * (uint32_t)(xp ^ (m & 15))) * 2u : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xbuf + 1024 * i), 16, off, 0, 0, 0);
+        }
+    };
+    issue_x(0);
+    // weights: lane l reads row l % 16 of each tile, bytes 16 (l / 16) of the
+    // group's 64; the row and group parts of the offset are scalar
+    const uint32_t woff0 = (uint32_t)(lane & 15) * rowbytes + 16u * (uint32_t)(lane >> 4);
+    u32x4 W[2][R];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const __amdgpu_buffer_rsrc_t rwr = r < nv ? rw : make_rsrc(a.w, 0u);
+        const uint32_t gb = (uint32_t)(g0 + nr * wave + r) * 64u;
+#pragma unroll
+        for (int t = 0; t < R; ++t) W[r][t] = buf_load16(rwr, woff0, (uint32_t)(16 * t) * rowbytes + gb);
+    }
 
-    // ---- 2. the rounds.  D = X . W^T with the activations as the A operand:
-    // lane l holds batch rows 4 (l / 16) + v of weight row l % 16.
+    // ---- 2. the rounds
     const bf16x8_t ones = as_b8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     f32x4 acc[R][MT];
 #pragma unroll
     for (int t = 0; t < R; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kWLoads = 2 * R;   // weight loads issued after the round-0 activations
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        if (r >= nr || nr * wave + r >= ng) break;   // wave-uniform
-        // activations in the pairing of the nibble unpack; SX per batch row
-        // (an all-ones B operand: every column of the result is SX)
+        const int gl = nr * wave + r;   // group within the slice
+        if (r >= nr) break;             // wave-uniform
+        if (r >= nv) {
+            // a slot past the slice: no SX for it
+            if (lane < 16 * MT && (lane & 3) == 0)
+                *reinterpret_cast<f32x4*>(sxt + gl * 16 * MT + lane) = f32x4{0.f, 0.f, 0.f, 0.f};
+            continue;
+        }
+        // this round's activations (and, in round 0, the parameters) are in LDS
+        if (r == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWLoads));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        u32x4 X[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int m = 16 * mt + (lane & 15);
+                const int chunk = 4 * (lane >> 4) + s;
+                X[mt][s] = *reinterpret_cast<const u32x4*>(xbuf + m * 256 + 16 * (chunk ^ (m & 15)));
+            }
+        uint32_t sc16[R];   // this lane's row: the scale of this round's group (fp16 in the low half)
+#pragma unroll
+        for (int t = 0; t < R; ++t) sc16[t] = par[(wave * 2 + 0) * L::kParArr + 2 * (16 * t + (lane & 15)) + r];
+        if (r == 0 && nr > 1 && nv > 1) {
+            __builtin_amdgcn_s_waitcnt(kLgkm0);   // the region is read out before it is refilled
+            issue_x(1);
+        }
+        // pairing; SX (all-ones B operand: every column of the result is SX)
         u32x4 B[MT][4];
         f32x4 sx[MT];
 #pragma unroll
@@ -177,7 +246,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const u32x4 v = X[r][mt][s];
+                const u32x4 v = X[mt][s];
                 uint32_t p[4];
                 xq4_pairs(v.x, v.y, v.z, v.w, p);
                 B[mt][s] = u32x4{p[0], p[1], p[2], p[3]};
@@ -185,6 +254,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             }
             sx[mt] = c;
         }
+        // lanes 0, 16, 32, 48 hold SX of batch rows 16 mt + 4 (l / 16) + v
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            if ((lane & 15) == 0) *reinterpret_cast<f32x4*>(sxt + gl * 16 * MT + 16 * mt + 4 * (lane >> 4)) = sx[mt];
 #pragma unroll
         for (int t = 0; t < R; ++t) {
             f32x4 D[MT];
@@ -198,33 +271,56 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) D[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(B[mt][s]), Wv, D[mt], 0, 0, 0);
             }
-            // acc += scale * D + (min - 128 scale) * SX for the lane's row
-            const float sc = f16_to_f32(S16[r][t]);
-            const float mq = fmaf(-128.0f, sc, f16_to_f32(M16[r][t]));
+            const float sc = f16_to_f32((uint16_t)sc16[t]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][mt][v] = fmaf(sc, D[mt][v], fmaf(mq, sx[mt][v], acc[t][mt][v]));
+                for (int v = 0; v < 4; ++v) acc[t][mt][v] = fmaf(sc, D[mt][v], acc[t][mt][v]);
         }
     }
 
-    // ---- 3. the eight waves meet in LDS: each writes its tiles, then each
-    // finishes whole tiles, summing the eight in wave order
+    // ---- 3. the waves meet: tiles to LDS (over the activation regions, so
+    // after every wave has read its last round), then each wave finishes whole
+    // tiles: the eight waves' tiles summed in wave order, plus the min term
+    //   sum over the slice's groups of SX[batch][g] * (min - 128 scale)[g][row]
+    // as fp32 MFMAs over chunks of four groups
     constexpr int kTiles = R * MT;
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < R; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) red[(wave * kTiles + t * MT + mt) * 64 + lane] = acc[t][mt];
     lds_sync();
     f32x4 fin[(kTiles + kSkWaves - 1) / kSkWaves];
+    const int nsh = nr - 1;   // group g of the slice belongs to wave g >> nsh, slot g & nsh
 #pragma unroll
     for (int j = 0; j * kSkWaves < kTiles; ++j) {
         const int p = wave + kSkWaves * j;
         if (p < kTiles) {
+            const int t = p / MT, mt = p - t * MT;
+            const int row = 16 * t + (lane & 15);
+            // operands of the min term for all four chunks first (LDS reads in flight together)
+            float av[kSkMaxGroups / 4], sv[kSkMaxGroups / 4], mv[kSkMaxGroups / 4];
+#pragma unroll
+            for (int c = 0; c < kSkMaxGroups / 4; ++c) {
+                const int g = 4 * c + (lane >> 4);
+                const int gi = g < ng ? g : 0;
+                const int w2 = gi >> nsh, slot = gi & nsh;
+                av[c] = sxt[gi * 16 * MT + 16 * mt + (lane & 15)];
+                sv[c] = f16_to_f32((uint16_t)par[(w2 * 2 + 0) * L::kParArr + 2 * row + slot]);
+                mv[c] = f16_to_f32((uint16_t)par[(w2 * 2 + 1) * L::kParArr + 2 * row + slot]);
+            }
             f32x4 v = red[p * 64 + lane];
 #pragma unroll
             for (int w = 1; w < kSkWaves; ++w) v += red[(w * kTiles + p) * 64 + lane];
-            fin[j] = v;
+            f32x4 dm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < kSkMaxGroups / 4; ++c) {
+                const bool ok = 4 * c + (lane >> 4) < ng;
+                dm = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? av[c] : 0.0f, ok ? fmaf(-128.0f, sv[c], mv[c]) : 0.0f, dm, 0, 0, 0);
+            }
+            fin[j] = v + dm;
         }
     }
 
@@ -380,7 +476,7 @@ hipError_t launch_sk_mt(const GemvArgs* tasks, int count, const SkPlan& p, void*
         }
         grid += blocks * p.ks[i];
     }
-    constexpr int kShmem = sk_lds_bytes<MT, R>();
+    constexpr int kShmem = SkLds<MT, R>::kBytes;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_q4_kernel<MT, R>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kShmem);
     if (attr != hipSuccess) return attr;
