@@ -62,15 +62,24 @@ class Workload:
         self.layers = []
         for i in range(N_LAYERS):
             self.layers.append({p: synth.q4_matrix(*synth.LAYER_SHAPES[p], ("step", i, p), device=dev) for p in synth.LAYER_ORDER})
-        self.head = synth.bf16_matrix(head_rows, 2048, ("step-head", head_rows), device=dev)
+        # the full audio head and the current-codebook slice (a step uses one or the other)
+        self.heads = {rows: synth.bf16_matrix(rows, 2048, ("step-head", rows), device=dev)
+                      for rows in (synth.HEAD_FULL[0], synth.HEAD_SLICE[0])}
+        self.head = self.heads[head_rows]
         torch.cuda.synchronize()
-        log(f"bench: generated {N_LAYERS} int4 layers + {head_rows}x2048 bf16 head in {time.time() - t0:.1f}s")
+        log(f"bench: generated {N_LAYERS} int4 layers + bf16 heads {sorted(self.heads)}x2048 in {time.time() - t0:.1f}s")
         self.shapes = synth.LAYER_SHAPES
         self.order = synth.LAYER_ORDER
         self.head_rows = head_rows
         self.io = {}
         self.res = {}
         self.ws = {}
+        self.yh = {}
+
+    def head_out(self, M, rows):
+        if (M, rows) not in self.yh:
+            self.yh[(M, rows)] = self.torch.empty((M, rows), dtype=self.torch.bfloat16, device="cuda")
+        return self.yh[(M, rows)]
 
     def buffers(self, M):
         if M not in self.io:
@@ -82,14 +91,14 @@ class Workload:
             xffn = synth.x_bf16(M, 8192, ("bench-xffn", M), device="cuda")
             xs = {"q": xin, "k": xin, "v": xin, "gate": xin, "up": xin, "o": xattn, "down": xffn}
             ys = {p: t.empty((M, self.shapes[p][0]), dtype=t.bfloat16, device="cuda") for p in self.order}
-            yh = t.empty((M, self.head_rows), dtype=t.bfloat16, device="cuda")
+            yh = self.head_out(M, self.head_rows)
             self.io[M] = (xs, ys, xin, yh)
             # stand-in residual-stream inputs of the fused o and down calls
             self.res[M] = (synth.x_bf16(M, 2048, ("bench-res-o", M), device="cuda"),
                            synth.x_bf16(M, 2048, ("bench-res-down", M), device="cuda"))
         return self.io[M]
 
-    def launches(self, M, mode="grouped"):
+    def launches(self, M, mode="grouped", head_rows=None):
         """[(callable, weight_bytes, is_q4)] for one step, in stream order.
 
         plain:   one launch per projection (7 per layer) and one for the head.
@@ -100,7 +109,9 @@ class Workload:
                  adds a residual, down reads silu(gate) * up -- the outputs of
                  the layer's first launch -- and adds a residual.
         """
-        xs, ys, xin, yh = self.buffers(M)
+        xs, ys, xin, _ = self.buffers(M)
+        head_rows = head_rows or self.head_rows
+        head, yh = self.heads[head_rows], self.head_out(M, head_rows)
         out = []
         q4 = self.q4
         for lay in self.layers:
@@ -126,12 +137,17 @@ class Workload:
                     out.append((lambda items=items, ws=ws: q4.q4g128_gemv_grouped(items, workspace=ws), wb, True))
         if mode in ("grouped", "fused") and M > 4:
             # the head as a one-task grouped call, so that it may split K
-            hitems = [(xin, self.head, yh)]
+            hitems = [(xin, head, yh)]
             hws = self.workspace(M, hitems, self.q4.bf16_workspace_bytes(hitems))
-            out.append((lambda: q4.bf16_gemv_grouped(hitems, workspace=hws), self.head_rows * 2048 * 2, False))
+            out.append((lambda: q4.bf16_gemv_grouped(hitems, workspace=hws), head_rows * 2048 * 2, False))
         else:
-            out.append((lambda: q4.bf16_gemv(xin, self.head, out=yh), self.head_rows * 2048 * 2, False))
+            out.append((lambda: q4.bf16_gemv(xin, head, out=yh), head_rows * 2048 * 2, False))
         return out
+
+    def outputs(self, M, head_rows=None):
+        """The step's output buffers (per projection the last layer's, and the head's)."""
+        xs, ys, _, _ = self.buffers(M)
+        return [ys[p] for p in self.order] + [self.head_out(M, head_rows or self.head_rows)]
 
     def workspace(self, M, items, need=None):
         """One split-K workspace per batch size (zero-filled once), shared by
@@ -148,16 +164,17 @@ class Workload:
             self.ws[M] = ws
         return ws
 
-    def step_bytes(self, M, mode="grouped"):
+    def step_bytes(self, M, mode="grouped", head_rows=None):
         """Algorithmic bytes of one step: packed weights + group scales, each
         distinct activation vector read once (layer input, attention output,
         FFN activation, head input), every output written once; the fused
         step reads the gate and up outputs instead of the FFN activation,
         plus two residuals per layer."""
-        w = sum(b for _, b, _ in self.launches(M, "plain"))
+        head_rows = head_rows or self.head_rows
+        w = sum(b for _, b, _ in self.launches(M, "plain", head_rows))
         per_layer_x = (2048 + 2048 + (2 * 8192 + 2 * 2048 if mode == "fused" else 8192)) * M * 2
         per_layer_y = sum(self.shapes[p][0] for p in self.order) * M * 2
-        head_io = 2048 * M * 2 + self.head_rows * M * 2
+        head_io = 2048 * M * 2 + head_rows * M * 2
         return w + N_LAYERS * (per_layer_x + per_layer_y) + head_io
 
 
@@ -403,35 +420,66 @@ def read_ceiling(torch, q4, wl, steps, warmup):
             groups.append([t for p in stage for t in lay[p]])
     groups.append([wl.head])
     sinks = [torch.empty(q4.stream_read_sink_words(g), dtype=torch.int32, device="cuda") for g in groups]
-    for g, k in zip(groups, sinks):
-        q4.stream_read(g, k)
+    return graph_ms(torch, lambda: [q4.stream_read(g, k) for g, k in zip(groups, sinks)], steps, warmup)
+
+
+def single_launch_read(torch, q4, steps, nbytes=1 << 30):
+    """The achievable streaming-read rate of one launch: the diagnostic
+    stream_read over one contiguous 1 GiB device buffer, replayed in a graph.
+    Returns (ms per launch, GB/s)."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(q4.stream_read_sink_words([buf]), dtype=torch.int32, device="cuda")
+    ms = graph_ms(torch, lambda: q4.stream_read([buf], sink), steps, 3)
+    del buf
+    return ms, nbytes / (ms * 1e-3) / 1e9
+
+
+def graph_ms(torch, fn, steps, warmup):
+    """Milliseconds per replay of fn captured once into a graph (events on
+    the stream the graph is replayed on)."""
+    fn()
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for g, k in zip(groups, sinks):
-            q4.stream_read(g, k)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
     for _ in range(warmup):
-        graph.replay()
+        g.replay()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(steps):
-        graph.replay()
+        g.replay()
     e.record()
     e.synchronize()
+    del g
     return s.elapsed_time(e) / steps
 
 
-def time_graph(torch, wl, M, steps, warmup, mode):
-    calls = wl.launches(M, mode)
-    for f, _, _ in calls:  # eager warm-up outside capture
+def time_graph(torch, wl, M, steps, warmup, mode, head_rows=None):
+    """The step at batch M captured once into a hipGraph and replayed.  Before
+    timing, one replay is checked bit for bit against the same calls run
+    eagerly (outputs poisoned in between).  Returns ms per step."""
+    return replay_checked(torch, wl.launches(M, mode, head_rows), wl.outputs(M, head_rows), steps, warmup, f"M={M} {mode}")
+
+
+def replay_checked(torch, calls, outs, steps, warmup, what):
+    for f, _, _ in calls:  # eager run outside capture
         f()
     torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for f, _, _ in calls:
             f()
+    for o in outs:
+        o.fill_(float("nan"))
     torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    for o, e in zip(outs, eager):
+        if not torch.equal(o.view(torch.int16), e.view(torch.int16)):
+            raise RuntimeError(f"{what}: the replayed step differs from the eager calls")
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -442,8 +490,22 @@ def time_graph(torch, wl, M, steps, warmup, mode):
     e.record()
     e.synchronize()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / steps
-    return ms, g
+    del g
+    return s.elapsed_time(e) / steps
+
+
+def layer_launches_in_graph(torch, wl, M, mode, steps, warmup):
+    """The step's int4 GEMV launches alone (the 72 grouped launches of the 36
+    layers, without the head), captured into one graph and replayed exactly as
+    in the step: milliseconds per launch -- each launch's duration inside the
+    replayed graph, dispatch gap included -- and the average algorithmic bytes
+    per launch (weights + activations read + outputs written)."""
+    calls = [c for c in wl.launches(M, mode) if c[2]]
+    xs, ys, _, _ = wl.buffers(M)
+    act = sum(ys[p].numel() * 2 for p in wl.order) + (2048 + 2048 + 8192) * M * 2   # per layer
+    nbytes = (sum(b for _, b, _ in calls) + act * N_LAYERS) / len(calls)
+    ms = graph_ms(torch, lambda: [f() for f, _, _ in calls], steps, warmup)
+    return ms / len(calls), nbytes
 
 
 class HipEvents:
@@ -503,12 +565,20 @@ def time_q4_launches(torch, q4, wl, M, mode, reps=3):
     return tot_ms / n, tot_bytes / n
 
 
-def time_nvfp4_launches(torch, q4, nv, M, reps=3):
-    """Average execution time of the NVFP4 GEMV launches of one NVFP4 step
-    (HIP events on the launch stream, as for the int4 launches) and their
-    average algorithmic bytes: weights + that projection's x and y."""
+def time_graph_nv(torch, nv, M, steps, warmup, mode):
+    """The NVFP4 step captured into a hipGraph and replayed, checked once
+    against the eager calls like time_graph.  Returns (ms per step, None)."""
+    return replay_checked(torch, nv.launches(M, mode), nv.int4.outputs(M), steps, warmup, f"NVFP4 M={M} {mode}"), None
+
+
+def nvfp4_launches_in_graph(torch, nv, M, steps, warmup):
+    """The NVFP4 projections' own launches of the per-projection NVFP4 step
+    (q, k, o, gate, up of the 36 layers: 180 launches), captured into one
+    graph and replayed: milliseconds per launch inside the graph and the
+    average algorithmic bytes per launch (weights + that projection's x and
+    y)."""
     xs, ys, _, _ = nv.int4.buffers(M)
-    calls = []
+    calls, nbytes = [], 0
     all_calls = nv.launches(M)
     k = 0
     for li in range(N_LAYERS):
@@ -516,74 +586,99 @@ def time_nvfp4_launches(torch, q4, nv, M, reps=3):
             f, b, is_nv = all_calls[k]
             k += 1
             if is_nv:
-                calls.append((f, b + xs[p].numel() * 2 + ys[p].numel() * 2))
-    he = HipEvents()
-    evs = [(he.create(), he.create()) for _ in calls]
-    tot_ms, tot_bytes, n = 0.0, 0, 0
-    for _ in range(reps):
-        for (f, b), (a, z) in zip(calls, evs):
-            q4.lib.q4gemv_time_next_launch(a, z)
-            f()
-        torch.cuda.synchronize()
-        he.sync(evs[-1][1])
-        for (f, b), (a, z) in zip(calls, evs):
-            tot_ms += he.elapsed_ms(a, z)
-            tot_bytes += b
-            n += 1
-    for a, z in evs:
-        he.destroy(a)
-        he.destroy(z)
-    return tot_ms / n, tot_bytes / n
+                calls.append(f)
+                nbytes += b + xs[p].numel() * 2 + ys[p].numel() * 2
+    ms = graph_ms(torch, lambda: [f() for f in calls], steps, warmup)
+    return ms / len(calls), nbytes / len(calls)
 
 
-def cpu_baseline(wl, budget_s=15.0):
-    """The oracle (plain NumPy, fp64 product) on whole layers of the step's
-    weights, M = 1, until about budget_s seconds of CPU work."""
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle (plain NumPy: dequantize to fp32, fp64 matrix product) on
+    the step's own weights, on this host's cores.  Dequantization and the
+    product are timed separately, per projection, for whole layers until
+    about budget_s seconds of CPU time (the product at M = 1 and at M = 48),
+    then one layer again on a single thread; the head's BF16 GEMV once.  The
+    per-step figures extrapolate the per-layer means to the 36 layers plus
+    the head (one step = one dequantization of every matrix and one product;
+    the oracle has no cache of dequantized weights)."""
     import numpy as np
     import oracle
     import synth
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
-    x = {K: synth.bits16(synth.x_bf16(1, K, ("cpu-x", K))) for K in (2048, 8192)}
-    done_bytes, t_used, layers = 0, 0.0, 0
-    for lay in wl.layers:
-        host = {p: (t[0].cpu().numpy(), synth.bits16(t[1]), synth.bits16(t[2])) for p, t in lay.items()}
-        t0 = time.perf_counter()
+    x = {(M, K): synth.bits16(synth.x_bf16(M, K, ("cpu-x", M, K))) for M in (1, 48) for K in (2048, 8192)}
+
+    def layer(host):
+        t = {"dequant": 0.0, "mm1": 0.0, "mm48": 0.0}
         for p in wl.order:
             N, K = wl.shapes[p]
-            oracle.q4g128_gemv(x[K], *host[p])
-            done_bytes += q4_bytes(N, K, 1)
-        t_used += time.perf_counter() - t0
-        layers += 1
-        if t_used >= budget_s:
-            break
-    # the same on one thread, on one layer
-    one = None
-    try:
-        from threadpoolctl import threadpool_limits
-        host = {p: (t[0].cpu().numpy(), synth.bits16(t[1]), synth.bits16(t[2])) for p, t in wl.layers[0].items()}
-        with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            b1 = 0
-            for p in wl.order:
-                N, K = wl.shapes[p]
-                oracle.q4g128_gemv(x[K], *host[p])
-                b1 += q4_bytes(N, K, 1)
-            one = round(b1 / (time.perf_counter() - t0) / 1e9, 4)
-    except Exception:
-        pass
+            w32 = oracle.q4g128_dequant_f32(*host[p])
+            t1 = time.perf_counter()
+            oracle.gemv_f64(x[(1, K)], w32)
+            t2 = time.perf_counter()
+            oracle.gemv_f64(x[(48, K)], w32)
+            t3 = time.perf_counter()
+            t["dequant"] += t1 - t0
+            t["mm1"] += t2 - t1
+            t["mm48"] += t3 - t2
+        return t
+
+    def host_of(lay):
+        return {p: (t[0].cpu().numpy(), synth.bits16(t[1]), synth.bits16(t[2])) for p, t in lay.items()}
+
+    tot = {"dequant": 0.0, "mm1": 0.0, "mm48": 0.0}
+    layers = 0
+    for lay in wl.layers:
+        t = layer(host_of(lay))
+        for k in tot:
+            tot[k] += t[k]
+        layers += 1
+        if sum(tot.values()) >= budget_s:
+            break
+    per = {k: v / layers for k, v in tot.items()}
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            one = layer(host_of(wl.layers[0]))
+    # the head: BF16 widened to fp32, then the fp64 product
+    hb = synth.bits16(wl.heads[wl.head_rows].cpu())
+    t0 = time.perf_counter()
+    hw = oracle.bf16_dequant_f32(hb)
+    t1 = time.perf_counter()
+    oracle.gemv_f64(x[(1, 2048)], hw)
+    t2 = time.perf_counter()
+    oracle.gemv_f64(x[(48, 2048)], hw)
+    t3 = time.perf_counter()
+    head = {"dequant": t1 - t0, "mm1": t2 - t1, "mm48": t3 - t2}
+    step = {M: N_LAYERS * (per["dequant"] + per[f"mm{M}"]) + head["dequant"] + head[f"mm{M}"] for M in (1, 48)}
+    b1, b48 = wl.step_bytes(1), wl.step_bytes(48)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{layers} of {N_LAYERS} int4 layers (7 GEMVs each, M=1), NumPy dequant to fp32 + fp64 matmul, "
-                      f"{t_used:.1f} s", "value_1_thread": one, "cpu": model, "nproc": os.cpu_count()}
+    rec = {"value": round(b1 / step[1] / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{layers} of {N_LAYERS} int4 layers (7 projections each) + the {wl.head_rows}-row BF16 head, "
+                     f"NumPy dequantization to fp32 and fp64 matrix product timed separately at M=1 and M=48 "
+                     f"({sum(tot.values()) + sum(head.values()):.1f} s of CPU time); per-step figures extrapolate "
+                     f"the per-layer means to {N_LAYERS} layers",
+           "steps_per_s_M1": round(1.0 / step[1], 3), "steps_per_s_M48": round(1.0 / step[48], 3),
+           "GB_s_M48": round(b48 / step[48] / 1e9, 4),
+           "per_layer_s": {"dequant": round(per["dequant"], 4), "matmul_fp64_M1": round(per["mm1"], 4),
+                           "matmul_fp64_M48": round(per["mm48"], 4)},
+           "head_s": {k: round(v, 4) for k, v in head.items()},
+           "cpu": model, "nproc": os.cpu_count()}
+    if one is not None:
+        rec["one_thread_per_layer_s"] = {"dequant": round(one["dequant"], 4), "matmul_fp64_M1": round(one["mm1"], 4),
+                                         "matmul_fp64_M48": round(one["mm48"], 4)}
+        rec["value_1_thread"] = round(b1 / (N_LAYERS * (one["dequant"] + one["mm1"]) + head["dequant"] + head["mm1"]) / 1e9, 4)
+    return rec
 
 
 # per batch size: the kernel the grouped int4 launches run, the sources it is
@@ -591,8 +686,8 @@ def cpu_baseline(wl, budget_s=15.0):
 KERNELS = {
     1: ("gemv_stream_kernel<FmtQ4, 1, false>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
         os.path.join(ROOT, "profiles", "gemv_stream_q4_M1_grouped_traffic.json")),
-    48: ("tiled_mm_kernel<FmtQ4, 3, false, false>", ("common.h", "formats.h", "internal.h", "gemv_mm.hip"),
-         os.path.join(ROOT, "profiles", "tiled_mm_q4_M48_grouped_traffic.json")),
+    48: ("skinny_q4_kernel<3, R>", ("common.h", "formats.h", "internal.h", "gemv_skinny.hip"),
+         os.path.join(ROOT, "profiles", "skinny_q4_M48_grouped_traffic.json")),
 }
 
 
@@ -605,12 +700,21 @@ def _code_only(src):
     return " ".join(src.split())
 
 
+# the NVFP4 streaming kernel (M = 1, per-projection launches)
+NVFP4_KERNEL = ("gemv_stream_kernel<FmtNvfp4, 1, false>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
+                os.path.join(ROOT, "profiles", "gemv_stream_nvfp4_M1_traffic.json"))
+
+
 def csrc_digest(M):
     """sha256 over the code (comments and layout removed) of the sources of
     the kernel the grouped launches run at M."""
+    return csrc_digest_of(KERNELS[M][1])
+
+
+def csrc_digest_of(names):
     import hashlib
     h = hashlib.sha256()
-    for n in KERNELS[M][1]:
+    for n in names:
         with open(os.path.join(ROOT, "bit_weight_only_q4g128_amd", "csrc", n)) as fh:
             h.update(n.encode())
             h.update(_code_only(fh.read()).encode())
@@ -621,22 +725,32 @@ def measured_traffic(M):
     """HBM bytes per grouped int4 launch at M from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE runs, or None if the kernel sources changed since
     those counters were taken."""
+    return _traffic(KERNELS[M][2], KERNELS[M][1])
+
+
+def measured_traffic_nvfp4():
+    """The same for the NVFP4 streaming kernel's per-projection launches."""
+    return _traffic(NVFP4_KERNEL[2], NVFP4_KERNEL[1])
+
+
+def _traffic(path, sources):
     try:
-        with open(KERNELS[M][2]) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("csrc_digest") != csrc_digest(M):
+    if rec.get("csrc_digest") != csrc_digest_of(sources):
         return None
     return rec.get("traffic_bytes_per_launch")
 
 
-def counters_pass(q4, synth, torch, head_rows, M):
+def counters_pass(q4, synth, torch, head_rows, M, nvfp4=False):
     """Workload for hardware-counter runs (no timing): the grouped step at M
-    three times, eagerly, then a 256 MiB device-to-device copy whose byte
-    count is known (the reference that scales FETCH_SIZE / WRITE_SIZE)."""
+    (int4, or with nvfp4 the per-projection NVFP4 step) three times, eagerly,
+    then a 256 MiB device-to-device copy whose byte count is known (the
+    reference that scales FETCH_SIZE / WRITE_SIZE)."""
     wl = Workload(q4, synth, torch, head_rows)
-    calls = wl.launches(M, "grouped")
+    calls = Nvfp4Workload(q4, synth, torch, wl).launches(M, "plain") if nvfp4 else wl.launches(M, "grouped")
     for _ in range(3):
         for f, _, _ in calls:
             f()
@@ -647,7 +761,8 @@ def counters_pass(q4, synth, torch, head_rows, M):
     torch.cuda.synchronize()
     b.copy_(a)
     torch.cuda.synchronize()
-    log(f"bench: counters pass at M={M} done ({len(calls)} launches per step, csrc digest {csrc_digest(M)})")
+    log(f"bench: counters pass at M={M}{' NVFP4' if nvfp4 else ''} done ({len(calls)} launches per step, csrc digest "
+        f"{csrc_digest_of(NVFP4_KERNEL[1]) if nvfp4 else csrc_digest(M)})")
 
 
 def counters_prefill(q4, synth, torch):
@@ -677,10 +792,10 @@ def mode_record(k, r, int4_wbytes, ceil_ms):
     rec = {"ms_per_step": round(r["ms"], 5), "GB_s": round(r["gbs"], 1), "weight_GB_s": round(wb / (r["ms"] * 1e-3) / 1e9, 1),
            "pct_of_8TBps": round(100 * r["gbs"] / PEAK_GBS, 2), "steps_per_s": round(1e3 / r["ms"], 1),
            "tokens_per_s": round(batch * 1e3 / r["ms"], 1), "launches_per_step": r["launches"], "bytes_per_step": r["bytes"]}
-    if not isinstance(M, str):
+    rec["head_rows"] = r.get("head_rows")
+    rec["weight_bytes_per_step"] = wb
+    if not isinstance(M, str) and wb == int4_wbytes:
         rec["pct_of_read_ceiling"] = round(100 * ceil_ms / r["ms"], 1)
-    else:
-        rec["weight_bytes_per_step"] = wb
     return rec
 
 
@@ -689,15 +804,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--head", choices=("full", "slice"), default="full")
+    ap.add_argument("--head", choices=("full", "slice"), default="full",
+                    help="head of the headline step: the 16385-row audio head (default) or the 2049-row codebook slice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
     ap.add_argument("--counters-m", type=int, choices=(1, 48), default=1, help="batch size of the --counters workload")
+    ap.add_argument("--counters-nvfp4", action="store_true", help="the --counters workload with the NVFP4 step instead")
     ap.add_argument("--counters-prefill", action="store_true",
                     help="run the prefill GEMM (8192 x 2048, M = 4096) five times for rocprofv3 --pmc passes; no timing")
-    ap.add_argument("--modes", default="M1_grouped,M1_fused,M1_plain,M48_grouped,M48_fused,M48_plain,NVFP4_M1_grouped,NVFP4_M48_grouped,"
-                                       "NVFP4_M1_plain,NVFP4_M48_plain",
+    ap.add_argument("--modes", default="M1_grouped,M1_grouped_slice,M1_fused,M1_plain,M48_grouped,M48_grouped_slice,M48_fused,"
+                                       "M48_plain,NVFP4_M1_grouped,NVFP4_M48_grouped,NVFP4_M1_plain,NVFP4_M48_plain",
                     help="comma list of timed modes; M1_grouped is always timed (it is the headline value)")
+    ap.add_argument("--no-extras", action="store_true", help="skip the per-call records (fused calls, sampling, prefill, projections)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -714,24 +832,27 @@ def main():
         counters_prefill(q4, synth, torch)
         return
     if args.counters:
-        counters_pass(q4, synth, torch, head_rows, args.counters_m)
+        counters_pass(q4, synth, torch, head_rows, args.counters_m, args.counters_nvfp4)
         return
     wl = Workload(q4, synth, torch, head_rows)
+    other_head = synth.HEAD_SLICE[0] if head_rows == synth.HEAD_FULL[0] else synth.HEAD_FULL[0]
 
     modes = {"M1_grouped"} | set(m for m in args.modes.split(",") if m)
     res = {}
     for M in (1, 48):
-        for mode in ("grouped", "plain", "fused"):
+        for mode in ("grouped", "grouped_slice", "plain", "fused"):
             if f"M{M}_{mode}" not in modes:
                 continue
-            ms, g = time_graph(torch, wl, M, args.steps, args.warmup, mode)
-            by = wl.step_bytes(M, mode)
+            base_mode = "grouped" if mode == "grouped_slice" else mode
+            hr = other_head if mode == "grouped_slice" else head_rows
+            ms = time_graph(torch, wl, M, args.steps, args.warmup, base_mode, hr)
+            by = wl.step_bytes(M, base_mode, hr)
             # a fused call on the tiled kernel forms silu(gate) * up in a pass of its own
-            extra = N_LAYERS if mode == "fused" and M > 4 else 0
-            res[(M, mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(wl.launches(M, mode)) + extra)
-            log(f"bench: M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(M, mode)]['gbs']:6.0f} GB/s, "
-                f"{1e3 / ms:6.0f} steps/s, {res[(M, mode)]['launches']} launches")
-            del g
+            extra = N_LAYERS if base_mode == "fused" and M > 4 else 0
+            res[(M, mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(wl.launches(M, base_mode, hr)) + extra,
+                                  head_rows=hr, wbytes=sum(b for _, b, _ in wl.launches(1, "plain", hr)))
+            log(f"bench: M={M} {mode:13s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {res[(M, mode)]['gbs']:6.0f} GB/s, "
+                f"{1e3 / ms:6.0f} steps/s, {res[(M, mode)]['launches']} launches, head {hr} rows")
     nv = None
     for M in (1, 48):
         for mode in ("grouped", "plain"):
@@ -739,46 +860,55 @@ def main():
                 continue
             if nv is None:
                 nv = Nvfp4Workload(q4, synth, torch, wl)
-            ms, g = time_graph(torch, nv, M, args.steps, args.warmup, mode)
+            ms, g = time_graph_nv(torch, nv, M, args.steps, args.warmup, mode)
             by = nv.step_bytes(M)
             calls = nv.launches(M, mode)
             r = res[(f"NVFP4_M{M}", mode)] = dict(ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9, launches=len(calls),
-                                                  wbytes=sum(b for _, b, _ in calls))
+                                                  wbytes=sum(b for _, b, _ in calls), head_rows=head_rows)
             log(f"bench: NVFP4 M={M} {mode:7s} step {ms * 1e3:8.1f} us, {by / 1e6:.1f} MB, {r['gbs']:6.0f} GB/s, "
                 f"{1e3 / ms:6.0f} steps/s, {r['launches']} launches")
-            del g
+    # the roofline of the dominant kernel: its launches inside the replayed
+    # step (the step's graph without the head), per launch
     roof = {}
     for M in (1, 48):
         if M != 1 and f"M{M}_grouped" not in modes:
             continue
-        kms, kbytes = time_q4_launches(torch, q4, wl, M, "grouped")
+        kms, kbytes = layer_launches_in_graph(torch, wl, M, "grouped", args.steps, args.warmup)
         achieved = kbytes / (kms * 1e-3) / 1e9
         vname = q4.variant_name(q4.FMT_Q4G128, 0, M, 2048, 2048)
-        log(f"bench: int4 GEMV launches at M={M} ({vname}): avg {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, "
-            f"{achieved:.0f} GB/s")
-        roof[M] = {"bound": "hbm", "kernel": f"{KERNELS[M][0]} ({vname}), M={M} grouped launches",
+        step_us = res[(M, "grouped")]["ms"] * 1e3
+        nl = 2 * N_LAYERS
+        log(f"bench: int4 GEMV launches at M={M} ({vname}) inside the replayed step: {kms * 1e3:.2f} us per launch, "
+            f"{kbytes / 1e6:.2f} MB/launch, {achieved:.0f} GB/s; {nl} launches = {nl * kms * 1e3:.1f} of {step_us:.1f} us per step")
+        roof[M] = {"bound": "hbm", "kernel": f"{KERNELS[M][0]} ({vname}), M={M}: the {nl} grouped launches of the step",
                    "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                   "traffic": measured_traffic(M), "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)}
-    fz = {f"M{M}": fused_calls(torch, q4, synth, wl, M) for M in (1, 48)}
-    for k, r in fz.items():
-        log(f"bench: fused calls {k}: " + ", ".join(f"{n} fused {v['fused_us']} us / unfused {v['unfused_us']} us / "
-                                                     f"plain GEMV {v['plain_gemv_us']} us" for n, v in r.items()))
-    hs = {f"M{M}": head_sample_calls(torch, q4, synth, M) for M in (1, 48)}
-    for k, r in hs.items():
-        log(f"bench: head + top-k sampling {k}: " + ", ".join(f"{n}: GEMV {v['gemv_us']} us, GEMV+sample {v['gemv_and_sample_us']} us, "
-                                                              f"sample alone {v['sample_only_us']} us" for n, v in r.items()))
-    pj = projection_calls(torch, q4, wl)
-    log("bench: projections alone (36-copy rotation): " + ", ".join(f"{k} {v['us']} us {v['GB_s']} GB/s" for k, v in pj.items()
-                                                                    if k.startswith(("gate", "down"))))
-    pf = prefill_calls(torch, q4, synth)
-    log("bench: int4 prefill GEMM: " + ", ".join(f"{k} {v['int4_us']} us ({v['int4_TFLOP_s']} TFLOP/s; BF16 library on dequantized "
-                                                  f"weights {v['bf16_library_on_dequantized_us']} us)" for k, v in pf.items()))
+                   "traffic": measured_traffic(M), "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes),
+                   "timing": f"{nl} launches captured in one graph exactly as in the step (head left out), replayed; per-launch "
+                             f"period including the dispatch gap",
+                   "launches_x_avg_us": round(nl * kms * 1e3, 1), "step_us": round(step_us, 1)}
+    fz = hs = pj = pf = None
+    if not args.no_extras:
+        fz = {f"M{M}": fused_calls(torch, q4, synth, wl, M) for M in (1, 48)}
+        for k, r in fz.items():
+            log(f"bench: fused calls {k}: " + ", ".join(f"{n} fused {v['fused_us']} us / unfused {v['unfused_us']} us / "
+                                                         f"plain GEMV {v['plain_gemv_us']} us" for n, v in r.items()))
+        hs = {f"M{M}": head_sample_calls(torch, q4, synth, M) for M in (1, 48)}
+        for k, r in hs.items():
+            log(f"bench: head + top-k sampling {k}: " + ", ".join(f"{n}: GEMV {v['gemv_us']} us, GEMV+sample {v['gemv_and_sample_us']} us, "
+                                                                  f"sample alone {v['sample_only_us']} us" for n, v in r.items()))
+        pj = projection_calls(torch, q4, wl)
+        log("bench: projections alone (36-copy rotation): " + ", ".join(f"{k} {v['us']} us {v['GB_s']} GB/s" for k, v in pj.items()
+                                                                        if k.startswith(("gate", "down"))))
+        pf = prefill_calls(torch, q4, synth)
+        log("bench: int4 prefill GEMM: " + ", ".join(f"{k} {v['int4_us']} us ({v['int4_TFLOP_s']} TFLOP/s; BF16 library on dequantized "
+                                                      f"weights {v['bf16_library_on_dequantized_us']} us)" for k, v in pf.items()))
     head = res[(1, "grouped")]
     wbytes = weight_bytes(wl)
     ceil_ms = read_ceiling(torch, q4, wl, args.steps, args.warmup)
     ceil_gbs = wbytes / (ceil_ms * 1e-3) / 1e9
-    log(f"bench: plain read of the step's weight buffers in the same 73 launches: {ceil_ms * 1e3:.1f} us, "
-        f"{ceil_gbs:.0f} GB/s")
+    one_ms, one_gbs = single_launch_read(torch, q4, 20)
+    log(f"bench: plain read of the step's weight buffers in the same 73 launches: {ceil_ms * 1e3:.1f} us, {ceil_gbs:.0f} GB/s; "
+        f"one launch over 1 GiB: {one_ms * 1e3:.1f} us, {one_gbs:.0f} GB/s")
 
     out = {
         "metric": METRIC,
@@ -804,25 +934,30 @@ def main():
             "weight_bytes_per_step": wbytes,
             "read_ceiling": {"what": "diagnostic plain read of the same weight buffers in the same 73 launches, hipGraph",
                              "ms_per_step": round(ceil_ms, 5), "weight_GB_s": round(ceil_gbs, 1),
-                             "pct_of_8TBps": round(100 * ceil_gbs / PEAK_GBS, 2)},
+                             "pct_of_8TBps": round(100 * ceil_gbs / PEAK_GBS, 2),
+                             "single_launch": {"what": "one diagnostic plain-read launch over one contiguous 1 GiB buffer, hipGraph",
+                                               "us": round(one_ms * 1e3, 1), "GB_s": round(one_gbs, 1),
+                                               "pct_of_8TBps": round(100 * one_gbs / PEAK_GBS, 2)},
+                             "value_pct_of_single_launch": round(100 * head["gbs"] / one_gbs, 1)},
             "modes": {mode_key(k): mode_record(k, r, wbytes, ceil_ms) for k, r in res.items()},
-            "fused_calls": fz,
-            "head_sample": hs,
-            "prefill": pf,
-            "projections": pj,
         },
         "roofline": roof[1],
     }
+    for name, val in (("fused_calls", fz), ("head_sample", hs), ("prefill", pf), ("projections", pj)):
+        if val is not None:
+            out["config"][name] = val
     if 48 in roof:
         out["roofline_M48"] = roof[48]
     if nv is not None:
-        kms, kbytes = time_nvfp4_launches(torch, q4, nv, 1)
+        kms, kbytes = nvfp4_launches_in_graph(torch, nv, 1, args.steps, args.warmup)
         achieved = kbytes / (kms * 1e-3) / 1e9
         vname = q4.variant_name(q4.FMT_NVFP4G16, 0, 1, 2048, 2048)
-        log(f"bench: NVFP4 GEMV launches at M=1 ({vname}): avg {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
-        out["roofline_nvfp4_M1"] = {"bound": "hbm", "kernel": f"gemv_stream_kernel<FmtNvfp4, 1, false> ({vname}), M=1 per-projection launches",
+        log(f"bench: NVFP4 GEMV launches at M=1 ({vname}) inside a replayed graph: {kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, "
+            f"{achieved:.0f} GB/s")
+        out["roofline_nvfp4_M1"] = {"bound": "hbm", "kernel": f"gemv_stream_kernel<FmtNvfp4, 1, false> ({vname}), M=1: the 180 NVFP4 "
+                                                              f"projection launches of the per-projection step",
                                     "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                                    "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                                    "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic_nvfp4(),
                                     "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
