@@ -9,15 +9,19 @@
 // groups of the slice (its rounds) for all R tiles, so a wave needs only its
 // own data and the waves meet only once, at the end.
 //
-// Memory.  A wave issues everything it will need as soon as it starts: the
-// weights of all its rounds (16 bytes a lane per tile and round, straight into
-// registers), its rows' scales and mins, and the first round's activations
-// (MT x 16 batch rows x 256 bytes) -- the last two straight into LDS with
-// buffer_load ... lds, in whole cache lines (each instruction reads four
-// activation rows), into a region of its own, so no barrier is involved.  The
-// second round's activations follow once the first round's are read out.
-// Every buffer offset is scalar plus one per-lane base, so the address
-// arithmetic costs no vector instructions.
+// Memory.  A wave issues everything it will need as soon as it starts: its
+// rows' scales for its groups and a share of the workgroup's mins, the first
+// round's activations (MT x 16 batch rows x 256 bytes) -- these straight into
+// LDS with buffer_load ... lds, into regions of their own, so no barrier is
+// involved -- and the weights of both its rounds, straight into registers.
+// The workgroup's vector-memory path delivers cache lines at a bounded rate,
+// so every load reads whole 128-byte lines: four activation rows per
+// instruction, and for the weights eight rows x the wave's two adjacent
+// groups (128 bytes), the lanes then exchanging chunks with DPP row shifts to
+// reach the matrix-core operand layout.  The second round's activations
+// follow once the first round's are read out.  Every buffer offset is scalar
+// plus one per-lane base, so the address arithmetic costs no vector
+// instructions.
 //
 // Arithmetic per round: the activation fragments are read from LDS (an XOR
 // swizzle of the 16-byte chunks by row makes every read conflict-free) and
@@ -78,11 +82,14 @@ struct SkTable {
 //   [0, kArea)           per wave: one round of activations, MT * 16 rows x
 //                        256 bytes; after the rounds, the eight waves' result
 //                        tiles [8][R * MT][64 lanes] x 16 bytes (the larger)
-//   [kArea, + kPar)      per wave: scales then mins of its 16 R rows for its
-//                        two group slots, [2][16 R][2] dwords holding the fp16
-//                        value in the low half (a 2-byte load to LDS writes one
-//                        zero-extended dword per lane), each array padded to
-//                        whole 64-lane loads
+//   [kArea, + kPar)      per wave: the scales of its 16 R rows for its two
+//                        group slots, [16 R][2] dwords holding the fp16 value
+//                        in the low half (a 2-byte load to LDS writes one
+//                        zero-extended dword per lane), padded to whole 64-lane
+//                        loads
+//   [.., + kMin)         the mins of the workgroup's 16 R rows for the slice's
+//                        groups, [16 R][16] dwords (fp16 in the low half),
+//                        padded to whole 64-lane loads of all eight waves
 //   [.., + kSx)          SX per group of the slice and batch row, fp32 [16][16 MT]
 template <int MT, int R>
 struct SkLds {
@@ -90,9 +97,11 @@ struct SkLds {
     static constexpr int kRed = kSkWaves * R * MT * 1024;
     static constexpr int kArea = (kSkWaves * kX > kRed) ? kSkWaves * kX : kRed;
     static constexpr int kParArr = ((32 * R + 63) / 64) * 64;   // dwords per (wave, array), whole 64-lane loads
-    static constexpr int kPar = kSkWaves * 2 * kParArr * 4;
+    static constexpr int kPar = kSkWaves * kParArr * 4;
+    static constexpr int kMinLoads = (16 * R * kSkMaxGroups / 64 + kSkWaves - 1) / kSkWaves;   // per wave
+    static constexpr int kMin = kSkWaves * kMinLoads * 64 * 4;
     static constexpr int kSx = kSkMaxGroups * 16 * MT * 4;
-    static constexpr int kBytes = kArea + kPar + kSx;
+    static constexpr int kBytes = kArea + kPar + kMin + kSx;
 };
 
 // Workgroup barrier that waits only for this wave's LDS traffic, so the
@@ -152,8 +161,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     const int nv = ng - nr * wave;                       // this wave's valid rounds (may be <= 0)
 
     uint8_t* xbuf = lds + wave * L::kX;
-    uint32_t* par = reinterpret_cast<uint32_t*>(lds + L::kArea);     // [8][2][kParArr]
-    float* sxt = reinterpret_cast<float*>(lds + L::kArea + L::kPar);  // [16][16 MT]
+    uint32_t* par = reinterpret_cast<uint32_t*>(lds + L::kArea);               // scales [8][kParArr]
+    uint32_t* mtab = reinterpret_cast<uint32_t*>(lds + L::kArea + L::kPar);    // mins [16 R][16]
+    float* sxt = reinterpret_cast<float*>(lds + L::kArea + L::kPar + L::kMin);  // [16][16 MT]
 
     // ---- 1. issue: group parameters (to LDS), round-0 activations (to LDS),
     // all weights (to registers).  Out-of-range offsets read zero.
@@ -161,7 +171,8 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)nrows * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.K * 2u);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)row0 * rowbytes, (uint32_t)nrows * rowbytes);
-    // parameters: element e = 64 i + lane is (row e / 2, slot e % 2) -> group g0 + nr w + slot
+    // scales, per wave: element e = 64 i + lane is (row e / 2, slot e % 2) ->
+    // group g0 + nr w + slot
     {
         constexpr int kPI = (16 * R * 2 + 63) / 64;
 #pragma unroll
@@ -170,9 +181,19 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             const int row = e >> 1, slot = e & 1;
             const bool ok = row < 16 * R && slot < nv;
             const uint32_t off = ok ? ((uint32_t)row * (uint32_t)G + (uint32_t)(g0 + nr * wave + slot)) * 2u : 0xFFFFFFF0u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(par + (wave * 2 + 0) * L::kParArr + 64 * i), 2, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(par + (wave * 2 + 1) * L::kParArr + 64 * i), 2, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(par + wave * L::kParArr + 64 * i), 2, off, 0, 0, 0);
         }
+    }
+    // mins, once per workgroup (they are read only after the waves meet):
+    // element e = 64 (wave + 8 j) + lane is (row e / 16, group e % 16 of the
+    // slice); four rows' slices of a whole-K task share one cache line
+#pragma unroll
+    for (int j = 0; j < L::kMinLoads; ++j) {
+        const int e = 64 * (wave + kSkWaves * j) + lane;
+        const int row = e >> 4, gi = e & 15;
+        const bool ok = row < 16 * R && gi < ng;
+        const uint32_t off = ok ? ((uint32_t)row * (uint32_t)G + (uint32_t)(g0 + gi)) * 2u : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(mtab + 64 * (wave + kSkWaves * j)), 2, off, 0, 0, 0);
     }
     // activations of round r: instruction i covers batch rows 4 i .. 4 i + 3;
     // lane l writes position p = l % 16 of row m = 4 i + l / 16 and fetches
@@ -189,16 +210,22 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
         }
     };
     issue_x(0);
-    // weights: lane l reads row l % 16 of each tile, bytes 16 (l / 16) of the
-    // group's 64; the row and group parts of the offset are scalar
-    const uint32_t woff0 = (uint32_t)(lane & 15) * rowbytes + 16u * (uint32_t)(lane >> 4);
-    u32x4 W[2][R];
+    // weights.  A wave's two groups are adjacent, 128 bytes of each row (one
+    // cache line), so a load instruction reads eight rows in whole lines:
+    // lane l reads row l % 8 of the tile's lower (L0) or upper (L1) eight
+    // rows, 16-byte chunk l / 16 of the first group (l % 16 < 8) or of the
+    // second (l % 16 >= 8).  (A wave with one group reads that group's chunk
+    // l / 16 in both halves of the lane range.)  The row and group parts of
+    // the offset are scalar.
+    const bool pair = nr == 2;
+    const uint32_t woff = (uint32_t)(lane & 7) * rowbytes + 16u * (uint32_t)(lane >> 4) + (pair ? 64u * (uint32_t)((lane >> 3) & 1) : 0u);
+    const __amdgpu_buffer_rsrc_t rw0 = nv > 0 ? rw : make_rsrc(a.w, 0u);
+    const uint32_t gb = (uint32_t)(g0 + nr * wave) * 64u;
+    u32x4 L0[R], L1[R];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const __amdgpu_buffer_rsrc_t rwr = r < nv ? rw : make_rsrc(a.w, 0u);
-        const uint32_t gb = (uint32_t)(g0 + nr * wave + r) * 64u;
-#pragma unroll
-        for (int t = 0; t < R; ++t) W[r][t] = buf_load16(rwr, woff0, (uint32_t)(16 * t) * rowbytes + gb);
+    for (int t = 0; t < R; ++t) {
+        L0[t] = buf_load16(rw0, woff, (uint32_t)(16 * t) * rowbytes + gb);
+        L1[t] = buf_load16(rw0, woff, (uint32_t)(16 * t + 8) * rowbytes + gb);
     }
 
     // ---- 2. the rounds
@@ -233,7 +260,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             }
         uint32_t sc16[R];   // this lane's row: the scale of this round's group (fp16 in the low half)
 #pragma unroll
-        for (int t = 0; t < R; ++t) sc16[t] = par[(wave * 2 + 0) * L::kParArr + 2 * (16 * t + (lane & 15)) + r];
+        for (int t = 0; t < R; ++t) sc16[t] = par[wave * L::kParArr + 2 * (16 * t + (lane & 15)) + r];
         if (r == 0 && nr > 1 && nv > 1) {
             __builtin_amdgcn_s_waitcnt(kLgkm0);   // the region is read out before it is refilled
             issue_x(1);
@@ -263,10 +290,19 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             f32x4 D[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) D[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // the operand (lane l: row l % 16, chunk l / 16 of the round's
+            // group): lanes l % 16 >= 8 take their chunk from eight lanes
+            // down in L1 (round 0), lanes l % 16 < 8 from eight lanes up in
+            // L0 (round 1) -- DPP row shifts, within rows of 16 lanes
+            u32x4 Wt;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                Wt[d] = r == 0 ? (uint32_t)__builtin_amdgcn_update_dpp((int)L0[t][d], (int)L1[t][d], 0x118, 0xF, 0xC, false)
+                               : (uint32_t)__builtin_amdgcn_update_dpp((int)L1[t][d], (int)L0[t][d], 0x108, 0xF, 0x3, false);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 uint32_t A[4];
-                q4_pairs(W[r][t][s], A);
+                q4_pairs(Wt[s], A);
                 const bf16x8_t Wv = as_b8(u32x4{A[0], A[1], A[2], A[3]});
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) D[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(B[mt][s]), Wv, D[mt], 0, 0, 0);
@@ -308,8 +344,8 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
                 const int gi = g < ng ? g : 0;
                 const int w2 = gi >> nsh, slot = gi & nsh;
                 av[c] = sxt[gi * 16 * MT + 16 * mt + (lane & 15)];
-                sv[c] = f16_to_f32((uint16_t)par[(w2 * 2 + 0) * L::kParArr + 2 * row + slot]);
-                mv[c] = f16_to_f32((uint16_t)par[(w2 * 2 + 1) * L::kParArr + 2 * row + slot]);
+                sv[c] = f16_to_f32((uint16_t)par[w2 * L::kParArr + 2 * row + slot]);
+                mv[c] = f16_to_f32((uint16_t)mtab[16 * row + gi]);
             }
             f32x4 v = red[p * 64 + lane];
 #pragma unroll
