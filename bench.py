@@ -350,17 +350,24 @@ def fused_calls(torch, q4, synth, wl, M):
 
 def head_sample_calls(torch, q4, synth, M):
     """Sampling from the head at temperature 0.8, top-k 30 (caller-supplied
-    uniforms): the 2049-row head GEMV alone, GEMV + sampling in one call, and
-    the sampler alone on 2049 and 16385 logits; microseconds per call."""
+    uniforms), 2049- and 16385-row heads: the head GEMV alone, GEMV +
+    sampling as two launches, GEMV + sampling in one launch (where it
+    applies: M <= 4), and the sampler alone; microseconds per call."""
     rec = {}
     x = synth.x_bf16(M, 2048, ("bench-hs-x", M), device="cuda")
     u = torch.rand(M, generator=torch.Generator(device="cuda").manual_seed(M), device="cuda")
     for N in (2049, 16385):
         w = synth.bf16_matrix(N, 2048, ("bench-hs-w", N), device="cuda")
         lg = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        rec[f"head{N}"] = {"gemv_us": round(graph_us(torch, lambda: q4.bf16_gemv(x, w, out=lg)), 2),
-                           "gemv_and_sample_us": round(graph_us(torch, lambda: q4.bf16_head_sample(x, w, u, logits=lg)), 2),
-                           "sample_only_us": round(graph_us(torch, lambda: q4.sample_topk(lg, u)), 2)}
+        r = {"gemv_us": round(graph_us(torch, lambda: q4.bf16_gemv(x, w, out=lg)), 2),
+             "gemv_and_sample_us": round(graph_us(torch, lambda: q4.bf16_head_sample(x, w, u, logits=lg)), 2),
+             "sample_only_us": round(graph_us(torch, lambda: q4.sample_topk(lg, u)), 2)}
+        need = q4.bf16_head_sample_workspace_bytes(M, N, 2048, 30)
+        if need:
+            ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+            r["gemv_and_sample_one_launch_us"] = round(graph_us(torch, lambda: q4.bf16_head_sample(x, w, u, logits=lg, workspace=ws)), 2)
+            r["one_launch_over_gemv"] = round(r["gemv_and_sample_one_launch_us"] / r["gemv_us"], 2)
+        rec[f"head{N}"] = r
     return rec
 
 
@@ -895,6 +902,7 @@ def main():
         hs = {f"M{M}": head_sample_calls(torch, q4, synth, M) for M in (1, 48)}
         for k, r in hs.items():
             log(f"bench: head + top-k sampling {k}: " + ", ".join(f"{n}: GEMV {v['gemv_us']} us, GEMV+sample {v['gemv_and_sample_us']} us, "
+                                                                  f"one launch {v.get('gemv_and_sample_one_launch_us')} us, "
                                                                   f"sample alone {v['sample_only_us']} us" for n, v in r.items()))
         pj = projection_calls(torch, q4, wl)
         log("bench: projections alone (36-copy rotation): " + ", ".join(f"{k} {v['us']} us {v['GB_s']} GB/s" for k, v in pj.items()

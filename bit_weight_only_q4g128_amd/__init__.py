@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "q4g128_gemv", "q4g128_gemv_grouped", "q4g128_gemv_grouped_noalloc", "NOALLOC_SCRATCH_BYTES", "nvfp4g16_gemv", "bf16_gemv", "q4g128_dequant_f32", "nvfp4g16_dequant_f32",
     "nvfp4g16_gemv_grouped", "nvfp4g16_workspace_bytes", "bf16_gemv_grouped", "bf16_workspace_bytes",
-    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample", "q4g128_gemm", "gemv_grouped_mixed", "mixed_workspace_bytes",
+    "q4g128_gemv_fused", "q4g128_fused_workspace_bytes", "sample_topk", "bf16_head_sample", "bf16_head_sample_workspace_bytes", "q4g128_gemm", "gemv_grouped_mixed", "mixed_workspace_bytes",
     "variant_name", "strerror", "Q4GemvError", "LIB_PATH", "lib", "stream_read", "stream_read_sink_words",
     "VARIANT_AUTO", "VARIANT_DOT2", "VARIANT_MFMA", "VARIANT_STREAM", "VARIANT_TILED", "VARIANT_GEMM", "FMT_Q4G128", "FMT_NVFP4G16", "FMT_BF16",
 ]
@@ -115,6 +115,10 @@ lib.q4_sample_topk.argtypes = [_p, _i, _i, _f, _i, _p, _p, _p, _p, _p]
 lib.q4_sample_topk.restype = ctypes.c_int
 lib.bf16_head_sample.argtypes = [_p, _i, _i, _p, _i, _p, _f, _i, _p, _p, _p, _p, _p]
 lib.bf16_head_sample.restype = ctypes.c_int
+lib.bf16_head_sample_ws.argtypes = [_p, _i, _i, _p, _i, _p, _f, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
+lib.bf16_head_sample_ws.restype = ctypes.c_int
+lib.bf16_head_sample_workspace_bytes.argtypes = [_i, _i, _i, _i]
+lib.bf16_head_sample_workspace_bytes.restype = ctypes.c_size_t
 
 
 class Q4GemvError(ValueError):
@@ -479,10 +483,19 @@ def sample_topk(logits, u, temperature: float = 0.8, top_k: int = 30, return_top
     return (tok, ti, tp) if return_topk else tok
 
 
-def bf16_head_sample(x, w, u, temperature: float = 0.8, top_k: int = 30, logits=None, return_topk: bool = False):
-    """The BF16 head GEMV logits = x W^T followed by top-k sampling (two
-    launches).  Returns (token, logits) or (token, topk_index, topk_prob,
-    logits) with return_topk."""
+def bf16_head_sample_workspace_bytes(M: int, N: int, K: int, top_k: int = 30) -> int:
+    """Bytes of zero-filled workspace for the one-launch head sampling (0 if
+    it does not apply to this shape)."""
+    return int(lib.bf16_head_sample_workspace_bytes(M, N, K, top_k))
+
+
+def bf16_head_sample(x, w, u, temperature: float = 0.8, top_k: int = 30, logits=None, return_topk: bool = False,
+                     workspace=None):
+    """The BF16 head GEMV logits = x W^T followed by top-k sampling: two
+    launches, or one (bf16_head_sample_ws in the C header) when a zero-filled
+    uint8 workspace of at least bf16_head_sample_workspace_bytes() is given
+    and that size is nonzero.  Returns (token, logits) or (token, topk_index,
+    topk_prob, logits) with return_topk."""
     _check(x, "x", _U16, 2); _check(w, "w", _U16, 2); _check(u, "u", (torch.float32,), 1)
     M, K = x.shape
     N = w.shape[0]
@@ -490,9 +503,16 @@ def bf16_head_sample(x, w, u, temperature: float = 0.8, top_k: int = 30, logits=
         raise ValueError("inconsistent shapes")
     lg = _out(logits, (M, N), torch.bfloat16, x)
     tok, ti, tp = _sample_outputs(M, top_k, x, return_topk)
-    _raise(lib.bf16_head_sample(x.data_ptr(), M, K, w.data_ptr(), N, lg.data_ptr(), float(temperature), int(top_k), u.data_ptr(),
-                                tok.data_ptr(), ti.data_ptr() if ti is not None else None, tp.data_ptr() if tp is not None else None,
-                                _stream(x)))
+    ti_p = ti.data_ptr() if ti is not None else None
+    tp_p = tp.data_ptr() if tp is not None else None
+    if workspace is None:
+        _raise(lib.bf16_head_sample(x.data_ptr(), M, K, w.data_ptr(), N, lg.data_ptr(), float(temperature), int(top_k), u.data_ptr(),
+                                    tok.data_ptr(), ti_p, tp_p, _stream(x)))
+    else:
+        if workspace.device != x.device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the activations' device")
+        _raise(lib.bf16_head_sample_ws(x.data_ptr(), M, K, w.data_ptr(), N, lg.data_ptr(), float(temperature), int(top_k),
+                                       u.data_ptr(), tok.data_ptr(), ti_p, tp_p, workspace.data_ptr(), workspace.numel(), _stream(x)))
     return (tok, ti, tp, lg) if return_topk else (tok, lg)
 
 

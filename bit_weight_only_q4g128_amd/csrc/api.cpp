@@ -752,6 +752,38 @@ int bf16_head_sample(const uint16_t* x, int M, int K, const uint16_t* w, int N, 
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 
+size_t bf16_head_sample_workspace_bytes(int M, int N, int K, int top_k) {
+    if (M < 1 || N < 1 || K < 1 || top_k < 1 || top_k > N) return 0;
+    return q4::head_sample_workspace_bytes(M, N, K, top_k);
+}
+
+int bf16_head_sample_ws(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* logits, float temperature, int top_k,
+                        const float* u, int32_t* token, int32_t* topk_index, float* topk_prob, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    const size_t need = bf16_head_sample_workspace_bytes(M, N, K, top_k);
+    if (need == 0 || workspace == nullptr || ws_bytes < need)
+        return bf16_head_sample(x, M, K, w, N, logits, temperature, top_k, u, token, topk_index, topk_prob, stream);
+    GemvArgs a;
+    Range in[4], out;
+    int rc = check_bf(x, M, K, w, N, logits, a, in, out);
+    if (rc) return rc;
+    for (int r = 0; r < 2; ++r)
+        if (overlaps(out, in[r])) return Q4_EALIAS;
+    if (u && overlaps(out, range_of(u, (size_t)M * 4))) return Q4_EALIAS;
+    rc = check_sample(logits, M, N, temperature, top_k, u, token, topk_index, topk_prob, in, 2);
+    if (rc) return rc;
+    if (!aligned(workspace, 4)) return Q4_EALIGN;
+    const Range wr = range_of(workspace, need);
+    const Range others[7] = {in[0], in[1], out, range_of(u, (size_t)M * 4), range_of(token, (size_t)M * 4),
+                             topk_index ? range_of(topk_index, (size_t)M * top_k * 4) : Range{0, 0},
+                             topk_prob ? range_of(topk_prob, (size_t)M * top_k * 4) : Range{0, 0}};
+    for (const Range& r : others)
+        if (overlaps(wr, r)) return Q4_EALIAS;
+    hipError_t e = q4::launch_head_sample(a, temperature, top_k, u, token, topk_index, topk_prob, workspace,
+                                          reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
 size_t q4gemv_stream_read_sink_words(const size_t* bytes, int count) {
     if (!bytes || count < 1 || count > q4::kMaxReadBufs) return 0;
     for (int i = 0; i < count; ++i)

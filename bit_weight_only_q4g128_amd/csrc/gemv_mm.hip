@@ -87,7 +87,7 @@ struct MmTask {
     int y8;            // y rows can be written 8 bytes at a time (y 8-byte aligned, N % 4 == 0)
     int fmt;           // weight format (the mixed-format kernel)
     float* part;       // partial tiles (ks > 1): [blocks][ks][4 tiles][MT][64 lanes] x 4 floats
-    unsigned* cnt;     // arrival counters (ks > 1): [blocks]
+    unsigned* cnt;     // arrival counters (ks > 1): [blocks], kCtrStride bytes apart
 };
 
 struct MmTable {
@@ -625,7 +625,7 @@ __device__ __forceinline__ void tiled_body(const MmTable& tt, const int ti, uint
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __shared__ unsigned s_prev;
-    if (tid == 0) s_prev = __hip_atomic_fetch_add(&cnt[blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) s_prev = __hip_atomic_fetch_add(&cnt[(size_t)blk * kCtrWords], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_prev != (unsigned)(KS - 1)) return;
     asm volatile("" ::: "memory");
@@ -657,7 +657,7 @@ __device__ __forceinline__ void tiled_body(const MmTable& tt, const int ti, uint
         }
         write_y_tile<MT, kFused>(a, tt.t[ti].y8 != 0, gs, row0 + 32 * rp + 16 * t, lane, sum);
     }
-    if (tid == 0) __hip_atomic_store(&cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&cnt[(size_t)blk * kCtrWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class F, int MT, bool kFused = false, bool kChunks = false>
@@ -768,7 +768,7 @@ size_t ws_bytes_mt(const GemvArgs* tasks, int count) {
         if (ks[i] <= 1) continue;
         const size_t blocks = (tasks[i].N + kRows - 1) / kRows;
         part += blocks * ks[i] * kCompute * MT * 64 * 16;
-        cnt += blocks * 4;
+        cnt += blocks * kCtrStride;
     }
     return (part > 0 && cnt <= kCntBytes) ? kCntBytes + part : 0;
 }
@@ -820,7 +820,7 @@ int build_table(const GemvArgs* tasks, const Fmt* fmts, int count, void* ws, siz
         tt.t[j].fmt = fmts ? fmts[i] : 0;
         if (ks[i] > 1) {
             tt.t[j].cnt = reinterpret_cast<unsigned*>(pc);
-            pc += (size_t)blocks * 4;
+            pc += (size_t)blocks * kCtrStride;
             tt.t[j].part = reinterpret_cast<float*>(pp);
             pp += (size_t)blocks * ks[i] * kCompute * MT * 64 * 16;
         }

@@ -70,7 +70,7 @@ struct SkTask {
     int ks;          // workgroups (K slices) per row block
     int gs;          // groups per slice
     float* part;     // ks > 1: partial tiles [blocks][ks][R * MT][64 lanes] x 4 floats
-    unsigned* cnt;   // ks > 1: arrival counters [blocks]
+    unsigned* cnt;   // ks > 1: arrival counters [blocks], kCtrStride bytes apart
 };
 
 struct SkTable {
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __shared__ unsigned s_prev;
-    if (tid == 0) s_prev = __hip_atomic_fetch_add(&tk.cnt[blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) s_prev = __hip_atomic_fetch_add(&tk.cnt[(size_t)blk * kCtrWords], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_prev != (unsigned)(KS - 1)) return;
     asm volatile("" ::: "memory");
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
         }
         sk_write_tile(tk, row0 + 16 * (p / MT), p % MT, lane, sum);
     }
-    if (tid == 0) __hip_atomic_store(&tk.cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&tk.cnt[(size_t)blk * kCtrWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kCUs = 256;
@@ -444,7 +444,7 @@ size_t sk_ws_bytes(const GemvArgs* tasks, int count, int R, const int* ks) {
         if (ks[i] <= 1) continue;
         const size_t blocks = (tasks[i].N + 16 * R - 1) / (16 * R);
         part += blocks * ks[i] * R * MT * 1024;
-        cnt += blocks * 4;
+        cnt += blocks * kCtrStride;
     }
     if (part == 0) return 0;
     if (cnt > kWsCounterBytes) return (size_t)-1;
@@ -506,7 +506,7 @@ hipError_t launch_sk_mt(const GemvArgs* tasks, int count, const SkPlan& p, void*
         t.gs = p.gs[i];
         if (p.ks[i] > 1) {
             t.cnt = reinterpret_cast<unsigned*>(pc);
-            pc += (size_t)blocks * 4;
+            pc += (size_t)blocks * kCtrStride;
             t.part = reinterpret_cast<float*>(pp);
             pp += (size_t)blocks * p.ks[i] * R * MT * 1024;
         }

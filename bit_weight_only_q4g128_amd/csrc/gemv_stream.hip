@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "topk.h"
 
 namespace q4 {
 
@@ -88,8 +89,22 @@ __device__ __forceinline__ int stream_task(const StreamTable& tt) {
     return t;
 }
 
+constexpr int kAuxCoherent = 16;   // buffer cache policy sc1: device-coherent, not held in the per-XCD L2
+
+// One output element; kCoh: a device-coherent store (read back by other
+// workgroups of the same launch).
+template <bool kCoh>
+__device__ __forceinline__ void store_y(const GemvArgs& a, size_t off, uint16_t v) {
+    if constexpr (kCoh) {
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, (uint32_t)((size_t)a.M * a.N * 2));
+        __builtin_amdgcn_raw_buffer_store_b16(v, ry, (int)(off * 2), 0, kAuxCoherent);
+    } else {
+        a.y[off] = v;
+    }
+}
+
 // One workgroup block of task `a`: blk is the block's index within the task.
-template <class F, int MT, bool kFused>
+template <class F, int MT, bool kFused, bool kCoh = false>
 __device__ __forceinline__ void stream_block(const GemvArgs a, const int cl, const int blk, uint8_t* lds) {
     constexpr int kXP = MT * 4;   // most x pieces a thread stages (K <= 8192 for the 4-bit formats)
 
@@ -250,7 +265,7 @@ __device__ __forceinline__ void stream_block(const GemvArgs a, const int cl, con
             v += dpp<0x142, 0xA>(v);
             v += dpp<0x143, 0xC>(v);
             if constexpr (kFused) v += res[r][m];   // (F::finish is the identity for int4)
-            if (lane == 63 && row < a.N) a.y[(size_t)m * a.N + row] = f32_to_bf16(F::finish(a, v));
+            if (lane == 63 && row < a.N) store_y<kCoh>(a, (size_t)m * a.N + row, f32_to_bf16(F::finish(a, v)));
             out[m] = 0.f;
         }
     };
@@ -304,7 +319,7 @@ __device__ __forceinline__ void stream_block(const GemvArgs a, const int cl, con
             for (int m = 0; m < MT; ++m) {
                 float v = parts[wave][m];
                 for (int p = 1; p < wpr; ++p) v += parts[wave + p][m];
-                a.y[(size_t)m * a.N + wrow0] = f32_to_bf16(F::finish(a, v));
+                store_y<kCoh>(a, (size_t)m * a.N + wrow0, f32_to_bf16(F::finish(a, v)));
             }
         }
     }
@@ -433,6 +448,203 @@ hipError_t launch_stream_mixed(const Fmt* fmts, const GemvArgs* tasks, int count
         case 2: return launch_stream_mixed_mt<2>(fmts, tasks, count, s);
         case 3: return launch_stream_mixed_mt<3>(fmts, tasks, count, s);
         default: return launch_stream_mixed_mt<4>(fmts, tasks, count, s);
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// The BF16 head GEMV with top-k sampling in the same launch (M = 1).
+//
+// The workgroups run the streaming BF16 GEMV and store their logits
+// device-coherently.  They are grouped into super-blocks of consecutive
+// workgroups; the last workgroup to finish in a super-block (an arrival
+// counter tree) reads the super-block's logits back and selects, per batch row,
+// the top k entries (topk.h).  With one super-block (heads up to 3072 rows)
+// that workgroup also sorts and draws; otherwise it publishes the k entries
+// as candidates, and the last super-block to finish selects the top k of all
+// candidates, sorts and draws.  Nothing waits on another workgroup, and every
+// counter is back at zero when the launch ends.  Atomics on one cache line
+// serialize (about 12 ns each), so arrivals go through a tree of counters
+// on separate lines, with at most 16 arrivals at the first level.  The
+// hand-overs are those of
+// the split-K completion: device-coherent (sc1) stores, a wait for their
+// acknowledgements and a barrier before the counter update, sc1 loads after
+// it.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kHsE = 12;                       // entries per thread in one selection
+constexpr int kHsMaxEntries = 256 * kHsE;      // rows of a super-block, candidates of all
+constexpr int kHsFan = 16;                     // workgroups per first-level counter
+constexpr int kHsCtrWords = kCtrWords;         // counters a cache line apart
+
+struct HsArgs {
+    GemvArgs a;          // the head GEMV; a.y receives the logits
+    int cl, nwg;         // row chunking and GEMV workgroups
+    int sbw, nsb;        // workgroups per super-block, super-blocks
+    int k;
+    float temperature;
+    const float* u;
+    int32_t* token;
+    int32_t* topk_index;
+    float* topk_prob;
+    unsigned* cnt;       // arrival counters, zero, kHsCtrWords apart: [0, nsb) super-blocks,
+                         // [nsb] all, [nsb + 1 + g] first-level group g (workgroups 16 g ..)
+    uint32_t* cand;      // [M][nsb][k] candidate entries (nsb > 1)
+};
+
+// This workgroup's device-coherent stores are acknowledged, then it arrives
+// at counter c; true in the last of `n` arrivals, which also resets c.
+__device__ __forceinline__ bool hs_arrive(unsigned* c, int n, int tid, unsigned* s_prev) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) *s_prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const bool last = *s_prev == (unsigned)(n - 1);
+    if (last && tid == 0) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");
+    return last;
+}
+
+template <int MT>
+__global__ __launch_bounds__(256) void head_sample_kernel(HsArgs h) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ uint32_t lists[4 * 64];
+    __shared__ uint32_t scratch[4 * 64 * kHsE];
+    __shared__ unsigned s_prev;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int blk = blockIdx.x;
+    stream_block<FmtBf16, MT, false, true>(h.a, h.cl, blk, lds);
+
+    // stage 1: the super-block's rows, once all of its workgroups are done
+    // (its first-level groups of 16, then the super-block's count of groups)
+    const int g1 = blk / kHsFan;
+    const int g1_wgs = (h.nwg - g1 * kHsFan < kHsFan) ? h.nwg - g1 * kHsFan : kHsFan;
+    if (!hs_arrive(h.cnt + (size_t)(h.nsb + 1 + g1) * kHsCtrWords, g1_wgs, tid, &s_prev)) return;
+    const int sb = blk / h.sbw;
+    const int sb_wgs = (h.nwg - sb * h.sbw < h.sbw) ? h.nwg - sb * h.sbw : h.sbw;
+    if (!hs_arrive(h.cnt + (size_t)sb * kHsCtrWords, (sb_wgs + kHsFan - 1) / kHsFan, tid, &s_prev)) return;
+    const int N = h.a.N, k = h.k;
+    const int rw = rows_per_wg(h.cl);
+    const int r0 = sb * h.sbw * rw;
+    const int r1 = (N < r0 + sb_wgs * rw) ? N : r0 + sb_wgs * rw;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(h.a.y, (uint32_t)(MT * N * 2));
+#pragma unroll 1
+    for (int m = 0; m < MT; ++m) {
+        // every load issued before any is used (rows past the block read as
+        // zero through the range check and are masked to the empty entry)
+        uint32_t v[kHsE];
+#pragma unroll
+        for (int j = 0; j < kHsE; ++j) {
+            const int row = r0 + tid + 256 * j;
+            const uint32_t off = row < r1 ? (uint32_t)(m * N + row) * 2u : 0xFFFFFFF0u;
+            v[j] = __builtin_amdgcn_raw_buffer_load_b16(ry, (int)off, 0, kAuxCoherent);
+        }
+#pragma unroll
+        for (int j = 0; j < kHsE; ++j) {
+            const int row = r0 + tid + 256 * j;
+            v[j] = topk_entry(v[j], row) & (row < r1 ? 0xFFFFFFFFu : 0u);
+        }
+        const uint32_t top = wg_topk<kHsE>(v, k, lists, scratch, wave, lane);
+        if (wave == 0) {
+            if (h.nsb == 1) {
+                draw_sorted(top, k, h.temperature, h.u[m], lane, h.token + m, h.topk_index ? h.topk_index + m * k : nullptr,
+                              h.topk_prob ? h.topk_prob + m * k : nullptr);
+            } else if (lane < k) {
+                const __amdgpu_buffer_rsrc_t rc = make_rsrc(h.cand, (uint32_t)(MT * h.nsb * k * 4));
+                __builtin_amdgcn_raw_buffer_store_b32(top, rc, ((m * h.nsb + sb) * k + lane) * 4, 0, kAuxCoherent);
+            }
+        }
+    }
+    if (h.nsb == 1) return;
+
+    // stage 2: all super-blocks' candidates
+    if (!hs_arrive(h.cnt + (size_t)h.nsb * kHsCtrWords, h.nsb, tid, &s_prev)) return;
+    const int nc = h.nsb * k;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(h.cand, (uint32_t)(MT * nc * 4));
+#pragma unroll 1
+    for (int m = 0; m < MT; ++m) {
+        uint32_t v[kHsE];
+#pragma unroll
+        for (int j = 0; j < kHsE; ++j) {
+            const int i = tid + 256 * j;
+            const uint32_t off = i < nc ? (uint32_t)(m * nc + i) * 4u : 0xFFFFFFF0u;
+            v[j] = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)off, 0, kAuxCoherent);
+        }
+        const uint32_t top = wg_topk<kHsE>(v, k, lists, scratch, wave, lane);
+        if (wave == 0)
+            draw_sorted(top, k, h.temperature, h.u[m], lane, h.token + m, h.topk_index ? h.topk_index + m * k : nullptr,
+                          h.topk_prob ? h.topk_prob + m * k : nullptr);
+    }
+}
+
+struct HsPlan {
+    int cl = -1, rw = 0, nwg = 0, sbw = 0, nsb = 0;
+    size_t ws = 0;
+};
+
+size_t hs_counter_bytes(const HsPlan& p) {
+    return (size_t)(p.nsb + 1 + (p.nwg + kHsFan - 1) / kHsFan) * kHsCtrWords * 4;
+}
+
+bool hs_plan(int M, int N, int K, int k, HsPlan& p) {
+    // one batch row: the last workgroup selects and draws row after row, so
+    // for M > 1 the two launches (one sampling workgroup per row) are faster
+    if (M != 1 || k < 1 || k > 64 || N < k || !stream_ok<FmtBf16>(M, K)) return false;
+    p.cl = chunk_log2<FmtBf16>(K);
+    p.rw = rows_per_wg(p.cl);
+    p.nwg = (N + p.rw - 1) / p.rw;
+    if (p.nwg * p.rw <= kHsMaxEntries) {
+        p.sbw = p.nwg;
+        p.nsb = 1;
+    } else {
+        p.sbw = 128;
+        while ((size_t)((p.nwg + p.sbw - 1) / p.sbw) * k > (size_t)kHsMaxEntries) p.sbw *= 2;
+        if (p.sbw * p.rw > kHsMaxEntries) return false;
+        p.nsb = (p.nwg + p.sbw - 1) / p.sbw;
+    }
+    p.ws = hs_counter_bytes(p) + (p.nsb > 1 ? (size_t)M * p.nsb * k * 4 : 0);
+    return true;
+}
+
+template <int MT>
+hipError_t launch_hs_mt(const GemvArgs& a, const HsPlan& p, int k, float temperature, const float* u, int32_t* token,
+                        int32_t* topk_index, float* topk_prob, void* ws, hipStream_t st) {
+    HsArgs h{};
+    h.a = a;
+    h.cl = p.cl;
+    h.nwg = p.nwg;
+    h.sbw = p.sbw;
+    h.nsb = p.nsb;
+    h.k = k;
+    h.temperature = temperature;
+    h.u = u;
+    h.token = token;
+    h.topk_index = topk_index;
+    h.topk_prob = topk_prob;
+    h.cnt = static_cast<unsigned*>(ws);
+    h.cand = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + hs_counter_bytes(p));
+    return launch_kernel(head_sample_kernel<MT>, dim3(p.nwg), dim3(256), (size_t)stream_shmem<FmtBf16>(MT, a.K), st, h);
+}
+
+}  // namespace
+
+size_t head_sample_workspace_bytes(int M, int N, int K, int top_k) {
+    HsPlan p;
+    return hs_plan(M, N, K, top_k, p) ? p.ws : 0;
+}
+
+hipError_t launch_head_sample(const GemvArgs& a, float temperature, int top_k, const float* u, int32_t* token, int32_t* topk_index,
+                              float* topk_prob, void* ws, hipStream_t s) {
+    HsPlan p;
+    if (!hs_plan(a.M, a.N, a.K, top_k, p)) return hipErrorInvalidValue;
+    switch (a.M) {
+        case 1: return launch_hs_mt<1>(a, p, top_k, temperature, u, token, topk_index, topk_prob, ws, s);
+        case 2: return launch_hs_mt<2>(a, p, top_k, temperature, u, token, topk_index, topk_prob, ws, s);
+        case 3: return launch_hs_mt<3>(a, p, top_k, temperature, u, token, topk_index, topk_prob, ws, s);
+        default: return launch_hs_mt<4>(a, p, top_k, temperature, u, token, topk_index, topk_prob, ws, s);
     }
 }
 

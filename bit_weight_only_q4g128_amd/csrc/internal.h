@@ -66,6 +66,10 @@ bool mm_supported(Fmt fmt, int M, int K, bool split);
 // Every workspace starts with this many bytes of arrival counters that each
 // call leaves at zero; scratch lies after them.
 constexpr size_t kWsCounterBytes = 64 * 1024;
+// Bytes between two arrival counters: device-scope atomics on one cache line
+// serialize (about 12 ns each), on different lines they proceed in parallel.
+constexpr size_t kCtrStride = 128;
+constexpr int kCtrWords = (int)(kCtrStride / 4);
 // The built-in scratch of the allocation-free entry point (noalloc.hip): its
 // size, and its device address on the stream's device (set up on first use:
 // address lookup, counters cleared on stream s).
@@ -115,6 +119,12 @@ constexpr int kMaxTopK = 64;
 constexpr int kMaxVocab = 30720;
 hipError_t launch_topk_sample(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, int32_t* token,
                               int32_t* topk_index, float* topk_prob, hipStream_t s);
+// The BF16 head GEMV with top-k sampling in one launch (M = 1,
+// streaming row sizes, top_k <= 64): workspace bytes it needs (zero-filled,
+// left zero), or 0 if the fused launch does not apply.
+size_t head_sample_workspace_bytes(int M, int N, int K, int top_k);
+hipError_t launch_head_sample(const GemvArgs& a, float temperature, int top_k, const float* u, int32_t* token, int32_t* topk_index,
+                              float* topk_prob, void* ws, hipStream_t s);
 
 // 16x16x32 BF16 matrix-core GEMV (any M <= 64), one launch per task.
 hipError_t launch_mfma(Fmt fmt, const GemvArgs* tasks, int count, hipStream_t s);

@@ -11,25 +11,17 @@
 //      order (a block-wide prefix count) until there are k;
 //   4. one wave sorts the k entries by (logit descending, index ascending)
 //      with a bitonic network over its lanes;
-//   5. the lanes form e_i = exp(z_i - z_0), z = logit / T, and sum them in
-//      that order; the token is the first entry whose running sum exceeds
-//      u * S, and p_i = e_i / S.
+//   5. the lanes form e_i = exp(z_i - z_0), z = logit / T, their running
+//      sums (a prefix scan over the lanes) and total S; the token is the
+//      first entry whose running sum exceeds u * S, and p_i = e_i / S.
 #include "internal.h"
+#include "topk.h"
 
 namespace q4 {
 
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ uint32_t order_key(uint32_t bits) {
-    if (bits == 0x8000u) bits = 0;                      // -0 ties with +0
-    return (bits & 0x8000u) ? (~bits & 0xFFFFu) : (bits | 0x8000u);
-}
-__device__ __forceinline__ float key_value(uint32_t key) {
-    const uint32_t bits = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
-    return __builtin_bit_cast(float, bits << 16);
-}
 
 // Wave 0: the bin b (counting down from bin 255) where the running count
 // first reaches k; writes b and how many of bin b are still wanted.  Lane l
@@ -143,46 +135,10 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(const uint16_t* _
     }
     __syncthreads();
 
-    // 4. sort the k entries descending on (key, -index) in wave 0; an entry
-    // is key << 16 | (0xFFFF - index) (V <= 30720 fits 16 bits)
-    if (wave == 0) {
-        uint32_t v = lane < k ? list[lane] : 0u;                 // padding sorts last
-        for (int size = 2; size <= 64; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                const uint32_t o = __shfl_xor(v, stride);
-                const bool up = ((lane & size) == 0);            // this half of the sequence descends
-                const bool lower = (lane & stride) == 0;
-                const bool keep_max = (up == lower);
-                v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
-            }
-        }
-        // 5. probabilities and the draw: e_i in lane i; the sums run in entry
-        // order, one lane value at a time, identically on every lane
-        const float z = key_value(v >> 16) / temperature;
-        const float z0 = __shfl(z, 0);
-        const float e = lane < k ? expf(z - z0) : 0.f;
-        const int eb = __builtin_bit_cast(int, e);
-        float S = 0.f;
-#pragma unroll
-        for (int i = 0; i < 64; ++i)
-            if (i < k) S += __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, i));
-        const float target = um * S;
-        int pick = k - 1;
-        float c = 0.f;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            if (i < k) {
-                c += __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, i));
-                if (c > target && pick == k - 1 && i < k - 1) pick = i;
-            }
-        }
-        const int index = (int)(0xFFFFu - (v & 0xFFFFu));
-        if (lane == pick) token[m] = index;
-        if (lane < k) {
-            if (topk_index) topk_index[(size_t)m * k + lane] = index;
-            if (topk_prob) topk_prob[(size_t)m * k + lane] = e / S;
-        }
-    }
+    // 4-5. sort the k entries (bitonic network over the lanes) and draw, in wave 0
+    if (wave == 0)
+        draw_sorted(wave_sort64_desc(lane < k ? list[lane] : 0u, lane), k, temperature, um, lane, token + m,
+                      topk_index ? topk_index + (size_t)m * k : nullptr, topk_prob ? topk_prob + (size_t)m * k : nullptr);
 }
 
 }  // namespace

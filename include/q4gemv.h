@@ -352,6 +352,32 @@ int bf16_head_sample(const uint16_t* x, int M, int K, const uint16_t* w, int N, 
                      const float* u, int32_t* token, int32_t* topk_index, float* topk_prob, void* stream);
 
 /*
+ * The head GEMV and the sampling above in ONE launch (the pages replay the
+ * decode step, sampling included, as one graph; "Rumik TTS Fast Inference",
+ * "What Made It Faster").  Same arguments, rules, results and status codes
+ * as bf16_head_sample, plus a caller workspace of ws_bytes bytes, 4-byte
+ * aligned and zero-filled before its first use: it holds arrival counters
+ * (every call leaves them at zero) and, for heads over 3072 rows, the
+ * per-block top-k candidates (scratch).  It must not
+ * overlap any other argument (Q4_EALIAS, as are Q4_EALIGN and the sampling
+ * checks, returned before anything is enqueued).
+ * The streaming GEMV workgroups store their logits; the last to finish in
+ * each block of workgroups selects that block's top_k entries, and the last
+ * block selects among the candidates, sorts and draws -- no workgroup waits
+ * for another.  The logits and the selection are bitwise those of
+ * bf16_head_sample.  Applies when bf16_head_sample_workspace_bytes(M, N, K,
+ * top_k) is nonzero (M = 1 -- the single-stream decode of the pages; a
+ * batch is faster as two launches, one sampling workgroup per row -- K in
+ * {512, 1024, 2048, 4096, 8192}, top_k <= 64, heads up to 30720 rows) and
+ * ws_bytes is at least that; otherwise the call runs bf16_head_sample's two
+ * launches.  Calls that share a workspace must not overlap in time.
+ */
+size_t bf16_head_sample_workspace_bytes(int M, int N, int K, int top_k);
+int bf16_head_sample_ws(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* logits, float temperature, int top_k,
+                        const float* u, int32_t* token, int32_t* topk_index, float* topk_prob, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/*
  * Diagnostic dequantization of a whole matrix to fp32 w [N, K] (16-byte
  * aligned).  Bitwise equal to the format definitions above: int4 rounds
  * code*scale+min once; NVFP4 rounds e2m1*e4m3*G once (the first product is

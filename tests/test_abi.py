@@ -283,6 +283,23 @@ def test_sample_validation():
     assert h(ti=W + 128) == EALIAS
     assert h(lg=U - 64) == EALIAS             # logits written over the uniforms before they are read
 
+    # the one-launch form: workspace size rule, alignment and aliasing (checked before any launch)
+    wsb = lib.bf16_head_sample_workspace_bytes
+    wsb.restype = ctypes.c_size_t
+    assert wsb(1, 2049, 2048, 30) > 0                      # one block of workgroups: counters only
+    assert wsb(1, 16385, 2048, 30) > wsb(1, 2049, 2048, 30)   # blocks of workgroups: counters + candidates
+    assert wsb(2, 2049, 2048, 30) == 0 and wsb(1, 2049, 1000, 30) == 0 and wsb(1, 2049, 2048, 65) == 0
+    WS = A + (1 << 30) + (1 << 29)
+
+    def hw(ws=WS, nb=1 << 20, lg=LG, tok=T, N=16385):
+        return lib.bf16_head_sample_ws(X, 1, 2048, W, N, lg, f(0.8), 30, U, tok, None, None, ws, nb, None)
+
+    assert hw(ws=WS + 2) == EALIGN
+    assert hw(ws=LG + 4096) == EALIAS                       # over the logits
+    assert hw(ws=W + 4096) == EALIAS                        # over the weights
+    assert hw(ws=T - 128) == EALIAS                         # over the tokens
+    assert hw(lg=W + 64) == EALIAS                          # the head checks still apply
+
 
 def test_mixed_validation():
     """q4gemv_grouped_mixed / q4gemv_mixed_workspace_bytes reject bad arguments

@@ -100,3 +100,85 @@ def test_sample_signed_zero_ties(q4):
     lg[0, 1] = 0.0
     tok, ti, tp = q4.sample_topk(gpu(lg), gpu(torch.zeros(1)), top_k=2, return_topk=True)
     assert ti.cpu().tolist() == [[1, 3]] and int(tok[0]) == 1
+
+
+def _head_inputs(M, N, K, seed, ties=False):
+    """Random activations and a BF16 head; with ties, weights on a coarse grid
+    and one-hot activations, so that many logits are exactly equal."""
+    if ties:
+        w = torch.round(synth.bf16_matrix(N, K, ("head-ties", N, K, seed), std=1.0).float() * 2) / 2
+        w = w.to(torch.bfloat16)
+        ks = np.random.default_rng(seed).choice(K, size=M, replace=False)
+        x = torch.zeros(M, K, dtype=torch.bfloat16)
+        x[torch.arange(M), torch.from_numpy(ks)] = 1.0
+    else:
+        w = synth.bf16_matrix(N, K, ("head-fused", N, K, seed), std=0.05)
+        x = synth.x_bf16(M, K, ("head-fused-x", M, K, seed))
+    u = np.random.default_rng(seed + 17).uniform(0, 1, M).astype(np.float32)
+    u[0] = 0.0
+    return x, w, u
+
+
+FUSED = [(1, 2049, 2048, 30, False), (4, 2049, 2048, 30, False), (1, 16385, 2048, 30, False), (1, 16385, 2048, 64, False),
+         (1, 30720, 2048, 64, False), (1, 3000, 1024, 1, False), (1, 5000, 512, 17, False), (1, 64, 2048, 64, False),
+         (1, 4097, 4096, 30, False), (1, 2049, 8192, 30, False), (1, 2049, 2048, 30, True), (1, 16385, 2048, 64, True),
+         (2, 2049, 2048, 30, True)]
+
+
+@pytest.mark.parametrize("M,N,K,k,ties", FUSED)
+def test_head_sample_one_launch(q4, M, N, K, k, ties):
+    """The one-launch head sampling equals the two-launch path bitwise (logits,
+    token, top-k indices and probabilities) and the oracle's sampling of its
+    logits; repeated calls on the same workspace (never re-zeroed) give the
+    same results, and a head of at most 3072 rows, whose workspace is all
+    counters, leaves it zero."""
+    print(f"head sample one launch: M={M} N={N} K={K} k={k} ties={ties}", flush=True)
+    x, w, u = _head_inputs(M, N, K, M * 131 + N + K, ties)
+    need = q4.bf16_head_sample_workspace_bytes(M, N, K, k)
+    assert (need > 0) == (M == 1)              # batches fall back to the two launches
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    xg, wg, ug = gpu(x), gpu(w), gpu(torch.from_numpy(u))
+    ref = q4.bf16_head_sample(xg, wg, ug, top_k=k, return_topk=True)
+    for rep in range(3):
+        got = q4.bf16_head_sample(xg, wg, ug, top_k=k, return_topk=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got[3].view(torch.int16), ref[3].view(torch.int16)), "logits differ from the two-launch path"
+        for a, b, name in zip(got[:3], ref[:3], ("token", "topk_index", "topk_prob")):
+            assert torch.equal(a, b), f"{name} differs from the two-launch path (call {rep})"
+        if N <= 3072 or M > 1:
+            assert int(ws.count_nonzero()) == 0, "arrival counters not left at zero"
+    check_sample(got[0], got[1], got[2], bits(got[3]), 0.8, k, u.astype(np.float64))
+    if ties:
+        # one-hot rows: the logits are weight columns, exactly, full of ties
+        # (a -0 weight gives a +0 logit: compare with -0 read as +0)
+        cols = [int(np.flatnonzero(x.float().numpy()[m])[0]) for m in range(M)]
+        have, want = bits(got[3]).copy(), bits(w)[:, cols].T.copy()
+        have[have == 0x8000] = 0
+        want[want == 0x8000] = 0
+        assert np.array_equal(have, want)
+
+
+def test_head_sample_one_launch_graph_replay(q4):
+    """The one-launch head sampling captured in a graph and replayed three
+    times, outputs poisoned before each replay, equals the eager call."""
+    M, N, K, k = 1, 16385, 2048, 30
+    x, w, u = _head_inputs(M, N, K, 5)
+    ws = torch.zeros(q4.bf16_head_sample_workspace_bytes(M, N, K, k), dtype=torch.uint8, device="cuda")
+    xg, wg, ug = gpu(x), gpu(w), gpu(torch.from_numpy(u))
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    lg = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    eager = q4.bf16_head_sample(xg, wg, ug, top_k=k, return_topk=True, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = q4.bf16_head_sample(xg, wg, ug, top_k=k, return_topk=True, workspace=ws, logits=lg)
+    for r in range(3):
+        for t in out[:3]:
+            t.fill_(-1)
+        lg.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(out, eager):
+            assert a.dtype == b.dtype and torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {r}"
+    del g
