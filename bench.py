@@ -416,18 +416,29 @@ def projection_calls(torch, q4, wl):
     return rec
 
 
-def read_ceiling(torch, q4, wl, steps, warmup):
+def read_ceiling(torch, q4, wl, steps, warmup, head=True):
     """Plain-read reference for the M=1 grouped step: the same 73 launches,
     each replaced by the library's diagnostic stream_read over exactly the
     weight buffers (codes, scales, mins; the head's BF16 rows) that GEMV launch
-    streams, captured and replayed like the step.  Returns ms per step."""
+    streams, captured and replayed like the step (head=False: the 72 layer
+    launches only).  Returns (ms per step, weight bytes read)."""
     groups = []
     for lay in wl.layers:
         for stage in (("q", "k", "v", "gate", "up"), ("o", "down")):
             groups.append([t for p in stage for t in lay[p]])
-    groups.append([wl.head])
+    if head:
+        groups.append([wl.head])
     sinks = [torch.empty(q4.stream_read_sink_words(g), dtype=torch.int32, device="cuda") for g in groups]
-    return graph_ms(torch, lambda: [q4.stream_read(g, k) for g, k in zip(groups, sinks)], steps, warmup)
+    nbytes = sum(t.numel() * t.element_size() for g in groups for t in g)
+    return graph_ms(torch, lambda: [q4.stream_read(g, k) for g, k in zip(groups, sinks)], steps, warmup), nbytes
+
+
+def launch_floor(torch, q4, steps, n=72):
+    """The cost of a launch that moves almost nothing: n diagnostic reads of
+    4 KB each (distinct buffers) back to back in one graph; ms per launch."""
+    bufs = [torch.ones(4096, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    sinks = [torch.empty(q4.stream_read_sink_words([b]), dtype=torch.int32, device="cuda") for b in bufs]
+    return graph_ms(torch, lambda: [q4.stream_read([b], k) for b, k in zip(bufs, sinks)], steps, 3) / n
 
 
 def single_launch_read(torch, q4, steps, nbytes=1 << 30):
@@ -912,11 +923,32 @@ def main():
                                                       f"weights {v['bf16_library_on_dequantized_us']} us)" for k, v in pf.items()))
     head = res[(1, "grouped")]
     wbytes = weight_bytes(wl)
-    ceil_ms = read_ceiling(torch, q4, wl, args.steps, args.warmup)
+    ceil_ms, _ = read_ceiling(torch, q4, wl, args.steps, args.warmup)
     ceil_gbs = wbytes / (ceil_ms * 1e-3) / 1e9
     one_ms, one_gbs = single_launch_read(torch, q4, 20)
     log(f"bench: plain read of the step's weight buffers in the same 73 launches: {ceil_ms * 1e3:.1f} us, {ceil_gbs:.0f} GB/s; "
         f"one launch over 1 GiB: {one_ms * 1e3:.1f} us, {one_gbs:.0f} GB/s")
+    # where the time of one M=1 layer launch goes
+    layers_ms, layer_read_bytes = read_ceiling(torch, q4, wl, args.steps, args.warmup, head=False)
+    floor_us = launch_floor(torch, q4, args.steps) * 1e3
+    read_us = layers_ms * 1e3 / (2 * N_LAYERS)
+    read_b = layer_read_bytes / (2 * N_LAYERS)
+    g_us, g_b = roof[1]["avg_launch_us"], roof[1]["alg_bytes_per_launch"]
+    breakdown = {
+        "what": "one grouped M=1 layer launch, in-graph periods: an almost empty launch; the plain read of the same "
+                "buffers in the step's 72 layer launches (its bytes at the 1 GiB single-launch rate, the rest its ramp "
+                "and drain); what the GEMV adds over that read",
+        "gemv_launch_us": g_us, "gemv_bytes": g_b,
+        "plain_read_launch_us": round(read_us, 3), "plain_read_bytes": round(read_b),
+        "empty_launch_us": round(floor_us, 3),
+        "parts_us": {"empty_launch": round(floor_us, 3),
+                     "read_bytes_at_single_launch_rate": round(read_b / one_gbs / 1e3, 3),
+                     "read_ramp_and_drain": round(read_us - floor_us - read_b / one_gbs / 1e3, 3),
+                     "gemv_over_plain_read": round(g_us - read_us, 3)},
+    }
+    log(f"bench: M=1 layer launch {g_us:.2f} us = empty launch {floor_us:.2f} + read at the 1 GiB rate "
+        f"{read_b / one_gbs / 1e3:.2f} + read ramp/drain {read_us - floor_us - read_b / one_gbs / 1e3:.2f} + GEMV over plain read "
+        f"{g_us - read_us:.2f}")
 
     out = {
         "metric": METRIC,
@@ -946,7 +978,8 @@ def main():
                              "single_launch": {"what": "one diagnostic plain-read launch over one contiguous 1 GiB buffer, hipGraph",
                                                "us": round(one_ms * 1e3, 1), "GB_s": round(one_gbs, 1),
                                                "pct_of_8TBps": round(100 * one_gbs / PEAK_GBS, 2)},
-                             "value_pct_of_single_launch": round(100 * head["gbs"] / one_gbs, 1)},
+                             "value_pct_of_single_launch": round(100 * head["gbs"] / one_gbs, 1),
+                             "launch_breakdown_M1": breakdown},
             "modes": {mode_key(k): mode_record(k, r, wbytes, ceil_ms) for k, r in res.items()},
         },
         "roofline": roof[1],

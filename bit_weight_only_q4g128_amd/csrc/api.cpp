@@ -543,6 +543,18 @@ int nvfp4g16_dequant_f32(const uint8_t* qweight, const uint8_t* scale_e4m3, floa
 // one h buffer per gated task.
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // h starts after the split-K part, and in any case past the arrival counters
+// The fused tiled-path plan: split-K workspace of the tiled kernel and, where
+// every task qualifies for the skinny kernel at this M (a workspace given),
+// of the skinny kernel; true if the skinny kernel may run.
+bool fused_skinny_ok(const GemvArgs* a, int count, int M, bool split, size_t* need_mm, size_t* need_sk) {
+    *need_mm = q4::mm_workspace_bytes(q4::kFmtQ4, a, count);
+    *need_sk = 0;
+    bool ok = split && M >= 5 && M <= q4::kSkinnyMaxM;
+    for (int i = 0; i < count && ok; ++i) ok = q4::skinny_supported(M, a[i].K, true);
+    if (ok) *need_sk = q4::skinny_workspace_bytes(a, count);
+    return ok;
+}
+
 size_t fused_h_offset(size_t need) { return align256(need > q4::kWsCounterBytes ? need : q4::kWsCounterBytes); }
 size_t fused_h_bytes(const GemvArgs* a, int count) {
     size_t n = 0;
@@ -640,12 +652,18 @@ int q4g128_gemv_fused(const q4g128_fused_task* tasks, int count, int M, void* wo
     }
     // Everything is planned and checked before the first enqueue.  The h
     // buffers start past the split-K part and never below the counter region,
-    // which other calls on the same workspace rely on staying zero.
-    const size_t need = q4::mm_workspace_bytes(q4::kFmtQ4, a, count);
+    // which other calls on the same workspace rely on staying zero.  With a
+    // workspace, 5 <= M <= 48 runs on the skinny kernel (residual epilogue;
+    // gated tasks read the h formed in the pass); otherwise the tiled kernel,
+    // which can also form h in its loader.
+    size_t need_mm = 0, need_sk = 0;
+    const bool sk_ok = fused_skinny_ok(a, count, M, split, &need_mm, &need_sk);
+    const size_t need = need_mm > need_sk ? need_mm : need_sk;
     const size_t h_off = fused_h_offset(need), h_bytes = fused_h_bytes(a, count);
     const bool form_h = split && h_bytes > 0 && workspace_bytes >= h_off + h_bytes;
     const size_t mm_bytes = form_h ? h_off : workspace_bytes;
-    if (split && (need == 0 || mm_bytes < need)) {
+    const bool use_sk = sk_ok && (h_bytes == 0 || form_h) && (need_sk == 0 || mm_bytes >= need_sk);
+    if (!use_sk && split && (need_mm == 0 || mm_bytes < need_mm)) {
         for (int i = 0; i < count; ++i)
             if (!q4::mm_supported(q4::kFmtQ4, M, a[i].K, false)) return Q4_EVARIANT;
     }
@@ -668,7 +686,7 @@ int q4g128_gemv_fused(const q4g128_fused_task* tasks, int count, int M, void* wo
         }
         if (q4::launch_silu_mul(g, u, h, n, ng, s) != hipSuccess) return Q4_ELAUNCH;
     }
-    e = q4::launch_mm_fused(a, count, workspace, mm_bytes, s);
+    e = use_sk ? q4::launch_skinny(a, count, workspace, mm_bytes, s) : q4::launch_mm_fused(a, count, workspace, mm_bytes, s);
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 
@@ -682,7 +700,9 @@ int q4g128_fused_workspace_bytes(const q4g128_fused_task* tasks, int count, int 
         *bytes = 0;
         return Q4_OK;
     }
-    const size_t need = q4::mm_workspace_bytes(q4::kFmtQ4, a, count);
+    size_t need_mm = 0, need_sk = 0;
+    fused_skinny_ok(a, count, M, true, &need_mm, &need_sk);
+    const size_t need = need_mm > need_sk ? need_mm : need_sk;
     const size_t h_bytes = fused_h_bytes(a, count);
     *bytes = h_bytes ? fused_h_offset(need) + h_bytes : need;
     return Q4_OK;

@@ -270,16 +270,18 @@ int q4gemv_mixed_workspace_bytes(const q4gemv_mixed_task* tasks, int count, int 
  * ulps), so h can differ from the exactly rounded value by one BF16 step when
  * the exact product lies within that error of a rounding boundary.  Kernels:
  * the streaming kernel when every task allows it (M <= 4, K = 2048, 4096 or
- * 8192), else the tiled kernel (K % 128 == 0); other shapes return
- * Q4_EVARIANT.  Tasks obey the q4g128_gemv rules; up is bf16 [M, K], 16-byte
+ * 8192), else the skinny or the tiled kernel (K % 128 == 0; see below);
+ * shapes the tiled kernel cannot run return Q4_EVARIANT.  Tasks obey the q4g128_gemv rules; up is bf16 [M, K], 16-byte
  * aligned; residual is bf16 [M, N], 2-byte aligned; no y may overlap any
  * input of any task or another y, except that a task's y may be exactly its
  * own residual.  workspace / workspace_bytes as for q4g128_gemv_grouped_ws
- * (q4g128_fused_workspace_bytes sizes it; NULL runs unsplit).  On the tiled
- * kernel a workspace of that size also holds h: it is then formed once by a
- * separate pass (one extra launch) instead of by the kernel's loader waves
- * for every 64-row block -- same arithmetic, same result bit for bit, and at
- * M = 48 about half the time (the loaders pace the tiled kernel's main loop).
+ * (q4g128_fused_workspace_bytes sizes it; NULL runs unsplit).  Beyond the
+ * streaming kernel, a workspace of that size also holds h: it is then formed
+ * once by a separate pass (one extra launch), and for 5 <= M <= 48 the
+ * skinny kernel (Q4_VARIANT_SKINNY) runs the GEMV with the residual in its
+ * epilogue; without a workspace, or for M > 48, the tiled kernel runs, its
+ * loader waves forming h for every 64-row block when no pass did (same h bit
+ * for bit).
  */
 typedef struct q4g128_fused_task {
     const uint16_t* x;         /* bf16 [M, K] (the gate activations when up is set) */
