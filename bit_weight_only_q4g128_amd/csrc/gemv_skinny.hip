@@ -19,7 +19,9 @@
 // instruction, and for the weights eight rows x the wave's two adjacent
 // groups (128 bytes), the lanes then exchanging chunks with DPP row shifts to
 // reach the matrix-core operand layout.  The second round's activations
-// follow once the first round's are read out.  Every buffer offset is scalar
+// follow once the first round has computed (the region it read out at its
+// start is then free, and the loads ahead of them have drained).  Every
+// buffer offset is scalar
 // plus one per-lane base, so the address arithmetic costs no vector
 // instructions.
 //
@@ -261,10 +263,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
         uint32_t sc16[R];   // this lane's row: the scale of this round's group (fp16 in the low half)
 #pragma unroll
         for (int t = 0; t < R; ++t) sc16[t] = par[wave * L::kParArr + 2 * (16 * t + (lane & 15)) + r];
-        if (r == 0 && nr > 1 && nv > 1) {
-            __builtin_amdgcn_s_waitcnt(kLgkm0);   // the region is read out before it is refilled
-            issue_x(1);
-        }
         // pairing; SX (all-ones B operand: every column of the result is SX)
         u32x4 B[MT][4];
         f32x4 sx[MT];
@@ -312,6 +310,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[t][mt][v] = fmaf(sc, D[mt][v], acc[t][mt][v]);
+        }
+        // the second round's activations, into the region this round read
+        // out at its start: issued only now, since an issue waits for room in
+        // the workgroup's queue of loads, which the weights still fill while
+        // the first round computes
+        if (r == 0 && nr > 1 && nv > 1) {
+            __builtin_amdgcn_s_waitcnt(kLgkm0);   // (the fragment reads of the region are long complete)
+            issue_x(1);
         }
     }
 
