@@ -119,12 +119,21 @@ def test_bf16_onehot_bitwise(q4, variant, M):
     assert np.array_equal(y.cpu().float().numpy(), w[:, ks].T.float().numpy()), (VNAME[variant], M)
 
 
-# the streaming kernel takes rows of 1, 2 or 4 KB only
-@pytest.mark.parametrize("K", [2048, 4096, 8192])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def _runs_on(fmt, variant, name, cases):
+    """The (K, M) cases a forced variant accepts (the host-side choice, no GPU
+    needed); the others are shapes that variant does not take -- the automatic
+    choice runs them on another kernel, tested elsewhere (e.g. M = 4, K = 8192
+    in test_q4_down_shape_M4_auto)."""
+    try:
+        import bit_weight_only_q4g128_amd as m
+    except ImportError:
+        return cases
+    return [(K, M) for K, M in cases if m.variant_name(fmt, variant, M, 1, K) == name]
+
+
+# the streaming kernel takes rows of 1, 2 or 4 KB only, and activations within its LDS budget
+@pytest.mark.parametrize("K,M", _runs_on(0, 3, "stream", [(K, M) for K in (2048, 4096, 8192) for M in (1, 2, 3, 4)]))
 def test_q4_onehot_bitwise_stream(q4, K, M):
-    if q4.variant_name(0, 3, M, 1, K) != "stream":
-        pytest.skip("activations of this (M, K) exceed the streaming kernel's LDS budget")
     N = 37   # rows past N in the last workgroup
     qw, sc, mn = synth.q4_matrix(N, K, ("onehot-st", K, M))
     w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
@@ -135,11 +144,8 @@ def test_q4_onehot_bitwise_stream(q4, K, M):
     assert np.array_equal(got, exp), (K, M, np.argwhere(got != exp)[:4])
 
 
-@pytest.mark.parametrize("K", [2048, 8192])
-@pytest.mark.parametrize("M", [1, 3, 4])
+@pytest.mark.parametrize("K,M", _runs_on(1, 3, "stream", [(K, M) for K in (2048, 8192) for M in (1, 3, 4)]))
 def test_nvfp4_onehot_bitwise_stream(q4, K, M):
-    if q4.variant_name(1, 3, M, 1, K) != "stream":
-        pytest.skip("activations of this (M, K) exceed the streaming kernel's LDS budget")
     N = 21
     qw, s8, G = synth.nvfp4_matrix(N, K, ("onehot-nv-st", K, M))
     w32 = oracle.nvfp4g16_dequant_f32(qw.numpy(), s8.numpy(), G)
@@ -162,11 +168,8 @@ def test_bf16_onehot_bitwise_stream(q4, K, M):
 
 # the tiled matrix-core kernel (int4): ragged row blocks, groups past a round
 # of eight, every batch-tile count
-@pytest.mark.parametrize("K", [128, 1152, 2048, 8192])
-@pytest.mark.parametrize("M", [5, 16, 17, 33, 48, 64])
+@pytest.mark.parametrize("K,M", _runs_on(0, 4, "tiled", [(K, M) for K in (128, 1152, 2048, 8192) for M in (5, 16, 17, 33, 48, 64)]))
 def test_q4_onehot_bitwise_tiled(q4, K, M):
-    if q4.variant_name(0, 4, M, 1, K) != "tiled":
-        pytest.skip("group parameters of this K exceed the tiled kernel's LDS budget at this M")
     N = 70
     qw, sc, mn = synth.q4_matrix(N, K, ("onehot-tl", K, M))
     w32 = oracle.q4g128_dequant_f32(qw.numpy(), synth.bits16(sc), synth.bits16(mn))
