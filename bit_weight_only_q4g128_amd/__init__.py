@@ -484,17 +484,19 @@ def sample_topk(logits, u, temperature: float = 0.8, top_k: int = 30, return_top
 
 
 def bf16_head_sample_workspace_bytes(M: int, N: int, K: int, top_k: int = 30) -> int:
-    """Bytes of zero-filled workspace for the one-launch head sampling (0 if
-    it does not apply to this shape)."""
+    """Bytes of zero-filled workspace for the workspace head sampling (one
+    launch at M = 1, the split sampler for a batch; 0 if it does not apply to
+    this shape)."""
     return int(lib.bf16_head_sample_workspace_bytes(M, N, K, top_k))
 
 
 def bf16_head_sample(x, w, u, temperature: float = 0.8, top_k: int = 30, logits=None, return_topk: bool = False,
                      workspace=None):
     """The BF16 head GEMV logits = x W^T followed by top-k sampling: two
-    launches, or one (bf16_head_sample_ws in the C header) when a zero-filled
-    uint8 workspace of at least bf16_head_sample_workspace_bytes() is given
-    and that size is nonzero.  Returns (token, logits) or (token, topk_index,
+    launches; with a zero-filled uint8 workspace of at least
+    bf16_head_sample_workspace_bytes() (when that is nonzero),
+    bf16_head_sample_ws in the C header -- one launch for one row, the split
+    sampler for a batch.  Returns (token, logits) or (token, topk_index,
     topk_prob, logits) with return_topk."""
     _check(x, "x", _U16, 2); _check(w, "w", _U16, 2); _check(u, "u", (torch.float32,), 1)
     M, K = x.shape

@@ -773,8 +773,11 @@ int bf16_head_sample(const uint16_t* x, int M, int K, const uint16_t* w, int N, 
 }
 
 size_t bf16_head_sample_workspace_bytes(int M, int N, int K, int top_k) {
-    if (M < 1 || N < 1 || K < 1 || top_k < 1 || top_k > N) return 0;
-    return q4::head_sample_workspace_bytes(M, N, K, top_k);
+    if (M < 1 || M > kMaxM || N < 1 || K < 1 || top_k < 1 || top_k > N || top_k > q4::kMaxTopK || N > q4::kMaxVocab) return 0;
+    // one row: GEMV and sampling in one launch; a batch: the GEMV, then the
+    // sampler split over blocks of each row (a row of one block gains nothing)
+    if (M == 1) return q4::head_sample_workspace_bytes(M, N, K, top_k);
+    return N > q4::kSplitBlock ? q4::topk_sample_split_ws_bytes(M, N, top_k) : 0;
 }
 
 int bf16_head_sample_ws(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* logits, float temperature, int top_k,
@@ -799,8 +802,17 @@ int bf16_head_sample_ws(const uint16_t* x, int M, int K, const uint16_t* w, int 
                              topk_prob ? range_of(topk_prob, (size_t)M * top_k * 4) : Range{0, 0}};
     for (const Range& r : others)
         if (overlaps(wr, r)) return Q4_EALIAS;
-    hipError_t e = q4::launch_head_sample(a, temperature, top_k, u, token, topk_index, topk_prob, workspace,
-                                          reinterpret_cast<hipStream_t>(stream));
+    if (M == 1) {
+        hipError_t e = q4::launch_head_sample(a, temperature, top_k, u, token, topk_index, topk_prob, workspace,
+                                              reinterpret_cast<hipStream_t>(stream));
+        return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+    }
+    const int chosen = pick(q4::kFmtBf16, Q4_VARIANT_AUTO, M, N, K);
+    if (chosen < 0) return Q4_EVARIANT;
+    rc = run(q4::kFmtBf16, chosen, a, stream);
+    if (rc) return rc;
+    hipError_t e = q4::launch_topk_sample_split(logits, M, N, temperature, top_k, u, token, topk_index, topk_prob, workspace,
+                                                reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 

@@ -493,20 +493,6 @@ struct HsArgs {
     uint32_t* cand;      // [M][nsb][k] candidate entries (nsb > 1)
 };
 
-// This workgroup's device-coherent stores are acknowledged, then it arrives
-// at counter c; true in the last of `n` arrivals, which also resets c.
-__device__ __forceinline__ bool hs_arrive(unsigned* c, int n, int tid, unsigned* s_prev) {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) *s_prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const bool last = *s_prev == (unsigned)(n - 1);
-    if (last && tid == 0) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("" ::: "memory");
-    return last;
-}
-
 template <int MT>
 __global__ __launch_bounds__(256) void head_sample_kernel(HsArgs h) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -522,10 +508,10 @@ __global__ __launch_bounds__(256) void head_sample_kernel(HsArgs h) {
     // (its first-level groups of 16, then the super-block's count of groups)
     const int g1 = blk / kHsFan;
     const int g1_wgs = (h.nwg - g1 * kHsFan < kHsFan) ? h.nwg - g1 * kHsFan : kHsFan;
-    if (!hs_arrive(h.cnt + (size_t)(h.nsb + 1 + g1) * kHsCtrWords, g1_wgs, tid, &s_prev)) return;
+    if (!arrive_last(h.cnt + (size_t)(h.nsb + 1 + g1) * kHsCtrWords, g1_wgs, tid, &s_prev)) return;
     const int sb = blk / h.sbw;
     const int sb_wgs = (h.nwg - sb * h.sbw < h.sbw) ? h.nwg - sb * h.sbw : h.sbw;
-    if (!hs_arrive(h.cnt + (size_t)sb * kHsCtrWords, (sb_wgs + kHsFan - 1) / kHsFan, tid, &s_prev)) return;
+    if (!arrive_last(h.cnt + (size_t)sb * kHsCtrWords, (sb_wgs + kHsFan - 1) / kHsFan, tid, &s_prev)) return;
     const int N = h.a.N, k = h.k;
     const int rw = rows_per_wg(h.cl);
     const int r0 = sb * h.sbw * rw;
@@ -561,7 +547,7 @@ __global__ __launch_bounds__(256) void head_sample_kernel(HsArgs h) {
     if (h.nsb == 1) return;
 
     // stage 2: all super-blocks' candidates
-    if (!hs_arrive(h.cnt + (size_t)h.nsb * kHsCtrWords, h.nsb, tid, &s_prev)) return;
+    if (!arrive_last(h.cnt + (size_t)h.nsb * kHsCtrWords, h.nsb, tid, &s_prev)) return;
     const int nc = h.nsb * k;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(h.cand, (uint32_t)(MT * nc * 4));
 #pragma unroll 1

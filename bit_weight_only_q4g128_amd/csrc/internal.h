@@ -123,6 +123,13 @@ hipError_t launch_topk_sample(const uint16_t* logits, int M, int V, float temper
 // streaming row sizes, top_k <= 64): workspace bytes it needs (zero-filled,
 // left zero), or 0 if the fused launch does not apply.
 size_t head_sample_workspace_bytes(int M, int N, int K, int top_k);
+// Top-k sampling split over workgroups of 1024 logits per row, the last
+// block of each row merging (a workspace: counters a cache line apart per
+// row, then candidates); its workspace bytes (0: not applicable).
+constexpr int kSplitBlock = 1024;  // logits per workgroup of the split sampler
+size_t topk_sample_split_ws_bytes(int M, int V, int top_k);
+hipError_t launch_topk_sample_split(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u,
+                                    int32_t* token, int32_t* topk_index, float* topk_prob, void* ws, hipStream_t s);
 hipError_t launch_head_sample(const GemvArgs& a, float temperature, int top_k, const float* u, int32_t* token, int32_t* topk_index,
                               float* topk_prob, void* ws, hipStream_t s);
 

@@ -141,7 +141,73 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(const uint16_t* _
                       topk_index ? topk_index + (size_t)m * k : nullptr, topk_prob ? topk_prob + (size_t)m * k : nullptr);
 }
 
+// The split form for batches (a caller workspace): each batch row's logits
+// are dealt to workgroups of 1024; each takes the top k of its block
+// (topk.h) and publishes them, device-coherently, as candidates; the last
+// block of the row to arrive at the row's counter takes the top k of all of
+// them, sorts and draws.  The rows' counters sit a cache line apart.
+constexpr int kSplitE2 = 8;         // candidate entries per thread in the merge (2048)
+
+__global__ __launch_bounds__(kThreads) void topk_sample_split_kernel(const uint16_t* __restrict__ logits, int V, float temperature,
+                                                                     int k, int nb, const float* __restrict__ u,
+                                                                     int32_t* __restrict__ token, int32_t* __restrict__ topk_index,
+                                                                     float* __restrict__ topk_prob, unsigned* cnt, uint32_t* cand,
+                                                                     int M) {
+    __shared__ uint32_t lists[4 * 64];
+    __shared__ uint32_t scratch[4 * 64 * kSplitE2];
+    __shared__ unsigned s_prev;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m = blockIdx.x / nb, j = blockIdx.x - m * nb;
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits + (size_t)m * V, (uint32_t)V * 2u);
+    uint32_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int col = j * kSplitBlock + tid + 256 * i;
+        v[i] = __builtin_amdgcn_raw_buffer_load_b16(rl, (int)(col < V ? col * 2 : 0x7FFFFFF0), 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int col = j * kSplitBlock + tid + 256 * i;
+        v[i] = topk_entry(v[i], col) & (col < V ? 0xFFFFFFFFu : 0u);
+    }
+    uint32_t top = wg_topk<4>(v, k, lists, scratch, wave, lane);
+    const int nc = nb * k;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(cand, (uint32_t)(M * nc * 4));
+    if (nb > 1) {
+        if (wave == 0 && lane < k)
+            __builtin_amdgcn_raw_buffer_store_b32(top, rc, (m * nc + j * k + lane) * 4, 0, 16);
+        if (!arrive_last(cnt + (size_t)m * kCtrWords, nb, tid, &s_prev)) return;
+        uint32_t w[kSplitE2];
+#pragma unroll
+        for (int i = 0; i < kSplitE2; ++i) {
+            const int c = tid + 256 * i;
+            w[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(c < nc ? (m * nc + c) * 4 : 0x7FFFFFF0), 0, 16);
+        }
+        top = wg_topk<kSplitE2>(w, k, lists, scratch, wave, lane);
+    }
+    if (wave == 0)
+        draw_sorted(top, k, temperature, u[m], lane, token + m, topk_index ? topk_index + (size_t)m * k : nullptr,
+                    topk_prob ? topk_prob + (size_t)m * k : nullptr);
+}
+
 }  // namespace
+
+size_t topk_sample_split_ws_bytes(int M, int V, int top_k) {
+    const int nb = (V + kSplitBlock - 1) / kSplitBlock;
+    if (nb * top_k > 256 * kSplitE2) return 0;
+    const size_t counters = (size_t)M * kCtrStride;
+    return counters + (nb > 1 ? (size_t)M * nb * top_k * 4 : 0);
+}
+
+hipError_t launch_topk_sample_split(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u,
+                                    int32_t* token, int32_t* topk_index, float* topk_prob, void* ws, hipStream_t s) {
+    const int nb = (V + kSplitBlock - 1) / kSplitBlock;
+    unsigned* cnt = static_cast<unsigned*>(ws);
+    uint32_t* cand = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + (size_t)M * kCtrStride);
+    return launch_kernel(topk_sample_split_kernel, dim3(M * nb), dim3(kThreads), 0, s, logits, V, temperature, top_k, nb, u, token,
+                         topk_index, topk_prob, cnt, cand, M);
+}
 
 hipError_t launch_topk_sample(const uint16_t* logits, int M, int V, float temperature, int top_k, const float* u, int32_t* token,
                               int32_t* topk_index, float* topk_prob, hipStream_t s) {

@@ -152,6 +152,25 @@ __device__ uint32_t wg_topk(const uint32_t (&v)[E], int k, uint32_t* lists, uint
     return top;
 }
 
+// Hand-over between the workgroups of one launch: this workgroup's
+// device-coherent (sc1) stores are acknowledged (vmcnt(0): the coherence
+// point has accepted them), the workgroup's threads meet, and one relaxed
+// agent-scope atomic arrives at counter c; true in the last of n arrivals,
+// which also resets c.  The last arriver then reads the others' data with sc1
+// loads, issued after its atomic returned.  Counters of different hand-overs
+// sit on different cache lines (atomics on one line serialize).
+__device__ __forceinline__ bool arrive_last(unsigned* c, int n, int tid, unsigned* s_prev) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) *s_prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const bool last = *s_prev == (unsigned)(n - 1);
+    if (last && tid == 0) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");
+    return last;
+}
+
 // Inclusive prefix sum over the 64 lanes (DPP: shifts within rows of 16,
 // then the row totals broadcast forward).
 __device__ __forceinline__ float wave_incl_scan(float x) {

@@ -354,25 +354,29 @@ int bf16_head_sample(const uint16_t* x, int M, int K, const uint16_t* w, int N, 
                      const float* u, int32_t* token, int32_t* topk_index, float* topk_prob, void* stream);
 
 /*
- * The head GEMV and the sampling above in ONE launch (the pages replay the
- * decode step, sampling included, as one graph; "Rumik TTS Fast Inference",
- * "What Made It Faster").  Same arguments, rules, results and status codes
- * as bf16_head_sample, plus a caller workspace of ws_bytes bytes, 4-byte
- * aligned and zero-filled before its first use: it holds arrival counters
- * (every call leaves them at zero) and, for heads over 3072 rows, the
- * per-block top-k candidates (scratch).  It must not
+ * bf16_head_sample with a caller workspace.  Same arguments, rules, results
+ * and status codes, plus a workspace of ws_bytes bytes, 4-byte aligned and
+ * zero-filled before its first use: it holds arrival counters (every call
+ * leaves them at zero) and per-block top-k candidates (scratch).  It must not
  * overlap any other argument (Q4_EALIAS, as are Q4_EALIGN and the sampling
- * checks, returned before anything is enqueued).
- * The streaming GEMV workgroups store their logits; the last to finish in
- * each block of workgroups selects that block's top_k entries, and the last
- * block selects among the candidates, sorts and draws -- no workgroup waits
- * for another.  The logits and the selection are bitwise those of
- * bf16_head_sample.  Applies when bf16_head_sample_workspace_bytes(M, N, K,
- * top_k) is nonzero (M = 1 -- the single-stream decode of the pages; a
- * batch is faster as two launches, one sampling workgroup per row -- K in
- * {512, 1024, 2048, 4096, 8192}, top_k <= 64, heads up to 30720 rows) and
- * ws_bytes is at least that; otherwise the call runs bf16_head_sample's two
- * launches.  Calls that share a workspace must not overlap in time.
+ * checks, returned before anything is enqueued).  The logits and the
+ * selection are bitwise those of bf16_head_sample.
+ *
+ * M = 1 (the single-stream decode of the pages, which replay the step,
+ * sampling included, as one graph; "Rumik TTS Fast Inference", "What Made It
+ * Faster"): the GEMV and the sampling run as ONE launch.  The streaming GEMV
+ * workgroups store their logits; the last to finish in each block of
+ * workgroups selects that block's top_k entries, and the last block selects
+ * among the candidates, sorts and draws -- no workgroup waits for another.
+ * Needs K in {512, 1024, 2048, 4096, 8192}.
+ * 2 <= M <= 64 and N > 1024: the GEMV, then the sampler split over blocks of
+ * 1024 logits per row (one workgroup each; the last of a row to finish
+ * selects among the blocks' candidates and draws) -- two launches, the second
+ * with M * ceil(N / 1024) workgroups instead of M.
+ * Applies when bf16_head_sample_workspace_bytes(M, N, K, top_k) is nonzero
+ * (top_k <= 64, heads up to 30720 rows, and the cases above) and ws_bytes is
+ * at least that; otherwise the call runs bf16_head_sample.  Calls that share
+ * a workspace must not overlap in time.
  */
 size_t bf16_head_sample_workspace_bytes(int M, int N, int K, int top_k);
 int bf16_head_sample_ws(const uint16_t* x, int M, int K, const uint16_t* w, int N, uint16_t* logits, float temperature, int top_k,

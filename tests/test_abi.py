@@ -288,7 +288,12 @@ def test_sample_validation():
     wsb.restype = ctypes.c_size_t
     assert wsb(1, 2049, 2048, 30) > 0                      # one block of workgroups: counters only
     assert wsb(1, 16385, 2048, 30) > wsb(1, 2049, 2048, 30)   # blocks of workgroups: counters + candidates
-    assert wsb(2, 2049, 2048, 30) == 0 and wsb(1, 2049, 1000, 30) == 0 and wsb(1, 2049, 2048, 65) == 0
+    assert wsb(1, 2049, 1000, 30) == 0 and wsb(1, 2049, 2048, 65) == 0
+    # a batch: the split sampler (counters a cache line apart per row, then
+    # ceil(N / 1024) x top_k candidates per row), any K; nothing for one block
+    assert wsb(2, 2049, 1000, 30) == 2 * 128 + 2 * 3 * 30 * 4
+    assert wsb(48, 16385, 2048, 64) == 48 * 128 + 48 * 17 * 64 * 4
+    assert wsb(2, 1024, 2048, 30) == 0 and wsb(65, 2049, 2048, 30) == 0 and wsb(2, 30721, 2048, 30) == 0
     WS = A + (1 << 30) + (1 << 29)
 
     def hw(ws=WS, nb=1 << 20, lg=LG, tok=T, N=16385):

@@ -122,7 +122,8 @@ def _head_inputs(M, N, K, seed, ties=False):
 FUSED = [(1, 2049, 2048, 30, False), (4, 2049, 2048, 30, False), (1, 16385, 2048, 30, False), (1, 16385, 2048, 64, False),
          (1, 30720, 2048, 64, False), (1, 3000, 1024, 1, False), (1, 5000, 512, 17, False), (1, 64, 2048, 64, False),
          (1, 4097, 4096, 30, False), (1, 2049, 8192, 30, False), (1, 2049, 2048, 30, True), (1, 16385, 2048, 64, True),
-         (2, 2049, 2048, 30, True)]
+         (2, 2049, 2048, 30, True), (48, 16385, 2048, 30, False), (48, 2049, 2048, 30, False), (3, 30720, 2048, 64, False),
+         (5, 1025, 2048, 30, False), (2, 1024, 2048, 30, False), (64, 16385, 2048, 64, True), (7, 4097, 4096, 1, True)]
 
 
 @pytest.mark.parametrize("M,N,K,k,ties", FUSED)
@@ -130,12 +131,13 @@ def test_head_sample_one_launch(q4, M, N, K, k, ties):
     """The one-launch head sampling equals the two-launch path bitwise (logits,
     token, top-k indices and probabilities) and the oracle's sampling of its
     logits; repeated calls on the same workspace (never re-zeroed) give the
-    same results, and a head of at most 3072 rows, whose workspace is all
-    counters, leaves it zero."""
+    same results and leave the arrival counters zero (for one row and a head
+    of at most 3072 rows the whole workspace; for a batch, split sampling, the
+    first M x 128 bytes)."""
     print(f"head sample one launch: M={M} N={N} K={K} k={k} ties={ties}", flush=True)
     x, w, u = _head_inputs(M, N, K, M * 131 + N + K, ties)
     need = q4.bf16_head_sample_workspace_bytes(M, N, K, k)
-    assert (need > 0) == (M == 1)              # batches fall back to the two launches
+    assert (need > 0) == (M == 1 or N > 1024)  # a batch row of one block gains nothing from the split
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
     xg, wg, ug = gpu(x), gpu(w), gpu(torch.from_numpy(u))
     ref = q4.bf16_head_sample(xg, wg, ug, top_k=k, return_topk=True)
@@ -145,8 +147,10 @@ def test_head_sample_one_launch(q4, M, N, K, k, ties):
         assert torch.equal(got[3].view(torch.int16), ref[3].view(torch.int16)), "logits differ from the two-launch path"
         for a, b, name in zip(got[:3], ref[:3], ("token", "topk_index", "topk_prob")):
             assert torch.equal(a, b), f"{name} differs from the two-launch path (call {rep})"
-        if N <= 3072 or M > 1:
+        if M == 1 and N <= 3072:
             assert int(ws.count_nonzero()) == 0, "arrival counters not left at zero"
+        elif M > 1:
+            assert int(ws[:M * 128].count_nonzero()) == 0, "arrival counters not left at zero"
     check_sample(got[0], got[1], got[2], bits(got[3]), 0.8, k, u.astype(np.float64))
     if ties:
         # one-hot rows: the logits are weight columns, exactly, full of ties
@@ -158,10 +162,12 @@ def test_head_sample_one_launch(q4, M, N, K, k, ties):
         assert np.array_equal(have, want)
 
 
-def test_head_sample_one_launch_graph_replay(q4):
-    """The one-launch head sampling captured in a graph and replayed three
-    times, outputs poisoned before each replay, equals the eager call."""
-    M, N, K, k = 1, 16385, 2048, 30
+@pytest.mark.parametrize("M", [1, 48])
+def test_head_sample_one_launch_graph_replay(q4, M):
+    """The workspace head sampling (one launch at M = 1, the split sampler for
+    a batch) captured in a graph and replayed three times, outputs poisoned
+    before each replay, equals the eager call."""
+    N, K, k = 16385, 2048, 30
     x, w, u = _head_inputs(M, N, K, 5)
     ws = torch.zeros(q4.bf16_head_sample_workspace_bytes(M, N, K, k), dtype=torch.uint8, device="cuda")
     xg, wg, ug = gpu(x), gpu(w), gpu(torch.from_numpy(u))
