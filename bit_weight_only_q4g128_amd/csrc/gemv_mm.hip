@@ -158,24 +158,31 @@ __device__ __forceinline__ uint32_t part_off(int blk, int KS, int ks, int rp, in
 // of batch row 16 mt + l % 16; write_y does the two tiles of a row pair.
 // (times gs: the NVFP4 global scale, 1 otherwise)
 // Fused instances add the residual (read by the lane that then writes the
-// same elements, so it may be y itself) before the one rounding.
-template <int MT, bool kFused = false>
-__device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, float gs, int trow0, int lane, const f32x4 (&v)[MT]) {
+// same elements, so it may be y itself) before the one rounding; every
+// residual read of a call is issued before its first store (with y possibly
+// the residual, a read after a store could not be moved ahead of it).
+template <int MT>
+__device__ __forceinline__ void add_resid_tile(const GemvArgs& a, int trow0, int lane, f32x4 (&rv)[MT]) {
+    const int row = trow0 + 4 * (lane >> 4);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = 16 * mt + (lane & 15);
-        const int row = trow0 + 4 * (lane >> 4);
+        if (m >= a.M || row >= a.N) continue;
+        const uint16_t* rs = a.resid + (size_t)m * a.N + row;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (row + q < a.N) rv[mt][q] += __builtin_bit_cast(float, (uint32_t)rs[q] << 16);
+    }
+}
+template <int MT>
+__device__ __forceinline__ void store_y_tile(const GemvArgs& a, bool y8, int trow0, int lane, const f32x4 (&rv)[MT]) {
+    const int row = trow0 + 4 * (lane >> 4);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + (lane & 15);
         if (m >= a.M || row >= a.N) continue;
         uint16_t* dst = a.y + (size_t)m * a.N + row;
-        f32x4 r = v[mt] * gs;
-        if constexpr (kFused) {
-            if (a.resid != nullptr) {
-                const uint16_t* rs = a.resid + (size_t)m * a.N + row;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (row + q < a.N) r[q] += __builtin_bit_cast(float, (uint32_t)rs[q] << 16);
-            }
-        }
+        const f32x4 r = rv[mt];
         if (y8 && row + 3 < a.N) {
             const uint32_t lo = (uint32_t)f32_to_bf16(r.x) | ((uint32_t)f32_to_bf16(r.y) << 16);
             const uint32_t hi = (uint32_t)f32_to_bf16(r.z) | ((uint32_t)f32_to_bf16(r.w) << 16);
@@ -188,9 +195,30 @@ __device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, float g
     }
 }
 template <int MT, bool kFused = false>
+__device__ __forceinline__ void write_y_tile(const GemvArgs& a, bool y8, float gs, int trow0, int lane, const f32x4 (&v)[MT]) {
+    f32x4 rv[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) rv[mt] = v[mt] * gs;
+    if constexpr (kFused)
+        if (a.resid != nullptr) add_resid_tile<MT>(a, trow0, lane, rv);
+    store_y_tile<MT>(a, y8, trow0, lane, rv);
+}
+template <int MT, bool kFused = false>
 __device__ __forceinline__ void write_y(const GemvArgs& a, bool y8, float gs, int prow0, int lane, const f32x4 (&v)[2][MT]) {
-    write_y_tile<MT, kFused>(a, y8, gs, prow0, lane, v[0]);
-    write_y_tile<MT, kFused>(a, y8, gs, prow0 + 16, lane, v[1]);
+    f32x4 r0[MT], r1[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        r0[mt] = v[0][mt] * gs;
+        r1[mt] = v[1][mt] * gs;
+    }
+    if constexpr (kFused) {
+        if (a.resid != nullptr) {
+            add_resid_tile<MT>(a, prow0, lane, r0);
+            add_resid_tile<MT>(a, prow0 + 16, lane, r1);
+        }
+    }
+    store_y_tile<MT>(a, y8, prow0, lane, r0);
+    store_y_tile<MT>(a, y8, prow0 + 16, lane, r1);
 }
 
 // Batch chunking (kChunks, one unsplit task): block row y of the grid takes

@@ -120,10 +120,11 @@ __host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4)
 constexpr int kLgkm0 = 0xC07F;
 
 // One result tile (16 weight rows x 16 batch rows) to y: lane l holds batch
-// rows 16 mt + 4 (l / 16) + v (v = 0..3) of weight row trow + l % 16; the
-// task's residual, if any, is added before the one rounding.  (16 lanes
-// store 32 contiguous bytes of a batch row.)
-__device__ __forceinline__ void sk_write_tile(const SkTask& tk, int trow, int mt, int lane, f32x4 r) {
+// rows 16 mt + 4 (l / 16) + v (v = 0..3) of weight row trow + l % 16; res
+// holds the task's residual at the same elements (BF16 bits, zero without a
+// residual), added before the one rounding.  (16 lanes store 32 contiguous
+// bytes of a batch row.)
+__device__ __forceinline__ void sk_write_tile(const SkTask& tk, int trow, int mt, int lane, f32x4 r, const uint32_t (&res)[4]) {
     const GemvArgs& a = tk.a;
     const int row = trow + (lane & 15);
     if (row >= a.N) return;
@@ -132,10 +133,7 @@ __device__ __forceinline__ void sk_write_tile(const SkTask& tk, int trow, int mt
     for (int v = 0; v < 4; ++v) {
         const int m = m0 + v;
         if (m >= a.M) break;
-        const size_t off = (size_t)m * a.N + row;
-        float val = r[v];
-        if (a.resid != nullptr) val += __builtin_bit_cast(float, (uint32_t)a.resid[off] << 16);
-        a.y[off] = f32_to_bf16(val);
+        a.y[(size_t)m * a.N + row] = f32_to_bf16(r[v] + __builtin_bit_cast(float, res[v] << 16));
     }
 }
 
@@ -230,6 +228,30 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
         L1[t] = buf_load16(rw0, woff, (uint32_t)(16 * t + 8) * rowbytes + gb);
     }
 
+    // the residual of the wave's output tiles (p = wave + 8 j, as in the
+    // epilogue), fetched behind the weights so that the epilogue does not wait
+    // for it: one element per lane and batch row (zero without a residual, or
+    // past M or N).  Each element is read only by the lane that then writes
+    // it, so the residual may be y itself.
+    constexpr int kTiles = R * MT;
+    constexpr int kJ = (kTiles + kSkWaves - 1) / kSkWaves;
+    uint32_t res[kJ][4];
+    {
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.resid, a.resid != nullptr ? (uint32_t)a.M * (uint32_t)a.N * 2u : 0u);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            const int p = wave + kSkWaves * j;
+            const int row = row0 + 16 * (p / MT) + (lane & 15);
+            const int m0 = 16 * (p % MT) + 4 * (lane >> 4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bool ok = p < kTiles && row < a.N && m0 + v < a.M;
+                const uint32_t off = ok ? ((uint32_t)(m0 + v) * (uint32_t)a.N + (uint32_t)row) * 2u : 0xFFFFFFF0u;
+                res[j][v] = __builtin_amdgcn_raw_buffer_load_b16(rr, off, 0, 0);
+            }
+        }
+    }
+
     // ---- 2. the rounds
     const bf16x8_t ones = as_b8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     f32x4 acc[R][MT];
@@ -237,7 +259,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     for (int t = 0; t < R; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int kWLoads = 2 * R;   // weight loads issued after the round-0 activations
+    constexpr int kWLoads = 2 * R + 4 * kJ;   // weight and residual loads issued after the round-0 activations
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int gl = nr * wave + r;   // group within the slice
@@ -326,7 +348,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     // tiles: the eight waves' tiles summed in wave order, plus the min term
     //   sum over the slice's groups of SX[batch][g] * (min - 128 scale)[g][row]
     // as fp32 MFMAs over chunks of four groups
-    constexpr int kTiles = R * MT;
     f32x4* red = reinterpret_cast<f32x4*>(lds);
     __syncthreads();
 #pragma unroll
@@ -371,7 +392,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
 #pragma unroll
         for (int j = 0; j * kSkWaves < kTiles; ++j) {
             const int p = wave + kSkWaves * j;
-            if (p < kTiles) sk_write_tile(tk, row0 + 16 * (p / MT), p % MT, lane, fin[j]);
+            if (p < kTiles) sk_write_tile(tk, row0 + 16 * (p / MT), p % MT, lane, fin[j], res[j]);
         }
         return;
     }
@@ -419,7 +440,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             for (int k = 0; k < 4; ++k)
                 if (s0 + k < KS) sum += __builtin_bit_cast(f32x4, pv[k]);
         }
-        sk_write_tile(tk, row0 + 16 * (p / MT), p % MT, lane, sum);
+        sk_write_tile(tk, row0 + 16 * (p / MT), p % MT, lane, sum, res[j]);
     }
     if (tid == 0) __hip_atomic_store(&tk.cnt[(size_t)blk * kCtrWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
