@@ -81,9 +81,9 @@ struct SkTable {
 };
 
 // LDS layout (bytes):
-//   [0, kArea)           per wave: one round of activations, MT * 16 rows x
-//                        256 bytes; after the rounds, the eight waves' result
-//                        tiles [8][R * MT][64 lanes] x 16 bytes (the larger)
+//   [0, kArea)           per wave, kWave bytes: one round of activations,
+//                        MT * 16 rows x 256 bytes; after its rounds, the
+//                        wave's result tiles [R * MT][64 lanes] x 16 bytes
 //   [kArea, + kPar)      per wave: the scales of its 16 R rows for its two
 //                        group slots, [16 R][2] dwords holding the fp16 value
 //                        in the low half (a 2-byte load to LDS writes one
@@ -96,8 +96,8 @@ struct SkTable {
 template <int MT, int R>
 struct SkLds {
     static constexpr int kX = MT * 16 * 256;
-    static constexpr int kRed = kSkWaves * R * MT * 1024;
-    static constexpr int kArea = (kSkWaves * kX > kRed) ? kSkWaves * kX : kRed;
+    static constexpr int kWave = (kX > R * MT * 1024) ? kX : R * MT * 1024;
+    static constexpr int kArea = kSkWaves * kWave;
     static constexpr int kParArr = ((32 * R + 63) / 64) * 64;   // dwords per (wave, array), whole 64-lane loads
     static constexpr int kPar = kSkWaves * kParArr * 4;
     static constexpr int kMinLoads = (16 * R * kSkMaxGroups / 64 + kSkWaves - 1) / kSkWaves;   // per wave
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     const uint32_t rowbytes = (uint32_t)a.K >> 1;
     const int nv = ng - nr * wave;                       // this wave's valid rounds (may be <= 0)
 
-    uint8_t* xbuf = lds + wave * L::kX;
+    uint8_t* xbuf = lds + wave * L::kWave;
     uint32_t* par = reinterpret_cast<uint32_t*>(lds + L::kArea);               // scales [8][kParArr]
     uint32_t* mtab = reinterpret_cast<uint32_t*>(lds + L::kArea + L::kPar);    // mins [16 R][16]
     float* sxt = reinterpret_cast<float*>(lds + L::kArea + L::kPar + L::kMin);  // [16][16 MT]
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xbuf + 1024 * i), 16, off, 0, 0, 0);
         }
     };
-    issue_x(0);
+    if (nv > 0) issue_x(0);   // (a wave without a group of the slice fills nothing)
     // weights.  A wave's two groups are adjacent, 128 bytes of each row (one
     // cache line), so a load instruction reads eight rows in whole lines:
     // lane l reads row l % 8 of the tile's lower (L0) or upper (L1) eight
@@ -228,30 +228,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
         L1[t] = buf_load16(rw0, woff, (uint32_t)(16 * t + 8) * rowbytes + gb);
     }
 
-    // the residual of the wave's output tiles (p = wave + 8 j, as in the
-    // epilogue), fetched behind the weights so that the epilogue does not wait
-    // for it: one element per lane and batch row (zero without a residual, or
-    // past M or N).  Each element is read only by the lane that then writes
-    // it, so the residual may be y itself.
-    constexpr int kTiles = R * MT;
-    constexpr int kJ = (kTiles + kSkWaves - 1) / kSkWaves;
-    uint32_t res[kJ][4];
-    {
-        const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.resid, a.resid != nullptr ? (uint32_t)a.M * (uint32_t)a.N * 2u : 0u);
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) {
-            const int p = wave + kSkWaves * j;
-            const int row = row0 + 16 * (p / MT) + (lane & 15);
-            const int m0 = 16 * (p % MT) + 4 * (lane >> 4);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bool ok = p < kTiles && row < a.N && m0 + v < a.M;
-                const uint32_t off = ok ? ((uint32_t)(m0 + v) * (uint32_t)a.N + (uint32_t)row) * 2u : 0xFFFFFFF0u;
-                res[j][v] = __builtin_amdgcn_raw_buffer_load_b16(rr, off, 0, 0);
-            }
-        }
-    }
-
     // ---- 2. the rounds
     const bf16x8_t ones = as_b8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     f32x4 acc[R][MT];
@@ -259,7 +235,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     for (int t = 0; t < R; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int kWLoads = 2 * R + 4 * kJ;   // weight and residual loads issued after the round-0 activations
+    constexpr int kWLoads = 2 * R;   // weight loads issued after the round-0 activations
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int gl = nr * wave + r;   // group within the slice
@@ -343,17 +319,48 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
         }
     }
 
-    // ---- 3. the waves meet: tiles to LDS (over the activation regions, so
-    // after every wave has read its last round), then each wave finishes whole
-    // tiles: the eight waves' tiles summed in wave order, plus the min term
+    // ---- 3. the waves meet: each wave's tiles to its own LDS region as soon
+    // as it is done (it has read its last round out of the region), then each
+    // wave finishes whole tiles: the eight waves' tiles summed in wave order,
+    // plus the min term
     //   sum over the slice's groups of SX[batch][g] * (min - 128 scale)[g][row]
-    // as fp32 MFMAs over chunks of four groups
-    f32x4* red = reinterpret_cast<f32x4*>(lds);
-    __syncthreads();
+    // as fp32 MFMAs over chunks of four groups.  Every wave's loads into LDS
+    // (its share of the group parameters, its activations) are complete
+    // before the barrier.
+    constexpr int kTiles = R * MT;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // the residual of the wave's output tiles (p = wave + 8 j, as in the
+    // epilogue), fetched now so that its latency hides behind the meeting of
+    // the waves: one element per lane and batch row (zero without a residual,
+    // or past M or N).  Each element is read only by the lane that then
+    // writes it, so the residual may be y itself.
+    constexpr int kJ = (kTiles + kSkWaves - 1) / kSkWaves;
+    uint32_t res[kJ][4];
+    if (a.resid == nullptr) {
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) res[j][v] = 0u;
+    } else {
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.resid, (uint32_t)a.M * (uint32_t)a.N * 2u);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            const int p = wave + kSkWaves * j;
+            const int row = row0 + 16 * (p / MT) + (lane & 15);
+            const int m0 = 16 * (p % MT) + 4 * (lane >> 4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bool ok = p < kTiles && row < a.N && m0 + v < a.M;
+                const uint32_t off = ok ? ((uint32_t)(m0 + v) * (uint32_t)a.N + (uint32_t)row) * 2u : 0xFFFFFFF0u;
+                res[j][v] = __builtin_amdgcn_raw_buffer_load_b16(rr, off, 0, 0);
+            }
+        }
+    }
+    f32x4* myred = reinterpret_cast<f32x4*>(xbuf);
 #pragma unroll
     for (int t = 0; t < R; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) red[(wave * kTiles + t * MT + mt) * 64 + lane] = acc[t][mt];
+        for (int mt = 0; mt < MT; ++mt) myred[(t * MT + mt) * 64 + lane] = acc[t][mt];
     lds_sync();
     f32x4 fin[(kTiles + kSkWaves - 1) / kSkWaves];
     const int nsh = nr - 1;   // group g of the slice belongs to wave g >> nsh, slot g & nsh
@@ -374,9 +381,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
                 sv[c] = f16_to_f32((uint16_t)par[w2 * L::kParArr + 2 * row + slot]);
                 mv[c] = f16_to_f32((uint16_t)mtab[16 * row + gi]);
             }
-            f32x4 v = red[p * 64 + lane];
+            f32x4 v = reinterpret_cast<const f32x4*>(lds)[p * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < kSkWaves; ++w) v += red[(w * kTiles + p) * 64 + lane];
+            for (int w = 1; w < kSkWaves; ++w) v += reinterpret_cast<const f32x4*>(lds + w * L::kWave)[p * 64 + lane];
             f32x4 dm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < kSkMaxGroups / 4; ++c) {
