@@ -59,7 +59,7 @@ int pick(Fmt fmt, int variant, int M, int N, int K, bool split = false) {
     if (variant == Q4_VARIANT_MFMA) return Q4_VARIANT_MFMA;
     if (variant == Q4_VARIANT_STREAM) return q4::stream_supported(fmt, M, K) ? Q4_VARIANT_STREAM : -1;
     if (variant == Q4_VARIANT_TILED) return q4::mm_supported(fmt, M, K, split) ? Q4_VARIANT_TILED : -1;
-    if (variant == Q4_VARIANT_SKINNY) return fmt == q4::kFmtQ4 && q4::skinny_supported(M, K, split) ? Q4_VARIANT_SKINNY : -1;
+    if (variant == Q4_VARIANT_SKINNY) return q4::skinny_supported(fmt, M, K, split) ? Q4_VARIANT_SKINNY : -1;
     if (M <= 4 && q4::stream_supported(fmt, M, K)) return Q4_VARIANT_STREAM;
     if (M <= 4 && q4::dot2_supported(fmt, K)) return Q4_VARIANT_DOT2;
     if (fmt == q4::kFmtQ4 && q4::skinny_supported(M, K, split)) return Q4_VARIANT_SKINNY;
@@ -74,7 +74,12 @@ int run(Fmt fmt, int chosen, const GemvArgs* a, int count, void* stream, void* w
         case Q4_VARIANT_DOT2: e = q4::launch_dot2(fmt, a, count, s); break;
         case Q4_VARIANT_STREAM: e = q4::launch_stream(fmt, a, count, s); break;
         case Q4_VARIANT_TILED: e = q4::launch_mm(fmt, a, count, ws, ws_bytes, s); break;
-        case Q4_VARIANT_SKINNY: e = q4::launch_skinny(a, count, ws, ws_bytes, s); break;
+        case Q4_VARIANT_SKINNY: {
+            Fmt f[q4::kMaxTasks];
+            for (int i = 0; i < count; ++i) f[i] = fmt;
+            e = q4::launch_skinny(f, a, count, ws, ws_bytes, s);
+            break;
+        }
         default: e = q4::launch_mfma(fmt, a, count, s); break;
     }
     return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
@@ -172,7 +177,11 @@ int plan_checked(Fmt fmt, const GemvArgs* a, const Range (*in)[4], const Range* 
 // Workspace a planned grouped launch can use (0: no K split planned).
 size_t grouped_ws_bytes(Fmt fmt, int chosen, const GemvArgs* a, int count) {
     if (chosen == Q4_VARIANT_TILED) return q4::mm_workspace_bytes(fmt, a, count);
-    if (chosen == Q4_VARIANT_SKINNY) return q4::skinny_workspace_bytes(a, count);
+    if (chosen == Q4_VARIANT_SKINNY) {
+        Fmt f[q4::kMaxTasks];
+        for (int i = 0; i < count; ++i) f[i] = fmt;
+        return q4::skinny_workspace_bytes(f, a, count);
+    }
     return 0;
 }
 
@@ -185,7 +194,7 @@ int run_grouped(Fmt fmt, int chosen, const GemvArgs* a, int count, int M, void* 
         const size_t need = grouped_ws_bytes(fmt, chosen, a, count);
         if (need == 0 || workspace_bytes < need) {
             for (int i = 0; i < count; ++i)
-                if (chosen == Q4_VARIANT_TILED ? !q4::mm_supported(fmt, M, a[i].K, false) : !q4::skinny_supported(M, a[i].K, false))
+                if (chosen == Q4_VARIANT_TILED ? !q4::mm_supported(fmt, M, a[i].K, false) : !q4::skinny_supported(fmt, M, a[i].K, false))
                     return Q4_EVARIANT;
         }
     }
@@ -229,6 +238,14 @@ int check_mixed(const q4gemv_mixed_task* tasks, int count, int M, GemvArgs* a, F
         }
     *one_launch = stream;
     return Q4_OK;
+}
+
+// 5 <= M <= 48 and every task on the skinny kernel (with K splits allowed):
+// the group can run as one mixed-format skinny launch.
+bool mixed_skinny(const GemvArgs* a, const Fmt* fmts, int count, int M) {
+    for (int i = 0; i < count; ++i)
+        if (!q4::skinny_supported(fmts[i], M, a[i].K, true)) return false;
+    return true;
 }
 
 // Every task NVFP4 or BF16 and on the tiled kernel (with K splits allowed):
@@ -575,6 +592,15 @@ int q4gemv_grouped_mixed(const q4gemv_mixed_task* tasks, int count, int M, void*
         return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
     }
     const bool split = workspace != nullptr && workspace_bytes > 0;
+    if (mixed_skinny(a, fmts, count, M)) {
+        const size_t need = q4::skinny_workspace_bytes(fmts, a, count);
+        bool unsplit_ok = true;
+        for (int i = 0; i < count; ++i) unsplit_ok = unsplit_ok && q4::skinny_supported(fmts[i], M, a[i].K, false);
+        if ((split && need <= workspace_bytes) || unsplit_ok) {
+            hipError_t e = q4::launch_skinny(fmts, a, count, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+            return e == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+        }
+    }
     if (split && mixed_tiled(a, fmts, count, M)) {
         const size_t need = q4::mm_workspace_bytes(q4::kFmtNvfp4, a, count);
         if (need <= workspace_bytes) {
@@ -601,7 +627,7 @@ int q4gemv_grouped_mixed(const q4gemv_mixed_task* tasks, int count, int M, void*
             if (need == 0 || workspace_bytes < need)
                 for (int i = 0; i < n[f]; ++i)
                     if (chosen[f] == Q4_VARIANT_TILED ? !q4::mm_supported(order[f], M, sub[f][i].K, false)
-                                                      : !q4::skinny_supported(M, sub[f][i].K, false))
+                                                      : !q4::skinny_supported(order[f], M, sub[f][i].K, false))
                         return Q4_EVARIANT;
         }
     }
@@ -620,7 +646,11 @@ int q4gemv_mixed_workspace_bytes(const q4gemv_mixed_task* tasks, int count, int 
     int rc = check_mixed(tasks, count, M, a, fmts, &one);
     if (rc) return rc;
     size_t need = 0;
-    if (!one && mixed_tiled(a, fmts, count, M)) need = q4::mm_workspace_bytes(q4::kFmtNvfp4, a, count);
+    if (!one && mixed_skinny(a, fmts, count, M)) need = q4::skinny_workspace_bytes(fmts, a, count);
+    if (!one && mixed_tiled(a, fmts, count, M)) {
+        const size_t b = q4::mm_workspace_bytes(q4::kFmtNvfp4, a, count);
+        need = b > need ? b : need;
+    }
     if (!one) {
         for (int f = 0; f < 3; ++f) {
             GemvArgs sub[q4::kMaxTasks];

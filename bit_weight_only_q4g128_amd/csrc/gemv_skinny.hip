@@ -1,5 +1,6 @@
-// Skinny matrix-core GEMV for batched decode with int4 g128 weights
-// (5 <= M <= 48, K % 128 == 0; gfx950, v_mfma_f32_16x16x32_bf16).
+// Skinny matrix-core GEMV for batched decode (5 <= M <= 48, K % 128 == 0;
+// gfx950, v_mfma_f32_16x16x32_bf16): int4 g128 weights, and in the same
+// launch NVFP4 and BF16 ones (the NVFP4 decode step keeps v and down in BF16).
 //
 // The decode batch shares one read of the weights: at M = 48 every weight byte
 // feeds 48 products ("rumik-oss-1-nvfp4-vllm" card, "Concurrent request
@@ -45,6 +46,17 @@
 // block's counter sums the slices in slice order, writes y and resets the
 // counter.
 //
+// NVFP4 rounds read their codes exactly as int4 rounds do (64 bytes of a row
+// per group, two groups per cache line).  Each 8-code dword becomes BF16
+// pairs e2m1 * e4m3 -- exact: at most 6 significant bits -- with the lane's
+// 16-column block scale staged in LDS, in natural column order (the
+// activations are not paired); the MFMAs accumulate across groups directly
+// and the global scale multiplies each finished output once.  BF16 rounds
+// take one group of 128 columns per wave (256 bytes of a row, two cache
+// lines; slices of 8 groups): the same row-shift exchange turns eight-row
+// whole-line loads into the operand layout, k-step s taking 16-byte chunk
+// 8 (s / 2) + 2 (l / 16) + s % 2 of the group.  Neither has a min term.
+//
 // MFMA operand layout (16x16x32): lane l holds A row l % 16 and B column
 // l % 16, k-values 8 (l / 16) .. + 8 of the k-step.  For k-step s of a group,
 // lane l's k-values are the 8 columns 32 (l / 16) + 8 s .. + 8 of the group
@@ -69,6 +81,7 @@ __device__ __forceinline__ bf16x8_t as_b8(u32x4 v) { return __builtin_bit_cast(b
 
 struct SkTask {
     GemvArgs a;
+    int fmt;         // Fmt of the task's weights
     int ks;          // workgroups (K slices) per row block
     int gs;          // groups per slice
     float* part;     // ks > 1: partial tiles [blocks][ks][R * MT][64 lanes] x 4 floats
@@ -85,20 +98,23 @@ struct SkTable {
 //                        MT * 16 rows x 256 bytes; after its rounds, the
 //                        wave's result tiles [R * MT][64 lanes] x 16 bytes
 //   [kArea, + kPar)      per wave: the scales of its 16 R rows for its two
-//                        group slots, [16 R][2] dwords holding the fp16 value
-//                        in the low half (a 2-byte load to LDS writes one
-//                        zero-extended dword per lane), padded to whole 64-lane
-//                        loads
+//                        group slots -- int4: [16 R][2] dwords holding the
+//                        fp16 value in the low half (a 2-byte load to LDS
+//                        writes one zero-extended dword per lane); NVFP4:
+//                        [16 R][2][2] dwords, the group's eight e4m3 bytes --
+//                        padded to whole 64-lane loads
 //   [.., + kMin)         the mins of the workgroup's 16 R rows for the slice's
 //                        groups, [16 R][16] dwords (fp16 in the low half),
 //                        padded to whole 64-lane loads of all eight waves
 //   [.., + kSx)          SX per group of the slice and batch row, fp32 [16][16 MT]
-template <int MT, int R>
+// FM: the formats a launch carries (bit 0 int4, bit 1 NVFP4, bit 2 BF16);
+// only their code is compiled into an instance
+template <int MT, int R, int FM>
 struct SkLds {
     static constexpr int kX = MT * 16 * 256;
     static constexpr int kWave = (kX > R * MT * 1024) ? kX : R * MT * 1024;
     static constexpr int kArea = kSkWaves * kWave;
-    static constexpr int kParArr = ((32 * R + 63) / 64) * 64;   // dwords per (wave, array), whole 64-lane loads
+    static constexpr int kParArr = (((FM & 2) ? 64 : 32) * R + 63) / 64 * 64;   // dwords per wave, whole 64-lane loads
     static constexpr int kPar = kSkWaves * kParArr * 4;
     static constexpr int kMinLoads = (16 * R * kSkMaxGroups / 64 + kSkWaves - 1) / kSkWaves;   // per wave
     static constexpr int kMin = kSkWaves * kMinLoads * 64 * 4;
@@ -137,27 +153,30 @@ __device__ __forceinline__ void sk_write_tile(const SkTask& tk, int trow, int mt
     }
 }
 
-template <int MT, int R>
+template <int MT, int R, int FM>
 __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
-    using L = SkLds<MT, R>;
+    using L = SkLds<MT, R, FM>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int ti = 0;
 #pragma unroll
     for (int i = 1; i < kMaxTasks; ++i) ti += ((int)blockIdx.x >= tt.blk0[i]) ? 1 : 0;
     const SkTask& tk = tt.t[ti];
     const GemvArgs& a = tk.a;
+    const bool q4f = (FM & 1) && (FM == 1 || tk.fmt == kFmtQ4);
+    const bool nvf = (FM & 2) && (FM == 2 || tk.fmt == kFmtNvfp4);
+    const bool bff = (FM & 4) && (FM == 4 || tk.fmt == kFmtBf16);
     const int KS = tk.ks;
     const int local = (int)blockIdx.x - tt.blk0[ti];
     const int blk = local / KS, ks = local - blk * KS;
     const int G = a.K >> 7;
     const int g0 = ks * tk.gs;
     const int ng = (G - g0 < tk.gs) ? G - g0 : tk.gs;   // groups of this slice, >= 1
-    const int nr = (ng + kSkWaves - 1) / kSkWaves;      // rounds per wave: 1 or 2
+    const int nr = (ng + kSkWaves - 1) / kSkWaves;      // rounds per wave: 1 or 2 (BF16: 1)
     const int row0 = blk * 16 * R;
     const int nrows = (a.N - row0 < 16 * R) ? a.N - row0 : 16 * R;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t rowbytes = (uint32_t)a.K >> 1;
+    const uint32_t rowbytes = bff ? (uint32_t)a.K * 2u : (uint32_t)a.K >> 1;
     const int nv = ng - nr * wave;                       // this wave's valid rounds (may be <= 0)
 
     uint8_t* xbuf = lds + wave * L::kWave;
@@ -171,9 +190,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.minv + (size_t)row0 * G, (uint32_t)nrows * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.K * 2u);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (size_t)row0 * rowbytes, (uint32_t)nrows * rowbytes);
-    // scales, per wave: element e = 64 i + lane is (row e / 2, slot e % 2) ->
-    // group g0 + nr w + slot
-    {
+    // scales, per wave.  int4: element e = 64 i + lane is (row e / 2, slot
+    // e % 2) -> group g0 + nr w + slot.  NVFP4: dword e = 64 i + lane is (row
+    // e / 4, slot (e / 2) % 2, half e % 2) -> bytes 4 half .. 4 half + 3 of the
+    // eight e4m3 scales of group g0 + nr w + slot.
+    if (q4f) {
         constexpr int kPI = (16 * R * 2 + 63) / 64;
 #pragma unroll
         for (int i = 0; i < kPI; ++i) {
@@ -183,12 +204,24 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             const uint32_t off = ok ? ((uint32_t)row * (uint32_t)G + (uint32_t)(g0 + nr * wave + slot)) * 2u : 0xFFFFFFF0u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(par + wave * L::kParArr + 64 * i), 2, off, 0, 0, 0);
         }
+    } else if (nvf) {
+        const uint32_t sb = (uint32_t)a.K >> 4;   // scale bytes per row
+        const __amdgpu_buffer_rsrc_t r8 = make_rsrc(a.scale8 + (size_t)row0 * sb, (uint32_t)nrows * sb);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int e = 64 * i + lane;
+            const int row = e >> 2, slot = (e >> 1) & 1, hf = e & 1;
+            const bool ok = row < 16 * R && slot < nv;
+            const uint32_t off = ok ? (uint32_t)row * sb + (uint32_t)(g0 + nr * wave + slot) * 8u + 4u * (uint32_t)hf : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r8, (lds_void*)(par + wave * L::kParArr + 64 * i), 4, off, 0, 0, 0);
+        }
     }
-    // mins, once per workgroup (they are read only after the waves meet):
-    // element e = 64 (wave + 8 j) + lane is (row e / 16, group e % 16 of the
-    // slice); four rows' slices of a whole-K task share one cache line
+    // int4 mins, once per workgroup (they are read only after the waves
+    // meet): element e = 64 (wave + 8 j) + lane is (row e / 16, group e % 16
+    // of the slice); four rows' slices of a whole-K task share one cache line
 #pragma unroll
     for (int j = 0; j < L::kMinLoads; ++j) {
+        if (!q4f) break;
         const int e = 64 * (wave + kSkWaves * j) + lane;
         const int row = e >> 4, gi = e & 15;
         const bool ok = row < 16 * R && gi < ng;
@@ -217,15 +250,23 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     // second (l % 16 >= 8).  (A wave with one group reads that group's chunk
     // l / 16 in both halves of the lane range.)  The row and group parts of
     // the offset are scalar.
+    // BF16: the wave's one group is 256 bytes of each row, two cache lines;
+    // a load reads eight rows of one line, lane l row l % 8, 16-byte chunk
+    // l / 8 (L0/L1: the first line, L2/L3: the second).
     const bool pair = nr == 2;
-    const uint32_t woff = (uint32_t)(lane & 7) * rowbytes + 16u * (uint32_t)(lane >> 4) + (pair ? 64u * (uint32_t)((lane >> 3) & 1) : 0u);
+    const uint32_t woff = bff ? (uint32_t)(lane & 7) * rowbytes + 16u * (uint32_t)(lane >> 3)
+                              : (uint32_t)(lane & 7) * rowbytes + 16u * (uint32_t)(lane >> 4) + (pair ? 64u * (uint32_t)((lane >> 3) & 1) : 0u);
     const __amdgpu_buffer_rsrc_t rw0 = nv > 0 ? rw : make_rsrc(a.w, 0u);
-    const uint32_t gb = (uint32_t)(g0 + nr * wave) * 64u;
-    u32x4 L0[R], L1[R];
+    const uint32_t gb = (uint32_t)(g0 + nr * wave) * (bff ? 256u : 64u);
+    u32x4 L0[R], L1[R], L2[R], L3[R];
 #pragma unroll
     for (int t = 0; t < R; ++t) {
         L0[t] = buf_load16(rw0, woff, (uint32_t)(16 * t) * rowbytes + gb);
         L1[t] = buf_load16(rw0, woff, (uint32_t)(16 * t + 8) * rowbytes + gb);
+        if (bff) {
+            L2[t] = buf_load16(rw0, woff, (uint32_t)(16 * t) * rowbytes + gb + 128u);
+            L3[t] = buf_load16(rw0, woff, (uint32_t)(16 * t + 8) * rowbytes + gb + 128u);
+        }
     }
 
     // ---- 2. the rounds
@@ -235,7 +276,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     for (int t = 0; t < R; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int kWLoads = 2 * R;   // weight loads issued after the round-0 activations
+    constexpr int kWLoads = 2 * R;   // weight loads issued after the round-0 activations (BF16: twice as many)
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int gl = nr * wave + r;   // group within the slice
@@ -247,17 +288,69 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             continue;
         }
         // this round's activations (and, in round 0, the parameters) are in LDS
-        if (r == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWLoads));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        if (r == 0) {
+            if (bff) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kWLoads));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWLoads));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        // k-step s: lane l takes 8 columns of the group -- 4-bit formats:
+        // 32 (l / 16) + 8 s .. (dword s of the lane's weight chunk); BF16:
+        // chunk 8 (s / 2) + 2 (l / 16) + s % 2 (line s / 2 after the exchange)
         u32x4 X[MT][4];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int m = 16 * mt + (lane & 15);
-                const int chunk = 4 * (lane >> 4) + s;
+                const int chunk = bff ? 8 * (s >> 1) + 2 * (lane >> 4) + (s & 1) : 4 * (lane >> 4) + s;
                 X[mt][s] = *reinterpret_cast<const u32x4*>(xbuf + m * 256 + 16 * (chunk ^ (m & 15)));
             }
+        if (!q4f) {
+            // NVFP4 and BF16: weights in natural column order, no group fold
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                if (nvf) {
+                    // the lane's scales for k-steps 0-1 and 2-3: 16-column
+                    // blocks 2 (l / 16) and 2 (l / 16) + 1 of the group
+                    const uint32_t sw = par[wave * L::kParArr + 4 * (16 * t + (lane & 15)) + 2 * r + (lane >> 5)] >> (16 * ((lane >> 4) & 1));
+                    const float sc0 = e4m3_to_f32<0>(sw), sc1 = e4m3_to_f32<1>(sw);
+                    u32x4 Wt;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        Wt[d] = r == 0 ? (uint32_t)__builtin_amdgcn_update_dpp((int)L0[t][d], (int)L1[t][d], 0x118, 0xF, 0xC, false)
+                                       : (uint32_t)__builtin_amdgcn_update_dpp((int)L1[t][d], (int)L0[t][d], 0x108, 0xF, 0x3, false);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const float sc = s < 2 ? sc0 : sc1;
+                        const bf16x8_t Wv = as_b8(u32x4{nv_pair_scaled<0>(Wt[s], sc), nv_pair_scaled<1>(Wt[s], sc),
+                                                        nv_pair_scaled<2>(Wt[s], sc), nv_pair_scaled<3>(Wt[s], sc)});
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(X[mt][s]), Wv, acc[t][mt], 0, 0, 0);
+                    }
+                } else {
+                    // BF16: rows 0-7 of the tile in L0 / L2, rows 8-15 in L1 / L3;
+                    // chunk 2 (l / 16) + s % 2 of row l % 16 comes from this lane or
+                    // eight lanes away (the same exchange as the 4-bit rounds)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const u32x4 La = s < 2 ? L0[t] : L2[t], Lb = s < 2 ? L1[t] : L3[t];
+                        u32x4 Wv;
+#pragma unroll
+                        for (int d = 0; d < 4; ++d)
+                            Wv[d] = (s & 1) == 0 ? (uint32_t)__builtin_amdgcn_update_dpp((int)La[d], (int)Lb[d], 0x118, 0xF, 0xC, false)
+                                                 : (uint32_t)__builtin_amdgcn_update_dpp((int)Lb[d], (int)La[d], 0x108, 0xF, 0x3, false);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(X[mt][s]), as_b8(Wv), acc[t][mt], 0, 0, 0);
+                    }
+                }
+            }
+            if (r == 0 && nr > 1 && nv > 1) {
+                __builtin_amdgcn_s_waitcnt(kLgkm0);
+                issue_x(1);
+            }
+            continue;
+        }
         uint32_t sc16[R];   // this lane's row: the scale of this round's group (fp16 in the low half)
 #pragma unroll
         for (int t = 0; t < R; ++t) sc16[t] = par[wave * L::kParArr + 2 * (16 * t + (lane & 15)) + r];
@@ -374,6 +467,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             float av[kSkMaxGroups / 4], sv[kSkMaxGroups / 4], mv[kSkMaxGroups / 4];
 #pragma unroll
             for (int c = 0; c < kSkMaxGroups / 4; ++c) {
+                if (!q4f) break;
                 const int g = 4 * c + (lane >> 4);
                 const int gi = g < ng ? g : 0;
                 const int w2 = gi >> nsh, slot = gi & nsh;
@@ -384,13 +478,17 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
             f32x4 v = reinterpret_cast<const f32x4*>(lds)[p * 64 + lane];
 #pragma unroll
             for (int w = 1; w < kSkWaves; ++w) v += reinterpret_cast<const f32x4*>(lds + w * L::kWave)[p * 64 + lane];
-            f32x4 dm = {0.f, 0.f, 0.f, 0.f};
+            if (q4f) {
+                f32x4 dm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < kSkMaxGroups / 4; ++c) {
-                const bool ok = 4 * c + (lane >> 4) < ng;
-                dm = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? av[c] : 0.0f, ok ? fmaf(-128.0f, sv[c], mv[c]) : 0.0f, dm, 0, 0, 0);
+                for (int c = 0; c < kSkMaxGroups / 4; ++c) {
+                    const bool ok = 4 * c + (lane >> 4) < ng;
+                    dm = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? av[c] : 0.0f, ok ? fmaf(-128.0f, sv[c], mv[c]) : 0.0f, dm, 0, 0, 0);
+                }
+                fin[j] = v + dm;
+            } else {
+                fin[j] = nvf ? v * a.gscale : v;   // NVFP4: the global scale, once per output
             }
-            fin[j] = v + dm;
         }
     }
 
@@ -485,7 +583,12 @@ size_t sk_ws_bytes(const GemvArgs* tasks, int count, int R, const int* ks) {
     return kWsCounterBytes + part;
 }
 
-bool sk_plan(const GemvArgs* tasks, int count, bool can_split, SkPlan& best) {
+// weight bytes per row and group of 128 columns (int4 counts its codes only)
+int sk_group_bytes(int fmt) { return fmt == kFmtBf16 ? 256 : fmt == kFmtNvfp4 ? 72 : 64; }
+// most groups per slice: BF16 rounds are one group per wave
+int sk_max_groups(int fmt) { return fmt == kFmtBf16 ? kSkMaxGroups / 2 : kSkMaxGroups; }
+
+bool sk_plan(const Fmt* fmts, const GemvArgs* tasks, int count, bool can_split, SkPlan& best) {
     const int MT = sk_mt(tasks[0].M);
     double best_cost = 0;
     bool found = false;
@@ -495,23 +598,25 @@ bool sk_plan(const GemvArgs* tasks, int count, bool can_split, SkPlan& best) {
             SkPlan p;
             p.R = R;
             long wgs = 0;
-            int smax = 0;
+            double per_wg = 0;
             bool ok = true, split = false;
             for (int i = 0; i < count; ++i) {
-                const int G = tasks[i].K >> 7;
-                int gs = G <= S ? G : S;
-                if (G > kSkMaxGroups && !can_split) { ok = false; break; }
+                const int G = tasks[i].K >> 7, cap = sk_max_groups(fmts[i]);
+                const int S1 = S < cap ? S : cap;
+                int gs = G <= S1 ? G : S1;
+                if (G > cap && !can_split) { ok = false; break; }
                 const int ks = (G + gs - 1) / gs;
                 p.gs[i] = gs;
                 p.ks[i] = ks;
                 split = split || ks > 1;
-                smax = gs > smax ? gs : smax;
+                const double c = 16.0 * R * gs * sk_group_bytes(fmts[i]) + 0.19 * gs * MT * 4096;
+                per_wg = c > per_wg ? c : per_wg;
                 wgs += (long)((tasks[i].N + 16 * R - 1) / (16 * R)) * ks;
             }
             if (!ok) continue;
             p.ws = split ? sk_ws_bytes(tasks, count, R, p.ks) : 0;
             if (p.ws == (size_t)-1) continue;
-            const double per_wg = 16.0 * R * smax * 64 + 0.19 * smax * MT * 4096 + (split ? 35000.0 : 0.0);
+            per_wg += split ? 35000.0 : 0.0;
             const double cost = (double)((wgs + kCUs - 1) / kCUs) * per_wg;
             if (!found || cost < best_cost * 0.999) {
                 best = p;
@@ -523,8 +628,17 @@ bool sk_plan(const GemvArgs* tasks, int count, bool can_split, SkPlan& best) {
     return found;
 }
 
+template <int MT, int R, int FM>
+hipError_t launch_sk_fm(const SkTable& tt, int grid, hipStream_t st) {
+    constexpr int kShmem = SkLds<MT, R, FM>::kBytes;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_q4_kernel<MT, R, FM>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kShmem);
+    if (attr != hipSuccess) return attr;
+    return launch_kernel(skinny_q4_kernel<MT, R, FM>, dim3(grid), dim3(kSkThreads), (size_t)kShmem, st, tt);
+}
+
 template <int MT, int R>
-hipError_t launch_sk_mt(const GemvArgs* tasks, int count, const SkPlan& p, void* ws, hipStream_t st) {
+hipError_t launch_sk_mt(const Fmt* fmts, const GemvArgs* tasks, int count, const SkPlan& p, void* ws, hipStream_t st) {
     SkTable tt{};
     for (int i = 0; i < kMaxTasks; ++i) tt.blk0[i] = 0x7fffffff;
     uint8_t* pc = static_cast<uint8_t*>(ws);
@@ -536,6 +650,7 @@ hipError_t launch_sk_mt(const GemvArgs* tasks, int count, const SkPlan& p, void*
         SkTask& t = tt.t[i];
         tt.blk0[i] = grid;
         t.a = a;
+        t.fmt = fmts[i];
         t.ks = p.ks[i];
         t.gs = p.gs[i];
         if (p.ks[i] > 1) {
@@ -546,46 +661,62 @@ hipError_t launch_sk_mt(const GemvArgs* tasks, int count, const SkPlan& p, void*
         }
         grid += blocks * p.ks[i];
     }
-    constexpr int kShmem = SkLds<MT, R>::kBytes;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_q4_kernel<MT, R>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kShmem);
-    if (attr != hipSuccess) return attr;
-    return launch_kernel(skinny_q4_kernel<MT, R>, dim3(grid), dim3(kSkThreads), (size_t)kShmem, st, tt);
+    int fm = 0;
+    for (int i = 0; i < count; ++i) fm |= 1 << fmts[i];
+    if (fm == 1) return launch_sk_fm<MT, R, 1>(tt, grid, st);
+    if (!(fm & 1)) return launch_sk_fm<MT, R, 6>(tt, grid, st);
+    return launch_sk_fm<MT, R, 7>(tt, grid, st);
 }
 
 template <int MT>
-hipError_t launch_sk_r(const GemvArgs* tasks, int count, const SkPlan& p, void* ws, hipStream_t st) {
+hipError_t launch_sk_r(const Fmt* fmts, const GemvArgs* tasks, int count, const SkPlan& p, void* ws, hipStream_t st) {
     switch (p.R) {
-        case 5: return launch_sk_mt<MT, 5>(tasks, count, p, ws, st);
-        case 3: return launch_sk_mt<MT, 3>(tasks, count, p, ws, st);
-        case 2: return launch_sk_mt<MT, 2>(tasks, count, p, ws, st);
-        default: return launch_sk_mt<MT, 1>(tasks, count, p, ws, st);
+        case 5: return launch_sk_mt<MT, 5>(fmts, tasks, count, p, ws, st);
+        case 3: return launch_sk_mt<MT, 3>(fmts, tasks, count, p, ws, st);
+        case 2: return launch_sk_mt<MT, 2>(fmts, tasks, count, p, ws, st);
+        default: return launch_sk_mt<MT, 1>(fmts, tasks, count, p, ws, st);
     }
 }
 
 }  // namespace
 
-bool skinny_supported(int M, int K, bool split) {
+bool skinny_supported(Fmt fmt, int M, int K, bool split) {
     if (M < 5 || M > kSkinnyMaxM || K % 128 != 0) return false;
-    return split || (K >> 7) <= kSkMaxGroups;
+    return split || (K >> 7) <= sk_max_groups(fmt);
 }
 
-size_t skinny_workspace_bytes(const GemvArgs* tasks, int count) {
+size_t skinny_workspace_bytes(const Fmt* fmts, const GemvArgs* tasks, int count) {
     SkPlan p;
-    if (!sk_plan(tasks, count, true, p)) return 0;
+    if (!sk_plan(fmts, tasks, count, true, p)) return 0;
     return p.ws;
 }
 
-hipError_t launch_skinny(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
+hipError_t launch_skinny(const Fmt* fmts, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
     SkPlan p;
-    const size_t need = skinny_workspace_bytes(tasks, count);
+    const size_t need = skinny_workspace_bytes(fmts, tasks, count);
     const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
-    if (!sk_plan(tasks, count, split, p)) return hipErrorInvalidValue;
+    if (!sk_plan(fmts, tasks, count, split, p)) return hipErrorInvalidValue;
     switch (sk_mt(tasks[0].M)) {
-        case 1: return launch_sk_r<1>(tasks, count, p, ws, s);
-        case 2: return launch_sk_r<2>(tasks, count, p, ws, s);
-        default: return launch_sk_r<3>(tasks, count, p, ws, s);
+        case 1: return launch_sk_r<1>(fmts, tasks, count, p, ws, s);
+        case 2: return launch_sk_r<2>(fmts, tasks, count, p, ws, s);
+        default: return launch_sk_r<3>(fmts, tasks, count, p, ws, s);
     }
+}
+
+// int4 tasks only
+namespace {
+struct AllQ4 {
+    Fmt f[kMaxTasks];
+    AllQ4() {
+        for (Fmt& x : f) x = kFmtQ4;
+    }
+};
+}  // namespace
+
+bool skinny_supported(int M, int K, bool split) { return skinny_supported(kFmtQ4, M, K, split); }
+size_t skinny_workspace_bytes(const GemvArgs* tasks, int count) { return skinny_workspace_bytes(AllQ4().f, tasks, count); }
+hipError_t launch_skinny(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s) {
+    return launch_skinny(AllQ4().f, tasks, count, ws, ws_bytes, s);
 }
 
 }  // namespace q4

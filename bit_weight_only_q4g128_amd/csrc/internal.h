@@ -77,15 +77,19 @@ constexpr size_t kNoAllocScratchBytes = 8u << 20;
 hipError_t noalloc_scratch(hipStream_t s, void** out);
 size_t mm_workspace_bytes(Fmt fmt, const GemvArgs* tasks, int count);
 hipError_t launch_mm(Fmt fmt, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
-// Skinny matrix-core GEMV (gemv_skinny.hip): int4, 5 <= M <= kSkinnyMaxM,
-// K % 128 == 0, up to kMaxTasks GEMVs of one batch size per launch.  A
-// workgroup owns up to 80 rows over a slice of at most 16 groups of K; with a
-// workspace of at least skinny_workspace_bytes() (same layout rules as the
-// tiled kernel's: counters first, left at zero) K may be split over
-// workgroups; without one every task must have K <= 2048
-// (skinny_supported(M, K, false)).  GemvArgs::resid is honoured (added
+// Skinny matrix-core GEMV (gemv_skinny.hip): int4, NVFP4 and BF16 tasks
+// (fmts[i] per task; the overloads without fmts take int4 tasks), 5 <= M <=
+// kSkinnyMaxM, K % 128 == 0, up to kMaxTasks GEMVs of one batch size per
+// launch.  A workgroup owns up to 80 rows over a slice of at most 16 groups
+// of K (BF16: 8); with a workspace of at least skinny_workspace_bytes() (same
+// layout rules as the tiled kernel's: counters first, left at zero) K may be
+// split over workgroups; without one every task must fit one slice
+// (skinny_supported(fmt, M, K, false)).  GemvArgs::resid is honoured (added
 // before the one rounding), GemvArgs::up is not.
 constexpr int kSkinnyMaxM = 48;
+bool skinny_supported(Fmt fmt, int M, int K, bool split);
+size_t skinny_workspace_bytes(const Fmt* fmts, const GemvArgs* tasks, int count);
+hipError_t launch_skinny(const Fmt* fmts, const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);
 bool skinny_supported(int M, int K, bool split);
 size_t skinny_workspace_bytes(const GemvArgs* tasks, int count);
 hipError_t launch_skinny(const GemvArgs* tasks, int count, void* ws, size_t ws_bytes, hipStream_t s);

@@ -58,10 +58,11 @@ extern "C" {
 #define Q4_VARIANT_STREAM 3 /* M <= 4, rows of exactly 1, 2 or 4 KB (int4/NVFP4 K = 2048, 4096, 8192;
                                BF16 K = 512, 1024, 2048): every weight load issued at once, activations
                                and group parameters shared through LDS */
-#define Q4_VARIANT_SKINNY 6 /* int4, 5 <= M <= 48, K % 128 == 0: workgroups of up to 80 rows over a slice of at
-                               most 16 groups of K, each wave loading its own weights and activation fragments
-                               straight into registers (no per-group barriers); split over K when given a
-                               workspace, else K <= 2048; the default for int4 at 5 <= M <= 48 */
+#define Q4_VARIANT_SKINNY 6 /* 5 <= M <= 48, K % 128 == 0: workgroups of up to 80 rows over a slice of at
+                               most 16 groups of 128 columns (BF16: 8), each wave loading its own weights and
+                               activation fragments straight into registers (no per-group barriers); split
+                               over K when given a workspace, else int4/NVFP4 K <= 2048, BF16 K <= 1024; the
+                               default for int4 at 5 <= M <= 48 and for mixed groups there */
 #define Q4_VARIANT_GEMM 5   /* int4 prefill only (q4g128_gemm_variant): workgroup tiles of 128 batch
                                rows x 128 or 256 weight rows over all of K, codes unpacked from LDS
                                per wave, scale and min folded per 128-column group */
@@ -223,14 +224,19 @@ int bf16_workspace_bytes(const bf16_task* tasks, int count, int M, size_t* bytes
  * a streaming shape (rows of 1, 2 or 4 KB: int4/NVFP4 K = 2048, 4096, 8192;
  * BF16 K = 512, 1024, 2048) they run as ONE launch -- the NVFP4 decode step's
  * BF16 v projection beside its NVFP4 q, k, gate, up (one launch per format
- * would otherwise be needed).  Above M = 4, with a workspace of at least
- * q4gemv_mixed_workspace_bytes, NVFP4 and BF16 tasks that all take the tiled
- * matrix-core kernel also run as one launch.  Otherwise the tasks run as one
- * grouped launch per format, in task order of first appearance, on the same
- * stream (sharing the workspace).
- * Results equal those of the single-format calls bit for bit.  Each task
- * obeys its format's single-call rules; no task's y may overlap any task's
- * inputs or another y.
+ * would otherwise be needed).  At 5 <= M <= 48 with K % 128 == 0 for every
+ * task they run as one launch of the skinny matrix-core kernel (given a
+ * workspace of at least q4gemv_mixed_workspace_bytes where a task's K needs
+ * more than one slice: int4/NVFP4 K > 2048, BF16 K > 1024).  Above that, with
+ * such a workspace, NVFP4 and BF16 tasks that all take the tiled matrix-core
+ * kernel also run as one launch.  Otherwise the tasks run as one grouped
+ * launch per format, in task order of first appearance, on the same stream
+ * (sharing the workspace).
+ * Streaming and per-format results equal those of the single-format calls bit
+ * for bit; the one-launch matrix-core forms follow the group's plan (its K
+ * slices), within the GEMV tolerance of the single calls.  Each task obeys its
+ * format's single-call rules; no task's y may overlap any task's inputs or
+ * another y.
  */
 typedef struct q4gemv_mixed_task {
     int format;              /* Q4_FMT_Q4G128, Q4_FMT_NVFP4G16 or Q4_FMT_BF16 */

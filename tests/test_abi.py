@@ -107,7 +107,10 @@ def test_variant_names():
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 8192) == "tiled"     # no workspace: K > 16 groups
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_TILED, 48, 2048, 2048) == "tiled"
     assert q4.variant_name(q4.FMT_Q4G128, 6, 4, 2048, 2048) == "invalid"                   # skinny: M >= 5
-    assert q4.variant_name(q4.FMT_NVFP4G16, 6, 48, 2048, 2048) == "invalid"                # skinny: int4 only
+    assert q4.variant_name(q4.FMT_NVFP4G16, 6, 48, 2048, 2048) == "skinny"                 # skinny: every format
+    assert q4.variant_name(q4.FMT_BF16, 6, 48, 2048, 1024) == "skinny"
+    assert q4.variant_name(q4.FMT_BF16, 6, 48, 2048, 2048) == "invalid"                    # BF16 slices: 8 groups, no workspace
+    assert q4.variant_name(q4.FMT_NVFP4G16, 6, 48, 2048, 2080) == "invalid"                # K % 128
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 16384) == "mfma"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_MFMA, 1, 2048, 2048) == "mfma"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_DOT2, 3, 16385, 2048) == "dot2"

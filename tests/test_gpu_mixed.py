@@ -1,10 +1,9 @@
 """GPU parity of mixed-format grouped GEMVs (q4gemv_grouped_mixed).
 
 At M <= 4 one streaming launch carries int4, NVFP4 and BF16 tasks: each
-output must equal the single-format streaming call bit for bit.  At larger M
-a group with int4 runs one grouped launch per format: bit for bit equal to
-the single-format grouped calls with the same workspace; NVFP4 and BF16 on
-the tiled kernel run as one launch, checked against the oracle.
+output must equal the single-format streaming call bit for bit.  At 5 <= M <=
+48 one skinny launch carries them, and NVFP4 with BF16 above that one tiled
+launch: checked against the oracle.
 """
 import numpy as np
 import pytest
@@ -57,27 +56,40 @@ def test_mixed_one_launch_equals_single_format_calls(q4, M):
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), (M, t[0])
 
 
-@pytest.mark.parametrize("M", [5, 48])
-def test_mixed_per_format_launches_equal_grouped_calls(q4, M):
-    items, _ = tasks_for(M)
+def _check_tasks(outs, src, tag):
+    xb1, xbq, xb2 = synth.bits16(src["x1"]), synth.bits16(src["xq"]), synth.bits16(src["x2"])
+    n1, n2, q, b = src["n1"], src["n2"], src["q"], src["b"]
+    w_n1 = oracle.nvfp4g16_dequant_f32(n1[0].numpy(), n1[1].numpy(), n1[2])
+    w_b = oracle.bf16_dequant_f32(synth.bits16(b))
+    w_q = oracle.q4g128_dequant_f32(q[0].numpy(), synth.bits16(q[1]), synth.bits16(q[2]))
+    w_n2 = oracle.nvfp4g16_dequant_f32(n2[0].numpy(), n2[1].numpy(), n2[2])
+    for y, w, xb, name in ((outs[0], w_n1, xb1, "nvfp4"), (outs[1], w_b, xb1, "bf16"), (outs[2], w_q, xbq, "int4"),
+                           (outs[3], w_n2, xb2, "nvfp4 second")):
+        check_gemv(y, oracle.gemv_f64(xb, w), w, xb, f"{tag} {name}")
+
+
+@pytest.mark.parametrize("M", [5, 16, 48])
+def test_mixed_one_skinny_launch(q4, M):
+    """At 5 <= M <= 48 int4, NVFP4 and BF16 tasks run as one skinny launch:
+    every output against the oracle, equal to itself on a second run on the
+    same workspace (whose counters are left at zero)."""
+    items, src = tasks_for(M)
     n = q4.mixed_workspace_bytes(items)
     ws = torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
     outs = q4.gemv_grouped_mixed(items, workspace=ws)
-    # the same per-format groups through the single-format grouped calls
-    nv = [t for t in items if t[0] == "nvfp4g16"]
-    ref_nv = q4.nvfp4g16_gemv_grouped([(t[1], t[2], t[3], t[4], None) for t in nv], workspace=ws)
-    ref_bf = q4.bf16_gemv_grouped([(items[1][1], items[1][2], None)], workspace=ws)
-    ref_q = q4.q4g128_gemv_grouped([(items[2][1], *items[2][2:5], None)], workspace=ws)
-    for y, r in zip([outs[0], outs[3], outs[1], outs[2]], ref_nv + ref_bf + ref_q):
-        assert torch.equal(y.view(torch.int16), r.view(torch.int16)), M
+    again = q4.gemv_grouped_mixed(items, workspace=ws)
+    for y, z in zip(outs, again):
+        assert torch.equal(y.view(torch.int16), z.view(torch.int16)), M
+    assert int(ws[:64 * 1024].count_nonzero()) == 0
+    _check_tasks(outs, src, f"mixed skinny M={M}")
 
 
 @pytest.mark.parametrize("M", [5, 48, 64])
-def test_mixed_tiled_one_launch_nvfp4_bf16(q4, M):
-    """NVFP4 and BF16 tasks on the tiled kernel run as one launch: each output
-    equal to the single-format grouped call with the same split plan (the plan
-    of the whole group), checked against the oracle, and equal to itself on a
-    second run (the workspace counters are left at zero)."""
+def test_mixed_one_launch_nvfp4_bf16(q4, M):
+    """NVFP4 and BF16 tasks run as one launch (the skinny kernel at M <= 48,
+    the tiled kernel above): each output checked against the oracle, and
+    equal to itself on a second run (the workspace counters are left at
+    zero)."""
     n1 = synth.nvfp4_matrix(2048, 2048, ("mxt-nv",))
     b = synth.bf16_matrix(512, 2048, ("mxt-bf",))
     bd = synth.bf16_matrix(2048, 8192, ("mxt-bfd",))
@@ -100,13 +112,4 @@ def test_mixed_tiled_one_launch_nvfp4_bf16(q4, M):
 
 def test_mixed_against_oracle(q4):
     items, src = tasks_for(1)
-    outs = q4.gemv_grouped_mixed(items)
-    xb1, xbq, xb2 = synth.bits16(src["x1"]), synth.bits16(src["xq"]), synth.bits16(src["x2"])
-    n1, n2, q, b = src["n1"], src["n2"], src["q"], src["b"]
-    w_n1 = oracle.nvfp4g16_dequant_f32(n1[0].numpy(), n1[1].numpy(), n1[2])
-    w_b = oracle.bf16_dequant_f32(synth.bits16(b))
-    w_q = oracle.q4g128_dequant_f32(q[0].numpy(), synth.bits16(q[1]), synth.bits16(q[2]))
-    w_n2 = oracle.nvfp4g16_dequant_f32(n2[0].numpy(), n2[1].numpy(), n2[2])
-    for y, w, xb, name in ((outs[0], w_n1, xb1, "nvfp4"), (outs[1], w_b, xb1, "bf16"), (outs[2], w_q, xbq, "int4"),
-                           (outs[3], w_n2, xb2, "nvfp4 K=8192")):
-        check_gemv(y, oracle.gemv_f64(xb, w), w, xb, f"mixed {name}")
+    _check_tasks(q4.gemv_grouped_mixed(items), src, "mixed stream")

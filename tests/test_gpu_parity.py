@@ -715,6 +715,56 @@ def test_q4_skinny_split_k_onehot_and_random(q4, K, M):
             check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"skinny split K={K} M={M}")
 
 
+# the skinny kernel on NVFP4 and BF16 weights (forced, and through the
+# grouped calls with a workspace): slices of 16 NVFP4 groups or 8 BF16 groups
+# of 128 columns, a ragged last slice (K = 1152: 9 groups), a slice of fewer
+# groups than waves (K = 640) and below one group's worth of waves (K = 128),
+# N ragged against every row block; one-hot bitwise (the e2m1 x e4m3 weights
+# are exact in BF16 and G is applied once), random within tolerance, repeats
+# bitwise on the reused workspace, which is left with its counters at zero
+@pytest.mark.parametrize("fmt", ["nv", "bf"])
+@pytest.mark.parametrize("K", [128, 640, 1152, 2048, 8192])
+@pytest.mark.parametrize("M", [5, 17, 48])
+def test_nvfp4_bf16_skinny_onehot_and_random(q4, fmt, K, M):
+    N = 300
+    mats, w32s = (_nv_mats if fmt == "nv" else _bf_mats)([(N, K)], "sk" + fmt)
+    m, w32 = mats[0], w32s[0]
+    grouped = q4.nvfp4g16_gemv_grouped if fmt == "nv" else q4.bf16_gemv_grouped
+    wsbytes = q4.nvfp4g16_workspace_bytes if fmt == "nv" else q4.bf16_workspace_bytes
+    ks = _onehot_ks(K, M, 870 + M)
+    for kind in ("onehot", "random"):
+        x = gpu(onehot_x(K, ks)) if kind == "onehot" else gpu(synth.x_bf16(M, K, ("sk-x", fmt, K, M)))
+        items = [(x, gpu(m[0]), gpu(m[1]), m[2], None)] if fmt == "nv" else [(x, gpu(m), None)]
+        ws = torch.zeros(max(wsbytes(items), 256), dtype=torch.uint8, device="cuda")
+        (y,) = grouped(items, variant=6, workspace=ws)
+        (y2,) = grouped(items, variant=6, workspace=ws)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "repeat on the reused workspace"
+        assert int(ws[:64 * 1024].count_nonzero()) == 0
+        if kind == "onehot":
+            exp = torch.from_numpy(rn_bf16_bits(w32[:, ks].T).view(np.int16)).view(torch.bfloat16).float().numpy()
+            got = y.cpu().float().numpy()
+            assert np.array_equal(got, exp), (fmt, K, M, np.argwhere(got != exp)[:4])
+        else:
+            xb = x_bits(x.cpu())
+            check_gemv(y, oracle.gemv_f64(xb, w32), w32, xb, f"{fmt} skinny K={K} M={M}")
+
+
+@pytest.mark.parametrize("fmt", ["nv", "bf"])
+@pytest.mark.parametrize("N", [16385, 4001])
+def test_nvfp4_bf16_skinny_row_blocks_unsplit(q4, fmt, N):
+    # one slice per row block (no workspace): tall matrices whose row count is
+    # ragged against the planner's blocks
+    K, M = 1024, 48
+    mats, w32s = (_nv_mats if fmt == "nv" else _bf_mats)([(N, K)], "skr" + fmt)
+    m, w32 = mats[0], w32s[0]
+    x = synth.x_bf16(M, K, ("skr-x", fmt, N))
+    if fmt == "nv":
+        y = q4.nvfp4g16_gemv(gpu(x), gpu(m[0]), gpu(m[1]), m[2], variant=6)
+    else:
+        y = q4.bf16_gemv(gpu(x), gpu(m), variant=6)
+    check_gemv(y, oracle.gemv_f64(x_bits(x), w32), w32, x_bits(x), f"{fmt} skinny unsplit N={N}")
+
+
 def test_q4_skinny_misaligned_params_and_output(q4):
     """Group parameters only 2-byte aligned (element loads instead of 16-byte
     pieces) and an output that is only 2-byte aligned (element stores)."""
