@@ -62,7 +62,7 @@ int pick(Fmt fmt, int variant, int M, int N, int K, bool split = false) {
     if (variant == Q4_VARIANT_SKINNY) return q4::skinny_supported(fmt, M, K, split) ? Q4_VARIANT_SKINNY : -1;
     if (M <= 4 && q4::stream_supported(fmt, M, K)) return Q4_VARIANT_STREAM;
     if (M <= 4 && q4::dot2_supported(fmt, K)) return Q4_VARIANT_DOT2;
-    if (fmt == q4::kFmtQ4 && q4::skinny_supported(M, K, split)) return Q4_VARIANT_SKINNY;
+    if (q4::skinny_supported(fmt, M, K, split)) return Q4_VARIANT_SKINNY;
     if (q4::mm_supported(fmt, M, K, split) && (fmt == q4::kFmtQ4 || split || N >= kTiledRowsAlone)) return Q4_VARIANT_TILED;
     return Q4_VARIANT_MFMA;
 }
@@ -494,7 +494,7 @@ int nvfp4g16_workspace_bytes(const nvfp4g16_task* tasks, int count, int M, size_
     int chosen = 0;
     int rc = plan_nv(tasks, count, M, Q4_VARIANT_AUTO, true, a, &chosen);
     if (rc) return rc;
-    *bytes = chosen == Q4_VARIANT_TILED ? q4::mm_workspace_bytes(q4::kFmtNvfp4, a, count) : 0;
+    *bytes = grouped_ws_bytes(q4::kFmtNvfp4, chosen, a, count);
     return Q4_OK;
 }
 
@@ -527,7 +527,7 @@ int bf16_workspace_bytes(const bf16_task* tasks, int count, int M, size_t* bytes
     int chosen = 0;
     int rc = plan_bf(tasks, count, M, Q4_VARIANT_AUTO, true, a, &chosen);
     if (rc) return rc;
-    *bytes = chosen == Q4_VARIANT_TILED ? q4::mm_workspace_bytes(q4::kFmtBf16, a, count) : 0;
+    *bytes = grouped_ws_bytes(q4::kFmtBf16, chosen, a, count);
     return Q4_OK;
 }
 

@@ -114,11 +114,14 @@ def test_variant_names():
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_AUTO, 48, 2048, 16384) == "mfma"
     assert q4.variant_name(q4.FMT_Q4G128, q4.VARIANT_MFMA, 1, 2048, 2048) == "mfma"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_DOT2, 3, 16385, 2048) == "dot2"
-    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2048) == "mfma"    # no workspace: rows alone too few
-    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 16384, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2048) == "skinny"   # one slice of 16 groups
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 4096) == "mfma"    # no workspace: rows alone too few
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 16384, 2048) == "skinny"
+    assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 16384, 4096) == "tiled"   # no workspace: K > 16 groups
     assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_TILED, 48, 8192, 2048) == "tiled"
     assert q4.variant_name(q4.FMT_NVFP4G16, q4.VARIANT_AUTO, 48, 8192, 2080) == "mfma"   # K % 128 != 0
-    assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 48, 16385, 2048) == "tiled"
+    assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 48, 16385, 2048) == "tiled"      # no workspace: K > 8 groups
+    assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 48, 16385, 1024) == "skinny"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_AUTO, 48, 16385, 2056) == "mfma"
     assert q4.variant_name(q4.FMT_BF16, q4.VARIANT_TILED, 48, 16385, 2056) == "invalid"
     assert q4.variant_name(7, 0, 1, 1, 128) == "invalid"
@@ -209,7 +212,10 @@ def test_grouped_nvfp4_bf16_validation():
         arr = (T * 2)(mk(0), mk(1))
         assert fnb(arr, 2, 48, None) == EPTR
         assert fnb(arr, 2, 1, ctypes.byref(nb)) == OK and nb.value == 0     # M = 1 never splits
-        assert fnb(arr, 2, 48, ctypes.byref(nb)) == OK and nb.value > 0     # 64 row blocks: K is split
+        assert fnb(arr, 2, 48, ctypes.byref(nb)) == OK
+        # the skinny kernel: NVFP4 K = 2048 is one slice of 16 groups; BF16
+        # slices hold 8 groups, so its K = 2048 is split
+        assert (nb.value > 0) == (T is BT)
 
 
 def test_fused_validation():
