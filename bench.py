@@ -189,8 +189,8 @@ class Nvfp4Workload:
     as the VoxCPM2-NVFP4 card quantizes them; then the same BF16 head.  plain:
     one launch per projection; grouped: per layer the NVFP4 q, k, gate, up with
     the BF16 v in one mixed-format call and the NVFP4 o with the BF16 down in
-    another (one launch each: the streaming kernel at M <= 4, the tiled
-    matrix-core kernel above), then the head."""
+    another (one launch each: the streaming kernel at M <= 4, the skinny
+    matrix-core kernel at 5 <= M <= 48), then the head."""
 
     def __init__(self, q4, synth, torch, int4_wl):
         self.q4, self.torch = q4, torch
@@ -612,6 +612,20 @@ def nvfp4_launches_in_graph(torch, nv, M, steps, warmup):
     return ms / len(calls), nbytes / len(calls)
 
 
+def nvfp4_grouped_launches_in_graph(torch, nv, M, steps, warmup):
+    """The grouped NVFP4 step's 72 layer launches (per layer the NVFP4 q, k,
+    gate, up with the BF16 v, and the NVFP4 o with the BF16 down; the head
+    left out), captured into one graph and replayed: milliseconds per launch
+    and the average algorithmic bytes per launch (weights + activations read
+    + outputs written)."""
+    xs, ys, _, _ = nv.int4.buffers(M)
+    calls = nv.launches(M, "grouped")[:-1]
+    act = sum(ys[p].numel() * 2 for p in nv.order) + (2048 + 2048 + 8192) * M * 2   # per layer
+    nbytes = (sum(b for _, b, _ in calls) + act * N_LAYERS) / len(calls)
+    ms = graph_ms(torch, lambda: [f() for f, _, _ in calls], steps, warmup)
+    return ms / len(calls), nbytes
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle (plain NumPy: dequantize to fp32, fp64 matrix product) on
     the step's own weights, on this host's cores.  Dequantization and the
@@ -706,9 +720,12 @@ def cpu_baseline(wl, budget_s=12.0):
 KERNELS = {
     1: ("gemv_stream_kernel<FmtQ4, 1, false>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
         os.path.join(ROOT, "profiles", "gemv_stream_q4_M1_grouped_traffic.json")),
-    48: ("skinny_q4_kernel<3, R>", ("common.h", "formats.h", "internal.h", "gemv_skinny.hip"),
+    48: ("skinny_q4_kernel<3, R, 1>", ("common.h", "formats.h", "internal.h", "gemv_skinny.hip"),
          os.path.join(ROOT, "profiles", "skinny_q4_M48_grouped_traffic.json")),
 }
+# the NVFP4 step's grouped launches at M = 48 (NVFP4 with BF16 v / down)
+NVFP4_KERNEL_M48 = ("skinny_q4_kernel<3, R, 6>", ("common.h", "formats.h", "internal.h", "gemv_skinny.hip"),
+                    os.path.join(ROOT, "profiles", "skinny_nvfp4_bf16_M48_grouped_traffic.json"))
 
 
 def _code_only(src):
@@ -748,9 +765,11 @@ def measured_traffic(M):
     return _traffic(KERNELS[M][2], KERNELS[M][1])
 
 
-def measured_traffic_nvfp4():
-    """The same for the NVFP4 streaming kernel's per-projection launches."""
-    return _traffic(NVFP4_KERNEL[2], NVFP4_KERNEL[1])
+def measured_traffic_nvfp4(M=1):
+    """The same for the NVFP4 step: the streaming kernel's per-projection
+    launches at M = 1, the grouped mixed-format skinny launches at M = 48."""
+    k = NVFP4_KERNEL if M == 1 else NVFP4_KERNEL_M48
+    return _traffic(k[2], k[1])
 
 
 def _traffic(path, sources):
@@ -766,11 +785,14 @@ def _traffic(path, sources):
 
 def counters_pass(q4, synth, torch, head_rows, M, nvfp4=False):
     """Workload for hardware-counter runs (no timing): the grouped step at M
-    (int4, or with nvfp4 the per-projection NVFP4 step) three times, eagerly,
-    then a 256 MiB device-to-device copy whose byte count is known (the
-    reference that scales FETCH_SIZE / WRITE_SIZE)."""
+    (int4, or with nvfp4 the NVFP4 step: per projection at M = 1, grouped at
+    M = 48) three times, eagerly, then a 256 MiB device-to-device copy whose
+    byte count is known (the reference that scales FETCH_SIZE / WRITE_SIZE)."""
     wl = Workload(q4, synth, torch, head_rows)
-    calls = Nvfp4Workload(q4, synth, torch, wl).launches(M, "plain") if nvfp4 else wl.launches(M, "grouped")
+    if nvfp4:
+        calls = Nvfp4Workload(q4, synth, torch, wl).launches(M, "plain" if M == 1 else "grouped")
+    else:
+        calls = wl.launches(M, "grouped")
     for _ in range(3):
         for f, _, _ in calls:
             f()
@@ -1002,6 +1024,22 @@ def main():
                                     "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                                     "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic_nvfp4(),
                                     "avg_launch_us": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes)}
+        kern = {1: "gemv_stream_mixed_kernel<1> (stream, NVFP4 and BF16 tasks)",
+                48: "skinny_q4_kernel<3, R, 6> (skinny, NVFP4 and BF16 tasks)"}
+        for M in (1, 48):
+            if f"NVFP4_M{M}_grouped" not in modes:
+                continue
+            kms, kbytes = nvfp4_grouped_launches_in_graph(torch, nv, M, args.steps, args.warmup)
+            achieved = kbytes / (kms * 1e-3) / 1e9
+            log(f"bench: NVFP4 step launches at M={M} (NVFP4 with BF16 v / down) inside the replayed step graph: "
+                f"{kms * 1e3:.2f} us, {kbytes / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
+            out[f"roofline_nvfp4_M{M}_grouped"] = {
+                "bound": "hbm", "kernel": f"{kern[M]}, M={M}: the 72 grouped mixed-format launches of the step",
+                "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                "traffic": measured_traffic_nvfp4(48) if M == 48 else None, "avg_launch_us": round(kms * 1e3, 3),
+                "alg_bytes_per_launch": round(kbytes),
+                "timing": "72 launches captured in one graph exactly as in the step (head left out), replayed; per-launch "
+                          "period including the dispatch gap"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
