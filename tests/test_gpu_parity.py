@@ -765,6 +765,22 @@ def test_nvfp4_bf16_skinny_row_blocks_unsplit(q4, fmt, N):
     check_gemv(y, oracle.gemv_f64(x_bits(x), w32), w32, x_bits(x), f"{fmt} skinny unsplit N={N}")
 
 
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_nvfp4_skinny_scales_any_alignment(q4, shift):
+    """The e4m3 scale array has no alignment rule: the skinny kernel reads a
+    row's group scales as 4-byte pieces, which must come out right from any
+    byte address (the array placed 1, 2, 3 bytes into a larger buffer)."""
+    N, K, M = 300, 2048, 48
+    qw, s8, G = synth.nvfp4_matrix(N, K, ("nv-mis",))
+    w32 = oracle.nvfp4g16_dequant_f32(qw.numpy(), s8.numpy(), G)
+    buf = torch.zeros(N * (K // 16) + 8, dtype=torch.uint8, device="cuda")
+    s8v = buf[shift:shift + N * (K // 16)].view(N, K // 16)
+    s8v.copy_(gpu(s8))
+    x = synth.x_bf16(M, K, ("nv-mis-x", shift))
+    y = q4.nvfp4g16_gemv(gpu(x), gpu(qw), s8v, G, variant=6)
+    check_gemv(y, oracle.gemv_f64(x_bits(x), w32), w32, x_bits(x), f"nvfp4 skinny scales +{shift}")
+
+
 def test_q4_skinny_misaligned_params_and_output(q4):
     """Group parameters only 2-byte aligned (element loads instead of 16-byte
     pieces) and an output that is only 2-byte aligned (element stores)."""
