@@ -15,7 +15,7 @@
 // round's activations (MT x 16 batch rows x 256 bytes) -- these straight into
 // LDS with buffer_load ... lds, into regions of their own, so no barrier is
 // involved -- and the weights of both its rounds, straight into registers
-// (at MT = 3 the weights once the first part has landed: see there).
+// (from MT = 2 on, the weights once the first part has landed: see there).
 // The workgroup's vector-memory path delivers cache lines at a bounded rate,
 // so every load reads whole 128-byte lines: four activation rows per
 // instruction, and for the weights eight rows x the wave's two adjacent
@@ -261,11 +261,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
     const uint32_t gb = (uint32_t)(g0 + nr * wave) * (bff ? 256u : 64u);
     // The two waves that share a SIMD issue vector-memory instructions oldest
     // first, so a wave that issued all its loads at once would queue the other
-    // wave's activations behind its own weights; at three batch tiles a wave
-    // first waits for its parameters and activations, and the SIMD's other
-    // wave issues its own meanwhile (at fewer batch tiles the wait costs more
-    // than it saves).
-    if constexpr (MT == 3) {
+    // wave's activations behind its own weights; from two batch tiles on a
+    // wave first waits for its parameters and activations, and the SIMD's
+    // other wave issues its own meanwhile (at one batch tile the wait costs
+    // more than it saves).
+    if constexpr (MT >= 2) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
