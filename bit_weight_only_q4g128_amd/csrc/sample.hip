@@ -10,7 +10,7 @@
 //   3. the keys above T are gathered, then the keys equal to T in index
 //      order (a block-wide prefix count) until there are k;
 //   4. one wave sorts the k entries by (logit descending, index ascending)
-//      with a bitonic network over its lanes;
+//      with a bitonic network over its lanes (lane exchanges in registers);
 //   5. the lanes form e_i = exp(z_i - z_0), z = logit / T, their running
 //      sums (a prefix scan over the lanes) and total S; the token is the
 //      first entry whose running sum exceeds u * S, and p_i = e_i / S.
@@ -25,20 +25,17 @@ constexpr int kThreads = 256;
 
 // Wave 0: the bin b (counting down from bin 255) where the running count
 // first reaches k; writes b and how many of bin b are still wanted.  Lane l
-// holds bins 4l .. 4l + 3; a shuffle suffix sum gives the count above its
-// bins, and the one lane whose bins cross k reports.
+// holds bins 4l .. 4l + 3; the count above its bins is the total less a
+// prefix scan over the lanes (DPP), and the one lane whose bins cross k
+// reports.
 __device__ void find_bin(const unsigned* hist, int k, int lane, int* s_bin, int* s_need) {
     unsigned h[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) h[j] = hist[4 * lane + j];
     const unsigned mine = h[0] + h[1] + h[2] + h[3];
-    unsigned suf = mine;                                  // sum over lanes >= this one
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned o = __shfl_down(suf, off);
-        if (lane + off < 64) suf += o;
-    }
-    unsigned cum = suf - mine;                            // count in the bins above this lane's
+    const unsigned incl = (unsigned)wave_incl_scan_i((int)mine);   // sum over lanes <= this one
+    const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+    unsigned cum = total - incl;                          // count in the bins above this lane's
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
         if (cum < (unsigned)k && cum + h[j] >= (unsigned)k) {
@@ -47,16 +44,6 @@ __device__ void find_bin(const unsigned* hist, int k, int lane, int* s_bin, int*
         }
         cum += h[j];
     }
-}
-
-// inclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ unsigned wave_scan(unsigned v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
-    return v;
 }
 
 __global__ __launch_bounds__(kThreads) void topk_sample_kernel(const uint16_t* __restrict__ logits, int V, float temperature, int k,
@@ -121,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(const uint16_t* _
         }
         n_eq += key == thr ? 1u : 0u;
     }
-    const unsigned incl = wave_scan(n_eq, lane);
+    const unsigned incl = (unsigned)wave_incl_scan_i((int)n_eq);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     unsigned rank = incl - n_eq;                                  // equal keys before this thread's range
@@ -137,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void topk_sample_kernel(const uint16_t* _
 
     // 4-5. sort the k entries (bitonic network over the lanes) and draw, in wave 0
     if (wave == 0)
-        draw_sorted(wave_sort64_desc(lane < k ? list[lane] : 0u, lane), k, temperature, um, lane, token + m,
+        draw_sorted(wave_sort64<true>(lane < k ? list[lane] : 0u, lane), k, temperature, um, lane, token + m,
                       topk_index ? topk_index + (size_t)m * k : nullptr, topk_prob ? topk_prob + (size_t)m * k : nullptr);
 }
 

@@ -75,77 +75,142 @@ __device__ __forceinline__ int wave_take(const uint32_t (&v)[E], uint32_t T, uin
     return __builtin_amdgcn_readlane(incl, 63);
 }
 
-// The 64 lanes' values sorted descending across the lanes (bitonic network).
-__device__ __forceinline__ uint32_t wave_sort64_desc(uint32_t v, int lane) {
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const uint32_t o = __shfl_xor(v, stride);
-            const bool up = ((lane & size) == 0);            // this half of the sequence descends
-            const bool lower = (lane & stride) == 0;
-            const bool keep_max = (up == lower);
-            v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
-        }
+// Compare-exchange partners of a bitonic network over the 64 lanes, with no
+// LDS traffic: the larger and the smaller of the values of lanes l and
+// l ^ S.  S = 1, 2: quad permutes; 4: row shifts with bank masks; 8: a row
+// rotation; 16, 32: the permlane swaps, whose two results hold, at every
+// lane, its own value and its partner's (in either order).
+template <int S>
+__device__ __forceinline__ void lane_pair(uint32_t v, uint32_t& hi, uint32_t& lo) {
+    uint32_t a = v, b;
+    if constexpr (S == 1) {
+        b = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);    // quad_perm [1,0,3,2]
+    } else if constexpr (S == 2) {
+        b = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);    // quad_perm [2,3,0,1]
+    } else if constexpr (S == 4) {
+        const int t = __builtin_amdgcn_update_dpp((int)v, (int)v, 0x104, 0xF, 0x5, false);  // row_shl:4 into lanes 0-3, 8-11
+        b = (uint32_t)__builtin_amdgcn_update_dpp(t, (int)v, 0x114, 0xF, 0xA, false);       // row_shr:4 into lanes 4-7, 12-15
+    } else if constexpr (S == 8) {
+        b = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);   // row_ror:8
+    } else if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        a = r[0];
+        b = r[1];
+    } else {
+        static_assert(S == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        a = r[0];
+        b = r[1];
     }
+    hi = a > b ? a : b;
+    lo = a > b ? b : a;
+}
+
+// One compare-exchange step at distance S: lane l keeps the larger value
+// when keep_max.
+template <int S>
+__device__ __forceinline__ uint32_t cx(uint32_t v, bool keep_max) {
+    uint32_t hi, lo;
+    lane_pair<S>(v, hi, lo);
+    return keep_max ? hi : lo;
+}
+
+// Step (SIZE, S) of the bitonic sort: blocks of SIZE lanes alternate
+// between descending and ascending (the last, SIZE = 64, in the sort's
+// direction), and within one the lower lane of each pair keeps the value
+// that comes first.
+template <bool DESC, int SIZE, int S>
+__device__ __forceinline__ uint32_t sort_step(uint32_t v, int lane) {
+    const bool first_desc = ((lane & SIZE) == 0) == DESC;   // (bit 6 of a lane is 0)
+    return cx<S>(v, first_desc == ((lane & S) == 0));
+}
+
+// The 64 lanes' values sorted across the lanes, descending (DESC) or
+// ascending: the bitonic network, 21 steps.
+template <bool DESC>
+__device__ __forceinline__ uint32_t wave_sort64(uint32_t v, int lane) {
+    v = sort_step<DESC, 2, 1>(v, lane);
+    v = sort_step<DESC, 4, 2>(v, lane);
+    v = sort_step<DESC, 4, 1>(v, lane);
+    v = sort_step<DESC, 8, 4>(v, lane);
+    v = sort_step<DESC, 8, 2>(v, lane);
+    v = sort_step<DESC, 8, 1>(v, lane);
+    v = sort_step<DESC, 16, 8>(v, lane);
+    v = sort_step<DESC, 16, 4>(v, lane);
+    v = sort_step<DESC, 16, 2>(v, lane);
+    v = sort_step<DESC, 16, 1>(v, lane);
+    v = sort_step<DESC, 32, 16>(v, lane);
+    v = sort_step<DESC, 32, 8>(v, lane);
+    v = sort_step<DESC, 32, 4>(v, lane);
+    v = sort_step<DESC, 32, 2>(v, lane);
+    v = sort_step<DESC, 32, 1>(v, lane);
+    v = sort_step<DESC, 64, 32>(v, lane);
+    v = sort_step<DESC, 64, 16>(v, lane);
+    v = sort_step<DESC, 64, 8>(v, lane);
+    v = sort_step<DESC, 64, 4>(v, lane);
+    v = sort_step<DESC, 64, 2>(v, lane);
+    v = sort_step<DESC, 64, 1>(v, lane);
+    return v;
+}
+
+// The top 64 of two lists sorted across the lanes, x descending and y
+// ascending, sorted: max(x_l, y_l) holds them as a bitonic sequence, which
+// a bitonic merge (6 steps) sorts.
+template <bool DESC>
+__device__ __forceinline__ uint32_t merge_top64(uint32_t x, uint32_t y, int lane) {
+    uint32_t v = x > y ? x : y;
+    v = cx<32>(v, ((lane & 32) == 0) == DESC);
+    v = cx<16>(v, ((lane & 16) == 0) == DESC);
+    v = cx<8>(v, ((lane & 8) == 0) == DESC);
+    v = cx<4>(v, ((lane & 4) == 0) == DESC);
+    v = cx<2>(v, ((lane & 2) == 0) == DESC);
+    v = cx<1>(v, ((lane & 1) == 0) == DESC);
     return v;
 }
 
 // The top k (1 <= k <= 64) of a wave's entries (E per lane, distinct where
-// nonzero), sorted descending in lanes 0 .. k-1 (fewer nonzero entries: all
-// of them, then zeros).  The k-th largest lane maximum L is a lower bound of
-// the k-th largest entry (k lanes hold an entry >= L), so the entries >= L --
+// nonzero), sorted across the lanes (descending: in lanes 0 .. k-1;
+// ascending: in lanes 64-k .. 63; fewer nonzero entries: all of them, the
+// other lanes 0).  The k-th largest lane maximum L is a lower bound of the
+// k-th largest entry (k lanes hold an entry >= L), so the entries >= L --
 // at least k, at most k * E, usually few more than k -- are the candidates:
 // up to 64 of them are sorted directly; more take the bit-by-bit threshold
 // first.  scratch: 64 E words of LDS, private to the wave.
-template <int E>
+template <int E, bool DESC>
 __device__ uint32_t wave_topk_sorted(const uint32_t (&v)[E], int k, uint32_t* scratch, int lane) {
     uint32_t mx = v[0];
 #pragma unroll
     for (int j = 1; j < E; ++j) mx = v[j] > mx ? v[j] : mx;
-    const uint32_t L = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort64_desc(mx, lane), k - 1);
-    const int n = wave_take<E>(v, L, scratch);
+    const uint32_t L = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort64<true>(mx, lane), k - 1);
+    int n = wave_take<E>(v, L, scratch);
     __builtin_amdgcn_wave_barrier();
-    if (n <= 64) return wave_sort64_desc(lane < n ? scratch[lane] : 0u, lane);
-    uint32_t w[E];
+    if (n > 64) {
+        uint32_t w[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) w[j] = lane + 64 * j < n ? scratch[lane + 64 * j] : 0u;
-    __builtin_amdgcn_wave_barrier();
-    const uint32_t T = wave_kth<E>(w, k);
-    const int m = wave_take<E>(w, T, scratch);
-    __builtin_amdgcn_wave_barrier();
-    return wave_sort64_desc(lane < m ? scratch[lane] : 0u, lane);
-}
-
-// The top 64 of two lists sorted descending across the lanes, sorted:
-// max(x_i, y_63-i) holds them as a bitonic sequence, which a bitonic merge
-// sorts.
-__device__ __forceinline__ uint32_t merge_top64(uint32_t x, uint32_t y, int lane) {
-    const uint32_t yr = __shfl(y, 63 - lane);
-    uint32_t v = x > yr ? x : yr;
-#pragma unroll
-    for (int stride = 32; stride > 0; stride >>= 1) {
-        const uint32_t o = __shfl_xor(v, stride);
-        v = (lane & stride) == 0 ? (v > o ? v : o) : (v < o ? v : o);
+        for (int j = 0; j < E; ++j) w[j] = lane + 64 * j < n ? scratch[lane + 64 * j] : 0u;
+        __builtin_amdgcn_wave_barrier();
+        n = wave_take<E>(w, wave_kth<E>(w, k), scratch);
+        __builtin_amdgcn_wave_barrier();
     }
-    return v;
+    return wave_sort64<DESC>(lane < n ? scratch[lane] : 0u, lane);
 }
 
 // Top k (1 <= k <= 64) of the entries of a 256-thread workgroup (E per
-// thread, distinct where nonzero, at least k nonzero): each wave takes its own
-// top k, sorted; wave 0 merges the four lists.  Returns, in wave 0, the top k
-// sorted descending in lanes 0 .. k-1 (0 elsewhere).  LDS: lists holds
-// 4 x 64 words, scratch 4 x 64 E words.  Every thread must call.
+// thread, distinct where nonzero, at least k nonzero): each wave sorts its
+// own top k (waves 0 and 2 descending, 1 and 3 ascending), and wave 0 merges
+// the four lists.  Returns, in wave 0, the top k sorted descending in lanes
+// 0 .. k-1 (0 elsewhere).  LDS: lists holds 4 x 64 words, scratch 4 x 64 E
+// words.  Every thread must call.
 template <int E>
 __device__ uint32_t wg_topk(const uint32_t (&v)[E], int k, uint32_t* lists, uint32_t* scratch, int wave, int lane) {
-    const uint32_t r = wave_topk_sorted<E>(v, k, scratch + 64 * E * wave, lane);
-    lists[64 * wave + lane] = lane < k ? r : 0u;
+    uint32_t* ws = scratch + 64 * E * wave;
+    lists[64 * wave + lane] = (wave & 1) ? wave_topk_sorted<E, false>(v, k, ws, lane) : wave_topk_sorted<E, true>(v, k, ws, lane);
     __syncthreads();
     uint32_t top = 0u;
     if (wave == 0) {
-        const uint32_t ab = merge_top64(lists[lane], lists[64 + lane], lane);
-        const uint32_t cd = merge_top64(lists[128 + lane], lists[192 + lane], lane);
-        top = merge_top64(ab, cd, lane);
+        const uint32_t ab = merge_top64<true>(lists[lane], lists[64 + lane], lane);
+        const uint32_t cd = merge_top64<false>(lists[128 + lane], lists[192 + lane], lane);
+        top = merge_top64<true>(ab, cd, lane);
         top = lane < k ? top : 0u;
     }
     __syncthreads();
