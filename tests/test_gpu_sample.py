@@ -162,6 +162,50 @@ def test_head_sample_one_launch(q4, M, N, K, k, ties):
         assert np.array_equal(have, want)
 
 
+def _concentrated_head(M, N, K, pattern, seed):
+    """One-hot activations (column m of the head for batch row m), so the logits
+    are the head's columns exactly.  "lanes": the largest logits sit at rows
+    t + 256 j (t < 16, j < 8) -- a few lanes of the selecting workgroup's first
+    wave hold all of them, so the lane-maximum bound leaves more than 64
+    candidates and the bit-by-bit threshold runs; "equal": every logit equal
+    (entries differ only by index)."""
+    w = synth.bf16_matrix(N, K, ("head-conc", N, K, seed), std=0.5)
+    cols = list(range(M))
+    if pattern == "lanes":
+        rows = np.array([t + 256 * j for j in range(8) for t in range(16) if t + 256 * j < N])
+        big = torch.from_numpy(np.random.default_rng(seed).permutation(len(rows)).astype(np.float32) * 0.125 + 40.0)
+        for c in cols:
+            w[torch.from_numpy(rows), c] = big.to(torch.bfloat16)
+    else:
+        w[:, cols] = 1.5
+    x = torch.zeros(M, K, dtype=torch.bfloat16)
+    x[torch.arange(M), torch.tensor(cols)] = 1.0
+    u = np.random.default_rng(seed + 5).uniform(0, 1, M).astype(np.float32)
+    return x, w, u
+
+
+@pytest.mark.parametrize("M,N,pattern", [(1, 2049, "lanes"), (2, 2049, "lanes"), (48, 2049, "lanes"), (1, 16385, "lanes"),
+                                         (3, 16385, "lanes"), (1, 2049, "equal"), (4, 4097, "equal")])
+def test_head_sample_concentrated_candidates(q4, M, N, pattern):
+    """Selections whose candidates crowd into a few lanes, or tie on every
+    logit, in the one-launch and split samplers: equal bitwise to the
+    two-launch path (a radix select) and to the oracle's sampling."""
+    print(f"head sample concentrated: M={M} N={N} {pattern}", flush=True)
+    K, k = 2048, 30
+    x, w, u = _concentrated_head(M, N, K, pattern, M * 7 + N)
+    ws = torch.zeros(max(q4.bf16_head_sample_workspace_bytes(M, N, K, k), 256), dtype=torch.uint8, device="cuda")
+    xg, wg, ug = gpu(x), gpu(w), gpu(torch.from_numpy(u))
+    ref = q4.bf16_head_sample(xg, wg, ug, top_k=k, return_topk=True)
+    got = q4.bf16_head_sample(xg, wg, ug, top_k=k, return_topk=True, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b, name in zip(got, ref, ("token", "topk_index", "topk_prob", "logits")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{name} differs from the two-launch path"
+    check_sample(got[0], got[1], got[2], bits(got[3]), 0.8, k, u.astype(np.float64))
+    if pattern == "lanes":
+        want = np.array(sorted(t + 256 * j for j in range(8) for t in range(16) if t + 256 * j < N))
+        assert set(got[1].cpu().numpy()[0].tolist()) <= set(want.tolist())
+
+
 @pytest.mark.parametrize("M", [1, 48])
 def test_head_sample_one_launch_graph_replay(q4, M):
     """The workspace head sampling (one launch at M = 1, the split sampler for
