@@ -740,6 +740,9 @@ def _code_only(src):
 # the NVFP4 streaming kernel (M = 1, per-projection launches)
 NVFP4_KERNEL = ("gemv_stream_kernel<FmtNvfp4, 1, false>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
                 os.path.join(ROOT, "profiles", "gemv_stream_nvfp4_M1_traffic.json"))
+# the NVFP4 step's grouped launches at M = 1 (one mixed-format streaming launch per stage)
+NVFP4_KERNEL_M1_GROUPED = ("gemv_stream_mixed_kernel<1>", ("common.h", "formats.h", "internal.h", "gemv_stream.hip"),
+                           os.path.join(ROOT, "profiles", "gemv_stream_mixed_nvfp4_M1_grouped_traffic.json"))
 
 
 def csrc_digest(M):
@@ -765,10 +768,11 @@ def measured_traffic(M):
     return _traffic(KERNELS[M][2], KERNELS[M][1])
 
 
-def measured_traffic_nvfp4(M=1):
+def measured_traffic_nvfp4(M=1, grouped=False):
     """The same for the NVFP4 step: the streaming kernel's per-projection
-    launches at M = 1, the grouped mixed-format skinny launches at M = 48."""
-    k = NVFP4_KERNEL if M == 1 else NVFP4_KERNEL_M48
+    launches at M = 1 (grouped: the mixed-format streaming launches of the
+    grouped step), the grouped mixed-format skinny launches at M = 48."""
+    k = NVFP4_KERNEL_M48 if M != 1 else (NVFP4_KERNEL_M1_GROUPED if grouped else NVFP4_KERNEL)
     return _traffic(k[2], k[1])
 
 
@@ -783,14 +787,15 @@ def _traffic(path, sources):
     return rec.get("traffic_bytes_per_launch")
 
 
-def counters_pass(q4, synth, torch, head_rows, M, nvfp4=False):
+def counters_pass(q4, synth, torch, head_rows, M, nvfp4=False, grouped=False):
     """Workload for hardware-counter runs (no timing): the grouped step at M
-    (int4, or with nvfp4 the NVFP4 step: per projection at M = 1, grouped at
-    M = 48) three times, eagerly, then a 256 MiB device-to-device copy whose
-    byte count is known (the reference that scales FETCH_SIZE / WRITE_SIZE)."""
+    (int4, or with nvfp4 the NVFP4 step: per projection at M = 1 unless
+    grouped, grouped at M = 48) three times, eagerly, then a 256 MiB
+    device-to-device copy whose byte count is known (the reference that scales
+    FETCH_SIZE / WRITE_SIZE)."""
     wl = Workload(q4, synth, torch, head_rows)
     if nvfp4:
-        calls = Nvfp4Workload(q4, synth, torch, wl).launches(M, "plain" if M == 1 else "grouped")
+        calls = Nvfp4Workload(q4, synth, torch, wl).launches(M, "plain" if M == 1 and not grouped else "grouped")
     else:
         calls = wl.launches(M, "grouped")
     for _ in range(3):
@@ -803,8 +808,9 @@ def counters_pass(q4, synth, torch, head_rows, M, nvfp4=False):
     torch.cuda.synchronize()
     b.copy_(a)
     torch.cuda.synchronize()
-    log(f"bench: counters pass at M={M}{' NVFP4' if nvfp4 else ''} done ({len(calls)} launches per step, csrc digest "
-        f"{csrc_digest_of(NVFP4_KERNEL[1]) if nvfp4 else csrc_digest(M)})")
+    kern = (NVFP4_KERNEL_M48 if M != 1 else NVFP4_KERNEL_M1_GROUPED if grouped else NVFP4_KERNEL) if nvfp4 else KERNELS[M]
+    log(f"bench: counters pass at M={M}{' NVFP4' if nvfp4 else ''}{' grouped' if nvfp4 and grouped else ''} done "
+        f"({len(calls)} launches per step, csrc digest {csrc_digest_of(kern[1])})")
 
 
 def counters_prefill(q4, synth, torch):
@@ -852,6 +858,8 @@ def main():
     ap.add_argument("--counters", action="store_true", help="run the fixed workload for rocprofv3 --pmc passes; no timing")
     ap.add_argument("--counters-m", type=int, choices=(1, 48), default=1, help="batch size of the --counters workload")
     ap.add_argument("--counters-nvfp4", action="store_true", help="the --counters workload with the NVFP4 step instead")
+    ap.add_argument("--counters-grouped", action="store_true",
+                    help="with --counters-nvfp4 at M=1: the grouped mixed-format launches instead of one per projection")
     ap.add_argument("--counters-prefill", action="store_true",
                     help="run the prefill GEMM (8192 x 2048, M = 4096) five times for rocprofv3 --pmc passes; no timing")
     ap.add_argument("--modes", default="M1_grouped,M1_grouped_slice,M1_fused,M1_plain,M48_grouped,M48_grouped_slice,M48_fused,"
@@ -874,7 +882,7 @@ def main():
         counters_prefill(q4, synth, torch)
         return
     if args.counters:
-        counters_pass(q4, synth, torch, head_rows, args.counters_m, args.counters_nvfp4)
+        counters_pass(q4, synth, torch, head_rows, args.counters_m, args.counters_nvfp4, args.counters_grouped)
         return
     wl = Workload(q4, synth, torch, head_rows)
     other_head = synth.HEAD_SLICE[0] if head_rows == synth.HEAD_FULL[0] else synth.HEAD_FULL[0]
@@ -1036,7 +1044,7 @@ def main():
             out[f"roofline_nvfp4_M{M}_grouped"] = {
                 "bound": "hbm", "kernel": f"{kern[M]}, M={M}: the 72 grouped mixed-format launches of the step",
                 "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                "traffic": measured_traffic_nvfp4(48) if M == 48 else None, "avg_launch_us": round(kms * 1e3, 3),
+                "traffic": measured_traffic_nvfp4(M, grouped=True), "avg_launch_us": round(kms * 1e3, 3),
                 "alg_bytes_per_launch": round(kbytes),
                 "timing": "72 launches captured in one graph exactly as in the step (head left out), replayed; per-launch "
                           "period including the dispatch gap"}
