@@ -121,7 +121,7 @@ __device__ __forceinline__ uint32_t cx(uint32_t v, bool keep_max) {
 // that comes first.
 template <bool DESC, int SIZE, int S>
 __device__ __forceinline__ uint32_t sort_step(uint32_t v, int lane) {
-    const bool first_desc = ((lane & SIZE) == 0) == DESC;   // (bit 6 of a lane is 0)
+    const bool first_desc = ((lane & SIZE) == 0) == DESC;   // (SIZE = 64: true for every lane when DESC)
     return cx<S>(v, first_desc == ((lane & S) == 0));
 }
 
@@ -168,14 +168,16 @@ __device__ __forceinline__ uint32_t merge_top64(uint32_t x, uint32_t y, int lane
     return v;
 }
 
-// The top k (1 <= k <= 64) of a wave's entries (E per lane, distinct where
-// nonzero), sorted across the lanes (descending: in lanes 0 .. k-1;
-// ascending: in lanes 64-k .. 63; fewer nonzero entries: all of them, the
-// other lanes 0).  The k-th largest lane maximum L is a lower bound of the
-// k-th largest entry (k lanes hold an entry >= L), so the entries >= L --
-// at least k, at most k * E, usually few more than k -- are the candidates:
-// up to 64 of them are sorted directly; more take the bit-by-bit threshold
-// first.  scratch: 64 E words of LDS, private to the wave.
+// The candidates for the top k (1 <= k <= 64) of a wave's entries (E per
+// lane, distinct where nonzero), sorted across the lanes: at most 64 entries
+// that include the k largest (all nonzero entries when there are fewer),
+// descending from lane 0 or ascending up to lane 63, zeros in the other
+// lanes.  The k-th largest lane maximum L is a lower bound of the k-th
+// largest entry (k lanes hold an entry >= L), so the entries >= L -- at
+// least k, at most k * E, usually few more than k -- are the candidates: up
+// to 64 of them are sorted directly; more are first cut to exactly the k
+// largest by the bit-by-bit threshold.  scratch: 64 E words of LDS, private
+// to the wave.
 template <int E, bool DESC>
 __device__ uint32_t wave_topk_sorted(const uint32_t (&v)[E], int k, uint32_t* scratch, int lane) {
     uint32_t mx = v[0];
@@ -197,8 +199,9 @@ __device__ uint32_t wave_topk_sorted(const uint32_t (&v)[E], int k, uint32_t* sc
 
 // Top k (1 <= k <= 64) of the entries of a 256-thread workgroup (E per
 // thread, distinct where nonzero, at least k nonzero): each wave sorts its
-// own top k (waves 0 and 2 descending, 1 and 3 ascending), and wave 0 merges
-// the four lists.  Returns, in wave 0, the top k sorted descending in lanes
+// own candidates (waves 0 and 2 descending, 1 and 3 ascending), and wave 0
+// merges the four lists (a descending and an ascending list merge in one
+// step, so no list is reversed).  Returns, in wave 0, the top k sorted descending in lanes
 // 0 .. k-1 (0 elsewhere).  LDS: lists holds 4 x 64 words, scratch 4 x 64 E
 // words.  Every thread must call.
 template <int E>
