@@ -105,8 +105,11 @@ struct SkTable {
 //                        [16 R][2][2] dwords, the group's eight e4m3 bytes --
 //                        padded to whole 64-lane loads
 //   [.., + kMin)         the mins of the workgroup's 16 R rows for the slice's
-//                        groups, [16 R][16] dwords (fp16 in the low half),
-//                        padded to whole 64-lane loads of all eight waves
+//                        groups, [16 R][17] dwords (fp16 in the low half; the
+//                        17th word of a row is padding, so that one group's
+//                        mins of 16 consecutive rows sit in 16 distinct
+//                        banks), padded to whole 64-lane loads of all eight
+//                        waves
 //   [.., + kSx)          SX per group of the slice and batch row, fp32 [16][16 MT]
 // FM: the formats a launch carries (bit 0 int4, bit 1 NVFP4, bit 2 BF16);
 // only their code is compiled into an instance
@@ -117,7 +120,8 @@ struct SkLds {
     static constexpr int kArea = kSkWaves * kWave;
     static constexpr int kParArr = (((FM & 2) ? 64 : 32) * R + 63) / 64 * 64;   // dwords per wave, whole 64-lane loads
     static constexpr int kPar = kSkWaves * kParArr * 4;
-    static constexpr int kMinLoads = (16 * R * kSkMaxGroups / 64 + kSkWaves - 1) / kSkWaves;   // per wave
+    static constexpr int kMinPitch = kSkMaxGroups + 1;                                         // dwords per row
+    static constexpr int kMinLoads = ((16 * R * kMinPitch + 63) / 64 + kSkWaves - 1) / kSkWaves;   // per wave
     static constexpr int kMin = kSkWaves * kMinLoads * 64 * 4;
     static constexpr int kSx = kSkMaxGroups * 16 * MT * 4;
     static constexpr int kBytes = kArea + kPar + kMin + kSx;
@@ -218,13 +222,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
         }
     }
     // int4 mins, once per workgroup (they are read only after the waves
-    // meet): element e = 64 (wave + 8 j) + lane is (row e / 16, group e % 16
-    // of the slice); four rows' slices of a whole-K task share one cache line
+    // meet): element e = 64 (wave + 8 j) + lane is (row e / 17, group e % 17
+    // of the slice; group 16 is the padding word, never loaded); four rows'
+    // slices of a whole-K task share one cache line
 #pragma unroll
     for (int j = 0; j < L::kMinLoads; ++j) {
         if (!q4f) break;
         const int e = 64 * (wave + kSkWaves * j) + lane;
-        const int row = e >> 4, gi = e & 15;
+        const int row = e / L::kMinPitch, gi = e - L::kMinPitch * row;
         const bool ok = row < 16 * R && gi < ng;
         const uint32_t off = ok ? ((uint32_t)row * (uint32_t)G + (uint32_t)(g0 + gi)) * 2u : 0xFFFFFFF0u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(mtab + 64 * (wave + kSkWaves * j)), 2, off, 0, 0, 0);
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_q4_kernel(SkTable tt) {
                 const int w2 = gi >> nsh, slot = gi & nsh;
                 av[c] = sxt[gi * 16 * MT + 16 * mt + (lane & 15)];
                 sv[c] = f16_to_f32((uint16_t)par[w2 * L::kParArr + 2 * row + slot]);
-                mv[c] = f16_to_f32((uint16_t)mtab[16 * row + gi]);
+                mv[c] = f16_to_f32((uint16_t)mtab[L::kMinPitch * row + gi]);
             }
             f32x4 v = reinterpret_cast<const f32x4*>(lds)[p * 64 + lane];
 #pragma unroll
